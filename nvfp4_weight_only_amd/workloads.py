@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the NVFP4 weight-only linear.
+
+This module holds the workload shapes and the random-input recipes only.  It
+contains none of the NVFP4 arithmetic: no scale choice, no rounding to E2M1 or
+E4M3, no dequantization.  Both the CPU oracle side (in the tests) and the GPU
+side consume the same BF16 bit patterns produced here, so an input never comes
+from either implementation.
+
+BF16 tensors are returned as ``numpy.uint16`` arrays of raw bit patterns,
+produced by rounding float32 normals to bfloat16 (round to nearest even, as
+torch's CPU cast does).
+
+Shapes and statistics follow the model card of the 27B W4A16 NVFP4 checkpoint
+(page "Qwen3.8-27B-NVFP4 (compressed-tensors)": linear weights NVFP4 with group
+size 16, activations left in BF16, merged gate/up members sharing one tensor
+scale with an amax spread of 3.7x) and the engine's decode/prefill workloads
+(tg128 -> M=1, pp512 -> M=512, pp4096-class long prefill -> M=2048).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+import torch
+
+# Seeds of every synthetic input.
+SEED_W = 0          # weights
+SEED_X = 1          # activations
+SEED_OUTLIER = 2    # which input columns are outliers (decode workload)
+SEED_UP = 3         # the "up" half of the merged gate/up weight
+
+W_STD = 0.02
+X_STD = 1.0
+OUTLIER_FRACTION = 0.01
+OUTLIER_GAIN = 8.0          # power of two: exact in BF16
+GATE_UP_AMAX_RATIO = 3.7    # amax(gate) / amax(up), the spread the model card reports
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round a float32 array to bfloat16 (RNE, torch's CPU cast); return the uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """Widen BF16 bit patterns to float32 values (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(shape: Tuple[int, ...], std: float, seed: int) -> np.ndarray:
+    """Seeded N(0, std^2) samples (PCG64, float32) rounded to BF16 bits."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return bf16_bits_from_f32(a)
+
+
+def outlier_columns(k: int, seed: int = SEED_OUTLIER, fraction: float = OUTLIER_FRACTION) -> np.ndarray:
+    """round(fraction*k) distinct input columns, drawn without replacement, sorted."""
+    n = int(round(fraction * k))
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(k, size=n, replace=False))
+
+
+def weight_plain(n: int, k: int, seed: int = SEED_W, std: float = W_STD) -> np.ndarray:
+    return normal_bf16((n, k), std, seed)
+
+
+def weight_with_outlier_columns(n: int, k: int, seed: int = SEED_W) -> np.ndarray:
+    """~N(0, 0.02^2) weights whose outlier input columns are multiplied by 8 (before BF16 rounding)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((n, k), dtype=np.float32)
+    a *= np.float32(W_STD)
+    cols = outlier_columns(k)
+    a[:, cols] *= np.float32(OUTLIER_GAIN)
+    return bf16_bits_from_f32(a)
+
+
+def weight_gate_up(n_half: int, k: int) -> Tuple[np.ndarray, np.ndarray, float]:
+    """Gate and up halves of a merged gate/up weight.
+
+    Gate ~N(0, 0.02^2) (seed 0).  Up is drawn independently (seed 3) and rescaled
+    in float32, before BF16 rounding, so that amax(gate)/amax(up) is about 3.7.
+    Returns (gate_bits, up_bits, exact post-rounding amax ratio).
+    """
+    gate = weight_plain(n_half, k, SEED_W)
+    amax_gate = float(np.abs(f32_from_bf16_bits(gate)).max())
+    rng = np.random.default_rng(SEED_UP)
+    up = rng.standard_normal((n_half, k), dtype=np.float32)
+    up *= np.float32(amax_gate / GATE_UP_AMAX_RATIO / float(np.abs(up).max()))
+    up_bits = bf16_bits_from_f32(up)
+    amax_up = float(np.abs(f32_from_bf16_bits(up_bits)).max())
+    return gate, up_bits, amax_gate / amax_up
+
+
+def activations(m: int, k: int, seed: int = SEED_X) -> np.ndarray:
+    return normal_bf16((m, k), X_STD, seed)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic linear problem: Y[m, n] = X[m, :] . W_hat[n, :]."""
+    name: str
+    description: str
+    n: int
+    k: int
+    ms: Tuple[int, ...]
+    weight_kind: str            # "plain" | "outliers" | "gate_up"
+
+    def weight(self) -> np.ndarray:
+        """BF16 bits of the (merged) weight, shape [n, k]."""
+        if self.weight_kind == "plain":
+            return weight_plain(self.n, self.k)
+        if self.weight_kind == "outliers":
+            return weight_with_outlier_columns(self.n, self.k)
+        if self.weight_kind == "gate_up":
+            g, u, _ = weight_gate_up(self.n // 2, self.k)
+            return np.concatenate([g, u], axis=0)
+        raise ValueError(self.weight_kind)
+
+    def activations(self, m: Optional[int] = None) -> np.ndarray:
+        return activations(self.ms[0] if m is None else m, self.k)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny", "tiny NVFP4 linear: W 256x512 ~N(0,0.02), X 1x512 ~N(0,1)",
+                 256, 512, (1,), "plain"),
+        Workload("decode", "decode GEMV: M=1, N=5120, K=5120, 1% outlier input columns x8",
+                 5120, 5120, (1,), "outliers"),
+        Workload("gate_up", "merged gate/up GEMV: M=1, N=2x17408, K=5120, amax ratio 3.7, one shared tensor scale",
+                 2 * 17408, 5120, (1,), "gate_up"),
+        Workload("small_m_up", "batched decode: M in {8,32}, N=17408, K=5120",
+                 17408, 5120, (8, 32), "plain"),
+        Workload("small_m_down", "batched decode down projection: M in {8,32}, N=5120, K=17408",
+                 5120, 17408, (8, 32), "plain"),
+        Workload("prefill", "prefill GEMM: M in {512,2048}, N=17408, K=5120",
+                 17408, 5120, (512, 2048), "plain"),
+    ]
+}
+
+
+def workload_names() -> List[str]:
+    return list(WORKLOADS)

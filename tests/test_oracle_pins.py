@@ -1,0 +1,455 @@
+"""Pins for the CPU oracle: checked against the pages, a library, exact rationals and invariants.
+
+None of these tests re-types the oracle's own formula.  Each pin reaches the
+expected value by another route:
+  * the E2M1 magnitudes printed on the pages (tests/golden/e2m1_magnitudes.txt);
+  * torch's float8_e4m3fn (an independent OCP E4M3FN implementation) for the
+    E4M3 table and for round-to-nearest-even onto the E4M3 grid;
+  * exhaustive nearest-point search in exact rational arithmetic (fractions)
+    on tiny inputs;
+  * closed-form facts (block absmax maps to +-6, idempotence, the shared-scale
+    identity of merged linears, amax recovery from the tensor scale).
+The mutation tests at the end plant plausible mistakes in the oracle and
+check that some pin fails.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as O
+from nvfp4_weight_only_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                vals.append(line)
+    return vals
+
+
+def _bits(values):
+    return WL.bf16_bits_from_f32(np.asarray(values, dtype=np.float32))
+
+
+# --------------------------------------------------------------------------
+# Pin functions (also reused by the mutation tests).
+# --------------------------------------------------------------------------
+def pin_e2m1_table():
+    mags = [float(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    assert len(mags) == 8
+    assert list(O.E2M1_TABLE[:8]) == mags
+    assert list(-O.E2M1_TABLE[8:]) == mags
+    assert np.signbit(O.E2M1_TABLE[8]) and not np.signbit(O.E2M1_TABLE[0])
+
+
+def pin_e4m3_table():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(O.E4M3_TABLE), nan_ref)
+    assert np.array_equal(O.E4M3_TABLE[~nan_ref], ref[~nan_ref])
+    assert np.array_equal(np.signbit(O.E4M3_TABLE[~nan_ref]), np.signbit(ref[~nan_ref]))
+
+
+def pin_nibble_layout():
+    # codes (1, 2) -> one byte 0x21 -> decoded [0.5, 1.0] (element 2j in the low nibble)
+    codes = np.array([[1, 2, 0xF, 0x8]], dtype=np.uint8)
+    packed = O.pack_nibbles(codes)
+    assert packed.tolist() == [[0x21, 0x8F]]
+    scales = np.array([[0x38]], dtype=np.uint8)   # E4M3 0x38 = 1.0
+    w = O.decoded_products(np.pad(packed, ((0, 0), (0, 6))), scales)
+    assert w[0, :4].tolist() == [0.5, 1.0, -6.0, -0.0]
+    assert np.signbit(w[0, 3])
+
+
+def _scales_via_torch(w_bits, amax):
+    """E4M3 code of fl32(448*bam/amax) by torch's float32 -> float8_e4m3fn cast (RNE)."""
+    w = np.abs(WL.f32_from_bf16_bits(w_bits).astype(np.float64))
+    n, k = w.shape
+    bam = w.reshape(n, k // 16, 16).max(axis=2)
+    ratio = (np.float32(448.0) * bam.astype(np.float32)) / np.float32(amax)  # 448*bam exact in fp32
+    return torch.from_numpy(ratio.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_scales_match_torch_rounding(w_bits):
+    amax = O.tensor_amax(w_bits)
+    got = O.block_scale_codes(w_bits, amax)
+    ref = _scales_via_torch(w_bits, amax)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} scale codes differ"
+
+
+def _nearest_even(x, grid):
+    """Exhaustive nearest point of ``grid`` to Fraction x, ties to the even index."""
+    best = None
+    for i, g in enumerate(grid):
+        d = abs(x - g)
+        if best is None or d < best[0] or (d == best[0] and i % 2 == 0):
+            best = (d, i)
+    return best[1]
+
+
+E4M3_GRID = [Fraction(v) for v in torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()]
+
+
+def pin_quantize_brute_force(w_bits, amax_override=None):
+    """Scale and element codes equal an exhaustive exact-rational nearest-point search."""
+    mags = [Fraction(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    packed, scales, tscale = O.quantize(w_bits, amax=amax_override)
+    codes = O.unpack_nibbles(packed)
+    w = [[Fraction(float(v)) for v in row] for row in WL.f32_from_bf16_bits(w_bits)]
+    amax = Fraction(O.tensor_amax(w_bits)) if amax_override is None else Fraction(amax_override)
+    assert float(tscale) == float(np.float32(float(amax) / 2688.0)) or amax == 0
+    n, k = len(w), len(w[0])
+    for r in range(n):
+        for b in range(k // 16):
+            blk = w[r][16 * b:16 * b + 16]
+            bam = max(abs(v) for v in blk)
+            exp_s = 0 if amax == 0 else _nearest_even(448 * bam / amax, E4M3_GRID)
+            assert scales[r, b] == exp_s, (r, b, scales[r, b], exp_s)
+            s = E4M3_GRID[exp_s]
+            for j, v in enumerate(blk):
+                mag = 0 if s == 0 else _nearest_even(2688 * abs(v) / (amax * s), mags)
+                sign = 1 if np.signbit(float(v)) or (v == 0 and _neg_zero(w_bits[r, 16 * b + j])) else 0
+                assert codes[r, 16 * b + j] == (sign << 3 | mag), (r, 16 * b + j, codes[r, 16 * b + j], sign, mag)
+
+
+def _neg_zero(bits):
+    return int(bits) == 0x8000
+
+
+def pin_dequant_closed_form(packed, scales, tscale):
+    """w_hat = bf16(f32(E2M1 * E4M3) * tscale), built from the page magnitudes and torch's E4M3."""
+    mags = np.array([float(v) for v in _read_golden("e2m1_magnitudes.txt")], dtype=np.float32)
+    e2m1 = np.concatenate([mags, -mags])
+    e4m3 = torch.from_numpy(np.asarray(scales, dtype=np.uint8).copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    codes = torch.from_numpy(O.unpack_nibbles(packed).astype(np.int64))
+    vals = torch.from_numpy(e2m1)[codes] * e4m3.repeat_interleave(16, dim=1)
+    ref = (vals * torch.tensor(float(tscale), dtype=torch.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.dequant(packed, scales, tscale)
+    assert np.array_equal(got, ref)
+
+
+def pin_linear_brute_force(x_bits, packed, scales, tscale):
+    mags = [Fraction(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    e2m1 = mags + [-m for m in mags]
+    e4m3 = torch.from_numpy(np.asarray(scales, dtype=np.uint8).copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    codes = O.unpack_nibbles(packed)
+    x = WL.f32_from_bf16_bits(x_bits).astype(np.float64)
+    t = Fraction(float(np.float32(tscale)))
+    y_ref, bound = O.linear_ref(x_bits, packed, scales, tscale)
+    m, k = x.shape
+    n = codes.shape[0]
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(x[i, kk]) * e2m1[codes[j, kk]] * Fraction(e4m3[j, kk // 16]) * t for kk in range(k))
+            babs = sum(abs(Fraction(x[i, kk]) * e2m1[codes[j, kk]] * Fraction(e4m3[j, kk // 16]) * t) for kk in range(k))
+            assert abs(Fraction(y_ref[i, j]) - exact) <= Fraction(1, 10 ** 12) * (babs + Fraction(1, 10 ** 30)), (i, j)
+            assert abs(Fraction(bound[i, j]) - babs) <= Fraction(1, 10 ** 12) * (babs + Fraction(1, 10 ** 30)), (i, j)
+
+
+# --------------------------------------------------------------------------
+# Tiny inputs with crafted ties.
+# --------------------------------------------------------------------------
+def tiny_inputs():
+    """Random tiny matrices plus rows that put elements and scales exactly on rounding midpoints."""
+    cases = []
+    for (n, k, seed) in [(2, 16, 10), (3, 32, 11), (4, 64, 12), (1, 48, 13)]:
+        cases.append(WL.normal_bf16((n, k), 0.02, seed))
+    # Ties on E2M1 midpoints: amax = 6 in block 0 gives scale 448 there, so q = 448*|w|*... choose
+    # a block with bam = 6 (scale 448 exactly -> tscale*scale = 1): q = |w| exactly.
+    row = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, -0.0]
+    # Second block: bam = 3 -> 448*3/6 = 224 (an E4M3 value) -> q = 2*|w|.
+    row2 = [3.0, 0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5, 0.0, -0.0, 1e-30, -1e-30, 2.0, 0.1, 0.2, 0.3]
+    cases.append(_bits([row + row2]))
+    # Ties on E4M3 midpoints: amax = 448 and bam = midpoint u gives 448*bam/amax = u exactly.
+    mids = (np.array(E4M3_GRID[:-1], dtype=np.float64) + np.array(E4M3_GRID[1:], dtype=np.float64)) / 2
+    blocks = []
+    for u in mids[::5]:
+        blk = [0.0] * 16
+        blk[3] = u
+        blk[7] = -u / 3
+        blocks.append(blk)
+    blocks.append([448.0] + [0.0] * 15)
+    cases.append(_bits([sum(blocks, [])]))
+    return cases
+
+
+def _ties_present(w_bits):
+    """Count exact E2M1 midpoint ties (sanity: the tie cases really are ties)."""
+    packed, scales, _ = O.quantize(w_bits)
+    amax = O.tensor_amax(w_bits)
+    s = np.repeat(O.E4M3_TABLE[scales.astype(np.int64)], 16, axis=1)
+    w = np.abs(WL.f32_from_bf16_bits(w_bits).astype(np.float64))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = 2688 * w / (amax * s)
+    return int(np.isin(q, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]).sum())
+
+
+# --------------------------------------------------------------------------
+# Tests.
+# --------------------------------------------------------------------------
+def test_e2m1_table_matches_page_magnitudes():
+    pin_e2m1_table()
+
+
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    pin_e4m3_table()
+    assert O.E4M3_TABLE[0x7E] == 448.0 and O.E4M3_TABLE[0x01] == 2.0 ** -9
+
+
+def test_nibble_layout_example():
+    pin_nibble_layout()
+
+
+def test_layout_sizes_follow_pages():
+    g = dict(line.split() for line in _read_golden("nvfp4_layout.txt"))
+    g = {k: int(v) for k, v in g.items()}
+    for wl in WL.WORKLOADS.values():
+        n, k = wl.n, wl.k
+        packed_bytes = n * k * g["element_bits"] // 8
+        scale_bytes = n * k // g["block_elements"] * g["block_scale_bits"] // 8
+        assert packed_bytes == n * k // g["elements_per_byte"]
+        bits_per_weight = (8 * (packed_bytes + scale_bytes) + g["tensor_scale_bits"]) / (n * k)
+        assert abs(bits_per_weight - (4 + 8 / 16 + 32 / (n * k))) < 1e-12
+    w = WL.normal_bf16((5, 48), 0.02, 7)
+    packed, scales, tscale = O.quantize(w)
+    assert packed.shape == (5, 24) and packed.dtype == np.uint8
+    assert scales.shape == (5, 3) and scales.dtype == np.uint8
+    assert isinstance(tscale, np.float32)
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_quantize_brute_force_tiny(idx):
+    w = tiny_inputs()[idx]
+    pin_quantize_brute_force(w)
+
+
+def test_tie_cases_really_tie():
+    cases = tiny_inputs()
+    assert _ties_present(cases[4]) >= 14
+
+
+def test_scales_match_torch_e4m3_rounding_random():
+    for wl_bits in [WL.normal_bf16((64, 512), 0.02, 0), WL.weight_with_outlier_columns(64, 5120)]:
+        pin_scales_match_torch_rounding(wl_bits)
+
+
+def test_scales_match_torch_e4m3_rounding_at_every_midpoint():
+    mids = (np.array(E4M3_GRID[:-1], dtype=np.float64) + np.array(E4M3_GRID[1:], dtype=np.float64)) / 2
+    rows = []
+    for u in mids:
+        blk = [0.0] * 16
+        blk[5] = u
+        rows.append(blk + [448.0] + [0.0] * 15)
+    w = _bits(rows)
+    pin_scales_match_torch_rounding(w)
+    codes = O.block_scale_codes(w, 448.0)[:, 0]
+    assert np.all(codes % 2 == 0)   # every exact midpoint went to the even neighbour
+
+
+def test_amax_recovered_from_tensor_scale_for_every_bf16():
+    """RNE_bf16(fl32(2688 * fl32(a / 2688))) == a for all 32639 positive finite BF16 a."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    a = WL.f32_from_bf16_bits(bits)
+    t = a / np.float32(2688.0)
+    back = (t * np.float32(2688.0)).astype(np.float32)
+    back_bits = WL.bf16_bits_from_f32(back)
+    assert np.array_equal(back_bits, bits)
+    for ai in a[::997]:
+        assert O.tensor_scale(float(ai)) == np.float32(ai) / np.float32(2688.0)
+
+
+@pytest.mark.parametrize("kind", ["plain", "outliers"])
+def test_block_absmax_maps_to_six(kind):
+    w = WL.weight_plain(64, 5120) if kind == "plain" else WL.weight_with_outlier_columns(64, 5120)
+    packed, scales, _ = O.quantize(w)
+    codes = O.unpack_nibbles(packed).reshape(64, -1, 16)
+    a = np.abs(WL.f32_from_bf16_bits(w)).reshape(64, -1, 16)
+    argmax = a.argmax(axis=2)
+    top = np.take_along_axis(codes, argmax[..., None], axis=2)[..., 0] & 7
+    normal = scales >= 0x08
+    assert normal.sum() > 0
+    assert np.all(top[normal] == 7)
+
+
+@pytest.mark.parametrize("kind", ["plain", "outliers"])
+def test_quantize_dequant_idempotent(kind):
+    w = WL.weight_plain(32, 5120) if kind == "plain" else WL.weight_with_outlier_columns(32, 5120)
+    p1, s1, t1 = O.quantize(w)
+    w2 = O.dequant(p1, s1, t1)
+    p2, s2, t2 = O.quantize(w2)
+    assert t2 == t1
+    normal = s1 >= 0x08
+    assert np.array_equal(s2[normal], s1[normal])
+    c1 = O.unpack_nibbles(p1).reshape(32, -1, 16)[normal]
+    c2 = O.unpack_nibbles(p2).reshape(32, -1, 16)[normal]
+    assert np.array_equal(c1, c2)
+
+
+def test_shared_scale_identity_and_wrong_scale_failure():
+    gate, up, ratio = WL.weight_gate_up(48, 512)
+    assert 3.5 < ratio < 3.9
+    merged = np.concatenate([gate, up], axis=0)
+    pm, sm, tm = O.quantize(merged)
+    (pg, sg), (pu, su) = O.quantize_shared([gate, up])[0]
+    _, ts = O.quantize_shared([gate, up])
+    assert ts == tm
+    assert np.array_equal(np.concatenate([pg, pu]), pm)
+    assert np.array_equal(np.concatenate([sg, su]), sm)
+    # The failure mode the model card warns about: U's codes decoded against U's own scale.
+    x = WL.activations(2, 512)
+    y_ref, bound = O.linear_ref(x, pu, su, tm)
+    wrong_t = O.tensor_scale(O.tensor_amax(up))
+    y_wrong, _ = O.linear_ref(x, pu, su, wrong_t)
+    assert O.linear_violations(y_wrong, y_ref, bound).mean() > 0.9
+    # U's own scale is smaller than the shared one by the amax spread.
+    ratio_seen = np.median(np.abs(y_ref) / np.maximum(np.abs(y_wrong), 1e-30))
+    assert abs(ratio_seen - ratio) / ratio < 0.02
+
+
+def test_dequant_closed_form_random_and_edges():
+    for w in [WL.weight_plain(16, 512), WL.weight_with_outlier_columns(16, 512), tiny_inputs()[4], tiny_inputs()[5]]:
+        pin_dequant_closed_form(*O.quantize(w))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 16), (2, 3, 32), (3, 2, 48)])
+def test_linear_brute_force_tiny(shape):
+    m, n, k = shape
+    w = WL.normal_bf16((n, k), 0.02, 20 + k)
+    x = WL.normal_bf16((m, k), 1.0, 30 + k)
+    pin_linear_brute_force(x, *O.quantize(w))
+
+
+def test_linear_unit_scales_is_plain_matvec():
+    """With every block scale 1.0 and tscale 1, the linear is a matvec over the E2M1 values."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(7, 64)).astype(np.uint8)
+    packed = O.pack_nibbles(codes)
+    scales = np.full((7, 4), 0x38, dtype=np.uint8)     # E4M3 0x38 == 1.0
+    x = WL.normal_bf16((3, 64), 1.0, 6)
+    mags = [float(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    vals = torch.tensor(mags + [-v for v in mags], dtype=torch.float64)[torch.from_numpy(codes.astype(np.int64))]
+    xt = torch.from_numpy(WL.f32_from_bf16_bits(x).astype(np.float64))
+    ref = torch.matmul(xt, vals.T).numpy()
+    y, _ = O.linear_ref(x, packed, scales, np.float32(1.0))
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_zero_sign_and_range_edges():
+    # all-zero tensor (with a -0): tscale 0, scales 0, codes keep the sign bit only
+    w = _bits([[0.0] * 15 + [-0.0]])
+    p, s, t = O.quantize(w)
+    assert t == 0 and s.tolist() == [[0]] and O.unpack_nibbles(p)[0].tolist() == [0] * 15 + [8]
+    assert np.array_equal(O.dequant(p, s, t), w)
+    # single nonzero element: it becomes +-6 * 448 * tscale, everything else 0
+    w = _bits([[0.0] * 7 + [-0.0371] + [0.0] * 24])
+    p, s, t = O.quantize(w)
+    c = O.unpack_nibbles(p)[0]
+    assert c[7] == 0xF and s[0, 0] == 0x7E and s[0, 1] == 0
+    # a block far below amax gets a subnormal or zero scale
+    w = _bits([[100.0] + [0.0] * 15 + [1e-3] + [0.0] * 15 + [1e-7] + [0.0] * 15])
+    p, s, t = O.quantize(w)
+    assert s[0, 0] == 0x7E and 0 < s[0, 1] < 0x08 and s[0, 2] == 0
+    assert O.unpack_nibbles(p)[0, 32] == 0
+
+
+def test_invalid_inputs_rejected():
+    with pytest.raises(ValueError):
+        O.quantize(np.zeros((2, 24), dtype=np.uint16))
+    with pytest.raises(ValueError):
+        O.quantize(_bits([[np.inf] + [0.0] * 15]))
+
+
+def test_linear_tolerance_gate():
+    y_ref = np.array([[1.0, -2.0, 0.0]])
+    bound = np.array([[10.0, 10.0, 0.0]])
+    assert not O.linear_violations(np.array([[1.019, -2.0, 0.0]]), y_ref, bound).any()
+    assert O.linear_violations(np.array([[1.021, -2.0, 0.0]]), y_ref, bound).tolist() == [[True, False, False]]
+    assert O.linear_violations(np.array([[1.0, -2.0, 1e-30]]), y_ref, bound).tolist() == [[False, False, True]]
+
+
+# --------------------------------------------------------------------------
+# Mutation tests: plant a mistake in the oracle, check that some pin fails.
+# --------------------------------------------------------------------------
+def _expect_pin_failure(monkeypatch, target, replacement, pins):
+    monkeypatch.setattr(O, target, replacement)
+    failed = False
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed = True
+            break
+    assert failed, f"planted mistake in {target} went unnoticed"
+
+
+def test_mutation_swapped_nibbles(monkeypatch):
+    _expect_pin_failure(monkeypatch, "pack_nibbles",
+                        lambda c: (np.asarray(c)[:, 1::2] | (np.asarray(c)[:, 0::2] << 4)).astype(np.uint8),
+                        [pin_nibble_layout])
+
+
+def test_mutation_ties_away_from_zero(monkeypatch):
+    def ties_up(lhs, mids, f):
+        code = np.zeros(np.shape(lhs), dtype=np.int64)
+        for u in mids:
+            code += lhs >= u * f
+        return code
+    _expect_pin_failure(monkeypatch, "_nearest_code_ties_even", ties_up,
+                        [lambda: pin_quantize_brute_force(tiny_inputs()[4])])
+
+
+def test_mutation_ties_down(monkeypatch):
+    def ties_down(lhs, mids, f):
+        code = np.zeros(np.shape(lhs), dtype=np.int64)
+        for u in mids:
+            code += lhs > u * f
+        return code
+    _expect_pin_failure(monkeypatch, "_nearest_code_ties_even", ties_down,
+                        [lambda: pin_quantize_brute_force(tiny_inputs()[4])])
+
+
+def test_mutation_transposed_operand(monkeypatch):
+    def linear_t(x_bits, packed, scales, tscale):
+        x = O.bf16_to_f64(x_bits)
+        w = O.dequant_exact(packed, scales, tscale)
+        return x @ w, np.abs(x) @ np.abs(w)      # W not transposed (square case)
+    w = WL.normal_bf16((16, 16), 0.02, 40)
+    x = WL.normal_bf16((16, 16), 1.0, 41)
+    _expect_pin_failure(monkeypatch, "linear_ref", linear_t,
+                        [lambda: pin_linear_brute_force(x, *O.quantize(w))])
+
+
+def test_mutation_dropped_tensor_scale(monkeypatch):
+    orig = O.decoded_products
+    w = WL.normal_bf16((4, 64), 0.02, 42)
+    q = O.quantize(w)
+    monkeypatch.setattr(O, "dequant", lambda p, s, t: O.f32_to_bf16_rne(orig(p, s).astype(np.float32)))
+    with pytest.raises(AssertionError):
+        pin_dequant_closed_form(*q)
+
+
+def test_mutation_scale_from_rounded_tscale(monkeypatch):
+    """Deciding codes against the rounded tscale instead of amax breaks exact ties."""
+    orig = O.element_codes
+
+    def via_tscale(w_bits, scale_codes, amax):
+        t = float(O.tensor_scale(amax))
+        return orig(w_bits, scale_codes, t * 2688.0 * (1 + 2 ** -22))
+    _expect_pin_failure(monkeypatch, "element_codes", via_tscale,
+                        [lambda: pin_quantize_brute_force(tiny_inputs()[4])])
+
+
+def test_mutation_wrong_e4m3_bias(monkeypatch):
+    bad = O.E4M3_TABLE * 2.0
+    monkeypatch.setattr(O, "E4M3_TABLE", bad)
+    with pytest.raises(AssertionError):
+        pin_e4m3_table()
