@@ -1,0 +1,315 @@
+"""Benchmark of the NVFP4 W4A16 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the decode GEMV (M = 1, N = K = 5120, BF16 ~N(0, 0.02) weights with
+1% outlier input columns x8, RTN-quantized to NVFP4; BF16 ~N(0, 1)
+activations).  A step is one call of the decode hot path, nvfp4_linear at
+M = 1 (GEMV + BF16 epilogue), on one of 37 rotated weight copies (the rotated
+set is 2x the 256 MB Infinity Cache, so every call streams its weights from
+HBM).  The K timed calls are replayed from a HIP graph of the rotated launch
+sequence, bracketed by HIP events on the stream they run on.
+
+The same run also measures every other row of the hot path once each
+(quantizer, dequantizer, merged gate/up GEMV, small-M batched decode, prefill
+GEMM) and reports them under "rows"; it times the CPU oracle on a bounded
+sample as a baseline ("cpu_baseline").  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import nvfp4_weight_only_amd as nv  # noqa: E402
+from nvfp4_weight_only_amd import workloads as WL  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (no sparsity)
+INFINITY_CACHE = 256 << 20
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def linear_bytes(m, n, k):
+    """Algorithmic HBM bytes of one linear call: packed + scales + X + Y + tensor scale."""
+    return n * k // 2 + n * k // 16 + 2 * m * k + 2 * m * n + 4
+
+
+def copies_needed(bytes_per_copy):
+    return max(2, -(-2 * INFINITY_CACHE // bytes_per_copy))
+
+
+class Rotated:
+    """C rotated copies of one quantized weight (distinct HBM addresses)."""
+
+    def __init__(self, packed, scales, tscale, c):
+        self.items = [(packed.clone(), scales.clone(), tscale.clone()) for _ in range(c)]
+
+    def __len__(self):
+        return len(self.items)
+
+
+def graph_of(calls):
+    """Capture a list of zero-argument launch closures into one HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:          # warm once outside the graph on the capture stream
+            c()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph_replays(graph, replays, launches_per_replay):
+    """Average duration per launch (ms) over `replays` back-to-back graph replays, by HIP events."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * launches_per_replay)
+
+
+def linear_calls(x, rot, y, kernel="auto"):
+    return [(lambda p=p, s=s, t=t: nv.linear(x, p, s, t, kernel=kernel, out=y)) for (p, s, t) in rot.items]
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "nvfp4_weight_only_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    e = table.get(kernel_key)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# Rows of the hot path.
+# ---------------------------------------------------------------------------
+def bench_linear_row(wname, m, reps, kernel="auto"):
+    wl = WL.WORKLOADS[wname]
+    w = wl.weight()
+    packed, scales, tscale = nv.quantize(dev_bf16(w))
+    del w
+    per_copy = packed.numel() + scales.numel()
+    rot = Rotated(packed, scales, tscale, copies_needed(per_copy))
+    x = dev_bf16(wl.activations(m))
+    y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+    g = graph_of(linear_calls(x, rot, y, kernel))
+    time_graph_replays(g, 2, len(rot))
+    ms = time_graph_replays(g, reps, len(rot))
+    nbytes = linear_bytes(m, wl.n, wl.k)
+    flops = 2.0 * m * wl.n * wl.k
+    out = {"m": m, "n": wl.n, "k": wl.k, "copies": len(rot), "us_per_call": round(ms * 1e3, 3),
+           "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "tflop_s": round(flops / (ms * 1e-3) / 1e12, 2),
+           "weight_streams_per_s": round(1.0 / (ms * 1e-3), 1)}
+    out["hbm_frac"] = round(out["gb_s"] / HBM_PEAK_GBS, 4)
+    out["mfma_frac"] = round(out["tflop_s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    del rot, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_quant_rows(reps):
+    """Quantizer (amax + quantize passes) and dequantizer on the decode weight, rotated."""
+    wl = WL.WORKLOADS["decode"]
+    w = dev_bf16(wl.weight())
+    n, k = wl.n, wl.k
+    c = copies_needed(2 * n * k)
+    ws = [w.clone() for _ in range(c)]
+    outs = [nv.quantize(wi) for wi in ws]
+    g = graph_of([(lambda wi=wi: nv.quantize(wi)) for wi in ws])
+    time_graph_replays(g, 1, c)
+    ms_q = time_graph_replays(g, reps, c)
+    dq = [torch.empty((n, k), dtype=torch.bfloat16, device="cuda") for _ in range(c)]
+    lib = nv.lib()
+
+    def dq_call(o, d):
+        return lambda: lib.nvfp4_dequant(o[0].data_ptr(), o[1].data_ptr(), o[2].data_ptr(), n, k, d.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream)
+    g2 = graph_of([dq_call(o, d) for o, d in zip(outs, dq)])
+    time_graph_replays(g2, 1, c)
+    ms_d = time_graph_replays(g2, reps, c)
+    e = n * k
+    q_bytes = 2 * e + 2 * e + e // 2 + e // 16 + 4     # amax read, quantize read, packed + scales write
+    d_bytes = e // 2 + e // 16 + 4 + 2 * e
+    rows = {
+        "quantize_decode_5120x5120": {"us_per_call": round(ms_q * 1e3, 2),
+                                      "gb_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(q_bytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "bytes": q_bytes, "note": "4 launches: zero, amax pass, quantize pass, tscale"},
+        "dequant_decode_5120x5120": {"us_per_call": round(ms_d * 1e3, 2),
+                                     "gb_s": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
+                                     "hbm_frac": round(d_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "bytes": d_bytes},
+    }
+    del ws, outs, dq, g, g2
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(budget_s=10.0):
+    """The oracle's linear (float64) on the decode workload, single-threaded, for about budget_s seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import nvfp4_oracle as O
+    wl = WL.WORKLOADS["decode"]
+    w = wl.weight()
+    x = wl.activations(1)
+    rows = 1024   # bounded sample: 1024 of the 5120 weight rows
+    p, s, t = O.quantize(w[:rows], amax=O.tensor_amax(w))
+    with threadpool_limits(limits=1):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            O.linear_ref(x, p, s, t)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    nbytes = linear_bytes(1, rows, wl.k) * calls
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle linear_ref (float64) on rows 0..{rows - 1} of the decode weight "
+                      f"(M=1, K=5120), {calls} calls in {el:.1f} s, single thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3700)
+    ap.add_argument("--warmup", type=int, default=370)
+    ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
+              f"MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    nv.lib()
+
+    wl = WL.WORKLOADS["decode"]
+    m, n, k = 1, wl.n, wl.k
+    log(f"decode workload: quantizing {n}x{k}")
+    w = wl.weight()
+    packed, scales, tscale = nv.quantize(dev_bf16(w))
+    x_bits = wl.activations(m)
+    x = dev_bf16(x_bits)
+
+    # Parity gate before timing (sampled output rows against the oracle).
+    from oracle import nvfp4_oracle as O
+    y = nv.linear(x, packed, scales, tscale)
+    cols = np.arange(0, n, 40)
+    y_ref, bound = O.linear_ref(x_bits, packed.cpu().numpy()[cols], scales.cpu().numpy()[cols], tscale.cpu().numpy()[0])
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[:, cols]
+    assert not O.linear_violations(WL.f32_from_bf16_bits(yb), y_ref, bound).any(), "parity gate failed"
+    del w
+
+    c = copies_needed(packed.numel() + scales.numel())
+    rot = Rotated(packed, scales, tscale, c)
+    yout = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    calls = linear_calls(x, rot, yout)
+    full = graph_of(calls)
+    rem = args.steps % c
+    part = graph_of(calls[:rem]) if rem else None
+    log(f"{c} rotated copies; warmup {args.warmup}, timed {args.steps} steps")
+    for _ in range(max(1, args.warmup // c)):
+        full.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps // c):
+        full.replay()
+    if part is not None:
+        part.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = linear_bytes(m, n, k)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode GEMV: {ms * 1e3:.3f} us/call, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak); wall {wall:.2f} s")
+    digest = source_digest(["gemv.hip", "device_common.hpp"])
+
+    rows = {}
+    if args.rows == "all":
+        for wname, mm, reps in [("gate_up", 1, 30), ("small_m_up", 8, 30), ("small_m_up", 32, 30),
+                                ("small_m_down", 8, 30), ("small_m_down", 32, 30),
+                                ("prefill", 512, 10), ("prefill", 2048, 3)]:
+            key = f"linear_{wname}_m{mm}"
+            log(f"row {key}")
+            rows[key] = bench_linear_row(wname, mm, reps)
+            log(f"  {rows[key]}")
+        log("rows quantize/dequant")
+        rows.update(bench_quant_rows(20))
+        log(f"  {rows['quantize_decode_5120x5120']} {rows['dequant_decode_5120x5120']}")
+
+    log("cpu baseline (oracle)")
+    cpu = cpu_baseline(args.cpu_budget)
+    result = {
+        "metric": "NVFP4 W4A16 linear: achieved HBM GB/s (M=1..32), TFLOP/s (M=512), % of peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded BF16 normals, RTN-quantized to NVFP4 on the GPU)",
+        "config": {"workload": "decode GEMV: M=1, N=5120, K=5120, 1% outlier input columns x8",
+                   "m": m, "n": n, "k": k, "rotated_weight_copies": c,
+                   "timing": "HIP-graph replay of the rotated launch sequence, HIP events on the launch stream",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gemv_decode_5120x5120", digest),
+                     "kernel": "gemv_kernel<4,2>", "bytes_per_launch": nbytes,
+                     "avg_launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

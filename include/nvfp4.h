@@ -1,0 +1,138 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so, the MI355X (gfx950) NVFP4 weight-only linear.
+ *
+ * Format (homepage "Raphael Friedmann", NVFP4 bit diagram; imp
+ * "docs/quantization.md", imp-quantize section; model card
+ * "Qwen3.8-27B-NVFP4 (compressed-tensors)", "What is quantized"):
+ *   - element: E2M1, 4 bits (sign, 2 exponent bits, 1 mantissa bit); magnitudes
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ *   - two elements per byte ("packed nibbles"); element 2j in the low nibble of
+ *     byte j, element 2j+1 in the high nibble;
+ *   - one FP8 E4M3 (OCP E4M3FN) micro-scale per 16 consecutive K elements;
+ *   - one FP32 tensor scale per tensor, stored as a multiplier;
+ *   - weight-only: activations and outputs stay BF16 (W4A16).
+ *
+ * Shapes: a weight W is [n, k] row-major (n output features, k input
+ * features), k a multiple of 16.  Its quantized form is
+ *   packed  uint8 [n, k/2]     row-major,
+ *   scales  uint8 [n, k/16]    row-major (E4M3 codes 0x00..0x7E),
+ *   tscale  float [1].
+ * Activations X are BF16 [m, k] row-major, outputs Y are BF16 [m, n]
+ * row-major: Y = X . W_hat^T with W_hat = E2M1 * E4M3 * tscale.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer into caller-owned memory and must be
+ *     16-byte aligned.  Nothing is allocated or freed by the library.
+ *   - BF16 values are passed as uint16_t bit patterns; sizes are int64_t.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     stream-ordered and asynchronous: it never synchronises the device.
+ *   - Arguments are validated on the host before any HIP call; a call that
+ *     fails validation launches nothing.  NVFP4_ERR_DEVICE reports a HIP
+ *     launch error (hipGetLastError) after launching.
+ *   - Outputs must not overlap inputs (NVFP4_ERR_ALIAS).
+ *   - Results are bitwise reproducible run to run (no floating-point atomics).
+ *   - W and X must be finite; for non-finite inputs the outputs are unspecified
+ *     but the call still terminates normally.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* m < 0, n <= 0, k <= 0, k % 16 != 0, or a byte size overflows int64 */
+  NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  NVFP4_ERR_ALIAS = 4,       /* an output buffer overlaps an input buffer */
+  NVFP4_ERR_DEVICE = 5,      /* HIP reported an error (no device, launch failure) */
+  NVFP4_ERR_UNSUPPORTED = 6, /* the current device is not gfx950, or an unknown kernel id */
+} nvfp4_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* Library version string, e.g. "nvfp4-mi355x 0.1.0". */
+const char* nvfp4_version(void);
+
+/*
+ * Round-to-nearest BF16 -> NVFP4 quantizer (imp "docs/quantization.md",
+ * imp-quantize section: uncalibrated round-to-nearest scales taken from the
+ * block absmax).
+ *   amax    = max |W|
+ *   tscale  = fl32(amax / 2688)                                 (2688 = 6 * 448)
+ *   scales  = per 16-element block, the E4M3 code nearest to 448 * bam / amax,
+ *             bam = the block's max |w|; ties to the even code; 0 when bam = 0
+ *   packed  = per element, sign = the BF16 sign bit, magnitude = the E2M1 code
+ *             nearest to 2688 * |w| / (amax * s), s = the block scale value;
+ *             ties to the even code, saturating at 6; 0 when s = 0
+ * Every rounding decision is taken on the exact real quotient.
+ * w: [n, k] BF16.  Outputs packed [n, k/2], scales [n, k/16], tscale [1].
+ * The tscale slot is used as scratch for amax during the call.
+ */
+nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k,
+                            uint8_t* packed, uint8_t* scales, float* tscale, void* stream);
+
+/*
+ * Merged linears (model card "Qwen3.8-27B-NVFP4", "What is quantized": q/k/v
+ * and gate/up members share one tensor scale; the amax spread inside a group
+ * reaches 3.7x).  To quantize members held as separate tensors:
+ *   1. set *amax = 0 (caller-owned device float),
+ *   2. call nvfp4_amax_accumulate on every member (amax <- max(amax, max|W|)),
+ *   3. call nvfp4_quantize_with_amax on every member with the same amax.
+ * The outputs then equal, bit for bit, the rows of nvfp4_quantize applied to
+ * the concatenated weight, and every member's tscale equals the shared one.
+ * amax must hold a finite non-negative float; it must not overlap the outputs.
+ */
+nvfp4_status nvfp4_amax_accumulate(const uint16_t* w, int64_t n, int64_t k, float* amax, void* stream);
+
+nvfp4_status nvfp4_quantize_with_amax(const uint16_t* w, int64_t n, int64_t k, const float* amax,
+                                      uint8_t* packed, uint8_t* scales, float* tscale, void* stream);
+
+/*
+ * Dequantize to BF16: w_out = RNE_bf16( fl32( fl32(E2M1 * E4M3) * tscale ) ).
+ * (The product of an E2M1 and an E4M3 value is exact in FP32.)
+ * packed [n, k/2], scales [n, k/16], tscale [1] -> w_out [n, k] BF16.
+ */
+nvfp4_status nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                           int64_t n, int64_t k, uint16_t* w_out, void* stream);
+
+/*
+ * The W4A16 linear (model card "Qwen3.8-27B-NVFP4": weights NVFP4,
+ * activations BF16; imp "docs/quantization.md", NVFP4 kernel pipeline: a
+ * decode GEMV and a prefill GEMM):
+ *   y[i, j] = RNE_bf16( tscale * sum_k x[i, k] * E2M1(w[j, k]) * E4M3(s[j, k/16]) )
+ * accumulated in FP32.  The kernel is chosen from m: m = 1 -> GEMV,
+ * 2 <= m <= 64 -> small-M MFMA kernel, m > 64 -> prefill MFMA GEMM.
+ * x [m, k] BF16, packed [n, k/2], scales [n, k/16], tscale [1] -> y [m, n] BF16.
+ * m = 0 is a no-op that returns NVFP4_OK once packed/scales/tscale/n/k are
+ * valid; x and y may then be NULL.
+ */
+nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                          const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                          uint16_t* y, void* stream);
+
+/* Kernel ids for nvfp4_linear_forced. */
+#define NVFP4_KERNEL_AUTO 0
+#define NVFP4_KERNEL_GEMV 1     /* VALU dot-product GEMV; any m (rows handled independently) */
+#define NVFP4_KERNEL_SMALL_M 2  /* MFMA kernel with 16/32-row X tiles; any m */
+#define NVFP4_KERNEL_PREFILL 3  /* MFMA GEMM with large tiles; any m */
+
+/*
+ * Same as nvfp4_linear but runs the named kernel for any m (used by tests to
+ * cross-check the kernels against each other and against the oracle).
+ * An unknown kernel id returns NVFP4_ERR_UNSUPPORTED.
+ */
+nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                                 uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,1 +1,11 @@
-"""MI355X-native NVFP4 weight-only (W4A16) linear: HIP kernels behind a C ABI, with a thin binding."""
+"""MI355X-native NVFP4 weight-only (W4A16) linear.
+
+The hot path runs in hand-written gfx950 HIP kernels behind the C ABI of
+libnvfp4.so (include/nvfp4.h).  This package holds the kernels (csrc/), the
+build script, the ctypes binding and the synthetic workload generators.
+"""
+from .binding import (KERNEL_IDS, NVFP4Error, amax_accumulate, dequant, lib, lib_path, linear, quantize,
+                      quantize_shared, quantize_with_amax)
+
+__all__ = ["KERNEL_IDS", "NVFP4Error", "amax_accumulate", "dequant", "lib", "lib_path", "linear", "quantize",
+           "quantize_shared", "quantize_with_amax"]

@@ -1,0 +1,161 @@
+"""Thin ctypes binding of libnvfp4.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels.  torch provides device
+memory and the current HIP stream; there is no CPU or PyTorch fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+_lib: Optional[ctypes.CDLL] = None
+
+KERNEL_AUTO, KERNEL_GEMV, KERNEL_SMALL_M, KERNEL_PREFILL = 0, 1, 2, 3
+KERNEL_IDS = {"auto": KERNEL_AUTO, "gemv": KERNEL_GEMV, "small_m": KERNEL_SMALL_M, "prefill": KERNEL_PREFILL}
+
+# Status codes (include/nvfp4.h).
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = range(7)
+
+# Every symbol include/nvfp4.h declares.
+EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
+            "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced")
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().nvfp4_status_string(status).decode()}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4.so (built in-tree by nvfp4_weight_only_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m nvfp4_weight_only_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.nvfp4_status_string.argtypes = [i32]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_version.argtypes = []
+        L.nvfp4_version.restype = ctypes.c_char_p
+        L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.nvfp4_amax_accumulate.argtypes = [vp, i64, i64, vp, vp]
+        L.nvfp4_quantize_with_amax.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        L.nvfp4_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+        L.nvfp4_linear.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.nvfp4_linear_forced.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        for name in EXPORTED[2:]:
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise NVFP4Error(status, what)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """BF16 [n, k] -> (packed uint8 [n, k/2], scales uint8 [n, k/16], tscale float32 [1])."""
+    _need(w, torch.bfloat16, "w")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=w.device)
+    tscale = torch.empty((1,), dtype=torch.float32, device=w.device)
+    _check(lib().nvfp4_quantize(w.data_ptr(), n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(),
+                                _stream(w)), "nvfp4_quantize")
+    return packed, scales, tscale
+
+
+def amax_accumulate(w: torch.Tensor, amax: torch.Tensor) -> None:
+    """amax <- max(amax, max|w|) on the device (amax: float32 [1], caller-initialised)."""
+    _need(w, torch.bfloat16, "w")
+    _need(amax, torch.float32, "amax")
+    n, k = w.shape
+    _check(lib().nvfp4_amax_accumulate(w.data_ptr(), n, k, amax.data_ptr(), _stream(w)), "nvfp4_amax_accumulate")
+
+
+def quantize_with_amax(w: torch.Tensor, amax: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Quantize one member of a merged linear against a shared amax (see nvfp4_quantize_with_amax)."""
+    _need(w, torch.bfloat16, "w")
+    _need(amax, torch.float32, "amax")
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=w.device)
+    tscale = torch.empty((1,), dtype=torch.float32, device=w.device)
+    _check(lib().nvfp4_quantize_with_amax(w.data_ptr(), n, k, amax.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                                          tscale.data_ptr(), _stream(w)), "nvfp4_quantize_with_amax")
+    return packed, scales, tscale
+
+
+def quantize_shared(members) -> Tuple[list, torch.Tensor]:
+    """Quantize the members of a merged linear (q/k/v, gate/up) against one tensor scale."""
+    amax = torch.zeros((1,), dtype=torch.float32, device=members[0].device)
+    for w in members:
+        amax_accumulate(w, amax)
+    outs = [quantize_with_amax(w, amax) for w in members]
+    return [(p, s) for p, s, _ in outs], outs[0][2]
+
+
+def dequant(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor) -> torch.Tensor:
+    """NVFP4 -> BF16 [n, k]."""
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    n, kh = packed.shape
+    k = 2 * kh
+    if scales.shape != (n, k // 16):
+        raise ValueError("scales must be [n, k/16]")
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=packed.device)
+    _check(lib().nvfp4_dequant(packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), n, k, out.data_ptr(),
+                               _stream(packed)), "nvfp4_dequant")
+    return out
+
+
+def linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+           kernel: str = "auto", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y[m, n] = X[m, k] . W_hat[n, k]^T in BF16 (FP32 accumulation)."""
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape != (n, k // 2) or scales.shape != (n, k // 16):
+        raise ValueError("packed/scales do not match x's k")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (m, n):
+            raise ValueError("out must be [m, n]")
+    kid = KERNEL_IDS[kernel]
+    args = (x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), _stream(x))
+    if kid == KERNEL_AUTO:
+        _check(lib().nvfp4_linear(*args), "nvfp4_linear")
+    else:
+        _check(lib().nvfp4_linear_forced(kid, *args), "nvfp4_linear_forced")
+    return out

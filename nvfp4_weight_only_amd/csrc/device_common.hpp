@@ -1,0 +1,135 @@
+// Device helpers for the gfx950 NVFP4 kernels: number formats and packing.
+//
+// Formats (homepage "Raphael Friedmann", NVFP4 bit diagram; imp
+// "docs/quantization.md", imp-quantize section and the micro-scale paragraph):
+//   E2M1 nibble  s|e1 e0|m, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7),
+//                code 8..15 the negatives (8 = -0);
+//   E4M3 byte    OCP E4M3FN: s|eeee|mmm, bias 7, e = 0 subnormal m/8 * 2^-6,
+//                0x7F/0xFF NaN, max 448;
+//   packing      element 2j in the low nibble of byte j, 2j+1 in the high nibble;
+//                one E4M3 scale per 16 consecutive K elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Scalars.
+// ---------------------------------------------------------------------------
+
+// E4M3FN byte -> float, exact (branch-free for the non-negative codes used as scales).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  const float vn = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+  const float vs = (float)m * 0x1p-9f;                               // m/8 * 2^-6
+  float v = e ? vn : vs;
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+  return (c & 0x80u) ? -v : v;
+}
+
+// E2M1 magnitude code 0..7 -> float, exact.
+__device__ __forceinline__ float e2m1_mag_to_f32(uint32_t mag) {
+  const uint32_t e = (mag >> 1) & 3u, m = mag & 1u;
+  const uint32_t nb = ((e + 126u) << 23) | (m << 22);   // 2^(e-1) * (1 + m/2)
+  return __uint_as_float(e ? nb : (m ? 0x3F000000u : 0u));
+}
+
+// float -> BF16 bits, round to nearest even (NaN -> canonical quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// BF16 bits -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// ---------------------------------------------------------------------------
+// Eight packed elements (one 32-bit word) -> BF16.
+// ---------------------------------------------------------------------------
+
+// BF16 bit patterns of the E2M1 magnitudes, split into byte planes for v_perm_b32.
+// magnitude:       0     0.5   1     1.5   2     3     4     6
+// low byte:        00    00    80    C0    00    40    80    C0
+// high byte:       00    3F    3F    3F    40    40    40    40
+constexpr uint32_t kLoLut0 = 0xC0800000u;  // magnitudes 0..3
+constexpr uint32_t kLoLut1 = 0xC0804000u;  // magnitudes 4..7
+constexpr uint32_t kHiLut0 = 0x3F3F3F00u;
+constexpr uint32_t kHiLut1 = 0x40404040u;
+
+// Unscaled decode of the 8 elements of `p` into 4 BF16 pairs in the order
+//   out.x = (e0, e2), out.y = (e4, e6), out.z = (e1, e3), out.w = (e5, e7)
+// (low half first).  Pair the result with activations permuted the same way.
+// Byte-permute lookups: 2 selector ops, 4 table lookups, 3 sign ops, 4 interleaves.
+__device__ __forceinline__ uint4 e2m1x8_to_bf16_interleaved(uint32_t p) {
+  const uint32_t se = p & 0x07070707u;          // magnitudes of elements 0, 2, 4, 6
+  const uint32_t so = (p >> 4) & 0x07070707u;   // magnitudes of elements 1, 3, 5, 7
+  const uint32_t lo_e = __builtin_amdgcn_perm(kLoLut1, kLoLut0, se);
+  const uint32_t hi_e = __builtin_amdgcn_perm(kHiLut1, kHiLut0, se) | ((p << 4) & 0x80808080u);
+  const uint32_t lo_o = __builtin_amdgcn_perm(kLoLut1, kLoLut0, so);
+  const uint32_t hi_o = __builtin_amdgcn_perm(kHiLut1, kHiLut0, so) | (p & 0x80808080u);
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u);
+  r.y = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);
+  r.z = __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u);
+  r.w = __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u);
+  return r;
+}
+
+// Permute 8 BF16 activations (4 natural-order pairs) into the order used above.
+__device__ __forceinline__ uint4 bf16x8_interleave(uint4 d) {
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);  // (x0, x2)
+  r.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);  // (x4, x6)
+  r.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);  // (x1, x3)
+  r.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);  // (x5, x7)
+  return r;
+}
+
+// Scaled decode: 8 elements of `p` times the block scale `s` (an E4M3 value)
+// as BF16 pairs in natural order.  E2M1 * E4M3 has at most 6 significant bits
+// and lies in [2^-10, 2688], so the product is exact in FP32 and its top half
+// is the exact BF16 value.
+__device__ __forceinline__ uint4 e2m1x8_scaled_to_bf16(uint32_t p, float s) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t c0 = (p >> (8 * j)) & 0xFu, c1 = (p >> (8 * j + 4)) & 0xFu;
+    const uint32_t b0 = (__float_as_uint(e2m1_mag_to_f32(c0 & 7u) * s) >> 16) | ((c0 & 8u) << 12);
+    const uint32_t b1 = (__float_as_uint(e2m1_mag_to_f32(c1 & 7u) * s) >> 16) | ((c1 & 8u) << 12);
+    o[j] = b0 | (b1 << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Dot products and wave reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,25 @@
+// Internal launchers of the gfx950 kernels (host side).  Callers validate every
+// argument first; the launchers assume valid shapes and aligned pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+void launch_fill_zero(float* p, hipStream_t s);
+void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s);
+void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s);
+void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
+                     hipStream_t s);
+void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n_elems,
+                    uint16_t* out, hipStream_t s);
+
+void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
+                 const float* tscale, uint16_t* y, hipStream_t s);
+void launch_gemm_small_m(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+
+}  // namespace nvfp4

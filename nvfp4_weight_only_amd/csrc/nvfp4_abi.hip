@@ -1,0 +1,201 @@
+// C ABI of libnvfp4.so: argument validation, device check, kernel dispatch.
+// Declarations and the meaning of every argument are in include/nvfp4.h.
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "launch.hpp"
+#include "nvfp4.h"
+
+namespace {
+
+constexpr int64_t kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges).
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+// a * b fits in int64 (a, b >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct WeightSizes {
+  int64_t elems, w_bytes, packed_bytes, scale_bytes;
+};
+
+nvfp4_status weight_sizes(int64_t n, int64_t k, WeightSizes* s) {
+  if (n <= 0 || k <= 0 || (k & 15) != 0) return NVFP4_ERR_SHAPE;
+  if (!mul_ok(n, k, &s->elems) || !mul_ok(s->elems, 2, &s->w_bytes)) return NVFP4_ERR_SHAPE;
+  s->packed_bytes = s->elems / 2;
+  s->scale_bytes = s->elems / 16;
+  return NVFP4_OK;
+}
+
+// Checks that the current device is a gfx950 (cached per device).
+nvfp4_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_DEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_ERR_DEVICE;
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? NVFP4_OK : NVFP4_ERR_UNSUPPORTED;
+}
+
+nvfp4_status launch_status() { return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE; }
+
+nvfp4_status validate_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                             const uint8_t* scales, const float* tscale, const uint16_t* y) {
+  // m = 0 is a no-op: x and y may then be NULL (empty tensors).
+  if (!packed || !scales || !tscale || (m != 0 && (!x || !y))) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  if (m < 0) return NVFP4_ERR_SHAPE;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (m == 0) return NVFP4_OK;
+  int64_t xe, ye, xb, yb;
+  if (!mul_ok(m, k, &xe) || !mul_ok(xe, 2, &xb) || !mul_ok(m, n, &ye) || !mul_ok(ye, 2, &yb)) return NVFP4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(tscale) || !aligned16(y))
+    return NVFP4_ERR_ALIGN;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, packed, ws.packed_bytes) || overlaps(y, yb, scales, ws.scale_bytes) ||
+      overlaps(y, yb, tscale, 4))
+    return NVFP4_ERR_ALIAS;
+  return NVFP4_OK;
+}
+
+nvfp4_status run_linear(int kernel, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                        const uint8_t* scales, const float* tscale, uint16_t* y, void* stream) {
+  if (kernel < NVFP4_KERNEL_AUTO || kernel > NVFP4_KERNEL_PREFILL) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4_status st = validate_linear(x, m, n, k, packed, scales, tscale, y);
+  if (st != NVFP4_OK) return st;
+  if (m == 0) return NVFP4_OK;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  if (kernel == NVFP4_KERNEL_AUTO) kernel = m == 1 ? NVFP4_KERNEL_GEMV : (m <= 64 ? NVFP4_KERNEL_SMALL_M : NVFP4_KERNEL_PREFILL);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (kernel) {
+    case NVFP4_KERNEL_GEMV: nvfp4::launch_gemv(x, m, n, k, packed, scales, tscale, y, s); break;
+    case NVFP4_KERNEL_SMALL_M: nvfp4::launch_gemm_small_m(x, m, n, k, packed, scales, tscale, y, s); break;
+    default: nvfp4::launch_gemm_prefill(x, m, n, k, packed, scales, tscale, y, s); break;
+  }
+  return launch_status();
+}
+
+nvfp4_status validate_quantize_outputs(const uint16_t* w, const WeightSizes& ws, const uint8_t* packed,
+                                       const uint8_t* scales, const float* tscale) {
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(scales) || !aligned16(tscale)) return NVFP4_ERR_ALIGN;
+  const void* outs[3] = {packed, scales, tscale};
+  const int64_t out_bytes[3] = {ws.packed_bytes, ws.scale_bytes, 4};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], out_bytes[i], w, ws.w_bytes)) return NVFP4_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return NVFP4_ERR_ALIAS;
+  }
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: invalid m/n/k (k must be a positive multiple of 16) or size overflow";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case NVFP4_ERR_ALIAS: return "NVFP4_ERR_ALIAS: an output overlaps an input";
+    case NVFP4_ERR_DEVICE: return "NVFP4_ERR_DEVICE: HIP error";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED: device is not gfx950 or unknown kernel id";
+    default: return "NVFP4_ERR_UNKNOWN";
+  }
+}
+
+const char* nvfp4_version(void) { return "nvfp4-mi355x 0.1.0"; }
+
+nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* packed, uint8_t* scales, float* tscale,
+                            void* stream) {
+  if (!w || !packed || !scales || !tscale) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if ((st = validate_quantize_outputs(w, ws, packed, scales, tscale)) != NVFP4_OK) return st;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The tscale slot holds amax until the last kernel turns it into amax / 2688.
+  nvfp4::launch_fill_zero(tscale, s);
+  nvfp4::launch_amax(w, ws.elems, tscale, s);
+  nvfp4::launch_quantize(w, ws.elems, tscale, packed, scales, s);
+  nvfp4::launch_finalize_tscale(tscale, tscale, s);
+  return launch_status();
+}
+
+nvfp4_status nvfp4_amax_accumulate(const uint16_t* w, int64_t n, int64_t k, float* amax, void* stream) {
+  if (!w || !amax) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(w) || !aligned16(amax)) return NVFP4_ERR_ALIGN;
+  if (overlaps(amax, 4, w, ws.w_bytes)) return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_amax(w, ws.elems, amax, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_quantize_with_amax(const uint16_t* w, int64_t n, int64_t k, const float* amax, uint8_t* packed,
+                                      uint8_t* scales, float* tscale, void* stream) {
+  if (!w || !amax || !packed || !scales || !tscale) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(amax)) return NVFP4_ERR_ALIGN;
+  if ((st = validate_quantize_outputs(w, ws, packed, scales, tscale)) != NVFP4_OK) return st;
+  if (overlaps(amax, 4, packed, ws.packed_bytes) || overlaps(amax, 4, scales, ws.scale_bytes) ||
+      overlaps(amax, 4, tscale, 4))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  nvfp4::launch_quantize(w, ws.elems, amax, packed, scales, s);
+  nvfp4::launch_finalize_tscale(amax, tscale, s);
+  return launch_status();
+}
+
+nvfp4_status nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n, int64_t k,
+                           uint16_t* w_out, void* stream) {
+  if (!packed || !scales || !tscale || !w_out) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(tscale) || !aligned16(w_out)) return NVFP4_ERR_ALIGN;
+  if (overlaps(w_out, ws.w_bytes, packed, ws.packed_bytes) || overlaps(w_out, ws.w_bytes, scales, ws.scale_bytes) ||
+      overlaps(w_out, ws.w_bytes, tscale, 4))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_dequant(packed, scales, tscale, ws.elems, w_out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                          const uint8_t* scales, const float* tscale, uint16_t* y, void* stream) {
+  return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, stream);
+}
+
+nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                 const uint8_t* packed, const uint8_t* scales, const float* tscale, uint16_t* y,
+                                 void* stream) {
+  return run_linear(kernel_id, x, m, n, k, packed, scales, tscale, y, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// Quantizer (BF16 -> NVFP4) and dequantizer kernels for gfx950.
+//
+// The quantizer is imp-quantize's round-to-nearest scheme (imp
+// "docs/quantization.md", imp-quantize section: plain round-to-nearest scales
+// over the weights, no calibration; the micro-scale paragraph: the scale is
+// taken from the block absmax, and the FP4 grid is 0, 0.5, 1, 1.5, 2, 3, 4, 6):
+//   tscale = fl32(amax / 2688)
+//   scale  = E4M3 code nearest to 448 * bam / amax           (ties to even)
+//   code   = sign(w) | E2M1 code nearest to 2688 |w| / (amax s)   (ties to even, saturating)
+// Every decision compares two exact products in FP32 (operands are rescaled
+// by powers of two so that both sides stay in range), so the result equals
+// the decision on the exact real quotients.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// amax: max |w| over the tensor, merged into *amax with an unsigned atomic max
+// on the FP32 bit pattern (order-free, so the result is deterministic).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p) { *p = 0.0f; }
+
+__global__ void __launch_bounds__(256) amax_kernel(const uint4* __restrict__ w, int64_t n_vec, float* amax) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
+    const uint4 v = w[i];
+    const uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+    const uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+    m = max(m, max(a, b));
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t part[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) part[wid] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
+    atomicMax(reinterpret_cast<unsigned int*>(amax), r << 16);  // BF16 magnitude -> FP32 bits
+  }
+}
+
+// tscale = fl32(amax / 2688), IEEE round-to-nearest division.
+__global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, float* tscale) {
+  const float a = *amax;
+  *tscale = __fdiv_rn(a, 2688.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Quantize.
+// ---------------------------------------------------------------------------
+
+// A finite BF16 magnitude b (bits & 0x7FFF) as sig * 2^ex with an integer sig < 256.
+__device__ __forceinline__ void bf16_split(uint32_t b, uint32_t& sig, int& ex) {
+  const uint32_t f = b >> 7;
+  sig = (b & 0x7Fu) | (f ? 0x80u : 0u);
+  ex = (f ? (int)f : 1) - 134;
+}
+
+// E4M3 value of a code as sig * 2^ex (sig <= 15).
+__device__ __forceinline__ void e4m3_split(uint32_t c, uint32_t& sig, int& ex) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  sig = e ? (8u + m) : m;
+  ex = e ? (int)e - 10 : -9;
+}
+
+// Round a non-negative float to an E4M3 code (RNE), clamped to 0..126.  Used
+// only for a first guess from an approximate quotient; the caller corrects it.
+__device__ __forceinline__ uint32_t e4m3_code_guess(float r) {
+  if (!(r < 448.0f)) return 126u;
+  if (r < 0x1p-6f) return (uint32_t)__builtin_rintf(r * 512.0f);
+  uint32_t u = __float_as_uint(r);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+  return c > 126u ? 126u : c;
+}
+
+// The E4M3 code nearest to 448 * bam / amax (ties to the even code).
+// bam = sb * 2^eb, amax = sa * 2^ea.  With A = 448 sb 2^(eb-ea) and D = sa the
+// quotient is A / D; the comparisons A vs u * D against the midpoints u are
+// exact (u has <= 5 significant bits, D <= 8, A <= 17).
+__device__ __forceinline__ uint32_t e4m3_scale_code(uint32_t bam_b, uint32_t sa, int ea) {
+  if (bam_b == 0u) return 0u;
+  uint32_t sb;
+  int eb;
+  bf16_split(bam_b, sb, eb);
+  const float A = ldexpf((float)(448u * sb), eb - ea);
+  const float D = (float)sa;
+  uint32_t c = e4m3_code_guess(A * __builtin_amdgcn_rcpf(D));
+  if (c < 126u) {
+    const float rhs = 0.5f * (e4m3_to_f32(c) + e4m3_to_f32(c + 1u)) * D;
+    if ((c & 1u) ? (A >= rhs) : (A > rhs)) ++c;
+  }
+  if (c > 0u) {
+    const float rhs = 0.5f * (e4m3_to_f32(c - 1u) + e4m3_to_f32(c)) * D;
+    if (((c - 1u) & 1u) ? (A < rhs) : (A <= rhs)) --c;
+  }
+  return c;
+}
+
+// Per-block element thresholds.  With t_j = T_j / 4 the E2M1 midpoints
+// (T = 1, 3, 5, 7, 10, 14, 20), the element decision 2688 |w| vs t_j amax s
+// becomes  L = 21 |w| 2^(9 - ea - es)  vs  R_j = T_j sa ss  (2688 = 21 * 2^7).
+struct ElemThresholds {
+  float r[7];
+  int shift;  // 9 - ea - es
+};
+
+__device__ __forceinline__ ElemThresholds element_thresholds(uint32_t scode, uint32_t sa, int ea) {
+  ElemThresholds t;
+  uint32_t ss;
+  int es;
+  e4m3_split(scode, ss, es);
+  // scale 0: every magnitude is 0 (compare against +inf)
+  const float S = scode ? (float)(sa * ss) : __builtin_huge_valf();
+  t.r[0] = 1.0f * S;
+  t.r[1] = 3.0f * S;
+  t.r[2] = 5.0f * S;
+  t.r[3] = 7.0f * S;
+  t.r[4] = 10.0f * S;
+  t.r[5] = 14.0f * S;
+  t.r[6] = 20.0f * S;
+  t.shift = 9 - ea - es;
+  return t;
+}
+
+// 4-bit code of one BF16 element (bits in the low 16 bits of b).
+__device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThresholds& t) {
+  const float L = 21.0f * ldexpf(__uint_as_float((b & 0x7FFFu) << 16), t.shift);
+  uint32_t mag = (uint32_t)(L > t.r[0]) + (uint32_t)(L >= t.r[1]) + (uint32_t)(L > t.r[2]) +
+                 (uint32_t)(L >= t.r[3]) + (uint32_t)(L > t.r[4]) + (uint32_t)(L >= t.r[5]) +
+                 (uint32_t)(L > t.r[6]);
+  return mag | ((b >> 12) & 8u);
+}
+
+// One thread per 8 consecutive elements (a half block); lanes 2i and 2i+1 hold
+// the two halves of one 16-element block.  w is read as uint4 (8 BF16),
+// packed is written as one 32-bit word per thread, the scale byte by the even lane.
+__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
+                                                       const float* __restrict__ amax_p,
+                                                       uint32_t* __restrict__ packed,
+                                                       uint8_t* __restrict__ scales) {
+  const uint32_t amax_b = __float_as_uint(*amax_p) >> 16;  // amax is a BF16 value held in FP32
+  uint32_t sa;
+  int ea;
+  bf16_split(amax_b & 0x7FFFu, sa, ea);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even: keeps the lane pairing
+  // n_half is even (k % 16 == 0), so both lanes of a pair leave the loop together.
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    const uint4 v = w[h];
+    const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    uint32_t lm = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lm = max(lm, e[i] & 0x7FFFu);
+    const uint32_t pm = (uint32_t)__shfl_xor((int)lm, 1, 64);
+    const uint32_t bam = max(lm, pm);
+    const uint32_t scode = (amax_b & 0x7FFFu) ? e4m3_scale_code(bam, sa, ea) : 0u;
+    const ElemThresholds t = element_thresholds(scode, sa, ea);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
+    packed[h] = word;
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)scode;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: w = RNE_bf16(fl32(fl32(E2M1 * E4M3) * tscale)).  One thread per
+// 8 elements: one packed word in, one uint4 (8 BF16) out.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict__ packed,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ tscale_p, int64_t n_half,
+                                                      uint4* __restrict__ out) {
+  const float t = *tscale_p;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    const uint32_t p = packed[h];
+    const float s = e4m3_to_f32(scales[h >> 1]);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t c = (p >> (8 * j + 4 * q)) & 0xFu;
+        float v = e2m1_mag_to_f32(c & 7u) * s;  // exact
+        v = v * t;                              // one FP32 rounding
+        if (c & 8u) v = -v;
+        pair |= f32_to_bf16_rne(v) << (16 * q);
+      }
+      o[j] = pair;
+    }
+    out[h] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(int64_t items, int threads, int64_t max_blocks) {
+  int64_t b = (items + threads - 1) / threads;
+  if (b > max_blocks) b = max_blocks;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+void launch_fill_zero(float* p, hipStream_t s) { fill_zero_kernel<<<1, 64, 0, s>>>(p); }
+
+void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s) {
+  const int64_t n_vec = n_elems / 8;
+  amax_kernel<<<grid_for(n_vec, 256, 4096), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, amax);
+}
+
+void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s) {
+  finalize_tscale_kernel<<<1, 64, 0, s>>>(amax, tscale);
+}
+
+void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
+                     hipStream_t s) {
+  const int64_t n_half = n_elems / 8;
+  quantize_kernel<<<grid_for(n_half, 256, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_half, amax,
+                                                                  reinterpret_cast<uint32_t*>(packed), scales);
+}
+
+void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n_elems,
+                    uint16_t* out, hipStream_t s) {
+  const int64_t n_half = n_elems / 8;
+  dequant_kernel<<<grid_for(n_half, 256, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales,
+                                                                 tscale, n_half, reinterpret_cast<uint4*>(out));
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,100 @@
+"""Host-side checks of libnvfp4.so: it loads, exports every declared symbol, and
+validates arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from nvfp4_weight_only_amd import binding as B
+from nvfp4_weight_only_amd import build as BUILD
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.lib_path()):
+        BUILD.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], check=True, capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(L):
+    for code in range(7):
+        s = L.nvfp4_status_string(code).decode()
+        assert s.startswith("NVFP4_")
+    assert L.nvfp4_status_string(99).decode() == "NVFP4_ERR_UNKNOWN"
+    assert L.nvfp4_version().decode().startswith("nvfp4-mi355x")
+
+
+# Fake, never-dereferenced device addresses: validation fails before any HIP call.
+A = 0x10000000
+Bp = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+
+
+def test_linear_validation(L):
+    lin = L.nvfp4_linear
+    assert lin(None, 1, 64, 64, Bp, C, D, E, None) == B.ERR_NULL
+    assert lin(A, 1, 64, 24, Bp, C, D, E, None) == B.ERR_SHAPE          # k % 16 != 0
+    assert lin(A, 1, 0, 64, Bp, C, D, E, None) == B.ERR_SHAPE           # n <= 0
+    assert lin(A, -1, 64, 64, Bp, C, D, E, None) == B.ERR_SHAPE         # m < 0
+    assert lin(A, 1, 64, 2 ** 62, Bp, C, D, E, None) == B.ERR_SHAPE     # size overflow
+    assert lin(A + 8, 1, 64, 64, Bp, C, D, E, None) == B.ERR_ALIGN
+    assert lin(A, 1, 64, 64, Bp, C, D + 4, E, None) == B.ERR_ALIGN
+    assert lin(A, 4, 64, 64, Bp, C, D, A + 16, None) == B.ERR_ALIAS     # y overlaps x
+    assert lin(A, 4, 64, 64, Bp, C, D, C, None) == B.ERR_ALIAS          # y overlaps scales
+    assert lin(A, 0, 64, 64, Bp, C, D, E, None) == B.OK                 # m = 0 is a no-op
+    assert lin(None, 0, 64, 64, Bp, C, D, None, None) == B.OK           # ... even with empty x and y
+    assert lin(None, 0, 64, 64, None, C, D, None, None) == B.ERR_NULL
+    assert lin(None, 0, 64, 24, Bp, C, D, None, None) == B.ERR_SHAPE
+    assert L.nvfp4_linear_forced(7, A, 1, 64, 64, Bp, C, D, E, None) == B.ERR_UNSUPPORTED
+    assert L.nvfp4_linear_forced(2, A, 1, 64, 24, Bp, C, D, E, None) == B.ERR_SHAPE
+
+
+def test_quantize_validation(L):
+    q = L.nvfp4_quantize
+    assert q(None, 4, 64, Bp, C, D, None) == B.ERR_NULL
+    assert q(A, 4, 40, Bp, C, D, None) == B.ERR_SHAPE
+    assert q(A, 0, 64, Bp, C, D, None) == B.ERR_SHAPE
+    assert q(A, 4, 64, Bp + 1, C, D, None) == B.ERR_ALIGN
+    assert q(A, 4, 64, A + 64, C, D, None) == B.ERR_ALIAS               # packed overlaps w (512 bytes)
+    assert q(A, 4, 64, Bp, Bp + 64, D, None) == B.ERR_ALIAS             # scales overlaps packed (128 bytes)
+    assert q(A, 4, 64, Bp, C, C, None) == B.ERR_ALIAS                   # tscale overlaps scales
+    qa = L.nvfp4_quantize_with_amax
+    assert qa(A, 4, 64, None, Bp, C, D, None) == B.ERR_NULL
+    assert qa(A, 4, 64, E + 4, Bp, C, D, None) == B.ERR_ALIGN
+    assert qa(A, 4, 64, D, Bp, C, D, None) == B.ERR_ALIAS               # amax overlaps tscale
+    am = L.nvfp4_amax_accumulate
+    assert am(A, 4, 64, None, None) == B.ERR_NULL
+    assert am(A, 4, 48 + 1, E, None) == B.ERR_SHAPE
+    assert am(A, 4, 64, A + 32, None) == B.ERR_ALIAS
+
+
+def test_dequant_validation(L):
+    dq = L.nvfp4_dequant
+    assert dq(None, C, D, 4, 64, E, None) == B.ERR_NULL
+    assert dq(A, C, D, 4, 8, E, None) == B.ERR_SHAPE
+    assert dq(A, C, D, 4, 64, E + 2, None) == B.ERR_ALIGN
+    assert dq(A, C, D, 4, 64, A, None) == B.ERR_ALIAS

@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Quantize and dequant must match bit for bit; the linear must satisfy
+|y - y_ref| <= 2e-3 * sum_k |x * w_hat| per output element (y_ref exact in
+float64).  Small and ragged shapes are checked in full; the full-size
+workloads are checked on sampled weight rows / output columns, in the launch
+configuration the benchmark times (auto dispatch).
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as O
+from nvfp4_weight_only_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["gemv", "small_m", "prefill"]
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def nv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_weight_only_amd as nv
+    nv.lib()   # fails loudly when the library is missing
+    return nv
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def bf16_host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def u8_host(t):
+    return t.cpu().numpy()
+
+
+def sample_rows(n, count, seed=123):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, size=min(count, n), replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(rows))
+
+
+def check_linear(y_bits, y_ref, bound, what):
+    y = WL.f32_from_bf16_bits(y_bits).astype(np.float64)
+    bad = O.linear_violations(y, y_ref, bound)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(bound > 0, np.abs(y - y_ref) / bound, 0.0)
+    log(f"{what}: max |y-y_ref|/B = {rel.max():.3e}, median {np.median(rel):.3e}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs outside 2e-3*B (max rel {rel.max():.3e})"
+    return rel
+
+
+# ---------------------------------------------------------------------------
+# Quantize / dequant, small and ragged shapes, bit-exact.
+# ---------------------------------------------------------------------------
+SMALL_WEIGHTS = [
+    ("tiny 256x512", lambda: WL.weight_plain(256, 512)),
+    ("ragged 300x1040", lambda: WL.normal_bf16((300, 1040), 0.02, 5)),   # k % 32 == 16
+    ("ragged 77x48", lambda: WL.normal_bf16((77, 48), 0.02, 6)),
+    ("one block 1x16", lambda: WL.normal_bf16((1, 16), 0.02, 7)),
+    ("outliers 64x5120", lambda: WL.weight_with_outlier_columns(64, 5120)),
+    ("wide range 33x272", lambda: WL.bf16_bits_from_f32(
+        (np.random.default_rng(8).standard_normal((33, 272)) *
+         np.exp(np.random.default_rng(9).uniform(-30, 30, (33, 272)))).astype(np.float32))),
+]
+
+
+def crafted_weights():
+    """Ties on every E2M1 and E4M3 midpoint, zeros, -0, BF16 subnormals, huge values."""
+    row = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, -0.0]
+    row2 = [3.0, 0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5, 0.0, -0.0, 1e-30, -1e-30, 2.0, 0.1, 0.2, 0.3]
+    e4 = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = (e4[:-1] + e4[1:]) / 2
+    blocks = []
+    for u in mids:
+        blk = [0.0] * 16
+        blk[3] = u
+        blk[9] = -u / 3
+        blocks.append(blk)
+    cases = {
+        "e2m1 ties": [row + row2],
+        "e4m3 ties": [sum(blocks[i:i + 2], []) + [448.0] + [0.0] * 15 for i in range(0, 126, 2)],
+        "zeros": [[0.0] * 31 + [-0.0]],
+        "single": [[0.0] * 7 + [-0.0371] + [0.0] * 24],
+        "subnormal amax": [[1e-40, -2e-39, 3e-41, 0.0] * 8],
+        "huge": [[3.0e38, -1.0e38, 1.0, -1e-30] * 8],
+        "far blocks": [[100.0] + [0.0] * 15 + [1e-3] + [0.0] * 15 + [1e-7] + [0.0] * 15],
+    }
+    return {k: WL.bf16_bits_from_f32(np.array(v, dtype=np.float32)) for k, v in cases.items()}
+
+
+def _quant_compare(nv, w_bits, what):
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w_bits))
+    rp, rs, rt = O.quantize(w_bits)
+    gp, gs, gt = u8_host(packed), u8_host(scales), tscale.cpu().numpy()[0]
+    assert gt.view(np.uint32) == np.float32(rt).view(np.uint32), f"{what}: tscale {gt} vs {rt}"
+    assert np.array_equal(gs, rs), f"{what}: {int((gs != rs).sum())} scale codes differ"
+    assert np.array_equal(gp, rp), f"{what}: {int((gp != rp).sum())} packed bytes differ"
+    dq = bf16_host(nv.dequant(packed, scales, tscale))
+    assert np.array_equal(dq, O.dequant(rp, rs, rt)), f"{what}: dequant differs"
+    return packed, scales, tscale
+
+
+@pytest.mark.parametrize("name,make", SMALL_WEIGHTS, ids=[s[0] for s in SMALL_WEIGHTS])
+def test_quantize_dequant_bit_exact_small(nv, name, make):
+    log(f"quantize/dequant {name}")
+    _quant_compare(nv, make(), name)
+
+
+def test_quantize_dequant_bit_exact_crafted(nv):
+    for name, w in crafted_weights().items():
+        log(f"quantize/dequant crafted: {name}")
+        _quant_compare(nv, w, name)
+
+
+# ---------------------------------------------------------------------------
+# Full-size weights: exact on sampled rows (the quantizer is row-local once amax is known).
+# ---------------------------------------------------------------------------
+FULL = ["decode", "gate_up", "small_m_up", "small_m_down"]
+
+
+@pytest.mark.parametrize("wname", FULL)
+def test_quantize_dequant_bit_exact_full_size(nv, wname):
+    wl = WL.WORKLOADS[wname]
+    log(f"full-size quantize {wname}: {wl.n}x{wl.k}")
+    w = wl.weight()
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
+    amax = O.tensor_amax(w)
+    assert tscale.cpu().numpy()[0].view(np.uint32) == O.tensor_scale(amax).view(np.uint32)
+    rows = sample_rows(wl.n, 96)
+    rp, rs, rt = O.quantize(w[rows], amax=amax)
+    rows_t = torch.from_numpy(rows).cuda()
+    gp = u8_host(packed.index_select(0, rows_t))
+    gs = u8_host(scales.index_select(0, rows_t))
+    assert np.array_equal(gs, rs), f"{int((gs != rs).sum())} scale codes differ"
+    assert np.array_equal(gp, rp), f"{int((gp != rp).sum())} packed bytes differ"
+    dq = nv.dequant(packed, scales, tscale)
+    assert np.array_equal(bf16_host(dq.index_select(0, rows_t)), O.dequant(rp, rs, rt))
+
+
+def test_gate_up_shared_scale(nv):
+    """Members quantized separately against a shared amax equal the merged quantization."""
+    wl = WL.WORKLOADS["gate_up"]
+    gate, up, ratio = WL.weight_gate_up(wl.n // 2, wl.k)
+    log(f"gate/up amax ratio {ratio:.4f}")
+    merged = nv.quantize(to_dev_bf16(np.concatenate([gate, up])))
+    (pg, sg), (pu, su) = nv.quantize_shared([to_dev_bf16(gate), to_dev_bf16(up)])[0]
+    _, ts = nv.quantize_shared([to_dev_bf16(gate), to_dev_bf16(up)])
+    assert torch.equal(torch.cat([pg, pu]), merged[0])
+    assert torch.equal(torch.cat([sg, su]), merged[1])
+    assert torch.equal(ts, merged[2])
+    # Wrong-scale failure mode: U decoded against its own tensor scale.
+    own = nv.quantize(to_dev_bf16(up))[2]
+    x = WL.activations(1, wl.k)
+    y_right = bf16_host(nv.linear(to_dev_bf16(x), pu, su, ts))
+    y_wrong = bf16_host(nv.linear(to_dev_bf16(x), pu, su, own))
+    rows = sample_rows(wl.n // 2, 64)
+    y_ref, bound = O.linear_ref(x, u8_host(pu)[rows], u8_host(su)[rows], ts.cpu().numpy()[0])
+    check_linear(y_right[:, rows], y_ref, bound, "gate/up shared scale (up rows)")
+    # U's own scale is smaller by the amax spread: outputs shrink by that factor, and every output
+    # whose |y| is not tiny against its bound falls outside the tolerance.
+    yw = WL.f32_from_bf16_bits(y_wrong[:, rows]).astype(np.float64)
+    bad = O.linear_violations(yw, y_ref, bound)
+    big = np.abs(y_ref) > 0.01 * bound
+    assert big.sum() > 20 and bad[big].all()
+    shrink = np.median(np.abs(y_ref[big]) / np.abs(yw[big]))
+    assert abs(shrink - ratio) / ratio < 0.02, shrink
+
+
+# ---------------------------------------------------------------------------
+# Linear: every kernel on small / ragged shapes, in full.
+# ---------------------------------------------------------------------------
+LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 64, 5120), (33, 200, 512),
+              (100, 300, 1040), (130, 257, 2064), (1, 1, 16), (5, 3, 16)]
+
+
+@pytest.mark.parametrize("m,n,k", LIN_SHAPES)
+def test_linear_all_kernels_small(nv, m, n, k):
+    w = WL.normal_bf16((n, k), 0.02, 100 + n)
+    x = WL.normal_bf16((m, k), 1.0, 200 + m)
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
+    y_ref, bound = O.linear_ref(x, u8_host(packed), u8_host(scales), tscale.cpu().numpy()[0])
+    xd = to_dev_bf16(x)
+    outs = {}
+    for kern in ["auto"] + KERNELS:
+        y = bf16_host(nv.linear(xd, packed, scales, tscale, kernel=kern))
+        check_linear(y, y_ref, bound, f"linear {kern} m={m} n={n} k={k}")
+        outs[kern] = y
+    # Deterministic: a second call is bitwise identical.
+    for kern in KERNELS:
+        assert np.array_equal(bf16_host(nv.linear(xd, packed, scales, tscale, kernel=kern)), outs[kern])
+
+
+def test_linear_edge_cases(nv):
+    # m = 0: a no-op
+    packed, scales, tscale = nv.quantize(to_dev_bf16(WL.normal_bf16((64, 64), 0.02, 1)))
+    y = nv.linear(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), packed, scales, tscale)
+    assert y.shape == (0, 64)
+    # zero weights and zero activations give exact zeros
+    zw = nv.quantize(torch.zeros((48, 96), dtype=torch.bfloat16, device="cuda"))
+    x = to_dev_bf16(WL.normal_bf16((5, 96), 1.0, 2))
+    rw = nv.quantize(to_dev_bf16(WL.normal_bf16((48, 96), 0.02, 4)))
+    for kern in KERNELS:
+        assert torch.count_nonzero(nv.linear(x, *zw, kernel=kern)) == 0
+        assert torch.count_nonzero(nv.linear(torch.zeros_like(x), *rw, kernel=kern)) == 0
+    # crafted weights through every kernel
+    for name, w in crafted_weights().items():
+        if name in ("huge", "subnormal amax"):
+            continue   # outputs overflow / underflow BF16 by construction
+        q = nv.quantize(to_dev_bf16(w))
+        x = WL.normal_bf16((3, w.shape[1]), 1.0, 3)
+        y_ref, bound = O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])
+        for kern in KERNELS:
+            check_linear(bf16_host(nv.linear(to_dev_bf16(x), *q, kernel=kern)), y_ref, bound, f"crafted {name} {kern}")
+
+
+# ---------------------------------------------------------------------------
+# Linear at full size, auto dispatch, sampled output columns.
+# ---------------------------------------------------------------------------
+FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8),
+               ("small_m_down", 32), ("prefill", 512), ("prefill", 2048)]
+
+_weights_cache = {}
+
+
+def _quantized(nv, wname):
+    if wname not in _weights_cache:
+        _weights_cache.clear()
+        w = WL.WORKLOADS["small_m_up" if wname == "prefill" else wname].weight()
+        _weights_cache[wname] = nv.quantize(to_dev_bf16(w))
+    return _weights_cache[wname]
+
+
+@pytest.mark.parametrize("wname,m", FULL_LINEAR, ids=[f"{a}-m{b}" for a, b in FULL_LINEAR])
+def test_linear_full_size_sampled(nv, wname, m):
+    wl = WL.WORKLOADS[wname]
+    log(f"full-size linear {wname} m={m} n={wl.n} k={wl.k}")
+    packed, scales, tscale = _quantized(nv, wname)
+    x = WL.activations(m, wl.k)
+    xd = to_dev_bf16(x)
+    y = nv.linear(xd, packed, scales, tscale)
+    y2 = nv.linear(xd, packed, scales, tscale)
+    assert torch.equal(y, y2), "not deterministic"
+    cols = sample_rows(wl.n, 64)
+    cols_t = torch.from_numpy(cols).cuda()
+    y_ref, bound = O.linear_ref(x, u8_host(packed.index_select(0, cols_t)), u8_host(scales.index_select(0, cols_t)),
+                                tscale.cpu().numpy()[0])
+    check_linear(bf16_host(y)[:, cols], y_ref, bound, f"{wname} m={m}")
