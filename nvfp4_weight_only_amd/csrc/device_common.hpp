@@ -109,6 +109,23 @@ __device__ __forceinline__ uint4 e2m1x8_scaled_to_bf16(uint32_t p, float s) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Unscaled decode with the gfx950 conversion instruction: byte `SEL` of `p`
+// (elements 2*SEL, 2*SEL+1) -> one BF16 pair in natural order.  The
+// instruction multiplies by 2^exponent(scale) only, so a scale of 1.0 gives the
+// exact E2M1 values (including -0 for code 8).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t p) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p, 1.0f, SEL));
+}
+
+// Two E4M3 (OCP E4M3FN) bytes -> two floats with the gfx950 FP8 conversion:
+// bytes 0 and 1 of `v` when HI is false, bytes 2 and 3 when HI is true.
+template <bool HI>
+__device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t v) {
+  const auto r = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, HI);
+  return make_float2(r[0], r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Dot products and wave reductions.
 // ---------------------------------------------------------------------------
@@ -120,6 +137,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 

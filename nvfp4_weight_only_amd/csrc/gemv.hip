@@ -2,16 +2,18 @@
 //
 // The engine's decode linear is a bandwidth-bound GEMV over packed NVFP4
 // weights (imp "docs/quantization.md", NVFP4 kernel pipeline: a GEMV with a
-// byte-permute register lookup table, split along K).  Here:
-//   - each wavefront owns RPW weight rows and streams them with 16-byte loads
-//     (32 elements = two 16-element blocks per lane per row);
-//   - the activation row is staged once per workgroup in LDS, pre-permuted so
-//     that v_perm_b32 decodes of the packed nibbles pair up with it directly;
-//   - nibbles are decoded with v_perm_b32 lookups into unscaled BF16 E2M1
-//     values and multiplied with v_dot2_f32_bf16 (FP32 accumulate); the E4M3
-//     block scale is applied once per 16 elements with an FMA, the tensor
-//     scale once per output in the epilogue;
-//   - the per-lane partial sums are reduced across the wavefront with shuffles.
+// register lookup table, split along K).  Design for CDNA4:
+//   - each wavefront owns R weight rows and splits K across its 64 lanes in
+//     16-byte units (32 elements = two 16-element blocks);
+//   - every lane issues all of its weight and scale loads for a batch of JB
+//     units before computing, so a whole launch keeps the weights in flight;
+//   - the activations for the lane's units are read straight into registers and
+//     reused for the R rows (no LDS, no barrier);
+//   - nibbles become BF16 pairs with one v_cvt_scalef32_pk_bf16_fp4 per byte
+//     (scale 1.0: exact E2M1 values), products accumulate with
+//     v_dot2_f32_bf16 in FP32; the E4M3 block scale is one FMA per 16
+//     elements and the tensor scale one multiply per output;
+//   - partial sums are reduced across the wavefront with shuffles.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -19,104 +21,255 @@ namespace nvfp4 {
 
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int64_t kGemvChunk = 16384;  // K elements of the activation row staged in LDS at a time (32 KiB)
 
-// UB = 16-element blocks per lane unit: 2 (16-byte loads, needs k % 32 == 0) or 1 (8-byte loads).
-template <int RPW, int UB>
-__global__ void __launch_bounds__(kGemvThreads) gemv_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t k,
+// Dot product of one packed word (8 elements, natural order) with 8 activations.
+__device__ __forceinline__ float dot8(uint32_t w, uint4 xq, float acc) {
+  acc = dot2_bf16(e2m1x2_to_bf16<0>(w), xq.x, acc);
+  acc = dot2_bf16(e2m1x2_to_bf16<1>(w), xq.y, acc);
+  acc = dot2_bf16(e2m1x2_to_bf16<2>(w), xq.z, acc);
+  acc = dot2_bf16(e2m1x2_to_bf16<3>(w), xq.w, acc);
+  return acc;
+}
+
+// R rows per wavefront; JB units per lane per batch; UB = 16-element blocks per
+// unit: 2 (16-byte loads, k % 32 == 0) or 1 (8-byte loads).
+template <int R, int JB, int UB>
+__global__ void __launch_bounds__(kGemvThreads) gemv_loop_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t k,
                                                             const uint8_t* __restrict__ packed,
                                                             const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ tscale_p,
                                                             uint16_t* __restrict__ y) {
-  __shared__ uint4 xs[kGemvChunk / 8];  // permuted activations, 8 per uint4
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t mrow = blockIdx.y;
-  const uint16_t* xr = x + mrow * k;
-  const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wid) * RPW;
-  const int64_t kblocks = k >> 4;
-  const int64_t pstride = k >> 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6)) * R;
+  if (row0 >= n) return;  // uniform per wavefront
+  const uint16_t* xr = x + (int64_t)blockIdx.y * k;
+  const int64_t units = k / (16 * UB);
+  const int64_t kblocks = k >> 4, pstride = k >> 1;
 
-  float acc[RPW];
+  float acc[R];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < k; k0 += kGemvChunk) {
-    const int64_t kc = (k - k0) < kGemvChunk ? (k - k0) : kGemvChunk;  // multiple of 16
-    __syncthreads();
-    for (int64_t g = threadIdx.x; g < (kc >> 3); g += kGemvThreads)
-      xs[g] = bf16x8_interleave(*reinterpret_cast<const uint4*>(xr + k0 + 8 * g));
-    __syncthreads();
-
-    const int64_t units = kc / (16 * UB);
-    for (int64_t u = lane; u < units; u += 64) {
-      uint4 xq[2 * UB];
+  for (int64_t u0 = 0; u0 < units; u0 += 64 * JB) {
+    uint32_t wv[JB][R][2 * UB];
+    uint32_t sv[JB][R];
+    uint4 xv[JB][2 * UB];
+    // Weights and scales first: they come from HBM.
 #pragma unroll
-      for (int q = 0; q < 2 * UB; ++q) xq[q] = xs[u * 2 * UB + q];
-      const int64_t blk = (k0 >> 4) + u * UB;  // first block of the unit within the row
+    for (int j = 0; j < JB; ++j) {
+      const int64_t u = u0 + 64 * j + lane;
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
+      for (int r = 0; r < R; ++r) {
         const int64_t row = row0 + r;
-        if (row < n) {
-          const uint8_t* prow = packed + row * pstride + blk * 8;
-          const uint8_t* srow = scales + row * kblocks + blk;
+        if (u < units && row < n) {
+          const uint8_t* pp = packed + row * pstride + u * 8 * UB;
+          const uint8_t* sp = scales + row * kblocks + u * UB;
           if constexpr (UB == 2) {
-            const uint4 pk = *reinterpret_cast<const uint4*>(prow);
-            const uint32_t sc = *reinterpret_cast<const uint16_t*>(srow);
-            float p0 = 0.0f, p1 = 0.0f;
-            uint4 d;
-            d = e2m1x8_to_bf16_interleaved(pk.x);
-            p0 = dot2_bf16(d.x, xq[0].x, p0); p0 = dot2_bf16(d.y, xq[0].y, p0);
-            p0 = dot2_bf16(d.z, xq[0].z, p0); p0 = dot2_bf16(d.w, xq[0].w, p0);
-            d = e2m1x8_to_bf16_interleaved(pk.y);
-            p0 = dot2_bf16(d.x, xq[1].x, p0); p0 = dot2_bf16(d.y, xq[1].y, p0);
-            p0 = dot2_bf16(d.z, xq[1].z, p0); p0 = dot2_bf16(d.w, xq[1].w, p0);
-            d = e2m1x8_to_bf16_interleaved(pk.z);
-            p1 = dot2_bf16(d.x, xq[2].x, p1); p1 = dot2_bf16(d.y, xq[2].y, p1);
-            p1 = dot2_bf16(d.z, xq[2].z, p1); p1 = dot2_bf16(d.w, xq[2].w, p1);
-            d = e2m1x8_to_bf16_interleaved(pk.w);
-            p1 = dot2_bf16(d.x, xq[3].x, p1); p1 = dot2_bf16(d.y, xq[3].y, p1);
-            p1 = dot2_bf16(d.z, xq[3].z, p1); p1 = dot2_bf16(d.w, xq[3].w, p1);
-            acc[r] = fmaf(p0, e4m3_to_f32(sc & 0xFFu), acc[r]);
-            acc[r] = fmaf(p1, e4m3_to_f32(sc >> 8), acc[r]);
+            const uint4 v = *reinterpret_cast<const uint4*>(pp);
+            wv[j][r][0] = v.x; wv[j][r][1] = v.y; wv[j][r][2] = v.z; wv[j][r][3] = v.w;
+            sv[j][r] = *reinterpret_cast<const uint16_t*>(sp);
           } else {
-            const uint2 pk = *reinterpret_cast<const uint2*>(prow);
-            const uint32_t sc = *srow;
-            float p0 = 0.0f;
-            uint4 d;
-            d = e2m1x8_to_bf16_interleaved(pk.x);
-            p0 = dot2_bf16(d.x, xq[0].x, p0); p0 = dot2_bf16(d.y, xq[0].y, p0);
-            p0 = dot2_bf16(d.z, xq[0].z, p0); p0 = dot2_bf16(d.w, xq[0].w, p0);
-            d = e2m1x8_to_bf16_interleaved(pk.y);
-            p0 = dot2_bf16(d.x, xq[1].x, p0); p0 = dot2_bf16(d.y, xq[1].y, p0);
-            p0 = dot2_bf16(d.z, xq[1].z, p0); p0 = dot2_bf16(d.w, xq[1].w, p0);
-            acc[r] = fmaf(p0, e4m3_to_f32(sc), acc[r]);
+            const uint2 v = *reinterpret_cast<const uint2*>(pp);
+            wv[j][r][0] = v.x; wv[j][r][1] = v.y;
+            sv[j][r] = *sp;
           }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2 * UB; ++q) wv[j][r][q] = 0u;
+          sv[j][r] = 0u;
         }
       }
+    }
+    // Activations (shared by every wavefront: L2/L1 resident).
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int64_t u = u0 + 64 * j + lane;
+#pragma unroll
+      for (int q = 0; q < 2 * UB; ++q)
+        xv[j][q] = (u < units) ? *reinterpret_cast<const uint4*>(xr + u * 16 * UB + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < UB; ++b) {
+          float p = dot8(wv[j][r][2 * b], xv[j][2 * b], 0.0f);
+          p = dot8(wv[j][r][2 * b + 1], xv[j][2 * b + 1], p);
+          acc[r] = fmaf(p, e4m3_to_f32((sv[j][r] >> (8 * b)) & 0xFFu), acc[r]);
+        }
+  }
+
+  const float t = *tscale_p;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum(acc[r]);
+    const int64_t row = row0 + r;
+    if (lane == 0 && row < n) y[(int64_t)blockIdx.y * n + row] = (uint16_t)f32_to_bf16_rne(v * t);
+  }
+}
+
+template <int R, int JB>
+static void launch_rj(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                      const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  const unsigned gx = (unsigned)((n + kGemvWaves * R - 1) / (kGemvWaves * R));
+  const int64_t max_y = 65535;  // gridDim.y limit: activation rows go in slices
+  for (int64_t m0 = 0; m0 < m; m0 += max_y) {
+    const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
+    if ((k & 31) == 0)
+      gemv_loop_kernel<R, JB, 2><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
+    else
+      gemv_loop_kernel<R, JB, 1><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
+  }
+}
+
+// GEMV with the activation row staged in LDS (k % 32 == 0, k <= kLdsMaxK).
+// Reading a small activation vector from every wavefront through the vector
+// memory path makes a few L2 lines the hottest spot of the chip, so each
+// workgroup of W wavefronts stages it once: every thread issues its share of
+// activation loads, then all of its weight and scale loads, then writes the
+// activations to LDS and meets the barrier (which waits only for LDS writes:
+// the weight loads stay in flight).  Units are then consumed in issue order.
+// LDS holds the activations quad-major (quad q of unit u at q * units + u), so
+// lanes reading consecutive units touch consecutive banks.
+constexpr int64_t kLdsMaxK = 16384;
+
+template <int LPR, int R, int JB, int W, bool RAGGED>
+__global__ void __launch_bounds__(64 * W) gemv_lds_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t k,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ tscale_p,
+                                                          uint16_t* __restrict__ y) {
+  constexpr int SUB = 64 / LPR;
+  constexpr int RPW = R * SUB;
+  constexpr int NT = 64 * W;
+  __shared__ uint4 xs[kLdsMaxK / 8];
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR, ul = lane % LPR;
+  const int units = (int)(k >> 5);
+  const int64_t wrow0 = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * RPW;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * k);
+  auto has = [&](int j) { return !RAGGED || ul + j * LPR < units; };
+
+  // 1. activation loads (this thread's share of the k/8 uint4 of the row)
+  constexpr int XPT = kLdsMaxK / 8 / NT + 1;  // upper bound of uint4 per thread
+  uint4 xl[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int g = threadIdx.x + i * NT;
+    xl[i] = g < (int)(k >> 3) ? xr[g] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // 2. weight and scale loads
+  uint4 wv[JB][R];
+  uint32_t sv[JB][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = wrow0 + r * SUB + sub;
+    const bool ok = row < n;
+    const uint8_t* pb = packed + row * (k >> 1) + ul * 16;
+    const uint8_t* sb = scales + row * (k >> 4) + ul * 2;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const bool okj = ok && has(j);
+      wv[j][r] = okj ? *reinterpret_cast<const uint4*>(pb + j * LPR * 16) : make_uint4(0u, 0u, 0u, 0u);
+      sv[j][r] = okj ? *reinterpret_cast<const uint16_t*>(sb + j * LPR * 2) : 0u;
+    }
+  }
+  // 3. activations to LDS, quad-major
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int g = threadIdx.x + i * NT;
+    if (g < (int)(k >> 3)) xs[(g & 3) * units + (g >> 2)] = xl[i];
+  }
+  __syncthreads();
+  if (wrow0 >= n) return;  // after the barrier: uniform per wavefront
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    if (!has(j)) continue;
+    const int u = ul + j * LPR;
+    const uint4 x0 = xs[u], x1 = xs[units + u], x2 = xs[2 * units + u], x3 = xs[3 * units + u];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float2 s = e4m3x2_to_f32<false>(sv[j][r]);
+      float p0 = dot8(wv[j][r].x, x0, 0.0f);
+      p0 = dot8(wv[j][r].y, x1, p0);
+      float p1 = dot8(wv[j][r].z, x2, 0.0f);
+      p1 = dot8(wv[j][r].w, x3, p1);
+      acc[r] = fmaf(p0, s.x, acc[r]);
+      acc[r] = fmaf(p1, s.y, acc[r]);
     }
   }
 
   const float t = *tscale_p;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float v = wave_sum(acc[r]);
-    const int64_t row = row0 + r;
-    if (lane == 0 && row < n) y[mrow * n + row] = (uint16_t)f32_to_bf16_rne(v * t);
+  for (int r = 0; r < R; ++r) {
+    const float v = group_sum<LPR>(acc[r]);
+    const int64_t row = wrow0 + r * SUB + sub;
+    if (ul == 0 && row < n) y[(int64_t)blockIdx.y * n + row] = (uint16_t)f32_to_bf16_rne(v * t);
   }
+}
+
+template <int LPR, int R, int JB, int W, bool RAGGED = false>
+static void launch_lds(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                       const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  constexpr int64_t rows_per_block = (int64_t)W * R * (64 / LPR);
+  const unsigned gx = (unsigned)((n + rows_per_block - 1) / rows_per_block);
+  const int64_t max_y = 65535;
+  for (int64_t m0 = 0; m0 < m; m0 += max_y) {
+    const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
+    gemv_lds_kernel<LPR, R, JB, W, RAGGED><<<dim3(gx, gy), 64 * W, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale,
+                                                                          y + m0 * n);
+  }
+}
+
+// Dispatch for the LDS kernel: 32 lanes per row when k / 32 splits evenly into
+// at most 8 units per lane, else 64 lanes per row with a ragged last unit.
+// Rows per workgroup: 20 (10 wavefronts x 2 rows) for moderate n, so that a
+// 5120-row weight maps onto exactly one workgroup per CU; 32 (8 x 2 x 2) for large n.
+template <int LPR, int JB, bool RAGGED>
+static void launch_lds_for_n(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                             const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  if (n >= 16384)
+    launch_lds<LPR, 2, JB, 8, RAGGED>(x, m, n, k, packed, scales, tscale, y, s);
+  else
+    launch_lds<LPR, 1, JB, 10, RAGGED>(x, m, n, k, packed, scales, tscale, y, s);
 }
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                  const float* tscale, uint16_t* y, hipStream_t s) {
-  constexpr int RPW = 4;
-  const unsigned gx = (unsigned)((n + kGemvWaves * RPW - 1) / (kGemvWaves * RPW));
-  const int64_t max_y = 65535;  // gridDim.y limit: activation rows go in slices
-  for (int64_t m0 = 0; m0 < m; m0 += max_y) {
-    const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
-    if ((k & 31) == 0)
-      gemv_kernel<RPW, 2><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
-    else
-      gemv_kernel<RPW, 1><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
+  const int64_t units = k >> 5;
+  if ((k & 31) == 0 && k <= kLdsMaxK) {
+    if (units == 160 && n >= 16384)
+      return launch_lds<64, 2, 3, 8, true>(x, m, n, k, packed, scales, tscale, y, s);
+    if (units % 32 == 0) {
+      switch (units / 32) {
+        case 1: return launch_lds_for_n<32, 1, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 2: return launch_lds_for_n<32, 2, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 3: return launch_lds_for_n<32, 3, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 4: return launch_lds_for_n<32, 4, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 5: return launch_lds_for_n<32, 5, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 6: return launch_lds_for_n<32, 6, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 7: return launch_lds_for_n<32, 7, false>(x, m, n, k, packed, scales, tscale, y, s);
+        case 8: return launch_lds_for_n<32, 8, false>(x, m, n, k, packed, scales, tscale, y, s);
+        default: break;
+      }
+    } else if (units < 32) {
+      return launch_lds_for_n<16, 2, true>(x, m, n, k, packed, scales, tscale, y, s);
+    } else {
+      switch ((units + 63) / 64) {
+        case 1: return launch_lds_for_n<64, 1, true>(x, m, n, k, packed, scales, tscale, y, s);
+        case 2: return launch_lds_for_n<64, 2, true>(x, m, n, k, packed, scales, tscale, y, s);
+        case 3: return launch_lds_for_n<64, 3, true>(x, m, n, k, packed, scales, tscale, y, s);
+        case 4: return launch_lds_for_n<64, 4, true>(x, m, n, k, packed, scales, tscale, y, s);
+        default: break;
+      }
+    }
   }
+  launch_rj<2, 1>(x, m, n, k, packed, scales, tscale, y, s);
 }
 
 }  // namespace nvfp4

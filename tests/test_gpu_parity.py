@@ -182,7 +182,10 @@ def test_gate_up_shared_scale(nv):
 # Linear: every kernel on small / ragged shapes, in full.
 # ---------------------------------------------------------------------------
 LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 64, 5120), (33, 200, 512),
-              (100, 300, 1040), (130, 257, 2064), (1, 1, 16), (5, 3, 16)]
+              (100, 300, 1040), (130, 257, 2064), (1, 1, 16), (5, 3, 16),
+              # GEMV dispatch branches: 32 lanes/row (k = 1024, 3072), ragged 64 lanes/row (k = 4608),
+              # the large-n tiling (n >= 16384), and k beyond the LDS-staged range (k = 17408)
+              (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (1, 40, 17408)]
 
 
 @pytest.mark.parametrize("m,n,k", LIN_SHAPES)

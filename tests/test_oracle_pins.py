@@ -371,9 +371,24 @@ def test_invalid_inputs_rejected():
 def test_linear_tolerance_gate():
     y_ref = np.array([[1.0, -2.0, 0.0]])
     bound = np.array([[10.0, 10.0, 0.0]])
-    assert not O.linear_violations(np.array([[1.019, -2.0, 0.0]]), y_ref, bound).any()
-    assert O.linear_violations(np.array([[1.021, -2.0, 0.0]]), y_ref, bound).tolist() == [[True, False, False]]
+    # accumulation allowance 2e-3 * 10 = 0.02, plus 2^-8 * (|y_ref| + 0.02) for the BF16 output rounding
+    allow = 0.02 + 2.0 ** -8 * (1.0 + 0.02)
+    assert not O.linear_violations(np.array([[1.0 + 0.999 * allow, -2.0, 0.0]]), y_ref, bound).any()
+    assert O.linear_violations(np.array([[1.0 + 1.001 * allow, -2.0, 0.0]]), y_ref, bound).tolist() == [[True, False, False]]
     assert O.linear_violations(np.array([[1.0, -2.0, 1e-30]]), y_ref, bound).tolist() == [[False, False, True]]
+
+
+def test_exact_sum_rounded_to_bf16_always_passes():
+    """A perfect implementation (exact sum, then RNE to BF16) passes even when one term dominates."""
+    rng = np.random.default_rng(11)
+    y_ref = rng.standard_normal((4, 4096)) * np.exp(rng.uniform(-20, 20, (4, 4096)))
+    bound = np.abs(y_ref) * rng.uniform(1.0, 1.001, y_ref.shape)      # |y| ~ bound: no cancellation
+    y_bf16 = WL.f32_from_bf16_bits(WL.bf16_bits_from_f32(y_ref.astype(np.float32))).astype(np.float64)
+    assert np.abs(y_bf16 - y_ref).max() > 0  # the rounding is visible
+    assert not O.linear_violations(y_bf16, y_ref, bound).any()
+    # ...while two BF16 ulps away fails when |y| ~ bound
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(y_ref))) - 7)
+    assert O.linear_violations(y_ref + 2 * ulp * np.sign(y_ref), y_ref, bound).all()
 
 
 # --------------------------------------------------------------------------
