@@ -118,6 +118,23 @@ __device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t p) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(p, 1.0f, SEL));
 }
 
+// Scaled decode with the conversion instruction: byte SEL of `p` (elements
+// 2*SEL, 2*SEL+1) times the E4M3 block scale `s`, as one BF16 pair in natural
+// order.  The FP4 -> FP32 conversion at scale 1.0 gives the exact E2M1 values;
+// E2M1 * E4M3 has at most 6 significant bits, so the FP32 products are exact
+// and their high halves are the exact BF16 values (signs and -0 included).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_to_bf16(uint32_t p, float s) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, SEL);
+  return __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
+}
+
+// Eight elements of `p` times `s` as four natural-order BF16 pairs.
+__device__ __forceinline__ uint4 e2m1x8_scaled_to_bf16_hw(uint32_t p, float s) {
+  return make_uint4(e2m1x2_scaled_to_bf16<0>(p, s), e2m1x2_scaled_to_bf16<1>(p, s), e2m1x2_scaled_to_bf16<2>(p, s),
+                    e2m1x2_scaled_to_bf16<3>(p, s));
+}
+
 // Two E4M3 (OCP E4M3FN) bytes -> two floats with the gfx950 FP8 conversion:
 // bytes 0 and 1 of `v` when HI is false, bytes 2 and 3 when HI is true.
 template <bool HI>
