@@ -208,6 +208,35 @@ def cpu_baseline(budget_s=10.0):
                       f"(M=1, K=5120), {calls} calls in {el:.1f} s, single thread"}
 
 
+def profile_run(what, launches):
+    """A short, untimed run for hardware-counter passes (rocprofv3 --pmc): `launches` launches of one kernel.
+
+    decode: nvfp4_linear on the decode workload, cycling through rotated weight copies so that every
+            launch streams its weights from HBM;
+    copy:   a plain 256 MiB device-to-device copy (torch's copy kernel), the calibration for the
+            FETCH_SIZE / WRITE_SIZE counters (each launch moves exactly 256 MiB each way).
+    """
+    torch.cuda.set_device(0)
+    if what == "copy":
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(launches):
+            dst.copy_(src)
+    else:
+        nv.lib()
+        wl = WL.WORKLOADS["decode"]
+        packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+        x = dev_bf16(wl.activations(1))
+        rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
+        y = torch.empty((1, wl.n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p, s, t = rot.items[i % len(rot)]
+            nv.linear(x, p, s, t, out=y)
+    torch.cuda.synchronize()
+    print(f"profile run done: {what} x{launches}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,12 +244,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--profile", choices=["decode", "copy"], default=None,
+                    help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
+    ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs on a single "
-              f"MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The library runs the linear on "
+              f"one MI355X; a multi-GPU layer would shard the weight rows (N) or whole 16-element K blocks "
+              f"across GPUs above this library.", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile:
+        profile_run(args.profile, args.launches)
+        return
     torch.cuda.set_device(0)
     nv.lib()
 
@@ -303,7 +339,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemv_decode_5120x5120", digest),
-                     "kernel": "gemv_kernel<4,2>", "bytes_per_launch": nbytes,
+                     "kernel": "gemv_lds_kernel<32, 1, 5, 10, false>", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "rows": rows,

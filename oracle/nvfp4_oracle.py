@@ -24,7 +24,7 @@ Sources (web pages, cited by title and section):
     weight-only (activations stay BF16), group size 16; merged q/k/v and
     gate/up members share one tensor scale.
 
-Readings taken where the pages are silent (listed with reasons in the design doc):
+Readings taken where the pages are silent or open:
   R1 tensor scale   tscale = fl32(amax / 2688), 2688 = 6 * 448, stored as a multiplier.
   R2 micro-scale    the E4M3 value nearest to the real number 448*bam/amax.
   R3 element        the E2M1 magnitude nearest to the real 2688*|w|/(amax*s), saturating at 6.
