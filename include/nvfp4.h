@@ -116,6 +116,36 @@ nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                           const uint8_t* packed, const uint8_t* scales, const float* tscale,
                           uint16_t* y, void* stream);
 
+/*
+ * The linear with a caller-provided workspace (same model card and page as
+ * nvfp4_linear).  For 2 <= m <= 64 the small-M kernel can then split K across
+ * workgroups: each workgroup writes FP32 partial sums of its K slice to the
+ * workspace, and the last workgroup of each row block to finish adds the
+ * slices in slice order and writes y.  The result is therefore the same bits
+ * on every run, but may differ in the last FP32 bits from nvfp4_linear's
+ * unsplit summation.
+ *
+ * nvfp4_linear_workspace_bytes(m, n, k) returns the bytes this shape can use:
+ * 0 when the chosen kernel needs none (m = 1, m > 64, or no split), -1 for an
+ * invalid shape.  It makes no HIP call.
+ *
+ * Workspace contract:
+ *   - a device pointer, 16-byte aligned, not overlapping any argument buffer;
+ *   - zero-filled once before its first use; every call leaves the bytes that
+ *     must start at zero (the arrival counters) at zero again, so later calls
+ *     need no clearing;
+ *   - calls that may run at the same time (other streams) need separate
+ *     workspaces;
+ *   - NULL, or workspace_bytes below the size returned above, runs the unsplit
+ *     kernel (the result of nvfp4_linear) instead;
+ *   - workspace_bytes < 0 is NVFP4_ERR_SHAPE.
+ */
+int64_t nvfp4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+nvfp4_status nvfp4_linear_ws(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                             const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                             uint16_t* y, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Kernel ids for nvfp4_linear_forced. */
 #define NVFP4_KERNEL_AUTO 0
 #define NVFP4_KERNEL_GEMV 1     /* VALU dot-product GEMV; any m (rows handled independently) */

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Dict, Optional, Tuple, Union
 
 import torch
 
@@ -23,7 +23,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = ran
 
 # Every symbol include/nvfp4.h declares.
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
-            "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced")
+            "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced",
+            "nvfp4_linear_ws", "nvfp4_linear_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -54,7 +55,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.nvfp4_linear.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_forced.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
-        for name in EXPORTED[2:]:
+        L.nvfp4_linear_ws.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_linear_workspace_bytes.restype = i64
+        for name in EXPORTED[2:-1]:
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -135,9 +139,40 @@ def dequant(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor) ->
     return out
 
 
+def linear_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Workspace bytes nvfp4_linear_ws can use for this shape (0: none)."""
+    b = lib().nvfp4_linear_workspace_bytes(m, n, k)
+    if b < 0:
+        raise ValueError(f"invalid linear shape m={m} n={n} k={k}")
+    return b
+
+
+# Workspaces owned by the binding, one per (device, stream): zero-filled when
+# allocated, and left with zero counters by every call, so they are reused as is.
+_workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def _workspace_for(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        # 256-byte aligned by the caching allocator; grown geometrically.
+        size = max(nbytes, 2 * ws.numel() if ws is not None else 0)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
-           kernel: str = "auto", out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y[m, n] = X[m, k] . W_hat[n, k]^T in BF16 (FP32 accumulation)."""
+           kernel: str = "auto", out: Optional[torch.Tensor] = None,
+           workspace: Union[str, None, torch.Tensor] = "auto") -> torch.Tensor:
+    """Y[m, n] = X[m, k] . W_hat[n, k]^T in BF16 (FP32 accumulation).
+
+    kernel: "auto" (by m), or "gemv" / "small_m" / "prefill" to force one kernel (no workspace).
+    workspace (auto kernel only): "auto" uses a binding-owned workspace for the current
+    device and stream (nvfp4_linear_ws); None calls nvfp4_linear (no workspace); a uint8
+    device tensor is passed through as the caller's workspace (zero-filled before first use).
+    """
     _need(x, torch.bfloat16, "x")
     _need(packed, torch.uint8, "packed")
     _need(scales, torch.uint8, "scales")
@@ -153,9 +188,21 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: 
         if out.shape != (m, n):
             raise ValueError("out must be [m, n]")
     kid = KERNEL_IDS[kernel]
-    args = (x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), _stream(x))
-    if kid == KERNEL_AUTO:
-        _check(lib().nvfp4_linear(*args), "nvfp4_linear")
+    stream = _stream(x)
+    head = (x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), out.data_ptr())
+    if kid != KERNEL_AUTO:
+        _check(lib().nvfp4_linear_forced(kid, *head, stream), "nvfp4_linear_forced")
+    elif workspace is None:
+        _check(lib().nvfp4_linear(*head, stream), "nvfp4_linear")
     else:
-        _check(lib().nvfp4_linear_forced(kid, *args), "nvfp4_linear_forced")
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+            need = linear_workspace_bytes(m, n, k)
+            ws = _workspace_for(x.device, stream, need) if need > 0 else None
+        else:
+            _need(workspace, torch.uint8, "workspace")
+            ws = workspace
+        wptr, wbytes = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+        _check(lib().nvfp4_linear_ws(*head, wptr, wbytes, stream), "nvfp4_linear_ws")
     return out

@@ -17,8 +17,12 @@ void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* t
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                  const float* tscale, uint16_t* y, hipStream_t s);
-void launch_gemm_small_m(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+// Small-M kernel.  With a workspace of at least skinny_workspace_bytes(m, n, k)
+// bytes (zero-filled before its first use; left that way by every launch) it may
+// split K across workgroups; with none it runs unsplit.
+int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
+void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
+                   const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes, hipStream_t s);
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                          const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
 

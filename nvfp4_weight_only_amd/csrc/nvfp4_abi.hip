@@ -76,18 +76,37 @@ nvfp4_status validate_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
   return NVFP4_OK;
 }
 
+int auto_kernel(int64_t m) {
+  return m == 1 ? NVFP4_KERNEL_GEMV : (m <= 64 ? NVFP4_KERNEL_SMALL_M : NVFP4_KERNEL_PREFILL);
+}
+
+// A workspace is used only by the small-M kernel (K split across workgroups).
 nvfp4_status run_linear(int kernel, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                        const uint8_t* scales, const float* tscale, uint16_t* y, void* stream) {
+                        const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
   if (kernel < NVFP4_KERNEL_AUTO || kernel > NVFP4_KERNEL_PREFILL) return NVFP4_ERR_UNSUPPORTED;
   nvfp4_status st = validate_linear(x, m, n, k, packed, scales, tscale, y);
   if (st != NVFP4_OK) return st;
+  if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+  if (workspace != nullptr && workspace_bytes > 0) {
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    int64_t xb = 0, yb = 0, pb = n * (k / 2), sb = n * (k / 16);
+    mul_ok(m, 2 * k, &xb);
+    mul_ok(m, 2 * n, &yb);
+    if (overlaps(workspace, workspace_bytes, x, xb) || overlaps(workspace, workspace_bytes, y, yb) ||
+        overlaps(workspace, workspace_bytes, packed, pb) || overlaps(workspace, workspace_bytes, scales, sb) ||
+        overlaps(workspace, workspace_bytes, tscale, 4))
+      return NVFP4_ERR_ALIAS;
+  }
   if (m == 0) return NVFP4_OK;
   if ((st = check_device()) != NVFP4_OK) return st;
-  if (kernel == NVFP4_KERNEL_AUTO) kernel = m == 1 ? NVFP4_KERNEL_GEMV : (m <= 64 ? NVFP4_KERNEL_SMALL_M : NVFP4_KERNEL_PREFILL);
+  if (kernel == NVFP4_KERNEL_AUTO) kernel = auto_kernel(m);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (kernel) {
     case NVFP4_KERNEL_GEMV: nvfp4::launch_gemv(x, m, n, k, packed, scales, tscale, y, s); break;
-    case NVFP4_KERNEL_SMALL_M: nvfp4::launch_gemm_small_m(x, m, n, k, packed, scales, tscale, y, s); break;
+    case NVFP4_KERNEL_SMALL_M:
+      nvfp4::launch_skinny(x, m, n, k, packed, scales, tscale, y, workspace, workspace ? workspace_bytes : 0, s);
+      break;
     default: nvfp4::launch_gemm_prefill(x, m, n, k, packed, scales, tscale, y, s); break;
   }
   return launch_status();
@@ -189,13 +208,28 @@ nvfp4_status nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, const f
 
 nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                           const uint8_t* scales, const float* tscale, uint16_t* y, void* stream) {
-  return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, stream);
+  return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, nullptr, 0, stream);
+}
+
+int64_t nvfp4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  WeightSizes ws;
+  if (m < 0 || weight_sizes(n, k, &ws) != NVFP4_OK) return -1;
+  int64_t ye;
+  if (!mul_ok(m, n, &ye) || ye > INT64_MAX / 32) return -1;
+  if (auto_kernel(m) != NVFP4_KERNEL_SMALL_M) return 0;
+  return nvfp4::skinny_workspace_bytes(m, n, k);
+}
+
+nvfp4_status nvfp4_linear_ws(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                             const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                  const uint8_t* packed, const uint8_t* scales, const float* tscale, uint16_t* y,
                                  void* stream) {
-  return run_linear(kernel_id, x, m, n, k, packed, scales, tscale, y, stream);
+  return run_linear(kernel_id, x, m, n, k, packed, scales, tscale, y, nullptr, 0, stream);
 }
 
 }  // extern "C"

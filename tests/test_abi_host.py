@@ -73,6 +73,29 @@ def test_linear_validation(L):
     assert L.nvfp4_linear_forced(2, A, 1, 64, 24, Bp, C, D, E, None) == B.ERR_SHAPE
 
 
+def test_linear_workspace_bytes(L):
+    wb = L.nvfp4_linear_workspace_bytes
+    assert wb(1, 5120, 5120) == 0            # GEMV: no workspace
+    assert wb(65, 17408, 5120) == 0          # prefill GEMM: no workspace
+    assert wb(8, 17408, 5120) == 0           # small-M, 68 rows x 1 K slice per workgroup
+    # small-M down projection: 64 blocks of 80 rows x 4 K slices; 256 B of counters + 4 * m * n FP32 partials
+    assert wb(8, 5120, 17408) == 256 + 4 * 8 * 5120 * 4
+    assert wb(32, 5120, 17408) == 256 + 4 * 32 * 5120 * 4
+    assert wb(-1, 64, 64) == -1 and wb(8, 64, 24) == -1 and wb(8, 0, 64) == -1
+
+
+def test_linear_ws_validation(L):
+    lw = L.nvfp4_linear_ws
+    W = 0x60000000
+    assert lw(A, 8, 64, 64, Bp, C, D, E, W, -1, None) == B.ERR_SHAPE     # negative workspace size
+    assert lw(A, 8, 64, 64, Bp, C, D, E, W + 8, 1024, None) == B.ERR_ALIGN
+    assert lw(A, 8, 64, 64, Bp, C, D, E, A + 64, 1024, None) == B.ERR_ALIAS   # overlaps x
+    assert lw(A, 8, 64, 64, Bp, C, D, E, E - 512, 1024, None) == B.ERR_ALIAS  # overlaps y
+    assert lw(A, 8, 64, 24, Bp, C, D, E, W, 1024, None) == B.ERR_SHAPE
+    assert lw(None, 8, 64, 64, Bp, C, D, E, W, 1024, None) == B.ERR_NULL
+    assert lw(None, 0, 64, 64, Bp, C, D, None, None, 0, None) == B.OK    # m = 0 no-op
+
+
 def test_quantize_validation(L):
     q = L.nvfp4_quantize
     assert q(None, 4, 64, Bp, C, D, None) == B.ERR_NULL

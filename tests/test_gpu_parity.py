@@ -229,6 +229,49 @@ def test_linear_edge_cases(nv):
 
 
 # ---------------------------------------------------------------------------
+# Small-M kernel with K split across workgroups (caller workspace).
+# ---------------------------------------------------------------------------
+SPLIT_SHAPES = [(8, 300, 1040), (17, 130, 272), (32, 64, 5120), (33, 200, 512), (64, 5120, 5120), (16, 33, 4608),
+                (64, 257, 2064), (9, 513, 784), (2, 5120, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
+def test_small_m_split_k(nv, m, n, k):
+    need = nv.linear_workspace_bytes(m, n, k)
+    assert need > 0, "shape expected to split K"
+    w = WL.normal_bf16((n, k), 0.02, 300 + n)
+    x = WL.normal_bf16((m, k), 1.0, 400 + m)
+    q = nv.quantize(to_dev_bf16(w))
+    y_ref, bound = O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])
+    xd = to_dev_bf16(x)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y1 = bf16_host(nv.linear(xd, *q, workspace=ws))
+    check_linear(y1, y_ref, bound, f"split-K m={m} n={n} k={k}")
+    # The arrival counters are back at zero: a second call on the same workspace
+    # gives the same bits (a stale counter would leave output rows unwritten).
+    for _ in range(2):
+        assert np.array_equal(bf16_host(nv.linear(xd, *q, workspace=ws)), y1)
+    # Unsplit, and a too-small workspace (which runs the unsplit kernel).
+    y0 = bf16_host(nv.linear(xd, *q, workspace=None))
+    check_linear(y0, y_ref, bound, f"unsplit m={m} n={n} k={k}")
+    assert np.array_equal(bf16_host(nv.linear(xd, *q, workspace=ws[:need - 16])), y0)
+
+
+def test_small_m_workspace_shared_by_shapes(nv):
+    # One workspace, large enough for both, used alternately by two shapes.
+    shapes = [(8, 300, 1040), (32, 5120, 2048)]
+    ws = torch.zeros(max(nv.linear_workspace_bytes(*s) for s in shapes), dtype=torch.uint8, device="cuda")
+    cases = []
+    for i, (m, n, k) in enumerate(shapes):
+        q = nv.quantize(to_dev_bf16(WL.normal_bf16((n, k), 0.02, 500 + i)))
+        x = WL.normal_bf16((m, k), 1.0, 600 + i)
+        cases.append((to_dev_bf16(x), q, O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])))
+    for _ in range(3):
+        for xd, q, (y_ref, bound) in cases:
+            check_linear(bf16_host(nv.linear(xd, *q, workspace=ws)), y_ref, bound, "shared workspace")
+
+
+# ---------------------------------------------------------------------------
 # Linear at full size, auto dispatch, sampled output columns.
 # ---------------------------------------------------------------------------
 FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8),
