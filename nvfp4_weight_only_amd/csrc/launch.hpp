@@ -25,5 +25,9 @@ void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uin
                    const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes, hipStream_t s);
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                          const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+// Streaming prefill GEMM (K a multiple of 256); launch_gemm_prefill uses it when supported.
+bool prefill_dma_supported(int64_t m, int64_t n, int64_t k);
+void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                        const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
 
 }  // namespace nvfp4

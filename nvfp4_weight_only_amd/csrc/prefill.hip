@@ -1,0 +1,421 @@
+// Prefill W4A16 GEMM for K a multiple of 256 on gfx950: Y = X W^T with bf16
+// v_mfma_f32_32x32x16_bf16 and FP32 accumulation (model card
+// "Qwen3.8-27B-NVFP4 (compressed-tensors)": weights NVFP4, activations BF16;
+// imp "docs/quantization.md", NVFP4 kernel pipeline: prefill is the dense GEMM).
+//
+// A workgroup computes a 128 x 272 tile of Y (272 = 17 x 16 divides the MLP
+// width 17408 into 64 tiles: 256 workgroups at m = 512) with four wavefronts,
+// one per SIMD.  LDS read bandwidth (about 64 B per clock per CU for 128-bit
+// reads) is what bounds a GEMM that dequantizes through LDS, so:
+//   * every wavefront owns 64 of the 272 columns for all 128 rows: the BF16
+//     activations are read from LDS by every wavefront, but each weight element
+//     is read (packed, 4 bits) and decoded by exactly one wavefront, straight
+//     into the MFMA B operand;
+//   * columns 256..271 form a fifth 32-column MFMA tile (upper 16 columns
+//     unused) whose four 16-wide K steps per 64-column step are shared out one
+//     per wavefront; its partial sums are added in wavefront order at the end;
+//   * activations (128 rows x 64 K per step, a 5-stage ring), packed weights
+//     and scales (272 rows x 256 K per group, double-buffered) move from global
+//     memory to LDS with global_load_lds_dwordx4, whole 128-byte lines per
+//     instruction, without passing through registers.
+//
+// K order inside a 64-element step: lane half h (lanes 32h .. 32h + 31) of an
+// MFMA covers the step's elements [32h, 32h + 32); K step s (0..3) takes
+// [32h + 8s, 32h + 8s + 8).  A weight lane thus reads 16 contiguous packed bytes
+// per step; activations follow the same order (a dot product does not depend on
+// the order of its terms; only the FP32 summation order changes).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) const void pd_lds_t;
+
+constexpr int kPdBM = 128, kPdBN = 272, kPdBK = 64, kPdGroupK = 256;
+constexpr int kPdSRows = 320;  // scale rows in LDS: 5 instructions of 64 rows cover the 272 block rows
+
+struct PdArgs {
+  const uint16_t* x;  // [m, k]
+  int64_t m, n, k;
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* tscale;
+  uint16_t* y;
+  int n_tiles, m_tiles;
+};
+
+// LDS (16-byte slots; the XOR with the row makes 8 consecutive rows at the same
+// piece hit different banks):
+//   x stage: activation row r (of 128), piece p (8 elements) at 8 r + (p ^ (r & 7));
+//   w group: weight row r (of 272), piece p (32 elements) at 8 r + (p ^ (r & 7));
+//   s group: weight row r's 16 scale bytes at slot r.
+struct PdX {
+  uint4 v[kPdBM * 8];
+};
+struct PdW {
+  uint4 v[kPdBN * 8];
+};
+struct PdS {
+  uint4 v[kPdSRows];
+};
+// Five activation stages (16 KB each), two weight groups (34 KB) and two scale
+// groups (5 KB): 161,792 bytes of the 160 KB of LDS.
+constexpr int kPdXStages = 5;
+struct PdLds {
+  PdX xs[kPdXStages];
+  PdW wg[2];
+  PdS sg[2];
+};
+
+__device__ __forceinline__ void pd_lds_dma16(const void* src, uint32_t lds) {
+  // One global_load_lds_dwordx4 (16 bytes per lane to LDS address lds + 16 * lane).
+  // Written out rather than through the compiler builtin, whose wait insertion
+  // loses track of which buffer a pending load writes at a loop head and drains
+  // every load in flight; the instruction has no register result, and the
+  // kernel orders LDS reads after it with explicit vmcnt waits.  M0 is not used
+  // by anything else in this kernel.
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory");
+}
+
+template <typename U>
+__device__ __forceinline__ uint32_t pd_lds_addr(const U* p) {
+  return (uint32_t)(uintptr_t)(pd_lds_t*)p;
+}
+
+template <int N>
+__device__ __forceinline__ void pd_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// vmcnt(N) and lgkmcnt(0) in one wait.  Before a step's barrier the LDS reads
+// of the previous step have long completed; saying so lets the MFMAs that use
+// them start without waiting behind the reads issued after the barrier (the
+// LDS counter tracks at most 15 reads in flight).
+template <int N>
+__device__ __forceinline__ void pd_wait_vmcnt_lds0() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+// Load instructions per wavefront: X 4 per step (16 instructions of 8 rows);
+// weights 9 per group (34 instructions of 8 rows, two spare slots repeat the
+// last); scales 2 per group (5 instructions of 64 rows, three spare slots).
+constexpr int kPdLX = 4, kPdLW = 9, kPdLS = 2;
+
+struct PdSrc {
+  const uint16_t* x[kPdLX];  // step 0 sources
+  const uint8_t* w[kPdLW];   // group 0 sources
+  const uint8_t* s[kPdLS];
+};
+
+// Loads of step t into X stage `xst` and, when the step starts a group
+// (P == 0), of group t / 4 into weight / scale buffer (t / 4) % 2.  Past the
+// end, the last step / group is loaded again into buffers nothing reads.
+template <int P>
+__device__ __forceinline__ void pd_issue(const PdSrc& src, int t, int nsteps, PdLds& L, int xst, int w) {
+  const int tc = t < nsteps ? t : nsteps - 1;
+#pragma unroll
+  for (int i = 0; i < kPdLX; ++i)
+    pd_lds_dma16(src.x[i] + (int64_t)tc * kPdBK, pd_lds_addr(&L.xs[xst].v[64 * (w + 4 * i)]));
+  if (P == 0) {
+    const int gc = tc >> 2, gb = (t >> 2) & 1;
+#pragma unroll
+    for (int i = 0; i < kPdLW; ++i) {
+      const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1;
+      pd_lds_dma16(src.w[i] + (int64_t)gc * (kPdGroupK / 2), pd_lds_addr(&L.wg[gb].v[64 * q]));
+    }
+#pragma unroll
+    for (int i = 0; i < kPdLS; ++i) {
+      const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4;
+      pd_lds_dma16(src.s[i] + (int64_t)gc * (kPdGroupK / 16), pd_lds_addr(&L.sg[gb].v[64 * q]));
+    }
+  }
+}
+
+// One step's operands for one wavefront, read from LDS a step ahead of use.
+struct PdFrag {
+  uint4 xa[4][4];  // A fragments: row tile rt, K step s
+  uint4 wb[2];     // own weight columns 64 W + 32 c + l32: 16 packed bytes (32 elements)
+  uint32_t sb[2];  // their scale word for this step (bytes 4P .. 4P + 3 of the group row)
+  uint32_t w5, s5;  // fifth tile: packed word of K step W and the scale word
+};
+
+// Reads of step t's operands (its place in the group is P), in two kinds:
+// weights and scales from group buffer `gb`, and one K step's A fragments from
+// X stage `xst`.  K order: lane half h covers the step's elements [32h, 32h + 32),
+// K step s takes [32h + 8s, 32h + 8s + 8) (a dot product does not depend on the
+// order of its terms; only the FP32 summation order changes).  Only plain
+// reads here: anything computed from them would wait for them.
+template <int P, int W>
+__device__ __forceinline__ void pd_load_w(const PdLds& L, int gb, int lane, PdFrag& F) {
+  const int l32 = lane & 31, h = lane >> 5;
+  const PdW& Wg = L.wg[gb];
+  const PdS& S = L.sg[gb];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int n = 64 * W + 32 * c + l32;
+    F.wb[c] = Wg.v[n * 8 + ((2 * P + h) ^ (n & 7))];
+    F.sb[c] = reinterpret_cast<const uint32_t*>(&S.v[n])[P];
+  }
+  // Fifth tile rows 256 + l32 (the upper 16 lanes' rows do not exist and are clamped).
+  const int n5 = 256 + (l32 < 16 ? l32 : 15);
+  F.w5 = reinterpret_cast<const uint32_t*>(&Wg.v[n5 * 8 + ((2 * P + h) ^ (n5 & 7))])[W];
+  F.s5 = reinterpret_cast<const uint32_t*>(&S.v[n5])[P];
+}
+
+template <int S>
+__device__ __forceinline__ void pd_load_x(const PdLds& L, int xst, int lane, PdFrag& F) {
+  const int l32 = lane & 31, h = lane >> 5;
+  const PdX& X = L.xs[xst];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = 32 * rt + l32;
+    F.xa[rt][S] = X.v[r * 8 + ((4 * h + S) ^ (r & 7))];
+  }
+}
+
+// Decoded B fragment of one 16-wide K step: packed word `p` (8 elements) times
+// the E4M3 scale byte `sc`.
+__device__ __forceinline__ bf16x8_t pd_decode(uint32_t p, uint32_t sc) {
+  return __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(p, e4m3x2_to_f32<false>(sc).x));
+}
+
+// K step S of a step: two 32-column tiles x four 32-row tiles.
+template <int S>
+__device__ __forceinline__ void pd_mma(const PdFrag& F, int h, f32x16_t (&acc)[4][2]) {
+  bf16x8_t b[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t word = S == 0 ? F.wb[c].x : S == 1 ? F.wb[c].y : S == 2 ? F.wb[c].z : F.wb[c].w;
+    // scale byte of block 4P + 2h + S / 2
+    b[c] = pd_decode(word, (F.sb[c] >> (16 * h + 8 * (S >> 1))) & 0xFFu);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, F.xa[rt][S]), b[c],
+                                                           acc[rt][c], 0, 0, 0);
+}
+
+// The fifth tile's K step W.
+template <int W>
+__device__ __forceinline__ void pd_mma5(const PdFrag& F, int h, f32x16_t (&acc5)[4]) {
+  const bf16x8_t b5 = pd_decode(F.w5, (F.s5 >> (16 * h + 8 * (W >> 1))) & 0xFFu);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+    acc5[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, F.xa[rt][W]), b5, acc5[rt], 0,
+                                                       0, 0);
+}
+
+// The MFMAs of one step on operands `C` read during the previous step, with
+// the reads of the next step's operands `N` (from X stage `xst`, group buffer
+// `gb`, place in group PN) spread between them: a wavefront keeps at most 15
+// LDS reads in flight, so a burst of all 22 would hold up its MFMAs.
+template <int PN, int W>
+__device__ __forceinline__ void pd_step(const PdLds& L, int xst, int gb, int lane, const PdFrag& C, PdFrag& N,
+                                        f32x16_t (&acc)[4][2], f32x16_t (&acc5)[4]) {
+  const int h = lane >> 5;
+  pd_load_w<PN, W>(L, gb, lane, N);
+  pd_load_x<0>(L, xst, lane, N);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_mma<0>(C, h, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_load_x<1>(L, xst, lane, N);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_mma<1>(C, h, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_load_x<2>(L, xst, lane, N);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_mma<2>(C, h, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_load_x<3>(L, xst, lane, N);
+  __builtin_amdgcn_sched_barrier(0);
+  pd_mma<3>(C, h, acc);
+  pd_mma5<W>(C, h, acc5);
+}
+
+__device__ __forceinline__ int pd_next_stage(int s) { return s == kPdXStages - 1 ? 0 : s + 1; }
+
+// Copy the BF16 tile (128 x 272, row-major in LDS) to Y rows m0.., columns
+// n0..: 34 pieces of 8 columns per row, 17 per thread.  Pieces that are whole,
+// inside Y and 16-byte aligned go as one store; the others element by element.
+__device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* yt, int64_t m0, int64_t n0, int tid) {
+  const int64_t rows = p.m - m0 < kPdBM ? p.m - m0 : kPdBM;
+  const int64_t cols = p.n - n0 < kPdBN ? p.n - n0 : kPdBN;
+  constexpr int kPieces = kPdBN / 8;
+#pragma unroll 1
+  for (int j = tid; j < kPdBM * kPieces; j += 256) {
+    const int r = j / kPieces, c8 = 8 * (j - r * kPieces);
+    if (r >= rows || c8 >= cols) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kPdBN + c8);
+    uint16_t* dst = p.y + (m0 + r) * p.n + n0 + c8;
+    if (c8 + 8 <= cols && ((uintptr_t)dst & 15) == 0) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+      for (int i = 0; i < 8 && c8 + i < cols; ++i) dst[i] = e[i];
+    }
+  }
+}
+
+// Wavefront W's whole K loop and epilogue (a template, so that the fifth
+// tile's operand choice is static and every accumulator stays in place).
+template <int W>
+__device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds& L, int lane, int64_t m0,
+                                        int64_t n0, int nsteps) {
+  f32x16_t acc[4][2], acc5[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[rt][0][e] = acc[rt][1][e] = acc5[rt][e] = 0.0f;
+  }
+
+  pd_issue<0>(src, 0, nsteps, L, 0, W);
+  pd_issue<1>(src, 1, nsteps, L, 1, W);
+  pd_issue<2>(src, 2, nsteps, L, 2, W);
+  pd_issue<3>(src, 3, nsteps, L, 3, W);
+  pd_wait_vmcnt<3 * kPdLX>();  // step 0 (and group 0) landed; steps 1..3 may be in flight
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  PdFrag f0, f1;
+  pd_load_w<0, W>(L, 0, lane, f0);
+  pd_load_x<0>(L, 0, lane, f0);
+  pd_load_x<1>(L, 0, lane, f0);
+  pd_load_x<2>(L, 0, lane, f0);
+  pd_load_x<3>(L, 0, lane, f0);
+  int xld = 4, xrd = 1;  // X stages of the next step to load into LDS / to read from LDS
+
+  // Step t: wait for this wavefront's loads of step t + 1 (steps t + 2 and t + 3
+  // may stay in flight: 2 x 4, plus 11 when one of them starts a group), meet
+  // the barrier (after it every wavefront has finished step t - 1, so X stage
+  // (t - 1) % 5 and, at a group start, the weight buffer of group t / 4 - 1 are
+  // free), start the loads of step t + 4, read step t + 1's operands, and run
+  // step t's MFMAs on the operands read during the previous step.  The raw
+  // barrier has no fence, so the compiler adds no wait of its own.
+#define PD_STEP(P, CUR, NXT)                                                          \
+  {                                                                                  \
+    const int t = tb + (P);                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+    pd_wait_vmcnt_lds0<((P) == 0 || (P) == 3) ? 2 * kPdLX : 2 * kPdLX + kPdLW + kPdLS>(); \
+    asm volatile("" ::: "memory");                                                   \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    pd_issue<P>(src, t + 4, nsteps, L, xld, W);                                      \
+    xld = pd_next_stage(xld);                                                        \
+    pd_step<((P) + 1) & 3, W>(L, xrd, ((t + 1) >> 2) & 1, lane, CUR, NXT, acc, acc5); \
+    xrd = pd_next_stage(xrd);                                                        \
+  }
+  for (int tb = 0; tb < nsteps; tb += 4) {
+    PD_STEP(0, f0, f1)
+    PD_STEP(1, f1, f0)
+    PD_STEP(2, f0, f1)
+    PD_STEP(3, f1, f0)
+  }
+#undef PD_STEP
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeat loads past the end have landed
+
+  // Fifth tile: add the wavefronts' partial sums in wavefront order; wavefront
+  // W finishes row tile W.
+  __syncthreads();
+  f32x16_t* red = reinterpret_cast<f32x16_t*>(&L.wg[0]);  // 4 x 4 x 64 lanes x 64 B = 64 KB of the 68 KB weight groups
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) red[(W * 4 + rt) * 64 + lane] = acc5[rt];
+  __syncthreads();
+  f32x16_t t5 = red[(0 * 4 + W) * 64 + lane];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) t5 += red[(ww * 4 + W) * 64 + lane];
+
+  // Epilogue: the BF16 tile goes through LDS (the X stages, free now) so that
+  // the stores to Y are whole 16-byte pieces of rows.  32x32 D layout: item v
+  // of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+  const float ts = *p.tscale;
+  const int l32 = lane & 31, h = lane >> 5;
+  uint16_t* yt = reinterpret_cast<uint16_t*>(&L.xs[0]);  // [128][272] BF16, 69,632 bytes
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        yt[(32 * rt + 8 * (v >> 2) + 4 * h + (v & 3)) * kPdBN + 64 * W + 32 * c + l32] =
+            (uint16_t)f32_to_bf16_rne(acc[rt][c][v] * ts);
+  if (l32 < 16) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      yt[(32 * W + 8 * (v >> 2) + 4 * h + (v & 3)) * kPdBN + 256 + l32] = (uint16_t)f32_to_bf16_rne(t5[v] * ts);
+  }
+  __syncthreads();
+  pd_store_tile(p, yt, m0, n0, W * 64 + lane);
+}
+
+__global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
+  __shared__ PdLds L;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
+  // Tile order: workgroups are dispatched to the 8 XCDs round-robin by id, so
+  // when the tile count allows, consecutive ids of one XCD cover all m tiles of
+  // consecutive n tiles (the weight tile is then fetched into that XCD's L2 once).
+  const int nwg = p.n_tiles * p.m_tiles;
+  int id = (int)blockIdx.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  const int nt = id / p.m_tiles, mt = id % p.m_tiles;
+  const int64_t m0 = (int64_t)mt * kPdBM, n0 = (int64_t)nt * kPdBN;
+  const int nsteps = (int)(p.k / kPdBK);  // a multiple of 4
+  const int64_t kh = p.k >> 1, ks = p.k >> 4;
+
+  // Per-lane sources; rows past m or n repeat the last valid row (never stored).
+  PdSrc src;
+#pragma unroll
+  for (int i = 0; i < kPdLX; ++i) {
+    const int q = w + 4 * i, r = 8 * q + (lane >> 3);
+    const int64_t gm = m0 + r < p.m ? m0 + r : p.m - 1;
+    src.x[i] = p.x + gm * p.k + 8 * ((lane & 7) ^ (r & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < kPdLW; ++i) {
+    const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1, r = 8 * q + (lane >> 3);
+    const int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1;
+    src.w[i] = p.packed + gn * kh + 16 * ((lane & 7) ^ (r & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < kPdLS; ++i) {
+    const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4, r = 64 * q + lane;
+    const int rr = r < kPdBN ? r : kPdBN - 1;  // LDS rows 272..319 hold a repeat (never read)
+    const int64_t gn = n0 + rr < p.n ? n0 + rr : p.n - 1;
+    src.s[i] = p.scales + gn * ks;
+  }
+
+  switch (w) {
+    case 0: pd_body<0>(p, src, L, lane, m0, n0, nsteps); break;
+    case 1: pd_body<1>(p, src, L, lane, m0, n0, nsteps); break;
+    case 2: pd_body<2>(p, src, L, lane, m0, n0, nsteps); break;
+    default: pd_body<3>(p, src, L, lane, m0, n0, nsteps); break;
+  }
+}
+
+}  // namespace
+
+bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) { return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0; }
+
+void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                        const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = (m + kPdBM - 1) / kPdBM;
+  // One launch covers up to 2^31 - 1 workgroups; larger m is split by row.
+  const int64_t max_m_tiles = ((int64_t)1 << 30) / n_tiles;
+  for (int64_t t0 = 0; t0 < m_tiles; t0 += max_m_tiles) {
+    const int64_t mt = m_tiles - t0 < max_m_tiles ? m_tiles - t0 : max_m_tiles;
+    const int64_t mm = (m - t0 * kPdBM) < mt * kPdBM ? (m - t0 * kPdBM) : mt * kPdBM;
+    const PdArgs a{x + t0 * kPdBM * k, mm, n, k, packed, scales, tscale, y + t0 * kPdBM * n, (int)n_tiles, (int)mt};
+    prefill_dma_kernel<<<dim3((unsigned)(n_tiles * mt)), 256, 0, s>>>(a);
+  }
+}
+
+}  // namespace nvfp4

@@ -185,7 +185,9 @@ LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 6
               (100, 300, 1040), (130, 257, 2064), (1, 1, 16), (5, 3, 16),
               # GEMV dispatch branches: 32 lanes/row (k = 1024, 3072), ragged 64 lanes/row (k = 4608),
               # the large-n tiling (n >= 16384), and k beyond the LDS-staged range (k = 17408)
-              (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (1, 40, 17408)]
+              (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (1, 40, 17408),
+              # prefill with K a multiple of 256: several 128 x 272 tiles with ragged edges, one K group
+              (200, 560, 768), (129, 545, 256), (300, 300, 2560)]
 
 
 @pytest.mark.parametrize("m,n,k", LIN_SHAPES)
@@ -275,7 +277,7 @@ def test_small_m_workspace_shared_by_shapes(nv):
 # Linear at full size, auto dispatch, sampled output columns.
 # ---------------------------------------------------------------------------
 FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8),
-               ("small_m_down", 32), ("prefill", 512), ("prefill", 2048)]
+               ("small_m_down", 32), ("prefill", 512), ("prefill", 2048), ("small_m_down", 512)]
 
 _weights_cache = {}
 
