@@ -179,65 +179,126 @@ __device__ __forceinline__ void pd_load_x(const PdLds& L, int xst, int lane, PdF
   }
 }
 
-// Decoded B fragment of one 16-wide K step: packed word `p` (8 elements) times
-// the E4M3 scale byte `sc`.
-__device__ __forceinline__ bf16x8_t pd_decode(uint32_t p, uint32_t sc) {
-  return __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(p, e4m3x2_to_f32<false>(sc).x));
-}
+// Decoded B fragments: two own column tiles, four BF16 pairs each.
+struct PdB {
+  uint32_t v[2][4];
+};
 
-// K step S of a step: two 32-column tiles x four 32-row tiles.
+// The E4M3 scale of K step S of tile c, as a float (lane half h: blocks
+// 4P + 2h and 4P + 2h + 1 of the group row; K step S uses block 4P + 2h + S / 2).
 template <int S>
-__device__ __forceinline__ void pd_mma(const PdFrag& F, int h, f32x16_t (&acc)[4][2]) {
-  bf16x8_t b[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const uint32_t word = S == 0 ? F.wb[c].x : S == 1 ? F.wb[c].y : S == 2 ? F.wb[c].z : F.wb[c].w;
-    // scale byte of block 4P + 2h + S / 2
-    b[c] = pd_decode(word, (F.sb[c] >> (16 * h + 8 * (S >> 1))) & 0xFFu);
-  }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, F.xa[rt][S]), b[c],
-                                                           acc[rt][c], 0, 0, 0);
+__device__ __forceinline__ float pd_scale(const PdFrag& F, int h, int c) {
+  return e4m3x2_to_f32<false>((F.sb[c] >> (16 * h + 8 * (S >> 1))) & 0xFFu).x;
 }
 
-// The fifth tile's K step W.
-template <int W>
-__device__ __forceinline__ void pd_mma5(const PdFrag& F, int h, f32x16_t (&acc5)[4]) {
-  const bf16x8_t b5 = pd_decode(F.w5, (F.s5 >> (16 * h + 8 * (W >> 1))) & 0xFFu);
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-    acc5[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, F.xa[rt][W]), b5, acc5[rt], 0,
-                                                       0, 0);
+template <int S>
+__device__ __forceinline__ uint32_t pd_word(const PdFrag& F, int c) {
+  return S == 0 ? F.wb[c].x : S == 1 ? F.wb[c].y : S == 2 ? F.wb[c].z : F.wb[c].w;
 }
 
-// The MFMAs of one step on operands `C` read during the previous step, with
-// the reads of the next step's operands `N` (from X stage `xst`, group buffer
-// `gb`, place in group PN) spread between them: a wavefront keeps at most 15
-// LDS reads in flight, so a burst of all 22 would hold up its MFMAs.
+__device__ __forceinline__ void pd_mfma(f32x16_t& acc, const uint4& a, const uint32_t (&b)[4]) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, make_uint4(b[0], b[1], b[2], b[3])),
+                                                acc, 0, 0, 0);
+}
+
+// Pair J of an 8-element decode (4 instructions).
+template <int J>
+__device__ __forceinline__ uint32_t pd_dec(uint32_t word, float sc) {
+  return e2m1x2_scaled_to_bf16<J>(word, sc);
+}
+
+// One K step S of the current step: its 8 MFMAs (row tile i / 2, column tile
+// i % 2) on the decoded fragments `bc`, each followed by one pair of the next
+// K step's decode into `bn` (tile i / 4) and, for the first four, the read of
+// one A fragment of the next step (K step S).  The fixed order keeps the
+// decode in the MFMAs' shadow and at most a few LDS reads in flight.
+template <int S>
+__device__ __forceinline__ void pd_kstep(const PdLds& L, int xst, int lane, const PdFrag& C, PdFrag& N,
+                                         const PdB& bc, PdB& bn, f32x16_t (&acc)[4][2]) {
+  const int l32 = lane & 31, h = lane >> 5;
+  const PdX& X = L.xs[xst];
+  const float sc0 = pd_scale<S + 1>(C, h, 0), sc1 = pd_scale<S + 1>(C, h, 1);
+  const uint32_t w0 = pd_word<S + 1>(C, 0), w1 = pd_word<S + 1>(C, 1);
+#define PD_G(I, DEC)                                                               \
+  pd_mfma(acc[(I) / 2][(I) % 2], C.xa[(I) / 2][S], bc.v[(I) % 2]);                  \
+  DEC;                                                                             \
+  if ((I) < 4) {                                                                   \
+    const int r = 32 * (I) + l32;                                                  \
+    N.xa[(I) & 3][S] = X.v[r * 8 + ((4 * h + S) ^ (r & 7))];                       \
+  }                                                                                \
+  __builtin_amdgcn_sched_barrier(0);
+  PD_G(0, bn.v[0][0] = pd_dec<0>(w0, sc0))
+  PD_G(1, bn.v[0][1] = pd_dec<1>(w0, sc0))
+  PD_G(2, bn.v[0][2] = pd_dec<2>(w0, sc0))
+  PD_G(3, bn.v[0][3] = pd_dec<3>(w0, sc0))
+  PD_G(4, bn.v[1][0] = pd_dec<0>(w1, sc1))
+  PD_G(5, bn.v[1][1] = pd_dec<1>(w1, sc1))
+  PD_G(6, bn.v[1][2] = pd_dec<2>(w1, sc1))
+  PD_G(7, bn.v[1][3] = pd_dec<3>(w1, sc1))
+#undef PD_G
+}
+
+// The decode of K step 0 of a step's operands (before the loop).
+__device__ __forceinline__ void pd_decode0(const PdFrag& F, int h, PdB& b) {
+  const float sc0 = pd_scale<0>(F, h, 0), sc1 = pd_scale<0>(F, h, 1);
+  b.v[0][0] = pd_dec<0>(F.wb[0].x, sc0);
+  b.v[0][1] = pd_dec<1>(F.wb[0].x, sc0);
+  b.v[0][2] = pd_dec<2>(F.wb[0].x, sc0);
+  b.v[0][3] = pd_dec<3>(F.wb[0].x, sc0);
+  b.v[1][0] = pd_dec<0>(F.wb[1].x, sc1);
+  b.v[1][1] = pd_dec<1>(F.wb[1].x, sc1);
+  b.v[1][2] = pd_dec<2>(F.wb[1].x, sc1);
+  b.v[1][3] = pd_dec<3>(F.wb[1].x, sc1);
+}
+
+// The MFMAs of one step on operands `C` (read during the previous step; `b`
+// holds their K step 0 decoded) while reading the next step's operands `N`
+// (X stage `xst`, group buffer `gb`, place in group PN) and decoding ahead:
+// K steps 1..3 during the K step before, the fifth tile's fragment and N's
+// K step 0 (left in `b`) during K step 3 and the fifth tile's MFMAs.
 template <int PN, int W>
 __device__ __forceinline__ void pd_step(const PdLds& L, int xst, int gb, int lane, const PdFrag& C, PdFrag& N,
-                                        f32x16_t (&acc)[4][2], f32x16_t (&acc5)[4]) {
-  const int h = lane >> 5;
+                                        PdB& b, f32x16_t (&acc)[4][2], f32x16_t (&acc5)[4]) {
+  const int l32 = lane & 31, h = lane >> 5;
+  PdB t;
   pd_load_w<PN, W>(L, gb, lane, N);
-  pd_load_x<0>(L, xst, lane, N);
   __builtin_amdgcn_sched_barrier(0);
-  pd_mma<0>(C, h, acc);
+  pd_kstep<0>(L, xst, lane, C, N, b, t, acc);
+  pd_kstep<1>(L, xst, lane, C, N, t, b, acc);
+  pd_kstep<2>(L, xst, lane, C, N, b, t, acc);
+  // K step 3: MFMAs on t; decode the fifth tile's fragment and N's K step 0, tile 0.
+  const PdX& X = L.xs[xst];
+  const float s5 = e4m3x2_to_f32<false>((C.s5 >> (16 * h + 8 * (W >> 1))) & 0xFFu).x;
+  uint32_t b5[4];
+#define PD_G3(I, DEC)                                                              \
+  pd_mfma(acc[(I) / 2][(I) % 2], C.xa[(I) / 2][3], t.v[(I) % 2]);                   \
+  DEC;                                                                             \
+  if ((I) < 4) {                                                                   \
+    const int r = 32 * (I) + l32;                                                  \
+    N.xa[(I) & 3][3] = X.v[r * 8 + ((4 * h + 3) ^ (r & 7))];                       \
+  }                                                                                \
   __builtin_amdgcn_sched_barrier(0);
-  pd_load_x<1>(L, xst, lane, N);
+  PD_G3(0, b5[0] = pd_dec<0>(C.w5, s5))
+  PD_G3(1, b5[1] = pd_dec<1>(C.w5, s5))
+  PD_G3(2, b5[2] = pd_dec<2>(C.w5, s5))
+  PD_G3(3, b5[3] = pd_dec<3>(C.w5, s5))
+  const float n0s = pd_scale<0>(N, h, 0), n1s = pd_scale<0>(N, h, 1);
+  PD_G3(4, b.v[0][0] = pd_dec<0>(N.wb[0].x, n0s))
+  PD_G3(5, b.v[0][1] = pd_dec<1>(N.wb[0].x, n0s))
+  PD_G3(6, b.v[0][2] = pd_dec<2>(N.wb[0].x, n0s))
+  PD_G3(7, b.v[0][3] = pd_dec<3>(N.wb[0].x, n0s))
+#undef PD_G3
+  // Fifth tile: K step W of rows 32 rt .. 32 rt + 31.
+#define PD_G5(RT, DEC)                                \
+  pd_mfma(acc5[RT], C.xa[RT][W], b5);                 \
+  DEC;                                                \
   __builtin_amdgcn_sched_barrier(0);
-  pd_mma<1>(C, h, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  pd_load_x<2>(L, xst, lane, N);
-  __builtin_amdgcn_sched_barrier(0);
-  pd_mma<2>(C, h, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  pd_load_x<3>(L, xst, lane, N);
-  __builtin_amdgcn_sched_barrier(0);
-  pd_mma<3>(C, h, acc);
-  pd_mma5<W>(C, h, acc5);
+  PD_G5(0, b.v[1][0] = pd_dec<0>(N.wb[1].x, n1s))
+  PD_G5(1, b.v[1][1] = pd_dec<1>(N.wb[1].x, n1s))
+  PD_G5(2, b.v[1][2] = pd_dec<2>(N.wb[1].x, n1s))
+  PD_G5(3, b.v[1][3] = pd_dec<3>(N.wb[1].x, n1s))
+#undef PD_G5
 }
 
 __device__ __forceinline__ int pd_next_stage(int s) { return s == kPdXStages - 1 ? 0 : s + 1; }
@@ -290,6 +351,8 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   pd_load_x<1>(L, 0, lane, f0);
   pd_load_x<2>(L, 0, lane, f0);
   pd_load_x<3>(L, 0, lane, f0);
+  PdB bdec;
+  pd_decode0(f0, lane >> 5, bdec);
   int xld = 4, xrd = 1;  // X stages of the next step to load into LDS / to read from LDS
 
   // Step t: wait for this wavefront's loads of step t + 1 (steps t + 2 and t + 3
@@ -309,7 +372,7 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
     asm volatile("" ::: "memory");                                                   \
     pd_issue<P>(src, t + 4, nsteps, L, xld, W);                                      \
     xld = pd_next_stage(xld);                                                        \
-    pd_step<((P) + 1) & 3, W>(L, xrd, ((t + 1) >> 2) & 1, lane, CUR, NXT, acc, acc5); \
+    pd_step<((P) + 1) & 3, W>(L, xrd, ((t + 1) >> 2) & 1, lane, CUR, NXT, bdec, acc, acc5); \
     xrd = pd_next_stage(xrd);                                                        \
   }
   for (int tb = 0; tb < nsteps; tb += 4) {
