@@ -196,10 +196,12 @@ __device__ __forceinline__ uint32_t pd_word(const PdFrag& F, int c) {
   return S == 0 ? F.wb[c].x : S == 1 ? F.wb[c].y : S == 2 ? F.wb[c].z : F.wb[c].w;
 }
 
+// One MFMA with the decoded weights as the A operand and the activations as
+// B: the accumulator holds the tile transposed (Y^T = W X^T), so that each
+// lane ends up with 4 consecutive columns of one row of Y.
 __device__ __forceinline__ void pd_mfma(f32x16_t& acc, const uint4& a, const uint32_t (&b)[4]) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                __builtin_bit_cast(bf16x8_t, make_uint4(b[0], b[1], b[2], b[3])),
-                                                acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, make_uint4(b[0], b[1], b[2], b[3])),
+                                                __builtin_bit_cast(bf16x8_t, a), acc, 0, 0, 0);
 }
 
 // Pair J of an 8-element decode (4 instructions).
@@ -303,6 +305,19 @@ __device__ __forceinline__ void pd_step(const PdLds& L, int xst, int gb, int lan
 
 __device__ __forceinline__ int pd_next_stage(int s) { return s == kPdXStages - 1 ? 0 : s + 1; }
 
+// Two floats as a BF16 pair, round to nearest even (v_cvt_pk_bf16_f32; a NaN
+// comes out as a quiet NaN).
+__device__ __forceinline__ uint32_t pd_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Items V .. V + 3 of an accumulator times the tensor scale, as 4 BF16.
+__device__ __forceinline__ uint2 pd_pack4(const f32x16_t& a, int V, float ts) {
+  return make_uint2(pd_bf16x2(a[V] * ts, a[V + 1] * ts), pd_bf16x2(a[V + 2] * ts, a[V + 3] * ts));
+}
+
 // Copy the BF16 tile (128 x 272, row-major in LDS) to Y rows m0.., columns
 // n0..: 34 pieces of 8 columns per row, 17 per thread.  Pieces that are whole,
 // inside Y and 16-byte aligned go as one store; the others element by element.
@@ -387,17 +402,27 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   // Fifth tile: add the wavefronts' partial sums in wavefront order; wavefront
   // W finishes row tile W.
   __syncthreads();
-  f32x16_t* red = reinterpret_cast<f32x16_t*>(&L.wg[0]);  // 4 x 4 x 64 lanes x 64 B = 64 KB of the 68 KB weight groups
+  // Only items 0..7 hold real columns (256 + 8 (v / 4) + 4h + v % 4 < 272).
+  float4* red = reinterpret_cast<float4*>(&L.wg[0]);  // 4 x 4 x 2 x 64 lanes x 16 B = 32 KB of the weight groups
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) red[(W * 4 + rt) * 64 + lane] = acc5[rt];
+  for (int rt = 0; rt < 4; ++rt) {
+    red[((W * 4 + rt) * 2 + 0) * 64 + lane] = make_float4(acc5[rt][0], acc5[rt][1], acc5[rt][2], acc5[rt][3]);
+    red[((W * 4 + rt) * 2 + 1) * 64 + lane] = make_float4(acc5[rt][4], acc5[rt][5], acc5[rt][6], acc5[rt][7]);
+  }
   __syncthreads();
-  f32x16_t t5 = red[(0 * 4 + W) * 64 + lane];
+  float4 t5a = red[((0 * 4 + W) * 2 + 0) * 64 + lane], t5b = red[((0 * 4 + W) * 2 + 1) * 64 + lane];
 #pragma unroll
-  for (int ww = 1; ww < 4; ++ww) t5 += red[(ww * 4 + W) * 64 + lane];
+  for (int ww = 1; ww < 4; ++ww) {
+    const float4 a = red[((ww * 4 + W) * 2 + 0) * 64 + lane], b = red[((ww * 4 + W) * 2 + 1) * 64 + lane];
+    t5a.x += a.x; t5a.y += a.y; t5a.z += a.z; t5a.w += a.w;
+    t5b.x += b.x; t5b.y += b.y; t5b.z += b.z; t5b.w += b.w;
+  }
 
   // Epilogue: the BF16 tile goes through LDS (the X stages, free now) so that
-  // the stores to Y are whole 16-byte pieces of rows.  32x32 D layout: item v
-  // of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+  // the stores to Y are whole 16-byte pieces of rows.  Transposed 32x32 D
+  // layout: item v of lane l is row l % 32 of Y's row tile and column
+  // 8 (v / 4) + 4 (l / 32) + v % 4 of the column tile, so items 4q .. 4q + 3
+  // are 4 consecutive columns (one 8-byte LDS write).
   const float ts = *p.tscale;
   const int l32 = lane & 31, h = lane >> 5;
   uint16_t* yt = reinterpret_cast<uint16_t*>(&L.xs[0]);  // [128][272] BF16, 69,632 bytes
@@ -406,14 +431,14 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        yt[(32 * rt + 8 * (v >> 2) + 4 * h + (v & 3)) * kPdBN + 64 * W + 32 * c + l32] =
-            (uint16_t)f32_to_bf16_rne(acc[rt][c][v] * ts);
-  if (l32 < 16) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      yt[(32 * W + 8 * (v >> 2) + 4 * h + (v & 3)) * kPdBN + 256 + l32] = (uint16_t)f32_to_bf16_rne(t5[v] * ts);
-  }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint2*>(yt + (32 * rt + l32) * kPdBN + 64 * W + 32 * c + 8 * q + 4 * h) =
+            pd_pack4(acc[rt][c], 4 * q, ts);
+  // Fifth tile: columns 256 + 8 (v / 4) + 4h + v % 4 exist for v < 8.
+  *reinterpret_cast<uint2*>(yt + (32 * W + l32) * kPdBN + 256 + 4 * h) =
+      make_uint2(pd_bf16x2(t5a.x * ts, t5a.y * ts), pd_bf16x2(t5a.z * ts, t5a.w * ts));
+  *reinterpret_cast<uint2*>(yt + (32 * W + l32) * kPdBN + 264 + 4 * h) =
+      make_uint2(pd_bf16x2(t5b.x * ts, t5b.y * ts), pd_bf16x2(t5b.z * ts, t5b.w * ts));
   __syncthreads();
   pd_store_tile(p, yt, m0, n0, W * 64 + lane);
 }
