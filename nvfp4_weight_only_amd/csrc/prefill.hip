@@ -24,6 +24,8 @@
 // [32h + 8s, 32h + 8s + 8).  A weight lane thus reads 16 contiguous packed bytes
 // per step; activations follow the same order (a dot product does not depend on
 // the order of its terms; only the FP32 summation order changes).
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -70,15 +72,20 @@ struct PdLds {
   PdS sg[2];
 };
 
-__device__ __forceinline__ void pd_lds_dma16(const void* src, uint32_t lds) {
-  // One global_load_lds_dwordx4 (16 bytes per lane to LDS address lds + 16 * lane).
-  // Written out rather than through the compiler builtin, whose wait insertion
-  // loses track of which buffer a pending load writes at a loop head and drains
-  // every load in flight; the instruction has no register result, and the
-  // kernel orders LDS reads after it with explicit vmcnt waits.  M0 is not used
-  // by anything else in this kernel.
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory");
+// One global_load_lds_dwordx4: 16 bytes per lane from base + off (a
+// wavefront-uniform base and a per-lane 32-bit byte offset) to LDS address
+// lds + 16 * lane.  Written out rather than through the compiler builtin, whose
+// wait insertion loses track of which buffer a pending load writes at a loop
+// head and drains every load in flight; the instruction has no register
+// result, and the kernel orders LDS reads after it with explicit vmcnt waits.
+// M0 is not used by anything else in this kernel.
+__device__ __forceinline__ void pd_lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // readfirstlane returns int: widen through uint32_t, never by sign extension.
+  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(bs) : "memory");
 }
 
 template <typename U>
@@ -107,34 +114,61 @@ __device__ __forceinline__ void pd_wait_vmcnt_lds0() {
 // last); scales 2 per group (5 instructions of 64 rows, three spare slots).
 constexpr int kPdLX = 4, kPdLW = 9, kPdLS = 2;
 
+// Per-lane byte offsets of the loads, from the tile's first row (X) or
+// column (weights, scales) at K = 0.
 struct PdSrc {
-  const uint16_t* x[kPdLX];  // step 0 sources
-  const uint8_t* w[kPdLW];   // group 0 sources
-  const uint8_t* s[kPdLS];
+  uint32_t x[kPdLX];
+  uint32_t w[kPdLW];
+  uint32_t s[kPdLS];
 };
 
-// Loads of step t into X stage `xst` and, when the step starts a group
-// (P == 0), of group t / 4 into weight / scale buffer (t / 4) % 2.  Past the
+// The loads of one step: wavefront-uniform global bases and LDS byte
+// addresses of the destination buffers.
+struct PdDma {
+  const uint8_t *xb, *wb, *sb;
+  uint32_t xs, wg, sg;
+};
+
+// Bases of the loads of step t into X stage `xst` and, when the step starts a
+// group, of group t / 4 into weight / scale buffer (t / 4) % 2.  Past the
 // end, the last step / group is loaded again into buffers nothing reads.
-template <int P>
-__device__ __forceinline__ void pd_issue(const PdSrc& src, int t, int nsteps, PdLds& L, int xst, int w) {
+__device__ __forceinline__ PdDma pd_dma_begin(const PdArgs& p, int64_t m0, int64_t n0, int t, int nsteps,
+                                              const PdLds& L, int xst) {
   const int tc = t < nsteps ? t : nsteps - 1;
-#pragma unroll
-  for (int i = 0; i < kPdLX; ++i)
-    pd_lds_dma16(src.x[i] + (int64_t)tc * kPdBK, pd_lds_addr(&L.xs[xst].v[64 * (w + 4 * i)]));
-  if (P == 0) {
-    const int gc = tc >> 2, gb = (t >> 2) & 1;
-#pragma unroll
-    for (int i = 0; i < kPdLW; ++i) {
-      const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1;
-      pd_lds_dma16(src.w[i] + (int64_t)gc * (kPdGroupK / 2), pd_lds_addr(&L.wg[gb].v[64 * q]));
-    }
-#pragma unroll
-    for (int i = 0; i < kPdLS; ++i) {
-      const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4;
-      pd_lds_dma16(src.s[i] + (int64_t)gc * (kPdGroupK / 16), pd_lds_addr(&L.sg[gb].v[64 * q]));
-    }
+  const int64_t gc = tc >> 2;
+  const int gb = (t >> 2) & 1;
+  return PdDma{reinterpret_cast<const uint8_t*>(p.x + m0 * p.k) + (int64_t)tc * (2 * kPdBK),
+               p.packed + n0 * (p.k >> 1) + gc * (kPdGroupK / 2), p.scales + n0 * (p.k >> 4) + gc * (kPdGroupK / 16),
+               pd_lds_addr(&L.xs[xst]), pd_lds_addr(&L.wg[gb]), pd_lds_addr(&L.sg[gb])};
+}
+
+// Load instruction I of a step (place in group P): 0..3 activations, then at a
+// group start 4..12 weights and 13..14 scales; nothing for other I.
+template <int P, int I>
+__device__ __forceinline__ void pd_dma_one(const PdSrc& src, const PdDma& d, int w) {
+  if constexpr (I < kPdLX) {
+    pd_lds_dma16(d.xb, src.x[I], d.xs + 1024 * (w + 4 * I));
+  } else if constexpr (P == 0 && I < kPdLX + kPdLW) {
+    constexpr int i = I - kPdLX;
+    const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1;
+    pd_lds_dma16(d.wb, src.w[i], d.wg + 1024 * q);
+  } else if constexpr (P == 0 && I < kPdLX + kPdLW + kPdLS) {
+    constexpr int i = I - kPdLX - kPdLW;
+    const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4;
+    pd_lds_dma16(d.sb, src.s[i], d.sg + 1024 * q);
   }
+}
+
+template <int P, int... I>
+__device__ __forceinline__ void pd_dma_all(const PdSrc& src, const PdDma& d, int w, std::integer_sequence<int, I...>) {
+  (pd_dma_one<P, I>(src, d, w), ...);
+}
+
+// All loads of step t (before the loop).
+template <int P>
+__device__ __forceinline__ void pd_issue(const PdArgs& p, const PdSrc& src, int64_t m0, int64_t n0, int t, int nsteps,
+                                         const PdLds& L, int xst, int w) {
+  pd_dma_all<P>(src, pd_dma_begin(p, m0, n0, t, nsteps, L, xst), w, std::make_integer_sequence<int, 15>{});
 }
 
 // One step's operands for one wavefront, read from LDS a step ahead of use.
@@ -212,12 +246,14 @@ __device__ __forceinline__ uint32_t pd_dec(uint32_t word, float sc) {
 
 // One K step S of the current step: its 8 MFMAs (row tile i / 2, column tile
 // i % 2) on the decoded fragments `bc`, each followed by one pair of the next
-// K step's decode into `bn` (tile i / 4) and, for the first four, the read of
-// one A fragment of the next step (K step S).  The fixed order keeps the
+// K step's decode into `bn` (tile i / 4), one of the step's global-to-LDS
+// loads (step place P, load 8 S + i) and, for the first four, the read of one
+// A fragment of the next step (K step S).  The fixed order keeps the
 // decode in the MFMAs' shadow and at most a few LDS reads in flight.
-template <int S>
+template <int S, int P>
 __device__ __forceinline__ void pd_kstep(const PdLds& L, int xst, int lane, const PdFrag& C, PdFrag& N,
-                                         const PdB& bc, PdB& bn, f32x16_t (&acc)[4][2]) {
+                                         const PdB& bc, PdB& bn, f32x16_t (&acc)[4][2], const PdSrc& src,
+                                         const PdDma& dma, int w) {
   const int l32 = lane & 31, h = lane >> 5;
   const PdX& X = L.xs[xst];
   const float sc0 = pd_scale<S + 1>(C, h, 0), sc1 = pd_scale<S + 1>(C, h, 1);
@@ -225,6 +261,7 @@ __device__ __forceinline__ void pd_kstep(const PdLds& L, int xst, int lane, cons
 #define PD_G(I, DEC)                                                               \
   pd_mfma(acc[(I) / 2][(I) % 2], C.xa[(I) / 2][S], bc.v[(I) % 2]);                  \
   DEC;                                                                             \
+  pd_dma_one<P, 8 * S + (I)>(src, dma, w);                                         \
   if ((I) < 4) {                                                                   \
     const int r = 32 * (I) + l32;                                                  \
     N.xa[(I) & 3][S] = X.v[r * 8 + ((4 * h + S) ^ (r & 7))];                       \
@@ -256,19 +293,22 @@ __device__ __forceinline__ void pd_decode0(const PdFrag& F, int h, PdB& b) {
 
 // The MFMAs of one step on operands `C` (read during the previous step; `b`
 // holds their K step 0 decoded) while reading the next step's operands `N`
-// (X stage `xst`, group buffer `gb`, place in group PN) and decoding ahead:
-// K steps 1..3 during the K step before, the fifth tile's fragment and N's
-// K step 0 (left in `b`) during K step 3 and the fifth tile's MFMAs.
+// (X stage `xst`, group buffer `gb`, place in group PN), issuing the loads
+// `dma` of the step four ahead, and decoding ahead: K steps 1..3 during the
+// K step before, the fifth tile's fragment and N's K step 0 (left in `b`)
+// during K step 3 and the fifth tile's MFMAs.
 template <int PN, int W>
 __device__ __forceinline__ void pd_step(const PdLds& L, int xst, int gb, int lane, const PdFrag& C, PdFrag& N,
-                                        PdB& b, f32x16_t (&acc)[4][2], f32x16_t (&acc5)[4]) {
+                                        PdB& b, f32x16_t (&acc)[4][2], f32x16_t (&acc5)[4], const PdSrc& src,
+                                        const PdDma& dma) {
+  constexpr int P = (PN + 3) & 3;  // place in group of this step (and of the step it loads)
   const int l32 = lane & 31, h = lane >> 5;
   PdB t;
   pd_load_w<PN, W>(L, gb, lane, N);
   __builtin_amdgcn_sched_barrier(0);
-  pd_kstep<0>(L, xst, lane, C, N, b, t, acc);
-  pd_kstep<1>(L, xst, lane, C, N, t, b, acc);
-  pd_kstep<2>(L, xst, lane, C, N, b, t, acc);
+  pd_kstep<0, P>(L, xst, lane, C, N, b, t, acc, src, dma, W);
+  pd_kstep<1, P>(L, xst, lane, C, N, t, b, acc, src, dma, W);
+  pd_kstep<2, P>(L, xst, lane, C, N, b, t, acc, src, dma, W);
   // K step 3: MFMAs on t; decode the fifth tile's fragment and N's K step 0, tile 0.
   const PdX& X = L.xs[xst];
   const float s5 = e4m3x2_to_f32<false>((C.s5 >> (16 * h + 8 * (W >> 1))) & 0xFFu).x;
@@ -352,10 +392,10 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
     for (int e = 0; e < 16; ++e) acc[rt][0][e] = acc[rt][1][e] = acc5[rt][e] = 0.0f;
   }
 
-  pd_issue<0>(src, 0, nsteps, L, 0, W);
-  pd_issue<1>(src, 1, nsteps, L, 1, W);
-  pd_issue<2>(src, 2, nsteps, L, 2, W);
-  pd_issue<3>(src, 3, nsteps, L, 3, W);
+  pd_issue<0>(p, src, m0, n0, 0, nsteps, L, 0, W);
+  pd_issue<1>(p, src, m0, n0, 1, nsteps, L, 1, W);
+  pd_issue<2>(p, src, m0, n0, 2, nsteps, L, 2, W);
+  pd_issue<3>(p, src, m0, n0, 3, nsteps, L, 3, W);
   pd_wait_vmcnt<3 * kPdLX>();  // step 0 (and group 0) landed; steps 1..3 may be in flight
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -385,9 +425,9 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
     asm volatile("" ::: "memory");                                                   \
     __builtin_amdgcn_s_barrier();                                                    \
     asm volatile("" ::: "memory");                                                   \
-    pd_issue<P>(src, t + 4, nsteps, L, xld, W);                                      \
+    const PdDma dma = pd_dma_begin(p, m0, n0, t + 4, nsteps, L, xld);                \
     xld = pd_next_stage(xld);                                                        \
-    pd_step<((P) + 1) & 3, W>(L, xrd, ((t + 1) >> 2) & 1, lane, CUR, NXT, bdec, acc, acc5); \
+    pd_step<((P) + 1) & 3, W>(L, xrd, ((t + 1) >> 2) & 1, lane, CUR, NXT, bdec, acc, acc5, src, dma); \
     xrd = pd_next_stage(xrd);                                                        \
   }
   for (int tb = 0; tb < nsteps; tb += 4) {
@@ -459,26 +499,26 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   const int nsteps = (int)(p.k / kPdBK);  // a multiple of 4
   const int64_t kh = p.k >> 1, ks = p.k >> 4;
 
-  // Per-lane sources; rows past m or n repeat the last valid row (never stored).
+  // Per-lane offsets; rows past m or n repeat the last valid row (never stored).
   PdSrc src;
 #pragma unroll
   for (int i = 0; i < kPdLX; ++i) {
     const int q = w + 4 * i, r = 8 * q + (lane >> 3);
-    const int64_t gm = m0 + r < p.m ? m0 + r : p.m - 1;
-    src.x[i] = p.x + gm * p.k + 8 * ((lane & 7) ^ (r & 7));
+    const int64_t gm = m0 + r < p.m ? r : p.m - 1 - m0;
+    src.x[i] = (uint32_t)(gm * p.k * 2 + 16 * ((lane & 7) ^ (r & 7)));
   }
 #pragma unroll
   for (int i = 0; i < kPdLW; ++i) {
     const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1, r = 8 * q + (lane >> 3);
-    const int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1;
-    src.w[i] = p.packed + gn * kh + 16 * ((lane & 7) ^ (r & 7));
+    const int64_t gn = n0 + r < p.n ? r : p.n - 1 - n0;
+    src.w[i] = (uint32_t)(gn * kh + 16 * ((lane & 7) ^ (r & 7)));
   }
 #pragma unroll
   for (int i = 0; i < kPdLS; ++i) {
     const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4, r = 64 * q + lane;
     const int rr = r < kPdBN ? r : kPdBN - 1;  // LDS rows 272..319 hold a repeat (never read)
-    const int64_t gn = n0 + rr < p.n ? n0 + rr : p.n - 1;
-    src.s[i] = p.scales + gn * ks;
+    const int64_t gn = n0 + rr < p.n ? rr : p.n - 1 - n0;
+    src.s[i] = (uint32_t)(gn * ks);
   }
 
   switch (w) {
@@ -491,7 +531,11 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
 
 }  // namespace
 
-bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) { return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0; }
+// The per-lane load offsets are 32-bit: a 128-row activation tile (256 k
+// bytes) must stay below 4 GiB.
+bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) {
+  return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0 && k < ((int64_t)1 << 24);
+}
 
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
