@@ -213,6 +213,8 @@ def profile_run(what, launches):
 
     decode: nvfp4_linear on the decode workload, cycling through rotated weight copies so that every
             launch streams its weights from HBM;
+    prefill / prefill2048: nvfp4_linear on the prefill workload (N=17408, K=5120) at M=512 / 2048,
+            rotated weight copies;
     copy:   a plain 256 MiB device-to-device copy (torch's copy kernel), the calibration for the
             FETCH_SIZE / WRITE_SIZE counters (each launch moves exactly 256 MiB each way).
     """
@@ -224,11 +226,12 @@ def profile_run(what, launches):
             dst.copy_(src)
     else:
         nv.lib()
-        wl = WL.WORKLOADS["decode"]
+        wl = WL.WORKLOADS["decode" if what == "decode" else "prefill"]
+        m = {"decode": 1, "prefill": 512, "prefill2048": 2048}[what]
         packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
-        x = dev_bf16(wl.activations(1))
+        x = dev_bf16(wl.activations(m))
         rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
-        y = torch.empty((1, wl.n), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
         for i in range(launches):
             p, s, t = rot.items[i % len(rot)]
@@ -244,7 +247,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--profile", choices=["decode", "copy"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()
