@@ -173,7 +173,7 @@ def bench_quant_rows(reps):
         "quantize_decode_5120x5120": {"us_per_call": round(ms_q * 1e3, 2),
                                       "gb_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
                                       "hbm_frac": round(q_bytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "bytes": q_bytes, "note": "4 launches: zero, amax pass, quantize pass, tscale"},
+                                      "bytes": q_bytes, "note": "4 launches: amax partial maxima, amax reduce, quantize pass, tscale"},
         "dequant_decode_5120x5120": {"us_per_call": round(ms_d * 1e3, 2),
                                      "gb_s": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
                                      "hbm_frac": round(d_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -72,7 +72,8 @@ const char* nvfp4_version(void);
  *             ties to the even code, saturating at 6; 0 when s = 0
  * Every rounding decision is taken on the exact real quotient.
  * w: [n, k] BF16.  Outputs packed [n, k/2], scales [n, k/16], tscale [1].
- * The tscale slot is used as scratch for amax during the call.
+ * The tscale slot is used as scratch for amax, and packed for per-workgroup
+ * maxima, during the call.
  */
 nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k,
                             uint8_t* packed, uint8_t* scales, float* tscale, void* stream);

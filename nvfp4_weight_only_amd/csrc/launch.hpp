@@ -7,8 +7,9 @@
 
 namespace nvfp4 {
 
-void launch_fill_zero(float* p, hipStream_t s);
 void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s);
+// *amax = max |w|, with per-workgroup maxima in part (at least n_elems / 8 32-bit words).
+void launch_amax_set(const uint16_t* w, int64_t n_elems, uint32_t* part, float* amax, hipStream_t s);
 void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s);
 void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
                      hipStream_t s);

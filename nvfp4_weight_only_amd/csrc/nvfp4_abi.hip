@@ -153,9 +153,10 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* pa
   if ((st = validate_quantize_outputs(w, ws, packed, scales, tscale)) != NVFP4_OK) return st;
   if ((st = check_device()) != NVFP4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The tscale slot holds amax until the last kernel turns it into amax / 2688.
-  nvfp4::launch_fill_zero(tscale, s);
-  nvfp4::launch_amax(w, ws.elems, tscale, s);
+  // The tscale slot holds amax until the last kernel turns it into amax / 2688;
+  // the packed output (n k / 2 bytes) holds the per-workgroup maxima until the
+  // quantize pass overwrites it.
+  nvfp4::launch_amax_set(w, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
   nvfp4::launch_quantize(w, ws.elems, tscale, packed, scales, s);
   nvfp4::launch_finalize_tscale(tscale, tscale, s);
   return launch_status();

@@ -16,30 +16,69 @@
 namespace nvfp4 {
 
 // ---------------------------------------------------------------------------
-// amax: max |w| over the tensor, merged into *amax with an unsigned atomic max
-// on the FP32 bit pattern (order-free, so the result is deterministic).
+// amax: max |w| over the tensor.  The maximum of BF16 magnitudes is taken on
+// their bit patterns (bits & 0x7FFF order like the values), so it is exact
+// and independent of the order.  Each thread keeps kAmaxU 16-byte loads in
+// flight; a workgroup reduces to one value, which goes either to a partial
+// slot (reduced by one more workgroup) or, to merge into a caller's running
+// maximum, through an unsigned atomic max on the FP32 bit pattern.  Same-
+// address atomics serialise, so the atomic form uses few workgroups.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) fill_zero_kernel(float* p) { *p = 0.0f; }
+constexpr int kAmaxU = 8;
+constexpr int kAmaxBlocks = 512;
 
-__global__ void __launch_bounds__(256) amax_kernel(const uint4* __restrict__ w, int64_t n_vec, float* amax) {
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(uint4 v) {
+  const uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  const uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+
+// The workgroup's maximum |w| (BF16 magnitude bits), valid in thread 0.
+__device__ __forceinline__ uint32_t amax_block(const uint4* __restrict__ w, int64_t n_vec) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
-    const uint4 v = w[i];
-    const uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-    const uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-    m = max(m, max(a, b));
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * kAmaxU;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x * kAmaxU + threadIdx.x; i0 < n_vec; i0 += stride) {
+    uint4 v[kAmaxU];
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) {
+      const int64_t i = i0 + (int64_t)u * blockDim.x;
+      v[u] = i < n_vec ? w[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) m = max(m, bf16x8_absmax_bits(v[u]));
   }
   m = wave_max_u32(m);
   __shared__ uint32_t part[4];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) part[wid] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = part[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
-    atomicMax(reinterpret_cast<unsigned int*>(amax), r << 16);  // BF16 magnitude -> FP32 bits
-  }
+  uint32_t r = part[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, part[i]);
+  return r;
+}
+
+// Per-workgroup maxima into part[blockIdx.x] (BF16 magnitude bits).
+__global__ void __launch_bounds__(256) amax_partial_kernel(const uint4* __restrict__ w, int64_t n_vec,
+                                                           uint32_t* __restrict__ part) {
+  const uint32_t r = amax_block(w, n_vec);
+  if (threadIdx.x == 0) part[blockIdx.x] = r;
+}
+
+// *amax = max of part[0 .. nb) as an FP32 value (the BF16 magnitude widened).
+__global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __restrict__ part, int nb, float* amax) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) m = max(m, part[i]);
+  m = wave_max_u32(m);
+  __shared__ uint32_t pw[4];
+  if ((threadIdx.x & 63) == 0) pw[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *amax = __uint_as_float(max(max(pw[0], pw[1]), max(pw[2], pw[3])) << 16);
+}
+
+// *amax = max(*amax, max |w|) through an atomic max on the FP32 bits.
+__global__ void __launch_bounds__(256) amax_kernel(const uint4* __restrict__ w, int64_t n_vec, float* amax) {
+  const uint32_t r = amax_block(w, n_vec);
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), r << 16);  // BF16 magnitude -> FP32 bits
 }
 
 // tscale = fl32(amax / 2688), IEEE round-to-nearest division.
@@ -135,21 +174,16 @@ __device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThreshold
   return mag | ((b >> 12) & 8u);
 }
 
-// One thread per 8 consecutive elements (a half block); lanes 2i and 2i+1 hold
-// the two halves of one 16-element block.  w is read as uint4 (8 BF16),
-// packed is written as one 32-bit word per thread, the scale byte by the even lane.
-__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
-                                                       const float* __restrict__ amax_p,
-                                                       uint32_t* __restrict__ packed,
-                                                       uint8_t* __restrict__ scales) {
-  const uint32_t amax_b = __float_as_uint(*amax_p) >> 16;  // amax is a BF16 value held in FP32
-  uint32_t sa;
-  int ea;
-  bf16_split(amax_b & 0x7FFFu, sa, ea);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even: keeps the lane pairing
-  // n_half is even (k % 16 == 0), so both lanes of a pair leave the loop together.
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
-    const uint4 v = w[h];
+// One thread per 8 consecutive elements (a half block) at a time; lanes 2i and
+// 2i+1 hold the two halves of one 16-element block.  w is read as uint4 (8
+// BF16), packed is written as one 32-bit word per half block, the scale byte by
+// the even lane.  Each thread loads kQuantU half blocks (blockDim apart) before
+// encoding them, to keep several loads in flight.
+constexpr int kQuantU = 4;
+
+__device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t amax_b, uint32_t sa, int ea,
+                                              uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  {
     const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
     uint32_t lm = 0;
@@ -167,19 +201,42 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
   }
 }
 
+__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
+                                                       const float* __restrict__ amax_p,
+                                                       uint32_t* __restrict__ packed,
+                                                       uint8_t* __restrict__ scales) {
+  const uint32_t amax_b = __float_as_uint(*amax_p) >> 16;  // amax is a BF16 value held in FP32
+  uint32_t sa;
+  int ea;
+  bf16_split(amax_b & 0x7FFFu, sa, ea);
+  // The stride and blockDim are even, and n_half is even (k % 16 == 0), so both
+  // lanes of a pair take the same branches.
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * kQuantU;
+  for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x * kQuantU + threadIdx.x; h0 < n_half; h0 += stride) {
+    uint4 v[kQuantU];
+#pragma unroll
+    for (int u = 0; u < kQuantU; ++u) {
+      const int64_t h = h0 + (int64_t)u * blockDim.x;
+      v[u] = h < n_half ? w[h] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantU; ++u) {
+      const int64_t h = h0 + (int64_t)u * blockDim.x;
+      if (h < n_half) quantize_half(v[u], h, amax_b, sa, ea, packed, scales);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Dequantize: w = RNE_bf16(fl32(fl32(E2M1 * E4M3) * tscale)).  One thread per
-// 8 elements: one packed word in, one uint4 (8 BF16) out.
+// 8 elements at a time: one packed word in, one uint4 (8 BF16) out; each
+// thread loads kDequantU words (blockDim apart) before decoding them.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict__ packed,
-                                                      const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ tscale_p, int64_t n_half,
-                                                      uint4* __restrict__ out) {
-  const float t = *tscale_p;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
-    const uint32_t p = packed[h];
-    const float s = e4m3_to_f32(scales[h >> 1]);
+constexpr int kDequantU = 4;
+
+__device__ __forceinline__ uint4 dequant_half(uint32_t p, uint32_t sbyte, float t) {
+  {
+    const float s = e4m3_to_f32(sbyte);
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -194,7 +251,29 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict
       }
       o[j] = pair;
     }
-    out[h] = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict__ packed,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ tscale_p, int64_t n_half,
+                                                      uint4* __restrict__ out) {
+  const float t = *tscale_p;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * kDequantU;
+  for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x * kDequantU + threadIdx.x; h0 < n_half; h0 += stride) {
+    uint32_t p[kDequantU], sb[kDequantU];
+#pragma unroll
+    for (int u = 0; u < kDequantU; ++u) {
+      const int64_t h = h0 + (int64_t)u * blockDim.x;
+      p[u] = h < n_half ? packed[h] : 0u;
+      sb[u] = h < n_half ? scales[h >> 1] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kDequantU; ++u) {
+      const int64_t h = h0 + (int64_t)u * blockDim.x;
+      if (h < n_half) out[h] = dequant_half(p[u], sb[u], t);
+    }
   }
 }
 
@@ -208,11 +287,19 @@ static inline unsigned grid_for(int64_t items, int threads, int64_t max_blocks) 
   return (unsigned)b;
 }
 
-void launch_fill_zero(float* p, hipStream_t s) { fill_zero_kernel<<<1, 64, 0, s>>>(p); }
-
 void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s) {
   const int64_t n_vec = n_elems / 8;
-  amax_kernel<<<grid_for(n_vec, 256, 4096), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, amax);
+  amax_kernel<<<grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec,
+                                                                          amax);
+}
+
+void launch_amax_set(const uint16_t* w, int64_t n_elems, uint32_t* part, float* amax, hipStream_t s) {
+  // part holds at least n_elems / 8 words (the packed output of a quantizer call), and the grid never exceeds
+  // n_elems / 8 workgroups.
+  const int64_t n_vec = n_elems / 8;
+  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
+  amax_partial_kernel<<<nb, 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part);
+  amax_reduce_kernel<<<1, 256, 0, s>>>(part, (int)nb, amax);
 }
 
 void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s) {
@@ -222,14 +309,14 @@ void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s) {
 void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
                      hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  quantize_kernel<<<grid_for(n_half, 256, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_half, amax,
+  quantize_kernel<<<grid_for(n_half, 256 * kQuantU, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_half, amax,
                                                                   reinterpret_cast<uint32_t*>(packed), scales);
 }
 
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n_elems,
                     uint16_t* out, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  dequant_kernel<<<grid_for(n_half, 256, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales,
+  dequant_kernel<<<grid_for(n_half, 256 * kDequantU, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales,
                                                                  tscale, n_half, reinterpret_cast<uint4*>(out));
 }
 
