@@ -37,7 +37,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) const void pd_lds_t;
 
 constexpr int kPdBM = 128, kPdBN = 272, kPdBK = 64, kPdGroupK = 256;
-constexpr int kPdSRows = 320;  // scale rows in LDS: 5 instructions of 64 rows cover the 272 block rows
 
 struct PdArgs {
   const uint16_t* x;  // [m, k]
@@ -49,28 +48,34 @@ struct PdArgs {
   int n_tiles, m_tiles;
 };
 
-// LDS (16-byte slots; the XOR with the row makes 8 consecutive rows at the same
-// piece hit different banks):
-//   x stage: activation row r (of 128), piece p (8 elements) at 8 r + (p ^ (r & 7));
-//   w group: weight row r (of 272), piece p (32 elements) at 8 r + (p ^ (r & 7));
-//   s group: weight row r's 16 scale bytes at slot r.
+// LDS (16-byte slots):
+//   x stage: activation row r (of 128), piece p (8 elements) at 8 r + (p ^ (r & 7))
+//            (the XOR makes 8 consecutive rows at the same piece hit different banks);
+//   w group: weight row r (of 272) in 9 slots at 9 r: its 8 packed pieces of 32
+//            elements, then its 16 scale bytes.  The odd row stride spreads 16
+//            consecutive rows over all banks, and a scale byte travels with
+//            its row's weights instead of in a 64-row gather of its own.
+constexpr int kPdWSlots = 9;
 struct PdX {
   uint4 v[kPdBM * 8];
 };
 struct PdW {
-  uint4 v[kPdBN * 8];
+  uint4 v[kPdBN * kPdWSlots];
 };
-struct PdS {
-  uint4 v[kPdSRows];
-};
-// Five activation stages (16 KB each), two weight groups (34 KB) and two scale
-// groups (5 KB): 161,792 bytes of the 160 KB of LDS.
+// Five activation stages (16 KB each) and two weight groups (38.25 KB):
+// 160,256 bytes of the 160 KB of LDS.
 constexpr int kPdXStages = 5;
 struct PdLds {
   PdX xs[kPdXStages];
   PdW wg[2];
-  PdS sg[2];
 };
+
+// One global_load_lds_dwordx4 from a per-lane 64-bit address (the weight group
+// loads mix the packed and the scale arrays in one instruction).
+__device__ __forceinline__ void pd_lds_dma16_ptr(const void* src, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+}
 
 // One global_load_lds_dwordx4: 16 bytes per lane from base + off (a
 // wavefront-uniform base and a per-lane 32-bit byte offset) to LDS address
@@ -110,23 +115,28 @@ __device__ __forceinline__ void pd_wait_vmcnt_lds0() {
 }
 
 // Load instructions per wavefront: X 4 per step (16 instructions of 8 rows);
-// weights 9 per group (34 instructions of 8 rows, two spare slots repeat the
-// last); scales 2 per group (5 instructions of 64 rows, three spare slots).
-constexpr int kPdLX = 4, kPdLW = 9, kPdLS = 2;
+// weights and scales 10 per group (272 x 9 slots = 38.25 instructions of 64
+// slots; the last instruction is placed to end at slot 2448, and the spare
+// repeats it).
+constexpr int kPdLX = 4, kPdLW = 10;
+constexpr int kPdWLast = kPdBN * kPdWSlots - 64;  // first slot of the last weight instruction
 
-// Per-lane byte offsets of the loads, from the tile's first row (X) or
-// column (weights, scales) at K = 0.
+// Per-lane sources of the loads: activation byte offsets from the tile's first
+// row at K = 0, and the group 0 addresses of the weight / scale slots, with a
+// bit per instruction that marks a scale slot (16 bytes further per group
+// instead of 128).
 struct PdSrc {
   uint32_t x[kPdLX];
-  uint32_t w[kPdLW];
-  uint32_t s[kPdLS];
+  const uint8_t* w[kPdLW];
+  uint32_t wscale;
 };
 
-// The loads of one step: wavefront-uniform global bases and LDS byte
-// addresses of the destination buffers.
+// The loads of one step: the activation base, the weight group index, and LDS
+// byte addresses of the destination buffers.
 struct PdDma {
-  const uint8_t *xb, *wb, *sb;
-  uint32_t xs, wg, sg;
+  const uint8_t* xb;
+  int64_t gc;
+  uint32_t xs, wg;
 };
 
 // Bases of the loads of step t into X stage `xst` and, when the step starts a
@@ -137,25 +147,23 @@ __device__ __forceinline__ PdDma pd_dma_begin(const PdArgs& p, int64_t m0, int64
   const int tc = t < nsteps ? t : nsteps - 1;
   const int64_t gc = tc >> 2;
   const int gb = (t >> 2) & 1;
-  return PdDma{reinterpret_cast<const uint8_t*>(p.x + m0 * p.k) + (int64_t)tc * (2 * kPdBK),
-               p.packed + n0 * (p.k >> 1) + gc * (kPdGroupK / 2), p.scales + n0 * (p.k >> 4) + gc * (kPdGroupK / 16),
-               pd_lds_addr(&L.xs[xst]), pd_lds_addr(&L.wg[gb]), pd_lds_addr(&L.sg[gb])};
+  (void)n0;
+  return PdDma{reinterpret_cast<const uint8_t*>(p.x + m0 * p.k) + (int64_t)tc * (2 * kPdBK), gc,
+               pd_lds_addr(&L.xs[xst]), pd_lds_addr(&L.wg[gb])};
 }
 
 // Load instruction I of a step (place in group P): 0..3 activations, then at a
-// group start 4..12 weights and 13..14 scales; nothing for other I.
+// group start 4..13 weight rows with their scales; nothing for other I.
 template <int P, int I>
 __device__ __forceinline__ void pd_dma_one(const PdSrc& src, const PdDma& d, int w) {
   if constexpr (I < kPdLX) {
     pd_lds_dma16(d.xb, src.x[I], d.xs + 1024 * (w + 4 * I));
   } else if constexpr (P == 0 && I < kPdLX + kPdLW) {
     constexpr int i = I - kPdLX;
-    const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1;
-    pd_lds_dma16(d.wb, src.w[i], d.wg + 1024 * q);
-  } else if constexpr (P == 0 && I < kPdLX + kPdLW + kPdLS) {
-    constexpr int i = I - kPdLX - kPdLW;
-    const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4;
-    pd_lds_dma16(d.sb, src.s[i], d.sg + 1024 * q);
+    const int q0 = 64 * (w + 4 * i);
+    const int q = q0 < kPdWLast ? q0 : kPdWLast;
+    const int64_t step = (src.wscale >> i) & 1u ? kPdGroupK / 16 : kPdGroupK / 2;
+    pd_lds_dma16_ptr(src.w[i] + d.gc * step, d.wg + 16 * q);
   }
 }
 
@@ -168,7 +176,8 @@ __device__ __forceinline__ void pd_dma_all(const PdSrc& src, const PdDma& d, int
 template <int P>
 __device__ __forceinline__ void pd_issue(const PdArgs& p, const PdSrc& src, int64_t m0, int64_t n0, int t, int nsteps,
                                          const PdLds& L, int xst, int w) {
-  pd_dma_all<P>(src, pd_dma_begin(p, m0, n0, t, nsteps, L, xst), w, std::make_integer_sequence<int, 15>{});
+  pd_dma_all<P>(src, pd_dma_begin(p, m0, n0, t, nsteps, L, xst), w,
+                std::make_integer_sequence<int, kPdLX + kPdLW>{});
 }
 
 // One step's operands for one wavefront, read from LDS a step ahead of use.
@@ -189,17 +198,16 @@ template <int P, int W>
 __device__ __forceinline__ void pd_load_w(const PdLds& L, int gb, int lane, PdFrag& F) {
   const int l32 = lane & 31, h = lane >> 5;
   const PdW& Wg = L.wg[gb];
-  const PdS& S = L.sg[gb];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int n = 64 * W + 32 * c + l32;
-    F.wb[c] = Wg.v[n * 8 + ((2 * P + h) ^ (n & 7))];
-    F.sb[c] = reinterpret_cast<const uint32_t*>(&S.v[n])[P];
+    F.wb[c] = Wg.v[n * kPdWSlots + 2 * P + h];
+    F.sb[c] = reinterpret_cast<const uint32_t*>(&Wg.v[n * kPdWSlots + 8])[P];
   }
   // Fifth tile rows 256 + l32 (the upper 16 lanes' rows do not exist and are clamped).
   const int n5 = 256 + (l32 < 16 ? l32 : 15);
-  F.w5 = reinterpret_cast<const uint32_t*>(&Wg.v[n5 * 8 + ((2 * P + h) ^ (n5 & 7))])[W];
-  F.s5 = reinterpret_cast<const uint32_t*>(&S.v[n5])[P];
+  F.w5 = reinterpret_cast<const uint32_t*>(&Wg.v[n5 * kPdWSlots + 2 * P + h])[W];
+  F.s5 = reinterpret_cast<const uint32_t*>(&Wg.v[n5 * kPdWSlots + 8])[P];
 }
 
 template <int S>
@@ -411,7 +419,7 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   int xld = 4, xrd = 1;  // X stages of the next step to load into LDS / to read from LDS
 
   // Step t: wait for this wavefront's loads of step t + 1 (steps t + 2 and t + 3
-  // may stay in flight: 2 x 4, plus 11 when one of them starts a group), meet
+  // may stay in flight: 2 x 4, plus 10 when one of them starts a group), meet
   // the barrier (after it every wavefront has finished step t - 1, so X stage
   // (t - 1) % 5 and, at a group start, the weight buffer of group t / 4 - 1 are
   // free), start the loads of step t + 4, read step t + 1's operands, and run
@@ -421,7 +429,7 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   {                                                                                  \
     const int t = tb + (P);                                                          \
     __builtin_amdgcn_sched_barrier(0);                                               \
-    pd_wait_vmcnt_lds0<((P) == 0 || (P) == 3) ? 2 * kPdLX : 2 * kPdLX + kPdLW + kPdLS>(); \
+    pd_wait_vmcnt_lds0<((P) == 0 || (P) == 3) ? 2 * kPdLX : 2 * kPdLX + kPdLW>();      \
     asm volatile("" ::: "memory");                                                   \
     __builtin_amdgcn_s_barrier();                                                    \
     asm volatile("" ::: "memory");                                                   \
@@ -507,18 +515,14 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
     const int64_t gm = m0 + r < p.m ? r : p.m - 1 - m0;
     src.x[i] = (uint32_t)(gm * p.k * 2 + 16 * ((lane & 7) ^ (r & 7)));
   }
+  src.wscale = 0;
 #pragma unroll
   for (int i = 0; i < kPdLW; ++i) {
-    const int q = (w + 4 * i) < kPdBN / 8 ? (w + 4 * i) : kPdBN / 8 - 1, r = 8 * q + (lane >> 3);
-    const int64_t gn = n0 + r < p.n ? r : p.n - 1 - n0;
-    src.w[i] = (uint32_t)(gn * kh + 16 * ((lane & 7) ^ (r & 7)));
-  }
-#pragma unroll
-  for (int i = 0; i < kPdLS; ++i) {
-    const int q = (w + 4 * i) < 5 ? (w + 4 * i) : 4, r = 64 * q + lane;
-    const int rr = r < kPdBN ? r : kPdBN - 1;  // LDS rows 272..319 hold a repeat (never read)
-    const int64_t gn = n0 + rr < p.n ? rr : p.n - 1 - n0;
-    src.s[i] = (uint32_t)(gn * ks);
+    const int q0 = 64 * (w + 4 * i), slot = (q0 < kPdWLast ? q0 : kPdWLast) + lane;
+    const int r = slot / kPdWSlots, piece = slot - r * kPdWSlots;
+    const int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1;
+    src.w[i] = piece < 8 ? p.packed + gn * kh + 16 * piece : p.scales + gn * ks;
+    src.wscale |= (uint32_t)(piece == 8) << i;
   }
 
   switch (w) {
