@@ -342,7 +342,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemv_decode_5120x5120", digest),
-                     "kernel": "gemv_lds_kernel<32, 1, 5, 10, false>", "bytes_per_launch": nbytes,
+                     "kernel": "gemv_ks_kernel<5, 1>", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "rows": rows,

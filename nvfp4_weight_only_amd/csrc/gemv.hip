@@ -3,17 +3,21 @@
 // The engine's decode linear is a bandwidth-bound GEMV over packed NVFP4
 // weights (imp "docs/quantization.md", NVFP4 kernel pipeline: a GEMV with a
 // register lookup table, split along K).  Design for CDNA4:
-//   - each wavefront owns R weight rows and splits K across its 64 lanes in
-//     16-byte units (32 elements = two 16-element blocks);
-//   - every lane issues all of its weight and scale loads for a batch of JB
-//     units before computing, so a whole launch keeps the weights in flight;
-//   - the activations for the lane's units are read straight into registers and
-//     reused for the R rows (no LDS, no barrier);
+//   - every lane issues all of its weight and scale loads (16-byte units of
+//     32 elements = two 16-element blocks) before computing, so a whole launch
+//     keeps the weights in flight;
 //   - nibbles become BF16 pairs with one v_cvt_scalef32_pk_bf16_fp4 per byte
 //     (scale 1.0: exact E2M1 values), products accumulate with
 //     v_dot2_f32_bf16 in FP32; the E4M3 block scale is one FMA per 16
-//     elements and the tensor scale one multiply per output;
-//   - partial sums are reduced across the wavefront with shuffles.
+//     elements and the tensor scale one multiply per output.
+// Three kernels, by k:
+//   - gemv_ks_kernel (k a multiple of 512, k <= 5120): K split across the
+//     wavefronts of a 20-row workgroup, activations and scales staged per
+//     wavefront with one wide load each, no barrier before the products;
+//   - gemv_lds_kernel (k a multiple of 32, k <= 16384): each wavefront owns
+//     whole rows, the activation row is staged once per workgroup in LDS;
+//   - gemv_loop_kernel (any k a multiple of 16): rows per wavefront, K in
+//     batches, activations read straight into registers.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -213,6 +217,120 @@ __global__ void __launch_bounds__(64 * W) gemv_lds_kernel(const uint16_t* __rest
   }
 }
 
+// K-split GEMV (k % 512 == 0).  A workgroup owns 4 I consecutive rows and
+// splits K across its W wavefronts: wavefront w owns the slice of 16 J units
+// (a unit is 32 elements: 16 packed bytes, 2 scale bytes) starting at unit
+// 16 J w.  Lane (g, u) = (lane / 16, lane % 16) takes rows g + 4 i (i < I) and
+// units u + 16 j (j < J) of the slice.
+//   - Per wavefront, the activation slice (1 KB per J) is one 16-byte load per
+//     lane and the slice's scales of all 4 I rows (32 J bytes a row) one
+//     16-byte load on 8 I J lanes; both go through the wavefront's own LDS
+//     area and come back in the layout the products use.  Each load
+//     instruction costs the address unit the same time whatever its width, so
+//     this halves the instructions a wavefront issues.  Only the wavefront
+//     itself reads its area: no barrier before the products.
+//   - Partial sums are reduced over the 16 lanes of a row, then across the
+//     wavefronts in wavefront order through LDS.
+// Rows past n repeat row n - 1 and are not stored.
+constexpr int kGemvKsMaxWaves = 10;
+constexpr int kGemvKsI = 5;  // 20 rows per workgroup: one workgroup per CU for n = 5120
+
+template <int I, int J>
+__global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                      int64_t k, const uint8_t* __restrict__ packed,
+                                                                      const uint8_t* __restrict__ scales,
+                                                                      const float* __restrict__ tscale_p,
+                                                                      uint16_t* __restrict__ y) {
+  constexpr int RB = 4 * I;
+  constexpr int SL = 8 * I * J;  // lanes that load scales: 2 J pieces of 16 bytes per row
+  static_assert(SL <= 64, "scale pieces per wavefront");
+  __shared__ uint4 xs[kGemvKsMaxWaves][64 * J];
+  __shared__ uint4 ss[kGemvKsMaxWaves][64];  // slots SL .. 63 take the repeated pieces
+  __shared__ float red[kGemvKsMaxWaves][RB];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int u = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * RB;
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const int64_t ub = (int64_t)w * 16 * J + u;  // this lane's first unit
+
+  // 1. activations: piece 64 j + lane of the slice (8 elements)
+  const uint4* xsl = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * k + (int64_t)w * 512 * J);
+  uint4 xg[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) xg[j] = xsl[64 * j + lane];
+  // 2. scales: lane l takes piece l % (2 J) of row (l % SL) / (2 J); lanes
+  //    past SL repeat a piece into spare slots (no branch, so the compiler
+  //    neither sinks the load nor drains the loads in flight at a join)
+  uint4 sg;
+  {
+    const int sp = lane % SL;
+    const int64_t r = row0 + sp / (2 * J), row = r < n ? r : n - 1;
+    sg = reinterpret_cast<const uint4*>(scales + row * kb + (int64_t)w * 32 * J)[sp % (2 * J)];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // activations and scales are issued before the weights
+  // 3. weights
+  uint4 wv[J][I];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int64_t r = row0 + g + 4 * i, row = r < n ? r : n - 1;
+      wv[j][i] = *reinterpret_cast<const uint4*>(packed + row * kh + (ub + 16 * j) * 16);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  // 4. through this wavefront's LDS area: activation piece q of unit v of
+  //    slice part j sits at 64 j + 16 q + v (conflict-free reads below)
+#pragma unroll
+  for (int j = 0; j < J; ++j) xs[w][64 * j + 16 * (lane & 3) + (lane >> 2)] = xg[j];
+  ss[w][lane] = sg;
+  uint4 xv[J][4];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[j][q] = xs[w][64 * j + 16 * q + u];
+  const uint16_t* srow = reinterpret_cast<const uint16_t*>(&ss[w][0]);
+
+  float acc[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const float2 sc = e4m3x2_to_f32<false>(srow[(g + 4 * i) * 16 * J + 16 * j + u]);
+      float p0 = dot8(wv[j][i].x, xv[j][0], 0.0f);
+      p0 = dot8(wv[j][i].y, xv[j][1], p0);
+      float p1 = dot8(wv[j][i].z, xv[j][2], 0.0f);
+      p1 = dot8(wv[j][i].w, xv[j][3], p1);
+      acc[i] = fmaf(p0, sc.x, acc[i]);
+      acc[i] = fmaf(p1, sc.y, acc[i]);
+    }
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    const float v = group_sum<16>(acc[i]);
+    if (u == 0) red[w][g + 4 * i] = v;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < RB && row0 + t < n) {
+    float v = red[0][t];
+    for (int ww = 1; ww < nw; ++ww) v += red[ww][t];
+    y[(int64_t)blockIdx.y * n + row0 + t] = (uint16_t)f32_to_bf16_rne(v * *tscale_p);
+  }
+}
+
+// waves = k / 512 (one 512-element slice per wavefront).
+static void launch_ks(const uint16_t* x, int64_t m, int64_t n, int64_t k, int waves, const uint8_t* packed,
+                      const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  constexpr int I = kGemvKsI;
+  const unsigned gx = (unsigned)((n + 4 * I - 1) / (4 * I));
+  const int64_t max_y = 65535;
+  for (int64_t m0 = 0; m0 < m; m0 += max_y) {
+    const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
+    gemv_ks_kernel<I, 1><<<dim3(gx, gy), 64 * waves, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
+  }
+}
+
 template <int LPR, int R, int JB, int W, bool RAGGED = false>
 static void launch_lds(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                        const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
@@ -241,10 +359,10 @@ static void launch_lds_for_n(const uint16_t* x, int64_t m, int64_t n, int64_t k,
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                  const float* tscale, uint16_t* y, hipStream_t s) {
+  if ((k & 511) == 0 && (k >> 9) <= kGemvKsMaxWaves)
+    return launch_ks(x, m, n, k, (int)(k >> 9), packed, scales, tscale, y, s);
   const int64_t units = k >> 5;
   if ((k & 31) == 0 && k <= kLdsMaxK) {
-    if (units == 160 && n >= 16384)
-      return launch_lds<64, 2, 3, 8, true>(x, m, n, k, packed, scales, tscale, y, s);
     if (units % 32 == 0) {
       switch (units / 32) {
         case 1: return launch_lds_for_n<32, 1, false>(x, m, n, k, packed, scales, tscale, y, s);

@@ -39,6 +39,15 @@ namespace {
 
 constexpr int kSkChunk = 256;   // K elements per chunk
 constexpr int kSkDepth = 6;     // weight chunks in flight per wavefront
+#ifndef SK_D8
+#define SK_D8 4
+#endif
+#ifndef SK_D16
+#define SK_D16 4
+#endif
+#ifndef SK_D32
+#define SK_D32 4
+#endif
 
 struct SkinnyArgs {
   const uint16_t* x;      // [m, k]
@@ -375,11 +384,21 @@ __device__ __forceinline__ void sk_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int MT, int TT>
+// One ring stage: the block's weight rows and the MX activation rows of one
+// chunk.
+template <int MX, int TT>
 struct SkStage {
   uint4 w[TT * 16 * 8];
-  uint4 x[MT * 32];
+  uint4 x[MX * 32];
 };
+
+// Scale groups (of 4 chunks) that start among the D - 2 chunks after chunk c,
+// c % 4 == P: their scale loads are issued after chunk c's.
+constexpr int sk_groups_after(int P, int D) {
+  int n = 0;
+  for (int t = 1; t <= D - 2; ++t) n += ((P + t) % 4) == 0;
+  return n;
+}
 
 // Per-lane global sources of one wavefront's loads, for chunk 0 (weights and
 // activations) or scale group 0.
@@ -400,18 +419,20 @@ struct SkDmaSrc {
 // piece 2 g + w / 2, scale block 4 g + w).  All LDS reads are issued first so
 // that their latency overlaps the decode; the MFMAs alternate between two
 // accumulator chains (even and odd steps), summed once after the K loop.
-template <int MT, int TT, bool FIVE>
-__device__ __forceinline__ void sk_dma_compute(const SkStage<MT, TT>& S, const uint4* sg, int q, int w, int r, int lane,
-                                               f32x4_t (*acc)[MT / 16], f32x4_t* acc5) {
+// Activation rows past MX (MX = 8 under a 16-wide tile) read row l15 % MX
+// instead; they only feed output columns that are never stored.
+template <int MT, int MX, int TT, bool FIVE>
+__device__ __forceinline__ void sk_dma_compute(const SkStage<MX, TT>& S, const uint4* sg, int q, int w, int r,
+                                               int lane, f32x4_t (*acc)[MT / 16], f32x4_t* acc5) {
   constexpr int NMT = MT / 16;
-  const int g = lane >> 4, f = (r >> 1) & 7, l15 = lane & 15;
+  const int g = lane >> 4, f = (r >> 1) & 7, l15 = lane & 15, xl = MX < 16 ? (l15 & (MX - 1)) : l15;
   const uint4 w0 = S.w[r * 8 + ((2 * g) ^ f)], w1 = S.w[r * 8 + ((2 * g + 1) ^ f)];
   const uint32_t sv = reinterpret_cast<const uint32_t*>(&sg[4 * r + q])[g];
   uint4 xb[8][NMT];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) xb[j][mt] = S.x[(16 * mt + l15) * 32 + ((8 * g + j) ^ l15)];
+    for (int mt = 0; mt < NMT; ++mt) xb[j][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + j) ^ xl)];
   uint2 wv5;
   uint32_t sv5 = 0;
   uint4 xb5[2][NMT];  // activation fragments of steps 2w and 2w + 1
@@ -422,7 +443,7 @@ __device__ __forceinline__ void sk_dma_compute(const SkStage<MT, TT>& S, const u
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) xb5[h][mt] = S.x[(16 * mt + l15) * 32 + ((8 * g + 2 * w + h) ^ l15)];
+      for (int mt = 0; mt < NMT; ++mt) xb5[h][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + 2 * w + h) ^ xl)];
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every LDS read above the decode and MFMAs
 
@@ -449,18 +470,18 @@ __device__ __forceinline__ void sk_dma_compute(const SkStage<MT, TT>& S, const u
   }
 }
 
-// Loads of chunk ci of the slice (and, when ci % 4 == 0, of scale group ci / 4)
-// into stage S.  Past the slice, the slice's last chunk is loaded again (never read).
-template <int MT, int TT, int LW, int LX, int LS>
+// Loads of chunk ci of the slice into stage S and, when ci % 4 == 0, of scale
+// group ci / 4 into sg.  Past the slice, the slice's last chunk is loaded again
+// (never read).
+template <int MX, int TT, int LW, int LX, int LS>
 __device__ __forceinline__ void sk_dma_issue(const SkinnyArgs& p, const SkDmaSrc<LW, LX, LS>& src, int ci, int nc,
-                                             int c0, SkStage<MT, TT>& S, uint4 (&sgr)[2][TT * 16 * 4], int lane) {
+                                             int c0, SkStage<MX, TT>& S, uint4* sg, int lane) {
   const int cc = ci < nc ? ci : nc - 1;
 #pragma unroll
   for (int i = 0; i < LW; ++i) sk_lds_dma16(src.w[i] + (int64_t)cc * 128, sk_lds_addr(&S.w[src.wslot[i]]));
 #pragma unroll
   for (int i = 0; i < LX; ++i) sk_lds_dma16(src.x[i] + (int64_t)cc * kSkChunk, sk_lds_addr(&S.x[src.xslot[i]]));
   if ((ci & 3) == 0) {
-    uint4* sg = sgr[(ci >> 2) & 1];
 #pragma unroll
     for (int i = 0; i < LS; ++i) {
       // this lane's chunk of the group; chunks past the weight's end read the last chunk's scales
@@ -473,8 +494,9 @@ __device__ __forceinline__ void sk_dma_issue(const SkinnyArgs& p, const SkDmaSrc
 
 // MX: activation rows loaded per launch row (8, 16 or 32; the launch's m is at
 // most MX, MFMA tiles cover MT >= MX rows and the rows past MX are never
-// stored).  FIVE: the block has 5 row tiles (68..80 rows), else 4.
-template <int MT, int MX, bool FIVE>
+// stored).  FIVE: the block has 5 row tiles (68..80 rows), else 4.  D: ring
+// stages (D - 1 chunks in flight).
+template <int MT, int MX, bool FIVE, int D>
 __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
   constexpr int NMT = MT / 16;
   constexpr int TT = FIVE ? 5 : 4;
@@ -483,9 +505,14 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
   constexpr int LX = XI / 4;                // ... per wavefront (MX is a multiple of 8)
   constexpr int LS = FIVE ? 2 : 1;          // scale instructions per wavefront per group of 4 chunks
   constexpr int LB = LW + LX;               // loads per wavefront per chunk, scales aside
-  typedef SkStage<MT, TT> Stage;
-  __shared__ Stage s0, s1, s2, s3;
-  __shared__ uint4 sgr[2][TT * 16 * 4];
+  // Scale buffers: group g + NB reuses g's buffer; it is issued with chunk
+  // 4 (g + NB) at step 4 (g + NB) - (D - 1), after g's last read at step 4 g + 3.
+  constexpr int NB = (D + 6) / 4;
+  static_assert(4 * NB >= D + 3, "scale ring too short");
+  static_assert(MX <= MT && (MX >= 16 || NMT == 1), "activation rows");
+  typedef SkStage<MX, TT> Stage;
+  __shared__ Stage st[D];
+  __shared__ uint4 sgr[NB][TT * 16 * 4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rb = (int)(blockIdx.x / (unsigned)p.slices), sl = (int)(blockIdx.x % (unsigned)p.slices);
@@ -530,32 +557,36 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
   for (int mt = 0; mt < NMT; ++mt) acc2[0][mt] = acc2[1][mt] = acc5[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int r = 16 * w + (lane & 15);
 
-  sk_dma_issue<MT, TT, LW, LX, LS>(p, src, 0, nc, c0, s0, sgr, lane);
-  sk_dma_issue<MT, TT, LW, LX, LS>(p, src, 1, nc, c0, s1, sgr, lane);
-  sk_dma_issue<MT, TT, LW, LX, LS>(p, src, 2, nc, c0, s2, sgr, lane);
-  // Step ci (ring position P = ci % 4, the chunk's place in its scale group):
-  // wait until this wavefront's loads of chunk ci are done (the loads of chunks
-  // ci + 1 and ci + 2 may still be in flight: 2 LB, plus LS when one of them
-  // starts a scale group), meet the barrier, refill stage (ci + 3) % 4, compute.
-  // The raw barrier carries no fence, so the compiler adds no wait of its own.
-#define SK_STEP(P, CUR, NXT)                                                      \
-  {                                                                              \
-    const int ci = cb + (P);                                                     \
-    if (ci < nc) {                                                               \
-      sk_wait_vmcnt<2 * LB + ((P) >= 2 ? LS : 0)>();                             \
-      asm volatile("" ::: "memory");                                             \
-      __builtin_amdgcn_s_barrier();                                              \
-      asm volatile("" ::: "memory");                                             \
-      sk_dma_issue<MT, TT, LW, LX, LS>(p, src, ci + 3, nc, c0, NXT, sgr, lane);  \
-      const uint4* sg = sgr[(ci >> 2) & 1];                                      \
-      sk_dma_compute<MT, TT, FIVE>(CUR, sg, (P), w, r, lane, acc2, acc5);        \
-    }                                                                            \
+#pragma unroll
+  for (int c = 0; c < D - 1; ++c)
+    sk_dma_issue<MX, TT, LW, LX, LS>(p, src, c, nc, c0, st[c], sgr[(c >> 2) % NB], lane);
+  // Step ci (P = ci % 4, the chunk's place in its scale group; stage si =
+  // ci % D): wait until this wavefront's loads of chunk ci are done (the loads
+  // of chunks ci + 1 .. ci + D - 2 may still be in flight: LB each, plus LS for
+  // each scale group that starts among them), meet the barrier, refill the
+  // stage that step ci - 1 freed with chunk ci + D - 1, compute.  The raw
+  // barrier carries no fence, so the compiler adds no wait of its own.
+  int si = 0;
+#define SK_STEP(P)                                                                                \
+  {                                                                                              \
+    const int ci = cb + (P);                                                                     \
+    if (ci < nc) {                                                                               \
+      sk_wait_vmcnt<(D - 2) * LB + LS * sk_groups_after((P), D)>();                              \
+      asm volatile("" ::: "memory");                                                             \
+      __builtin_amdgcn_s_barrier();                                                              \
+      asm volatile("" ::: "memory");                                                             \
+      const int cn = ci + D - 1;                                                                 \
+      sk_dma_issue<MX, TT, LW, LX, LS>(p, src, cn, nc, c0, st[si == 0 ? D - 1 : si - 1],         \
+                                       sgr[(cn >> 2) % NB], lane);                               \
+      sk_dma_compute<MT, MX, TT, FIVE>(st[si], sgr[(ci >> 2) % NB], (P), w, r, lane, acc2, acc5); \
+      si = si == D - 1 ? 0 : si + 1;                                                             \
+    }                                                                                            \
   }
   for (int cb = 0; cb < nc; cb += 4) {
-    SK_STEP(0, s0, s3)
-    SK_STEP(1, s1, s0)
-    SK_STEP(2, s2, s1)
-    SK_STEP(3, s3, s2)
+    SK_STEP(0)
+    SK_STEP(1)
+    SK_STEP(2)
+    SK_STEP(3)
   }
 #undef SK_STEP
   // The refills past the slice are repeats that nothing reads; let them land
@@ -569,7 +600,7 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
   if constexpr (FIVE) {
     // Fifth tile: add the four wavefronts' partial sums in wavefront order.
     __syncthreads();  // every wavefront is past its last read of the stages
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(&s0);
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(&st[0]);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) red[(w * NMT + mt) * 64 + lane] = acc5[mt];
     __syncthreads();
@@ -648,13 +679,13 @@ SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k, bool split) {
 // The streaming kernel takes K a multiple of 256 and m <= 32 (one launch row).
 bool use_dma(const SkinnyPlan& pl, int64_t m, int64_t k) { return (k % kSkChunk) == 0 && m <= 32 && pl.gy == 1; }
 
-template <int MT, int MX>
+template <int MT, int MX, int D>
 void launch_dma(const SkinnyPlan& pl, const SkinnyArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(pl.row_blocks * pl.slices), 1u);
   if (pl.tiles == 5)
-    skinny_dma_kernel<MT, MX, true><<<grid, 256, 0, s>>>(a);
+    skinny_dma_kernel<MT, MX, true, D><<<grid, 256, 0, s>>>(a);
   else
-    skinny_dma_kernel<MT, MX, false><<<grid, 256, 0, s>>>(a);
+    skinny_dma_kernel<MT, MX, false, D><<<grid, 256, 0, s>>>(a);
 }
 
 template <int MT, int T>
@@ -706,11 +737,11 @@ void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uin
   if (use_dma(pl, m, k)) {
     const SkinnyArgs a = args(0, m);
     if (m <= 8)
-      launch_dma<16, 8>(pl, a, s);
+      launch_dma<16, 8, SK_D8>(pl, a, s);
     else if (m <= 16)
-      launch_dma<16, 16>(pl, a, s);
+      launch_dma<16, 16, SK_D16>(pl, a, s);
     else
-      launch_dma<32, 32>(pl, a, s);
+      launch_dma<32, 32, SK_D32>(pl, a, s);
     return;
   }
   // gridDim.y is limited to 65535 launch rows; larger m is split into launches.
