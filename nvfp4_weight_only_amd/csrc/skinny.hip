@@ -39,15 +39,9 @@ namespace {
 
 constexpr int kSkChunk = 256;   // K elements per chunk
 constexpr int kSkDepth = 6;     // weight chunks in flight per wavefront
-#ifndef SK_D8
-#define SK_D8 4
-#endif
-#ifndef SK_D16
-#define SK_D16 4
-#endif
-#ifndef SK_D32
-#define SK_D32 4
-#endif
+// Ring stages of the streaming kernel by activation rows (D - 2 chunks in
+// flight behind the one whose operands are being read).
+constexpr int kSkRing8 = 5, kSkRing16 = 4, kSkRing32 = 4;
 
 struct SkinnyArgs {
   const uint16_t* x;      // [m, k]
@@ -353,9 +347,12 @@ __global__ void __launch_bounds__(64 * T) skinny_kernel(SkinnyArgs p) {
 //
 // Every wavefront issues the same number of load instructions for each chunk
 // (spare slots repeat a real instruction and rewrite the same bytes), so the
-// loads of chunk c are known to be complete at a fixed vmcnt: step c waits for
-// them, meets the barrier (after which every wavefront's share is in LDS),
-// issues chunk c + 3 into the stage that step c - 1 freed, and runs the MFMAs.
+// loads of a chunk are known to be complete at a fixed vmcnt.  The operand
+// reads from LDS run one chunk ahead of the products: step c waits for chunk
+// c + 1's loads, meets the barrier (after which every wavefront's share is in
+// LDS), refills the stage of chunk c - 1 with chunk c + D - 1, issues the
+// reads of chunk c + 1's operands and runs chunk c's MFMAs on the operands
+// read in step c - 1, so the LDS reads overlap the decode.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) const void sk_lds_t;
 
@@ -384,6 +381,13 @@ __device__ __forceinline__ void sk_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// vmcnt(N) and lgkmcnt(0): also this wavefront's LDS reads are done.
+template <int N>
+__device__ __forceinline__ void sk_wait_vmcnt_lds0() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
 // One ring stage: the block's weight rows and the MX activation rows of one
 // chunk.
 template <int MX, int TT>
@@ -392,11 +396,11 @@ struct SkStage {
   uint4 x[MX * 32];
 };
 
-// Scale groups (of 4 chunks) that start among the D - 2 chunks after chunk c,
-// c % 4 == P: their scale loads are issued after chunk c's.
-constexpr int sk_groups_after(int P, int D) {
+// Scale groups (of 4 chunks) that start among chunks c + T0 .. c + D - 2,
+// c % 4 == P.
+constexpr int sk_groups_after(int P, int D, int T0 = 1) {
   int n = 0;
-  for (int t = 1; t <= D - 2; ++t) n += ((P + t) % 4) == 0;
+  for (int t = T0; t <= D - 2; ++t) n += ((P + t) % 4) == 0;
   return n;
 }
 
@@ -413,59 +417,69 @@ struct SkDmaSrc {
   uint32_t sslot[LS];
 };
 
-// MFMAs of one chunk: this wavefront's own tile (rows 16 w .. 16 w + 15 of the
-// block) and, with FIVE, its two steps (2 w, 2 w + 1) of the fifth tile (block
-// rows 64 .. 79; bytes [32 g + 8 w, + 8) of each row's chunk, i.e. half w % 2 of
-// piece 2 g + w / 2, scale block 4 g + w).  All LDS reads are issued first so
-// that their latency overlaps the decode; the MFMAs alternate between two
-// accumulator chains (even and odd steps), summed once after the K loop.
-// Activation rows past MX (MX = 8 under a 16-wide tile) read row l15 % MX
-// instead; they only feed output columns that are never stored.
+// One chunk's MFMA operands as this wavefront reads them from LDS: its own
+// tile (rows 16 w .. 16 w + 15 of the block) and, with FIVE, its two steps
+// (2 w, 2 w + 1) of the fifth tile (block rows 64 .. 79; bytes [32 g + 8 w,
+// + 8) of each row's chunk, i.e. half w % 2 of piece 2 g + w / 2, scale block
+// 4 g + w).  Activation rows past MX (MX = 8 under a 16-wide tile) read row
+// l15 % MX instead; they only feed output columns that are never stored.
+template <int MT>
+struct SkFrag {
+  uint4 w0, w1;
+  uint32_t sv;
+  uint4 xb[8][MT / 16];
+  uint2 wv5;
+  uint32_t sv5;
+  uint4 xb5[2][MT / 16];  // activation fragments of steps 2w and 2w + 1
+};
+
 template <int MT, int MX, int TT, bool FIVE>
-__device__ __forceinline__ void sk_dma_compute(const SkStage<MX, TT>& S, const uint4* sg, int q, int w, int r,
-                                               int lane, f32x4_t (*acc)[MT / 16], f32x4_t* acc5) {
+__device__ __forceinline__ void sk_frag_read(SkFrag<MT>& F, const SkStage<MX, TT>& S, const uint4* sg, int q, int w,
+                                             int r, int lane) {
   constexpr int NMT = MT / 16;
   const int g = lane >> 4, f = (r >> 1) & 7, l15 = lane & 15, xl = MX < 16 ? (l15 & (MX - 1)) : l15;
-  const uint4 w0 = S.w[r * 8 + ((2 * g) ^ f)], w1 = S.w[r * 8 + ((2 * g + 1) ^ f)];
-  const uint32_t sv = reinterpret_cast<const uint32_t*>(&sg[4 * r + q])[g];
-  uint4 xb[8][NMT];
+  F.w0 = S.w[r * 8 + ((2 * g) ^ f)];
+  F.w1 = S.w[r * 8 + ((2 * g + 1) ^ f)];
+  F.sv = reinterpret_cast<const uint32_t*>(&sg[4 * r + q])[g];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) xb[j][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + j) ^ xl)];
-  uint2 wv5;
-  uint32_t sv5 = 0;
-  uint4 xb5[2][NMT];  // activation fragments of steps 2w and 2w + 1
+    for (int mt = 0; mt < NMT; ++mt) F.xb[j][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + j) ^ xl)];
   if constexpr (FIVE) {
     const int r5 = 64 + l15, f5 = (r5 >> 1) & 7;
-    wv5 = reinterpret_cast<const uint2*>(&S.w[r5 * 8 + ((2 * g + (w >> 1)) ^ f5)])[w & 1];
-    sv5 = reinterpret_cast<const uint32_t*>(&sg[4 * r5 + q])[g];
+    F.wv5 = reinterpret_cast<const uint2*>(&S.w[r5 * 8 + ((2 * g + (w >> 1)) ^ f5)])[w & 1];
+    F.sv5 = reinterpret_cast<const uint32_t*>(&sg[4 * r5 + q])[g];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) xb5[h][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + 2 * w + h) ^ xl)];
+      for (int mt = 0; mt < NMT; ++mt) F.xb5[h][mt] = S.x[(16 * mt + xl) * 32 + ((8 * g + 2 * w + h) ^ xl)];
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep every LDS read above the decode and MFMAs
+}
 
-  const float2 s01 = e4m3x2_to_f32<false>(sv), s23 = e4m3x2_to_f32<true>(sv);
-  const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+// Decode and MFMAs of one chunk's operands; the MFMAs alternate between two
+// accumulator chains (even and odd steps), summed once after the K loop.
+template <int MT, bool FIVE>
+__device__ __forceinline__ void sk_frag_compute(const SkFrag<MT>& F, int w, f32x4_t (*acc)[MT / 16], f32x4_t* acc5) {
+  constexpr int NMT = MT / 16;
+  const float2 s01 = e4m3x2_to_f32<false>(F.sv), s23 = e4m3x2_to_f32<true>(F.sv);
+  const uint32_t wd[8] = {F.w0.x, F.w0.y, F.w0.z, F.w0.w, F.w1.x, F.w1.y, F.w1.z, F.w1.w};
   const float sc[4] = {s01.x, s01.y, s23.x, s23.y};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bf16x8_t a = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(wd[j], sc[j >> 1]));
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
-      acc[j & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, xb[j][mt]),
+      acc[j & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, F.xb[j][mt]),
                                                                acc[j & 1][mt], 0, 0, 0);
   }
   if constexpr (FIVE) {
-    const float sc5 = e4m3x2_to_f32<false>((sv5 >> (8 * w)) & 0xFFu).x;
-    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(wv5.x, sc5));
-    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(wv5.y, sc5));
+    const float sc5 = e4m3x2_to_f32<false>((F.sv5 >> (8 * w)) & 0xFFu).x;
+    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(F.wv5.x, sc5));
+    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(F.wv5.y, sc5));
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
-      acc5[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, xb5[0][mt]), acc5[mt], 0, 0, 0);
-      acc5[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, xb5[1][mt]), acc5[mt], 0, 0, 0);
+      acc5[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8_t, F.xb5[0][mt]), acc5[mt], 0, 0, 0);
+      acc5[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, F.xb5[1][mt]), acc5[mt], 0, 0, 0);
     }
   }
 }
@@ -506,9 +520,11 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
   constexpr int LS = FIVE ? 2 : 1;          // scale instructions per wavefront per group of 4 chunks
   constexpr int LB = LW + LX;               // loads per wavefront per chunk, scales aside
   // Scale buffers: group g + NB reuses g's buffer; it is issued with chunk
-  // 4 (g + NB) at step 4 (g + NB) - (D - 1), after g's last read at step 4 g + 3.
+  // 4 (g + NB) at step 4 (g + NB) - (D - 1), after g's last read (issued at
+  // step 4 g + 2, complete at step 4 g + 3's barrier).
   constexpr int NB = (D + 6) / 4;
-  static_assert(4 * NB >= D + 3, "scale ring too short");
+  static_assert(4 * NB >= D + 2, "scale ring too short");
+  static_assert(D >= 3, "one chunk in flight behind the one being read");
   static_assert(MX <= MT && (MX >= 16 || NMT == 1), "activation rows");
   typedef SkStage<MX, TT> Stage;
   __shared__ Stage st[D];
@@ -560,33 +576,42 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
 #pragma unroll
   for (int c = 0; c < D - 1; ++c)
     sk_dma_issue<MX, TT, LW, LX, LS>(p, src, c, nc, c0, st[c], sgr[(c >> 2) % NB], lane);
-  // Step ci (P = ci % 4, the chunk's place in its scale group; stage si =
-  // ci % D): wait until this wavefront's loads of chunk ci are done (the loads
-  // of chunks ci + 1 .. ci + D - 2 may still be in flight: LB each, plus LS for
-  // each scale group that starts among them), meet the barrier, refill the
-  // stage that step ci - 1 freed with chunk ci + D - 1, compute.  The raw
-  // barrier carries no fence, so the compiler adds no wait of its own.
-  int si = 0;
-#define SK_STEP(P)                                                                                \
-  {                                                                                              \
-    const int ci = cb + (P);                                                                     \
-    if (ci < nc) {                                                                               \
-      sk_wait_vmcnt<(D - 2) * LB + LS * sk_groups_after((P), D)>();                              \
-      asm volatile("" ::: "memory");                                                             \
-      __builtin_amdgcn_s_barrier();                                                              \
-      asm volatile("" ::: "memory");                                                             \
-      const int cn = ci + D - 1;                                                                 \
-      sk_dma_issue<MX, TT, LW, LX, LS>(p, src, cn, nc, c0, st[si == 0 ? D - 1 : si - 1],         \
-                                       sgr[(cn >> 2) % NB], lane);                               \
-      sk_dma_compute<MT, MX, TT, FIVE>(st[si], sgr[(ci >> 2) % NB], (P), w, r, lane, acc2, acc5); \
-      si = si == D - 1 ? 0 : si + 1;                                                             \
-    }                                                                                            \
+  // The operand reads run one chunk ahead of the products: step ci waits for
+  // this wavefront's loads of chunk ci + 1 (chunks ci + 2 .. ci + D - 2 may
+  // still be in flight: LB each, plus LS for each scale group that starts
+  // among them) and for its own LDS reads of the previous step, meets the
+  // barrier, refills the stage of chunk ci - 1 (read two steps ago) with chunk
+  // ci + D - 1, reads chunk ci + 1's operands, and runs chunk ci's products on
+  // the operands read in the previous step.  The raw barrier carries no
+  // fence, so the compiler adds no wait of its own.
+  SkFrag<MT> fa, fb;
+  sk_wait_vmcnt_lds0<(D - 2) * LB + LS * sk_groups_after(0, D)>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  sk_frag_read<MT, MX, TT, FIVE>(fa, st[0], sgr[0], 0, w, r, lane);
+  int si = 0;  // stage of chunk ci
+#define SK_STEP(P, CUR, NXT)                                                                       \
+  {                                                                                               \
+    const int ci = cb + (P);                                                                      \
+    if (ci < nc) {                                                                                \
+      sk_wait_vmcnt_lds0<(D - 3) * LB + LS * sk_groups_after((P), D, 2)>();                       \
+      asm volatile("" ::: "memory");                                                              \
+      __builtin_amdgcn_s_barrier();                                                               \
+      asm volatile("" ::: "memory");                                                              \
+      const int cn = ci + D - 1, sn = si == D - 1 ? 0 : si + 1;                                   \
+      sk_dma_issue<MX, TT, LW, LX, LS>(p, src, cn, nc, c0, st[si == 0 ? D - 1 : si - 1],          \
+                                       sgr[(cn >> 2) % NB], lane);                                \
+      sk_frag_read<MT, MX, TT, FIVE>(NXT, st[sn], sgr[((ci + 1) >> 2) % NB], ((P) + 1) & 3, w, r, lane); \
+      sk_frag_compute<MT, FIVE>(CUR, w, acc2, acc5);                                              \
+      si = sn;                                                                                    \
+    }                                                                                             \
   }
   for (int cb = 0; cb < nc; cb += 4) {
-    SK_STEP(0)
-    SK_STEP(1)
-    SK_STEP(2)
-    SK_STEP(3)
+    SK_STEP(0, fa, fb)
+    SK_STEP(1, fb, fa)
+    SK_STEP(2, fa, fb)
+    SK_STEP(3, fb, fa)
   }
 #undef SK_STEP
   // The refills past the slice are repeats that nothing reads; let them land
@@ -737,11 +762,11 @@ void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uin
   if (use_dma(pl, m, k)) {
     const SkinnyArgs a = args(0, m);
     if (m <= 8)
-      launch_dma<16, 8, SK_D8>(pl, a, s);
+      launch_dma<16, 8, kSkRing8>(pl, a, s);
     else if (m <= 16)
-      launch_dma<16, 16, SK_D16>(pl, a, s);
+      launch_dma<16, 16, kSkRing16>(pl, a, s);
     else
-      launch_dma<32, 32, SK_D32>(pl, a, s);
+      launch_dma<32, 32, kSkRing32>(pl, a, s);
     return;
   }
   // gridDim.y is limited to 65535 launch rows; larger m is split into launches.
