@@ -162,6 +162,46 @@ nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, in
                                  const uint8_t* packed, const uint8_t* scales, const float* tscale,
                                  uint16_t* y, void* stream);
 
+/*
+ * Expert stacks (mixture-of-experts layers).  imp "docs/quantization.md": in
+ * the NVFP4 kernel pipeline, a MoE layer's per-expert weights become one
+ * contiguous [ne, N, K_packed] buffer per layer and projection, and the
+ * imp-quantize section notes that 3-D expert stacks need a per-expert path.
+ * Each expert is its own quantized tensor with its own tensor scale:
+ *   w [e, n, k] BF16 -> packed [e, n, k/2], scales [e, n, k/16], tscale [e]
+ * where matrix i of the outputs equals nvfp4_quantize applied to w[i], bit
+ * for bit.  e = 0 is a no-op.  The same scratch use as nvfp4_quantize:
+ * tscale[i] holds expert i's amax and its packed matrix holds per-workgroup
+ * maxima until the last kernels overwrite them.
+ */
+nvfp4_status nvfp4_quantize_experts(const uint16_t* w, int64_t e, int64_t n, int64_t k,
+                                    uint8_t* packed, uint8_t* scales, float* tscale, void* stream);
+
+/* Dequantize an expert stack: w_out[i] = nvfp4_dequant of matrix i (same
+ * layouts as nvfp4_quantize_experts; w_out [e, n, k] BF16). */
+nvfp4_status nvfp4_dequant_experts(const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                                   int64_t e, int64_t n, int64_t k, uint16_t* w_out, void* stream);
+
+/*
+ * Routed W4A16 linear over an expert stack (the decode path of a MoE layer
+ * with top-k routing; same stack layout as above):
+ *   y[t, j, :] = nvfp4_linear(x[t, :], matrix route[t, j] of the stack)
+ * for t < t_count, j < topk.  x [t_count, k] BF16, route [t_count, topk]
+ * int32 expert ids (device memory), packed [e, n, k/2], scales [e, n, k/16],
+ * tscale [e] -> y [t_count, topk, n] BF16.  Each (t, j) pair runs the GEMV
+ * on its expert's matrix (for k a multiple of 512 up to 5120 the same kernel,
+ * hence the same bits, as nvfp4_linear with m = 1).  Combining the topk
+ * outputs with the router's weights is the caller's.
+ * An expert id outside [0, e) gives a row of zeros for that pair (ids are
+ * device data, so they are checked on the device, not reported).
+ * t_count = 0 is a no-op; topk >= 1 and e >= 1 are required; route must be
+ * 4-byte aligned and the other pointers 16-byte aligned; y must not overlap
+ * an input.
+ */
+nvfp4_status nvfp4_linear_routed(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route,
+                                 int64_t e, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
+                                 const float* tscale, uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = ran
 # Every symbol include/nvfp4.h declares.
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
             "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced",
-            "nvfp4_linear_ws", "nvfp4_linear_workspace_bytes")
+            "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
+            "nvfp4_linear_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_forced.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_ws.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_quantize_experts.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+        L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+        L.nvfp4_linear_routed.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_workspace_bytes.restype = i64
         for name in EXPORTED[2:-1]:
@@ -205,4 +209,70 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: 
             ws = workspace
         wptr, wbytes = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
         _check(lib().nvfp4_linear_ws(*head, wptr, wbytes, stream), "nvfp4_linear_ws")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Expert stacks (mixture-of-experts layers).
+# ---------------------------------------------------------------------------
+def quantize_experts(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """BF16 [e, n, k] -> (packed uint8 [e, n, k/2], scales uint8 [e, n, k/16], tscale float32 [e]).
+
+    Matrix i equals quantize(w[i]) bit for bit (one tensor scale per expert).
+    """
+    _need(w, torch.bfloat16, "w")
+    e, n, k = w.shape
+    packed = torch.empty((e, n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((e, n, k // 16), dtype=torch.uint8, device=w.device)
+    tscale = torch.empty((e,), dtype=torch.float32, device=w.device)
+    _check(lib().nvfp4_quantize_experts(w.data_ptr(), e, n, k, packed.data_ptr(), scales.data_ptr(),
+                                        tscale.data_ptr(), _stream(w)), "nvfp4_quantize_experts")
+    return packed, scales, tscale
+
+
+def _stack_shape(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor):
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    e, n, kh = packed.shape
+    k = 2 * kh
+    if scales.shape != (e, n, k // 16) or tscale.shape != (e,):
+        raise ValueError("scales must be [e, n, k/16] and tscale [e]")
+    return e, n, k
+
+
+def dequant_experts(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor) -> torch.Tensor:
+    """NVFP4 expert stack -> BF16 [e, n, k]."""
+    e, n, k = _stack_shape(packed, scales, tscale)
+    out = torch.empty((e, n, k), dtype=torch.bfloat16, device=packed.device)
+    _check(lib().nvfp4_dequant_experts(packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), e, n, k,
+                                       out.data_ptr(), _stream(packed)), "nvfp4_dequant_experts")
+    return out
+
+
+def linear_routed(x: torch.Tensor, route: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                  tscale: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y[t, j, :] = X[t, :] . W_hat[route[t, j]]^T for an expert stack (top-k routed decode).
+
+    x BF16 [t, k]; route int32 [t, topk] (device); packed/scales/tscale an expert stack.
+    Expert ids outside [0, e) give zero rows.
+    """
+    _need(x, torch.bfloat16, "x")
+    _need(route, torch.int32, "route")
+    e, n, k = _stack_shape(packed, scales, tscale)
+    t, kx = x.shape
+    if kx != k:
+        raise ValueError("x's k does not match the stack")
+    if route.dim() != 2 or route.shape[0] != t:
+        raise ValueError("route must be [t, topk]")
+    topk = route.shape[1]
+    if out is None:
+        out = torch.empty((t, topk, n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (t, topk, n):
+            raise ValueError("out must be [t, topk, n]")
+    _check(lib().nvfp4_linear_routed(x.data_ptr(), t, topk, route.data_ptr(), e, n, k, packed.data_ptr(),
+                                     scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), _stream(x)),
+           "nvfp4_linear_routed")
     return out

@@ -26,6 +26,42 @@ namespace nvfp4 {
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
 
+// Routing over an expert stack (the MoE decode path): launch row blockIdx.y is
+// pair p = pair0 + blockIdx.y; it reads activation row p / topk, writes output
+// row p, and uses matrix route[p] of the stack (w_stride packed bytes,
+// w_stride / 8 scale bytes, one tensor scale per matrix apart).  A pair whose
+// expert id is outside [0, experts) writes zeros.
+struct GvRoute {
+  const int32_t* route;
+  int64_t topk, experts, pair0, w_stride;
+};
+
+// One launch row resolved: activation row, output row and the matrix to use;
+// ok is false when the pair's expert id is out of range.
+struct GvRow {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* tscale;
+  bool ok;
+};
+
+template <bool ROUTED>
+__device__ __forceinline__ GvRow gv_resolve(const GvRoute& rt, const uint16_t* x, uint16_t* y, int64_t k, int64_t n,
+                                            const uint8_t* packed, const uint8_t* scales, const float* tscale) {
+  if constexpr (ROUTED) {
+    const int64_t pair = rt.pair0 + blockIdx.y;
+    const int32_t e = rt.route[pair];
+    const bool ok = e >= 0 && (int64_t)e < rt.experts;
+    const int64_t ee = ok ? e : 0;
+    return GvRow{x + (pair / rt.topk) * k, y + pair * n, packed + ee * rt.w_stride, scales + ee * (rt.w_stride >> 3),
+                 tscale + ee, ok};
+  } else {
+    return GvRow{x + (int64_t)blockIdx.y * k, y + (int64_t)blockIdx.y * n, packed, scales, tscale, true};
+  }
+}
+
 // Dot product of one packed word (8 elements, natural order) with 8 activations.
 __device__ __forceinline__ float dot8(uint32_t w, uint4 xq, float acc) {
   acc = dot2_bf16(e2m1x2_to_bf16<0>(w), xq.x, acc);
@@ -37,16 +73,30 @@ __device__ __forceinline__ float dot8(uint32_t w, uint4 xq, float acc) {
 
 // R rows per wavefront; JB units per lane per batch; UB = 16-element blocks per
 // unit: 2 (16-byte loads, k % 32 == 0) or 1 (8-byte loads).
-template <int R, int JB, int UB>
+template <int R, int JB, int UB, bool ROUTED = false>
 __global__ void __launch_bounds__(kGemvThreads) gemv_loop_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t k,
                                                             const uint8_t* __restrict__ packed,
                                                             const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ tscale_p,
-                                                            uint16_t* __restrict__ y) {
+                                                            uint16_t* __restrict__ y, GvRoute rt = GvRoute{}) {
   const int lane = threadIdx.x & 63;
   const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6)) * R;
   if (row0 >= n) return;  // uniform per wavefront
-  const uint16_t* xr = x + (int64_t)blockIdx.y * k;
+  {
+    const GvRow rr = gv_resolve<ROUTED>(rt, x, y, k, n, packed, scales, tscale_p);
+    y = rr.y;
+    if (!rr.ok) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == 0 && row0 + r < n) y[row0 + r] = 0;
+      return;
+    }
+    x = rr.x;
+    packed = rr.packed;
+    scales = rr.scales;
+    tscale_p = rr.tscale;
+  }
+  const uint16_t* xr = x;
   const int64_t units = k / (16 * UB);
   const int64_t kblocks = k >> 4, pstride = k >> 1;
 
@@ -109,7 +159,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_loop_kernel(const uint16_t*
   for (int r = 0; r < R; ++r) {
     const float v = wave_sum(acc[r]);
     const int64_t row = row0 + r;
-    if (lane == 0 && row < n) y[(int64_t)blockIdx.y * n + row] = (uint16_t)f32_to_bf16_rne(v * t);
+    if (lane == 0 && row < n) y[row] = (uint16_t)f32_to_bf16_rne(v * t);
   }
 }
 
@@ -235,12 +285,12 @@ __global__ void __launch_bounds__(64 * W) gemv_lds_kernel(const uint16_t* __rest
 constexpr int kGemvKsMaxWaves = 10;
 constexpr int kGemvKsI = 5;  // 20 rows per workgroup: one workgroup per CU for n = 5120
 
-template <int I, int J>
+template <int I, int J, bool ROUTED = false>
 __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                                       int64_t k, const uint8_t* __restrict__ packed,
                                                                       const uint8_t* __restrict__ scales,
                                                                       const float* __restrict__ tscale_p,
-                                                                      uint16_t* __restrict__ y) {
+                                                                      uint16_t* __restrict__ y, GvRoute rt = GvRoute{}) {
   constexpr int RB = 4 * I;
   constexpr int SL = 8 * I * J;  // lanes that load scales: 2 J pieces of 16 bytes per row
   static_assert(SL <= 64, "scale pieces per wavefront");
@@ -252,9 +302,21 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
   const int64_t row0 = (int64_t)blockIdx.x * RB;
   const int64_t kh = k >> 1, kb = k >> 4;
   const int64_t ub = (int64_t)w * 16 * J + u;  // this lane's first unit
+  {
+    const GvRow rr = gv_resolve<ROUTED>(rt, x, y, k, n, packed, scales, tscale_p);
+    y = rr.y;
+    if (!rr.ok) {  // uniform per workgroup
+      if (threadIdx.x < RB && row0 + threadIdx.x < n) y[row0 + threadIdx.x] = 0;
+      return;
+    }
+    x = rr.x;
+    packed = rr.packed;
+    scales = rr.scales;
+    tscale_p = rr.tscale;
+  }
 
   // 1. activations: piece 64 j + lane of the slice (8 elements)
-  const uint4* xsl = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * k + (int64_t)w * 512 * J);
+  const uint4* xsl = reinterpret_cast<const uint4*>(x + (int64_t)w * 512 * J);
   uint4 xg[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) xg[j] = xsl[64 * j + lane];
@@ -315,7 +377,7 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
   if (t < RB && row0 + t < n) {
     float v = red[0][t];
     for (int ww = 1; ww < nw; ++ww) v += red[ww][t];
-    y[(int64_t)blockIdx.y * n + row0 + t] = (uint16_t)f32_to_bf16_rne(v * *tscale_p);
+    y[row0 + t] = (uint16_t)f32_to_bf16_rne(v * *tscale_p);
   }
 }
 
@@ -355,6 +417,27 @@ static void launch_lds_for_n(const uint16_t* x, int64_t m, int64_t n, int64_t k,
     launch_lds<LPR, 2, JB, 8, RAGGED>(x, m, n, k, packed, scales, tscale, y, s);
   else
     launch_lds<LPR, 1, JB, 10, RAGGED>(x, m, n, k, packed, scales, tscale, y, s);
+}
+
+void launch_gemv_routed(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route, int64_t experts,
+                        int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                        uint16_t* y, hipStream_t s) {
+  const int64_t pairs = t_count * topk, max_y = 65535;
+  for (int64_t p0 = 0; p0 < pairs; p0 += max_y) {
+    const unsigned gy = (unsigned)((pairs - p0) < max_y ? (pairs - p0) : max_y);
+    const GvRoute rt{route, topk, experts, p0, n * (k >> 1)};
+    if ((k & 511) == 0 && (k >> 9) <= kGemvKsMaxWaves) {
+      constexpr int I = kGemvKsI;
+      gemv_ks_kernel<I, 1, true><<<dim3((unsigned)((n + 4 * I - 1) / (4 * I)), gy), 64 * (unsigned)(k >> 9), 0, s>>>(
+          x, n, k, packed, scales, tscale, y, rt);
+    } else {
+      const unsigned gx = (unsigned)((n + kGemvWaves * 2 - 1) / (kGemvWaves * 2));
+      if ((k & 31) == 0)
+        gemv_loop_kernel<2, 1, 2, true><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x, n, k, packed, scales, tscale, y, rt);
+      else
+        gemv_loop_kernel<2, 1, 1, true><<<dim3(gx, gy), kGemvThreads, 0, s>>>(x, n, k, packed, scales, tscale, y, rt);
+    }
+  }
 }
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,

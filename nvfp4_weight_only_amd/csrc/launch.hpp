@@ -7,17 +7,30 @@
 
 namespace nvfp4 {
 
+// Quantizer and dequantizer over a stack of `count` matrices of n_elems
+// elements each, stored back to back (count = 1 for one matrix); amax and
+// tscale hold one value per matrix.
 void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s);
 // *amax = max |w|, with per-workgroup maxima in part (at least n_elems / 8 32-bit words).
 void launch_amax_set(const uint16_t* w, int64_t n_elems, uint32_t* part, float* amax, hipStream_t s);
-void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s);
-void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
-                     hipStream_t s);
-void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n_elems,
+// amax[i] = max |w_i|, with matrix i's per-workgroup maxima at part + i * n_elems / 8.
+void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* amax,
+                           hipStream_t s);
+void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hipStream_t s);
+void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
+                     uint8_t* scales, hipStream_t s);
+void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,
                     uint16_t* out, hipStream_t s);
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                  const float* tscale, uint16_t* y, hipStream_t s);
+// Routed GEMV over an expert stack: for pair p = t * topk + j (p < t_count * topk),
+// y[p, :] = x[t, :] . W_e^T with e = route[p]; W_e is matrix e of the stack
+// (packed + e n k / 2, scales + e n k / 16, tscale[e]).  Pairs whose expert id
+// is outside [0, experts) get zeros.
+void launch_gemv_routed(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route, int64_t experts,
+                        int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                        uint16_t* y, hipStream_t s);
 // Small-M kernel.  With a workspace of at least skinny_workspace_bytes(m, n, k)
 // bytes (zero-filled before its first use; left that way by every launch) it may
 // split K across workgroups; with none it runs unsplit.

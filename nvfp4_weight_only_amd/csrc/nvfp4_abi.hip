@@ -157,8 +157,8 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* pa
   // the packed output (n k / 2 bytes) holds the per-workgroup maxima until the
   // quantize pass overwrites it.
   nvfp4::launch_amax_set(w, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
-  nvfp4::launch_quantize(w, ws.elems, tscale, packed, scales, s);
-  nvfp4::launch_finalize_tscale(tscale, tscale, s);
+  nvfp4::launch_quantize(w, 1, ws.elems, tscale, packed, scales, s);
+  nvfp4::launch_finalize_tscale(tscale, tscale, 1, s);
   return launch_status();
 }
 
@@ -187,8 +187,8 @@ nvfp4_status nvfp4_quantize_with_amax(const uint16_t* w, int64_t n, int64_t k, c
     return NVFP4_ERR_ALIAS;
   if ((st = check_device()) != NVFP4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  nvfp4::launch_quantize(w, ws.elems, amax, packed, scales, s);
-  nvfp4::launch_finalize_tscale(amax, tscale, s);
+  nvfp4::launch_quantize(w, 1, ws.elems, amax, packed, scales, s);
+  nvfp4::launch_finalize_tscale(amax, tscale, 1, s);
   return launch_status();
 }
 
@@ -203,7 +203,7 @@ nvfp4_status nvfp4_dequant(const uint8_t* packed, const uint8_t* scales, const f
       overlaps(w_out, ws.w_bytes, tscale, 4))
     return NVFP4_ERR_ALIAS;
   if ((st = check_device()) != NVFP4_OK) return st;
-  nvfp4::launch_dequant(packed, scales, tscale, ws.elems, w_out, static_cast<hipStream_t>(stream));
+  nvfp4::launch_dequant(packed, scales, tscale, 1, ws.elems, w_out, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -231,6 +231,78 @@ nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, in
                                  const uint8_t* packed, const uint8_t* scales, const float* tscale, uint16_t* y,
                                  void* stream) {
   return run_linear(kernel_id, x, m, n, k, packed, scales, tscale, y, nullptr, 0, stream);
+}
+
+nvfp4_status nvfp4_quantize_experts(const uint16_t* w, int64_t e, int64_t n, int64_t k, uint8_t* packed,
+                                    uint8_t* scales, float* tscale, void* stream) {
+  if (!w || !packed || !scales || !tscale) return NVFP4_ERR_NULL;
+  if (e < 0 || e > 65535) return NVFP4_ERR_SHAPE;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  WeightSizes all;  // the whole stack
+  if (!mul_ok(ws.elems, e, &all.elems) || !mul_ok(all.elems, 2, &all.w_bytes)) return NVFP4_ERR_SHAPE;
+  all.packed_bytes = all.elems / 2;
+  all.scale_bytes = all.elems / 16;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(scales) || !aligned16(tscale)) return NVFP4_ERR_ALIGN;
+  const void* outs[3] = {packed, scales, tscale};
+  const int64_t out_bytes[3] = {all.packed_bytes, all.scale_bytes, 4 * e};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], out_bytes[i], w, all.w_bytes)) return NVFP4_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return NVFP4_ERR_ALIAS;
+  }
+  if (e == 0) return NVFP4_OK;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  nvfp4::launch_amax_set_stack(w, e, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
+  nvfp4::launch_quantize(w, e, ws.elems, tscale, packed, scales, s);
+  nvfp4::launch_finalize_tscale(tscale, tscale, e, s);
+  return launch_status();
+}
+
+nvfp4_status nvfp4_dequant_experts(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t e,
+                                   int64_t n, int64_t k, uint16_t* w_out, void* stream) {
+  if (!packed || !scales || !tscale || !w_out) return NVFP4_ERR_NULL;
+  if (e < 0 || e > 65535) return NVFP4_ERR_SHAPE;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  int64_t elems, w_bytes;
+  if (!mul_ok(ws.elems, e, &elems) || !mul_ok(elems, 2, &w_bytes)) return NVFP4_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(tscale) || !aligned16(w_out)) return NVFP4_ERR_ALIGN;
+  if (overlaps(w_out, w_bytes, packed, elems / 2) || overlaps(w_out, w_bytes, scales, elems / 16) ||
+      overlaps(w_out, w_bytes, tscale, 4 * e))
+    return NVFP4_ERR_ALIAS;
+  if (e == 0) return NVFP4_OK;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_dequant(packed, scales, tscale, e, ws.elems, w_out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_linear_routed(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route, int64_t e,
+                                 int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
+                                 const float* tscale, uint16_t* y, void* stream) {
+  if (!packed || !scales || !tscale || (t_count != 0 && (!x || !route || !y))) return NVFP4_ERR_NULL;
+  if (t_count < 0 || topk < 1 || e < 1) return NVFP4_ERR_SHAPE;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  int64_t elems, pairs, xe, xb, ye, yb;
+  if (!mul_ok(ws.elems, e, &elems) || !mul_ok(t_count, topk, &pairs) || !mul_ok(t_count, k, &xe) ||
+      !mul_ok(xe, 2, &xb) || !mul_ok(pairs, n, &ye) || !mul_ok(ye, 2, &yb) || pairs > INT64_MAX / 4)
+    return NVFP4_ERR_SHAPE;
+  if (t_count == 0) return NVFP4_OK;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(tscale) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(route) & 3u) != 0)
+    return NVFP4_ERR_ALIGN;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, route, 4 * pairs) || overlaps(y, yb, packed, elems / 2) ||
+      overlaps(y, yb, scales, elems / 16) || overlaps(y, yb, tscale, 4 * e))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_gemv_routed(x, t_count, topk, route, e, n, k, packed, scales, tscale, y,
+                            static_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 }  // extern "C"

@@ -57,15 +57,22 @@ __device__ __forceinline__ uint32_t amax_block(const uint4* __restrict__ w, int6
   return r;
 }
 
-// Per-workgroup maxima into part[blockIdx.x] (BF16 magnitude bits).
+// Per-workgroup maxima into part[blockIdx.x] (BF16 magnitude bits).  Over a
+// stack of matrices, blockIdx.y picks the matrix: w_stride 16-byte vectors and
+// part_stride words apart.
 __global__ void __launch_bounds__(256) amax_partial_kernel(const uint4* __restrict__ w, int64_t n_vec,
-                                                           uint32_t* __restrict__ part) {
-  const uint32_t r = amax_block(w, n_vec);
-  if (threadIdx.x == 0) part[blockIdx.x] = r;
+                                                           uint32_t* __restrict__ part, int64_t w_stride,
+                                                           int64_t part_stride) {
+  const uint32_t r = amax_block(w + (int64_t)blockIdx.y * w_stride, n_vec);
+  if (threadIdx.x == 0) part[(int64_t)blockIdx.y * part_stride + blockIdx.x] = r;
 }
 
-// *amax = max of part[0 .. nb) as an FP32 value (the BF16 magnitude widened).
-__global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __restrict__ part, int nb, float* amax) {
+// amax[y] = max of part[y][0 .. nb) as an FP32 value (the BF16 magnitude
+// widened); y = blockIdx.y over a stack.
+__global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __restrict__ part, int nb, float* amax,
+                                                          int64_t part_stride) {
+  part += (int64_t)blockIdx.y * part_stride;
+  amax += blockIdx.y;
   uint32_t m = 0;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) m = max(m, part[i]);
   m = wave_max_u32(m);
@@ -81,10 +88,11 @@ __global__ void __launch_bounds__(256) amax_kernel(const uint4* __restrict__ w, 
   if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), r << 16);  // BF16 magnitude -> FP32 bits
 }
 
-// tscale = fl32(amax / 2688), IEEE round-to-nearest division.
-__global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, float* tscale) {
-  const float a = *amax;
-  *tscale = __fdiv_rn(a, 2688.0f);
+// tscale = fl32(amax / 2688), IEEE round-to-nearest division; one value per
+// thread over a stack of n matrices.
+__global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, float* tscale, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) tscale[i] = __fdiv_rn(amax[i], 2688.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,11 +209,15 @@ __device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t
   }
 }
 
+// Over a stack, blockIdx.y picks the matrix (n_half half blocks each).
 __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
                                                        const float* __restrict__ amax_p,
                                                        uint32_t* __restrict__ packed,
                                                        uint8_t* __restrict__ scales) {
-  const uint32_t amax_b = __float_as_uint(*amax_p) >> 16;  // amax is a BF16 value held in FP32
+  w += (int64_t)blockIdx.y * n_half;
+  packed += (int64_t)blockIdx.y * n_half;
+  scales += (int64_t)blockIdx.y * (n_half >> 1);
+  const uint32_t amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;  // amax is a BF16 value held in FP32
   uint32_t sa;
   int ea;
   bf16_split(amax_b & 0x7FFFu, sa, ea);
@@ -255,11 +267,15 @@ __device__ __forceinline__ uint4 dequant_half(uint32_t p, uint32_t sbyte, float 
   }
 }
 
+// Over a stack, blockIdx.y picks the matrix (n_half half blocks each).
 __global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ tscale_p, int64_t n_half,
                                                       uint4* __restrict__ out) {
-  const float t = *tscale_p;
+  packed += (int64_t)blockIdx.y * n_half;
+  scales += (int64_t)blockIdx.y * (n_half >> 1);
+  out += (int64_t)blockIdx.y * n_half;
+  const float t = tscale_p[blockIdx.y];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * kDequantU;
   for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x * kDequantU + threadIdx.x; h0 < n_half; h0 += stride) {
     uint32_t p[kDequantU], sb[kDequantU];
@@ -294,30 +310,36 @@ void launch_amax(const uint16_t* w, int64_t n_elems, float* amax, hipStream_t s)
 }
 
 void launch_amax_set(const uint16_t* w, int64_t n_elems, uint32_t* part, float* amax, hipStream_t s) {
-  // part holds at least n_elems / 8 words (the packed output of a quantizer call), and the grid never exceeds
-  // n_elems / 8 workgroups.
+  launch_amax_set_stack(w, 1, n_elems, part, amax, s);
+}
+
+void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* amax,
+                           hipStream_t s) {
+  // Matrix i's partial maxima go to part + i * n_elems / 8: the packed output of matrix i (n_elems / 8 words), and
+  // the grid never exceeds n_elems / 8 workgroups.
   const int64_t n_vec = n_elems / 8;
   const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
-  amax_partial_kernel<<<nb, 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part);
-  amax_reduce_kernel<<<1, 256, 0, s>>>(part, (int)nb, amax);
+  amax_partial_kernel<<<dim3(nb, (unsigned)count), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part, n_vec,
+                                                                n_vec);
+  amax_reduce_kernel<<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, amax, n_vec);
 }
 
-void launch_finalize_tscale(const float* amax, float* tscale, hipStream_t s) {
-  finalize_tscale_kernel<<<1, 64, 0, s>>>(amax, tscale);
+void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hipStream_t s) {
+  finalize_tscale_kernel<<<(unsigned)((count + 63) / 64), 64, 0, s>>>(amax, tscale, count);
 }
 
-void launch_quantize(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
-                     hipStream_t s) {
+void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
+                     uint8_t* scales, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  quantize_kernel<<<grid_for(n_half, 256 * kQuantU, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_half, amax,
-                                                                  reinterpret_cast<uint32_t*>(packed), scales);
+  quantize_kernel<<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales);
 }
 
-void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t n_elems,
+void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,
                     uint16_t* out, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  dequant_kernel<<<grid_for(n_half, 256 * kDequantU, 1 << 20), 256, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales,
-                                                                 tscale, n_half, reinterpret_cast<uint4*>(out));
+  dequant_kernel<<<dim3(grid_for(n_half, 256 * kDequantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(packed), scales, tscale, n_half, reinterpret_cast<uint4*>(out));
 }
 
 }  // namespace nvfp4

@@ -599,8 +599,10 @@ __global__ void __launch_bounds__(256) skinny_dma_kernel(SkinnyArgs p) {
       asm volatile("" ::: "memory");                                                              \
       __builtin_amdgcn_s_barrier();                                                               \
       asm volatile("" ::: "memory");                                                              \
-      const int cn = ci + D - 1, sn = si == D - 1 ? 0 : si + 1;                                   \
-      sk_dma_issue<MX, TT, LW, LX, LS>(p, src, cn, nc, c0, st[si == 0 ? D - 1 : si - 1],          \
+      /* with D == 4 the stage of chunk ci is P: constant offsets */                              \
+      const int sc = D == 4 ? (P) : si;                                                           \
+      const int cn = ci + D - 1, sn = sc == D - 1 ? 0 : sc + 1;                                   \
+      sk_dma_issue<MX, TT, LW, LX, LS>(p, src, cn, nc, c0, st[sc == 0 ? D - 1 : sc - 1],          \
                                        sgr[(cn >> 2) % NB], lane);                                \
       sk_frag_read<MT, MX, TT, FIVE>(NXT, st[sn], sgr[((ci + 1) >> 2) % NB], ((P) + 1) & 3, w, r, lane); \
       sk_frag_compute<MT, FIVE>(CUR, w, acc2, acc5);                                              \

@@ -37,6 +37,12 @@ Readings taken where the pages are silent or open:
   R10 linear        Y[m, n] = sum_k X[m, k] * E2M1 * E4M3 * tscale, accepted within 2e-3 * sum_k |X * w_hat|.
   R11 output        the linear's output is BF16: on top of R10, the final rounding to BF16 may add up to
                     2^-8 of the output's magnitude.
+  R12 expert stack  imp "docs/quantization.md", NVFP4 kernel pipeline, MoE layers: per-expert weights
+                    become one contiguous [ne, N, K_packed] buffer per layer and projection.  Each expert
+                    is its own quantized tensor with its own tensor scale (matrix i of the stack is
+                    quantize(W[i])).
+  R13 routed        y[t, j] = X[t] . W_hat[route[t, j]]^T for top-k routing (each token's k chosen experts);
+                    an expert id outside [0, ne) gives a zero row.
 
 Parity pins: every function here is checked by tests/test_oracle_pins.py
 against values the pages print, library routines (torch float8_e4m3fn),
@@ -247,3 +253,40 @@ def linear_violations(y: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, tol: 
     y = np.asarray(y, dtype=np.float64)
     acc = tol * bound
     return ~(np.abs(y - y_ref) <= acc + out_roundoff * (np.abs(y_ref) + acc))
+
+
+# --------------------------------------------------------------------------
+# Expert stacks (mixture-of-experts layers).
+# --------------------------------------------------------------------------
+def quantize_experts(w_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """R12: BF16 [E, N, K] -> (packed [E, N, K/2], scales [E, N, K/16], tscale float32 [E]), one tensor per expert."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    if w_bits.ndim != 3:
+        raise ValueError("W must be [E, N, K]")
+    outs = [quantize(w_bits[i]) for i in range(w_bits.shape[0])]
+    return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]),
+            np.array([o[2] for o in outs], dtype=np.float32))
+
+
+def dequant_experts(packed: np.ndarray, scales: np.ndarray, tscale: np.ndarray) -> np.ndarray:
+    """R9 applied to every matrix of a stack: BF16 bits [E, N, K]."""
+    return np.stack([dequant(packed[i], scales[i], tscale[i]) for i in range(packed.shape[0])])
+
+
+def linear_routed_ref(x_bits: np.ndarray, route: np.ndarray, packed: np.ndarray, scales: np.ndarray,
+                      tscale: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """R13: (y_ref, bound), float64 [T, topk, N]; pairs routed to an expert outside [0, E) are zero."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    route = np.asarray(route, dtype=np.int64)
+    t_count, topk = route.shape
+    e_count, n = packed.shape[0], packed.shape[1]
+    y = np.zeros((t_count, topk, n))
+    bound = np.zeros((t_count, topk, n))
+    for e in range(e_count):
+        ts, js = np.nonzero(route == e)
+        if ts.size == 0:
+            continue
+        ye, be = linear_ref(x_bits[ts], packed[e], scales[e], tscale[e])
+        y[ts, js] = ye
+        bound[ts, js] = be
+    return y, bound

@@ -51,6 +51,18 @@ def sample_rows(n, count, seed=123):
     return np.array(sorted(rows))
 
 
+def q_both(nv, w_bits):
+    """w quantized on the GPU (device tensors) and by the oracle (host arrays), checked bit-equal.
+
+    The oracle's linear always runs on the oracle's own quantization, never on
+    the GPU's outputs."""
+    q = nv.quantize(to_dev_bf16(w_bits))
+    rp, rs, rt = O.quantize(w_bits)
+    assert np.array_equal(u8_host(q[0]), rp) and np.array_equal(u8_host(q[1]), rs), "quantization differs"
+    assert q[2].cpu().numpy()[0].view(np.uint32) == np.float32(rt).view(np.uint32), "tensor scale differs"
+    return q, (rp, rs, rt)
+
+
 def check_linear(y_bits, y_ref, bound, what):
     y = WL.f32_from_bf16_bits(y_bits).astype(np.float64)
     bad = O.linear_violations(y, y_ref, bound)
@@ -166,7 +178,11 @@ def test_gate_up_shared_scale(nv):
     y_right = bf16_host(nv.linear(to_dev_bf16(x), pu, su, ts))
     y_wrong = bf16_host(nv.linear(to_dev_bf16(x), pu, su, own))
     rows = sample_rows(wl.n // 2, 64)
-    y_ref, bound = O.linear_ref(x, u8_host(pu)[rows], u8_host(su)[rows], ts.cpu().numpy()[0])
+    shared = max(O.tensor_amax(gate), O.tensor_amax(up))
+    rp, rs, rt = O.quantize(up[rows], amax=shared)
+    assert np.array_equal(u8_host(pu)[rows], rp) and np.array_equal(u8_host(su)[rows], rs)
+    assert ts.cpu().numpy()[0].view(np.uint32) == O.tensor_scale(shared).view(np.uint32)
+    y_ref, bound = O.linear_ref(x, rp, rs, rt)
     check_linear(y_right[:, rows], y_ref, bound, "gate/up shared scale (up rows)")
     # U's own scale is smaller by the amax spread: outputs shrink by that factor, and every output
     # whose |y| is not tiny against its bound falls outside the tolerance.
@@ -197,8 +213,8 @@ LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 6
 def test_linear_all_kernels_small(nv, m, n, k):
     w = WL.normal_bf16((n, k), 0.02, 100 + n)
     x = WL.normal_bf16((m, k), 1.0, 200 + m)
-    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
-    y_ref, bound = O.linear_ref(x, u8_host(packed), u8_host(scales), tscale.cpu().numpy()[0])
+    (packed, scales, tscale), rq = q_both(nv, w)
+    y_ref, bound = O.linear_ref(x, *rq)
     xd = to_dev_bf16(x)
     outs = {}
     for kern in ["auto"] + KERNELS:
@@ -226,9 +242,9 @@ def test_linear_edge_cases(nv):
     for name, w in crafted_weights().items():
         if name in ("huge", "subnormal amax"):
             continue   # outputs overflow / underflow BF16 by construction
-        q = nv.quantize(to_dev_bf16(w))
+        q, rq = q_both(nv, w)
         x = WL.normal_bf16((3, w.shape[1]), 1.0, 3)
-        y_ref, bound = O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])
+        y_ref, bound = O.linear_ref(x, *rq)
         for kern in KERNELS:
             check_linear(bf16_host(nv.linear(to_dev_bf16(x), *q, kernel=kern)), y_ref, bound, f"crafted {name} {kern}")
 
@@ -246,8 +262,8 @@ def test_small_m_split_k(nv, m, n, k):
     assert need > 0, "shape expected to split K"
     w = WL.normal_bf16((n, k), 0.02, 300 + n)
     x = WL.normal_bf16((m, k), 1.0, 400 + m)
-    q = nv.quantize(to_dev_bf16(w))
-    y_ref, bound = O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])
+    q, rq = q_both(nv, w)
+    y_ref, bound = O.linear_ref(x, *rq)
     xd = to_dev_bf16(x)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     y1 = bf16_host(nv.linear(xd, *q, workspace=ws))
@@ -268,9 +284,9 @@ def test_small_m_workspace_shared_by_shapes(nv):
     ws = torch.zeros(max(nv.linear_workspace_bytes(*s) for s in shapes), dtype=torch.uint8, device="cuda")
     cases = []
     for i, (m, n, k) in enumerate(shapes):
-        q = nv.quantize(to_dev_bf16(WL.normal_bf16((n, k), 0.02, 500 + i)))
+        q, rq = q_both(nv, WL.normal_bf16((n, k), 0.02, 500 + i))
         x = WL.normal_bf16((m, k), 1.0, 600 + i)
-        cases.append((to_dev_bf16(x), q, O.linear_ref(x, u8_host(q[0]), u8_host(q[1]), q[2].cpu().numpy()[0])))
+        cases.append((to_dev_bf16(x), q, O.linear_ref(x, *rq)))
     for _ in range(3):
         for xd, q, (y_ref, bound) in cases:
             check_linear(bf16_host(nv.linear(xd, *q, workspace=ws)), y_ref, bound, "shared workspace")
@@ -286,10 +302,11 @@ _weights_cache = {}
 
 
 def _quantized(nv, wname):
+    """(device quantization, BF16 weight, tensor amax) of a full-size workload weight."""
     if wname not in _weights_cache:
         _weights_cache.clear()
         w = WL.WORKLOADS["small_m_up" if wname == "prefill" else wname].weight()
-        _weights_cache[wname] = nv.quantize(to_dev_bf16(w))
+        _weights_cache[wname] = (nv.quantize(to_dev_bf16(w)), w, O.tensor_amax(w))
     return _weights_cache[wname]
 
 
@@ -297,7 +314,7 @@ def _quantized(nv, wname):
 def test_linear_full_size_sampled(nv, wname, m):
     wl = WL.WORKLOADS[wname]
     log(f"full-size linear {wname} m={m} n={wl.n} k={wl.k}")
-    packed, scales, tscale = _quantized(nv, wname)
+    (packed, scales, tscale), w, amax = _quantized(nv, wname)
     x = WL.activations(m, wl.k)
     xd = to_dev_bf16(x)
     y = nv.linear(xd, packed, scales, tscale)
@@ -305,6 +322,95 @@ def test_linear_full_size_sampled(nv, wname, m):
     assert torch.equal(y, y2), "not deterministic"
     cols = sample_rows(wl.n, 64)
     cols_t = torch.from_numpy(cols).cuda()
-    y_ref, bound = O.linear_ref(x, u8_host(packed.index_select(0, cols_t)), u8_host(scales.index_select(0, cols_t)),
-                                tscale.cpu().numpy()[0])
+    # The oracle quantizes the sampled rows itself (against the full tensor's amax); they must
+    # equal the GPU's rows, and the oracle's linear runs on its own quantization.
+    rp, rs, rt = O.quantize(w[cols], amax=amax)
+    assert np.array_equal(u8_host(packed.index_select(0, cols_t)), rp)
+    assert np.array_equal(u8_host(scales.index_select(0, cols_t)), rs)
+    assert tscale.cpu().numpy()[0].view(np.uint32) == np.float32(rt).view(np.uint32)
+    y_ref, bound = O.linear_ref(x, rp, rs, rt)
     check_linear(bf16_host(y)[:, cols], y_ref, bound, f"{wname} m={m}")
+
+
+# ---------------------------------------------------------------------------
+# Expert stacks (MoE layers) and the routed decode linear.
+# ---------------------------------------------------------------------------
+def _expert_stack(e, n, k, seed):
+    """e experts with amaxes spread over a factor of ~5 (each expert gets its own tensor scale)."""
+    return np.stack([WL.normal_bf16((n, k), 0.02 * (1.0 + 0.7 * i), seed + i) for i in range(e)])
+
+
+@pytest.mark.parametrize("e,n,k", [(3, 48, 272), (4, 33, 5120), (1, 16, 16)])
+def test_quantize_experts_bit_exact(nv, e, n, k):
+    w = _expert_stack(e, n, k, 900 + k)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    rp, rs, rt = O.quantize_experts(w)
+    assert np.array_equal(tscale.cpu().numpy().view(np.uint32), rt.view(np.uint32))
+    assert np.array_equal(u8_host(scales), rs)
+    assert np.array_equal(u8_host(packed), rp)
+    assert np.array_equal(bf16_host(nv.dequant_experts(packed, scales, tscale)), O.dequant_experts(rp, rs, rt))
+    # matrix i equals the single-matrix quantizer on w[i]
+    for i in range(e):
+        qi = nv.quantize(to_dev_bf16(w[i]))
+        assert torch.equal(qi[0], packed[i]) and torch.equal(qi[1], scales[i]) and torch.equal(qi[2][0], tscale[i])
+
+
+# (tokens, topk, experts, n, k): K split GEMV (k = 5120, 2048, 512), and the loop GEMV
+# (k = 1040: 8-byte units; k = 768: 16-byte units); ragged n.
+ROUTED_SHAPES = [(1, 8, 16, 300, 5120), (3, 4, 6, 100, 2048), (2, 3, 5, 70, 1040), (4, 2, 3, 33, 768),
+                 (5, 2, 4, 21, 512), (1, 1, 1, 16, 16)]
+
+
+@pytest.mark.parametrize("t,topk,e,n,k", ROUTED_SHAPES)
+def test_linear_routed(nv, t, topk, e, n, k):
+    w = _expert_stack(e, n, k, 1000 + k)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    rq = O.quantize_experts(w)
+    assert np.array_equal(u8_host(packed), rq[0]) and np.array_equal(u8_host(scales), rq[1])
+    x = WL.normal_bf16((t, k), 1.0, 1100 + t)
+    rng = np.random.default_rng(1200 + e)
+    route = rng.integers(0, e, size=(t, topk)).astype(np.int32)
+    if t * topk >= 3:
+        route.flat[1] = route.flat[0]   # the same expert twice
+        route.flat[2] = -1              # out of range: zeros
+    if t * topk >= 4:
+        route.flat[3] = e               # out of range: zeros
+    y = nv.linear_routed(to_dev_bf16(x), torch.from_numpy(route).cuda(), packed, scales, tscale)
+    y_ref, bound = O.linear_routed_ref(x, route, *rq)
+    yb = bf16_host(y)
+    check_linear(yb.reshape(t * topk, n), y_ref.reshape(t * topk, n), bound.reshape(t * topk, n),
+                 f"routed t={t} topk={topk} e={e} n={n} k={k}")
+    bad = (route < 0) | (route >= e)
+    assert np.all(yb[bad] == 0), "out-of-range expert ids must give zero rows"
+    # deterministic; and, where the routed path runs the K-split GEMV, the same bits as the
+    # plain GEMV on the chosen expert
+    assert torch.equal(nv.linear_routed(to_dev_bf16(x), torch.from_numpy(route).cuda(), packed, scales, tscale), y)
+    if k % 512 == 0 and k <= 5120:
+        for (ti, j) in [(0, 0), (t - 1, topk - 1)]:
+            ei = int(route[ti, j])
+            if 0 <= ei < e:
+                yg = nv.linear(to_dev_bf16(x[ti:ti + 1]), packed[ei], scales[ei], tscale[ei:ei + 1].clone(),
+                               kernel="gemv")
+                assert np.array_equal(bf16_host(yg)[0], yb[ti, j])
+
+
+def test_linear_routed_edges(nv):
+    w = _expert_stack(2, 16, 512, 1300)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    # t = 0 is a no-op
+    y = nv.linear_routed(torch.empty((0, 512), dtype=torch.bfloat16, device="cuda"),
+                         torch.empty((0, 3), dtype=torch.int32, device="cuda"), packed, scales, tscale)
+    assert y.shape == (0, 3, 16)
+    # every id out of range: all zeros, nothing read from the stack
+    x = to_dev_bf16(WL.normal_bf16((2, 512), 1.0, 1301))
+    bad = torch.tensor([[-5, 2], [7, 2 ** 31 - 1]], dtype=torch.int32, device="cuda")
+    assert torch.count_nonzero(nv.linear_routed(x, bad, packed, scales, tscale)) == 0
+    # argument errors are reported before anything is launched
+    from nvfp4_weight_only_amd import binding as B
+    y = torch.empty((2, 2, 16), dtype=torch.bfloat16, device="cuda")
+    args = lambda topk, e, yp: (x.data_ptr(), 2, topk, bad.data_ptr(), e, 16, 512, packed.data_ptr(),  # noqa: E731
+                                scales.data_ptr(), tscale.data_ptr(), yp, 0)
+    assert nv.lib().nvfp4_linear_routed(*args(0, 2, y.data_ptr())) == B.ERR_SHAPE
+    assert nv.lib().nvfp4_linear_routed(*args(2, 0, y.data_ptr())) == B.ERR_SHAPE
+    assert nv.lib().nvfp4_linear_routed(*args(2, 2, x.data_ptr())) == B.ERR_ALIAS   # y overlaps x
+    assert nv.lib().nvfp4_linear_routed(*args(2, 2, y.data_ptr() + 2)) == B.ERR_ALIGN

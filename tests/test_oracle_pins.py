@@ -468,3 +468,51 @@ def test_mutation_wrong_e4m3_bias(monkeypatch):
     monkeypatch.setattr(O, "E4M3_TABLE", bad)
     with pytest.raises(AssertionError):
         pin_e4m3_table()
+
+
+# --------------------------------------------------------------------------
+# Expert stacks (R12, R13).
+# --------------------------------------------------------------------------
+def test_quantize_experts_one_tensor_scale_per_expert():
+    """Each expert's tensor scale is fl32(its own amax / 2688); a shared amax would fail this."""
+    w = np.stack([WL.normal_bf16((6, 48), 0.02 * 3.0 ** i, 40 + i) for i in range(3)])
+    packed, scales, tscale = O.quantize_experts(w)
+    assert packed.shape == (3, 6, 24) and scales.shape == (3, 6, 3) and tscale.shape == (3,)
+    for i in range(3):
+        amax = float(np.abs(WL.f32_from_bf16_bits(w[i])).max())
+        assert tscale[i] == np.float32(amax) / np.float32(2688.0)
+    assert len(set(tscale.tolist())) == 3
+    pin_quantize_brute_force(w[1])
+    p1, s1, _ = O.quantize(w[1])
+    assert np.array_equal(packed[1], p1) and np.array_equal(scales[1], s1)
+    d = O.dequant_experts(packed, scales, tscale)
+    assert np.array_equal(d[2], O.dequant(packed[2], scales[2], tscale[2]))
+
+
+def test_linear_routed_brute_force():
+    """y[t, j, n] against an exact-rational sum over the expert chosen for (t, j), with duplicate and out-of-range ids."""
+    mags = [Fraction(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    e2m1 = mags + [-m for m in mags]
+    w = np.stack([WL.normal_bf16((4, 32), 0.02 * (i + 1), 60 + i) for i in range(3)])
+    packed, scales, tscale = O.quantize_experts(w)
+    x_bits = WL.normal_bf16((3, 32), 1.0, 70)
+    route = np.array([[2, 0], [1, 1], [-1, 3]], dtype=np.int32)
+    y, bound = O.linear_routed_ref(x_bits, route, packed, scales, tscale)
+    assert y.shape == (3, 2, 4)
+    x = WL.f32_from_bf16_bits(x_bits).astype(np.float64)
+    for t in range(3):
+        for j in range(2):
+            e = int(route[t, j])
+            for n in range(4):
+                if not 0 <= e < 3:
+                    assert y[t, j, n] == 0 and bound[t, j, n] == 0
+                    continue
+                codes = O.unpack_nibbles(packed[e])
+                e4m3 = torch.from_numpy(scales[e].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                ts = Fraction(float(tscale[e]))
+                terms = [Fraction(x[t, kk]) * e2m1[codes[n, kk]] * Fraction(e4m3[n, kk // 16]) * ts for kk in range(32)]
+                exact, babs = sum(terms), sum(abs(v) for v in terms)
+                tol = Fraction(1, 10 ** 12) * (babs + Fraction(1, 10 ** 30))
+                assert abs(Fraction(y[t, j, n]) - exact) <= tol, (t, j, n)
+                assert abs(Fraction(bound[t, j, n]) - babs) <= tol, (t, j, n)
+    assert np.array_equal(y[1, 0], y[1, 1])  # the same expert twice
