@@ -145,3 +145,32 @@ WORKLOADS: Dict[str, Workload] = {
 
 def workload_names() -> List[str]:
     return list(WORKLOADS)
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    """Synthetic routed decode over an expert stack: t tokens, each routed to topk of `experts` matrices [n, k].
+
+    The stack is built from one seeded ~N(0, 0.02) matrix, expert i scaled by (1 + i / 64) (so every expert
+    has its own tensor scale); route r of a rotation of `experts / topk` routes sends the token to experts
+    r * topk .. r * topk + topk - 1, so consecutive calls read different experts.
+    """
+    name: str
+    description: str
+    experts: int
+    n: int
+    k: int
+    topk: int
+    t: int = 1
+
+    def base_weight(self) -> np.ndarray:
+        return weight_plain(self.n, self.k)
+
+    def routes(self) -> np.ndarray:
+        """int32 [experts // topk, t, topk]."""
+        r = np.arange(self.experts // self.topk, dtype=np.int32)[:, None, None] * self.topk
+        return (r + np.arange(self.topk, dtype=np.int32)[None, None, :]).repeat(self.t, axis=1).astype(np.int32)
+
+
+MOE_DECODE = MoeWorkload("moe_decode", "routed MoE decode: 128 experts of N=2048, K=4096, top-8, one token",
+                         experts=128, n=2048, k=4096, topk=8)
