@@ -184,15 +184,21 @@ def bench_quant_rows(reps):
     return rows
 
 
-def bench_moe_row(reps):
-    """Routed MoE decode (nvfp4_linear_routed) over a rotation of routes that reads every expert once."""
+def bench_moe_rows(reps):
+    """Routed MoE rows over one 128-expert stack (N=2048, K=4096):
+    decode: nvfp4_linear_routed, one token, over a rotation of routes that reads every expert once;
+    prefill: nvfp4_linear_grouped, 2048 tokens routed top-8 by a balanced random router (the whole call:
+             grouping kernels and the grouped GEMM)."""
     mw = WL.MOE_DECODE
     base = dev_bf16(mw.base_weight())
-    stack = torch.stack([(base.float() * (1.0 + i / 64.0)).to(torch.bfloat16) for i in range(mw.experts)])
+    stack = torch.stack([(base.float() * mw.expert_scale(i)).to(torch.bfloat16) for i in range(mw.experts)])
     del base
     packed, scales, tscale = nv.quantize_experts(stack)
     del stack
     torch.cuda.empty_cache()
+    w_bytes = mw.n * mw.k // 2 + mw.n * mw.k // 16 + 4
+    rows = {}
+
     routes = [torch.from_numpy(r).cuda() for r in mw.routes()]
     x = dev_bf16(WL.activations(mw.t, mw.k))
     y = torch.empty((mw.t, mw.topk, mw.n), dtype=torch.bfloat16, device="cuda")
@@ -200,15 +206,36 @@ def bench_moe_row(reps):
     g = graph_of(calls)
     time_graph_replays(g, 2, len(calls))
     ms = time_graph_replays(g, reps, len(calls))
-    nbytes = mw.t * mw.topk * (mw.n * mw.k // 2 + mw.n * mw.k // 16 + 4 + 2 * mw.n) + 2 * mw.t * mw.k + 4 * mw.t * mw.topk
+    nbytes = mw.t * mw.topk * (w_bytes + 2 * mw.n) + 2 * mw.t * mw.k + 4 * mw.t * mw.topk
     flops = 2.0 * mw.t * mw.topk * mw.n * mw.k
     row = {"experts": mw.experts, "n": mw.n, "k": mw.k, "topk": mw.topk, "tokens": mw.t, "routes": len(calls),
            "us_per_call": round(ms * 1e3, 3), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "tflop_s": round(flops / (ms * 1e-3) / 1e12, 2), "bytes": nbytes}
     row["hbm_frac"] = round(row["gb_s"] / HBM_PEAK_GBS, 4)
-    del g, packed, scales, tscale, routes
+    rows["moe_routed_decode_top8"] = row
+    del g, routes, x, y
+
+    pw = WL.MOE_PREFILL
+    route = torch.from_numpy(pw.random_routes()).cuda()
+    x = dev_bf16(WL.activations(pw.t, pw.k))
+    y = torch.empty((pw.t, pw.topk, pw.n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(nv.linear_grouped_workspace_bytes(pw.t, pw.topk, pw.experts), dtype=torch.uint8, device="cuda")
+    g = graph_of([lambda: nv.linear_grouped(x, route, packed, scales, tscale, out=y, workspace=ws)])
+    time_graph_replays(g, 2, 1)
+    ms = time_graph_replays(g, max(reps // 3, 3), 1)
+    pairs = pw.t * pw.topk
+    flops = 2.0 * pairs * pw.n * pw.k
+    nbytes = pw.experts * w_bytes + 2 * pw.t * pw.k + 2 * pairs * pw.n + 4 * pairs
+    row = {"experts": pw.experts, "n": pw.n, "k": pw.k, "topk": pw.topk, "tokens": pw.t,
+           "pairs_per_expert": [int(c) for c in torch.bincount(route.flatten().long(), minlength=pw.experts)
+                                .aminmax()],
+           "us_per_call": round(ms * 1e3, 3), "tflop_s": round(flops / (ms * 1e-3) / 1e12, 2),
+           "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes}
+    row["mfma_frac"] = round(row["tflop_s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    rows["moe_grouped_prefill_t2048_top8"] = row
+    del g, route, x, y, ws, packed, scales, tscale
     torch.cuda.empty_cache()
-    return row
+    return rows
 
 
 def cpu_baseline(budget_s=10.0):
@@ -337,8 +364,10 @@ def main():
         log("rows quantize/dequant")
         rows.update(bench_quant_rows(20))
         log(f"  {rows['quantize_decode_5120x5120']} {rows['dequant_decode_5120x5120']}")
-        rows["moe_routed_decode_top8"] = bench_moe_row(reps)
+        log("rows MoE")
+        rows.update(bench_moe_rows(reps))
         log(f"  {rows['moe_routed_decode_top8']}")
+        log(f"  {rows['moe_grouped_prefill_t2048_top8']}")
 
     log("cpu baseline (oracle)")
     cpu = cpu_baseline(args.cpu_budget)

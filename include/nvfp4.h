@@ -202,6 +202,33 @@ nvfp4_status nvfp4_linear_routed(const uint16_t* x, int64_t t_count, int64_t top
                                  int64_t e, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                                  const float* tscale, uint16_t* y, void* stream);
 
+/*
+ * Grouped W4A16 linear over an expert stack: the prefill path of a MoE layer
+ * (many tokens, top-k routing).  Same arguments, layouts and result as
+ * nvfp4_linear_routed (y [t_count, topk, n]; within the linear's tolerance,
+ * since a different kernel sums in a different order; an expert id outside
+ * [0, e) gives a row of zeros), plus a caller-owned device workspace of at
+ * least nvfp4_linear_grouped_workspace_bytes(t_count, topk, e) bytes,
+ * 16-byte aligned, overlapping no argument.  On the stream, the (t, j) pairs
+ * are counted and sorted by expert into the workspace, then one GEMM launch
+ * multiplies each expert's matrix with its pairs' activation rows in 128-row
+ * tiles, so an expert's weights are read once per 272 output columns however
+ * many tokens chose it (the routed GEMV reads them once per pair).  The order
+ * of pairs within an expert is not deterministic; the output is, bit for bit.
+ * Where the GEMM's limits are not met (k not a multiple of 256, t_count * k
+ * above 2^31, or 32-bit pair and tile counts exceeded) the call runs
+ * nvfp4_linear_routed's GEMV instead and leaves the workspace unused.
+ * Errors: as nvfp4_linear_routed; a NULL workspace (t_count > 0) is
+ * NVFP4_ERR_NULL, a workspace_bytes below the size above NVFP4_ERR_SHAPE.
+ * The workspace must not be shared by calls in flight at the same time.
+ */
+int64_t nvfp4_linear_grouped_workspace_bytes(int64_t t_count, int64_t topk, int64_t e);
+
+nvfp4_status nvfp4_linear_grouped(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route,
+                                  int64_t e, int64_t n, int64_t k, const uint8_t* packed,
+                                  const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = ran
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
             "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced",
             "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
-            "nvfp4_linear_workspace_bytes")
+            "nvfp4_linear_grouped", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -60,10 +60,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_experts.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
         L.nvfp4_linear_routed.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.nvfp4_linear_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
-        L.nvfp4_linear_workspace_bytes.restype = i64
-        for name in EXPORTED[2:-1]:
-            getattr(L, name).restype = i32
+        L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
+        for name in EXPORTED[2:]:
+            getattr(L, name).restype = i64 if name.endswith("_workspace_bytes") else i32
         _lib = L
     return _lib
 
@@ -275,4 +276,47 @@ def linear_routed(x: torch.Tensor, route: torch.Tensor, packed: torch.Tensor, sc
     _check(lib().nvfp4_linear_routed(x.data_ptr(), t, topk, route.data_ptr(), e, n, k, packed.data_ptr(),
                                      scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), _stream(x)),
            "nvfp4_linear_routed")
+    return out
+
+
+def linear_grouped_workspace_bytes(t: int, topk: int, e: int) -> int:
+    """Workspace bytes nvfp4_linear_grouped needs for t tokens, top-k routing over e experts."""
+    b = lib().nvfp4_linear_grouped_workspace_bytes(t, topk, e)
+    if b < 0:
+        raise ValueError(f"invalid grouped shape t={t} topk={topk} e={e}")
+    return b
+
+
+def linear_grouped(x: torch.Tensor, route: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                   tscale: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Same result as linear_routed through the grouped GEMM (the prefill form).
+
+    workspace: optional uint8 device tensor of at least linear_grouped_workspace_bytes(t, topk, e)
+    bytes; one is allocated when it is not given.
+    """
+    _need(x, torch.bfloat16, "x")
+    _need(route, torch.int32, "route")
+    e, n, k = _stack_shape(packed, scales, tscale)
+    t, kx = x.shape
+    if kx != k:
+        raise ValueError("x's k does not match the stack")
+    if route.dim() != 2 or route.shape[0] != t:
+        raise ValueError("route must be [t, topk]")
+    topk = route.shape[1]
+    if out is None:
+        out = torch.empty((t, topk, n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (t, topk, n):
+            raise ValueError("out must be [t, topk, n]")
+    need = linear_grouped_workspace_bytes(t, topk, e)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    else:
+        _need(workspace, torch.uint8, "workspace")
+    _check(lib().nvfp4_linear_grouped(x.data_ptr(), t, topk, route.data_ptr(), e, n, k, packed.data_ptr(),
+                                      scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream(x)),
+           "nvfp4_linear_grouped")
     return out

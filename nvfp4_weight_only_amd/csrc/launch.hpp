@@ -44,4 +44,20 @@ bool prefill_dma_supported(int64_t m, int64_t n, int64_t k);
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
 
+// Grouped prefill over an expert stack (K a multiple of 256, t_count * k <= 2^31,
+// int32 pair indices and workgroup ids):
+// the pairs of the top-k routing sorted by expert in a workspace of
+// grouped_workspace_bytes(pairs, experts) bytes, then the prefill GEMM per
+// expert tile.  Same result as launch_gemv_routed (within the linear's
+// tolerance), including zero rows for out-of-range expert ids.
+bool prefill_grouped_supported(int64_t t_count, int64_t topk, int64_t experts, int64_t n, int64_t k);
+int64_t prefill_grouped_tile_bound(int64_t pairs, int64_t experts);
+int64_t grouped_workspace_bytes(int64_t pairs, int64_t experts);
+void launch_prefill_grouped(const uint16_t* x, int64_t topk, const int32_t* groups, int64_t pairs, int64_t experts,
+                            int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                            uint16_t* y, hipStream_t s);
+void launch_linear_grouped(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route, int64_t experts,
+                           int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                           uint16_t* y, void* workspace, hipStream_t s);
+
 }  // namespace nvfp4

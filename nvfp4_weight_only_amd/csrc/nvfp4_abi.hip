@@ -305,4 +305,47 @@ nvfp4_status nvfp4_linear_routed(const uint16_t* x, int64_t t_count, int64_t top
   return launch_status();
 }
 
+int64_t nvfp4_linear_grouped_workspace_bytes(int64_t t_count, int64_t topk, int64_t e) {
+  int64_t pairs;
+  if (t_count < 0 || topk < 1 || e < 1 || !mul_ok(t_count, topk, &pairs) || pairs > INT64_MAX / 8 ||
+      e > INT64_MAX / 32)
+    return -1;
+  return nvfp4::grouped_workspace_bytes(pairs, e);
+}
+
+nvfp4_status nvfp4_linear_grouped(const uint16_t* x, int64_t t_count, int64_t topk, const int32_t* route, int64_t e,
+                                  int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
+                                  const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  if (!packed || !scales || !tscale || (t_count != 0 && (!x || !route || !y || !workspace))) return NVFP4_ERR_NULL;
+  if (t_count < 0 || topk < 1 || e < 1) return NVFP4_ERR_SHAPE;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  int64_t elems, pairs, xe, xb, ye, yb;
+  if (!mul_ok(ws.elems, e, &elems) || !mul_ok(t_count, topk, &pairs) || !mul_ok(t_count, k, &xe) ||
+      !mul_ok(xe, 2, &xb) || !mul_ok(pairs, n, &ye) || !mul_ok(ye, 2, &yb) || pairs > INT64_MAX / 8 ||
+      e > INT64_MAX / 32)
+    return NVFP4_ERR_SHAPE;
+  const int64_t need = nvfp4::grouped_workspace_bytes(pairs, e);
+  if (t_count == 0) return NVFP4_OK;
+  if (workspace_bytes < need) return NVFP4_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(tscale) || !aligned16(y) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(route) & 3u) != 0)
+    return NVFP4_ERR_ALIGN;
+  const void* ins[5] = {x, route, packed, scales, tscale};
+  const int64_t in_bytes[5] = {xb, 4 * pairs, elems / 2, elems / 16, 4 * e};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(y, yb, ins[i], in_bytes[i]) || overlaps(workspace, need, ins[i], in_bytes[i]))
+      return NVFP4_ERR_ALIAS;
+  if (overlaps(workspace, need, y, yb)) return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nvfp4::prefill_grouped_supported(t_count, topk, e, n, k))
+    nvfp4::launch_linear_grouped(x, t_count, topk, route, e, n, k, packed, scales, tscale, y, workspace, s);
+  else
+    nvfp4::launch_gemv_routed(x, t_count, topk, route, e, n, k, packed, scales, tscale, y, s);
+  return launch_status();
+}
+
 }  // extern "C"

@@ -46,7 +46,26 @@ struct PdArgs {
   const float* tscale;
   uint16_t* y;
   int n_tiles, m_tiles;
+  // Grouped form (an expert stack): the routed pairs sorted by expert, as
+  // built by the grouping kernels (see PdGroups), and the stack's layout.
+  const int32_t* groups;
+  int64_t topk, experts, w_stride;  // w_stride: packed bytes per expert
 };
+
+// Layout of the grouping workspace (int32): counts[E], cursors[E],
+// pair_off[E + 1] (first sorted position of each expert's pairs),
+// tile_off[E + 1] (first 128-row tile of each expert), perm[pairs] (pair
+// indices, grouped by expert).
+struct PdGroups {
+  const int32_t* pair_off;
+  const int32_t* tile_off;
+  const int32_t* perm;
+};
+
+__device__ __forceinline__ PdGroups pd_groups(const PdArgs& p) {
+  const int32_t* g = p.groups;
+  return PdGroups{g + 2 * p.experts, g + 3 * p.experts + 1, g + 4 * p.experts + 2};
+}
 
 // LDS (16-byte slots):
 //   x stage: activation row r (of 128), piece p (8 elements) at 8 r + (p ^ (r & 7))
@@ -68,6 +87,7 @@ constexpr int kPdXStages = 5;
 struct PdLds {
   PdX xs[kPdXStages];
   PdW wg[2];
+  int32_t rowmap[kPdBM];  // grouped form: the output row (pair index) of each tile row
 };
 
 // One global_load_lds_dwordx4 from a per-lane 64-bit address (the weight group
@@ -369,7 +389,9 @@ __device__ __forceinline__ uint2 pd_pack4(const f32x16_t& a, int V, float ts) {
 // Copy the BF16 tile (128 x 272, row-major in LDS) to Y rows m0.., columns
 // n0..: 34 pieces of 8 columns per row, 17 per thread.  Pieces that are whole,
 // inside Y and 16-byte aligned go as one store; the others element by element.
-__device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* yt, int64_t m0, int64_t n0, int tid) {
+template <bool G>
+__device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* yt, int64_t m0, int64_t n0, int tid,
+                                              const int32_t* rowmap) {
   const int64_t rows = p.m - m0 < kPdBM ? p.m - m0 : kPdBM;
   const int64_t cols = p.n - n0 < kPdBN ? p.n - n0 : kPdBN;
   constexpr int kPieces = kPdBN / 8;
@@ -378,7 +400,7 @@ __device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* y
     const int r = j / kPieces, c8 = 8 * (j - r * kPieces);
     if (r >= rows || c8 >= cols) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kPdBN + c8);
-    uint16_t* dst = p.y + (m0 + r) * p.n + n0 + c8;
+    uint16_t* dst = p.y + (G ? (int64_t)rowmap[r] : m0 + r) * p.n + n0 + c8;
     if (c8 + 8 <= cols && ((uintptr_t)dst & 15) == 0) {
       *reinterpret_cast<uint4*>(dst) = v;
     } else {
@@ -390,7 +412,7 @@ __device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* y
 
 // Wavefront W's whole K loop and epilogue (a template, so that the fifth
 // tile's operand choice is static and every accumulator stays in place).
-template <int W>
+template <int W, bool G>
 __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds& L, int lane, int64_t m0,
                                         int64_t n0, int nsteps) {
   f32x16_t acc[4][2], acc5[4];
@@ -488,9 +510,15 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   *reinterpret_cast<uint2*>(yt + (32 * W + l32) * kPdBN + 264 + 4 * h) =
       make_uint2(pd_bf16x2(t5b.x * ts, t5b.y * ts), pd_bf16x2(t5b.z * ts, t5b.w * ts));
   __syncthreads();
-  pd_store_tile(p, yt, m0, n0, W * 64 + lane);
+  pd_store_tile<G>(p, yt, m0, n0, W * 64 + lane, L.rowmap);
 }
 
+// G: the grouped form over an expert stack.  Workgroup tile mt of the launch
+// is tile mt of the sorted pair list: expert e with tile_off[e] <= mt <
+// tile_off[e + 1], its rows 128 (mt - tile_off[e]) .. of that expert's pairs.
+// Activation row of a pair = pair / topk, output row = pair; weights = matrix
+// e.  Tiles past the list's end exit at once.
+template <bool G>
 __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   __shared__ PdLds L;
 
@@ -503,17 +531,43 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   int id = (int)blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   const int nt = id / p.m_tiles, mt = id % p.m_tiles;
-  const int64_t m0 = (int64_t)mt * kPdBM, n0 = (int64_t)nt * kPdBN;
+  int64_t m0 = (int64_t)mt * kPdBM;
+  const int64_t n0 = (int64_t)nt * kPdBN;
   const int nsteps = (int)(p.k / kPdBK);  // a multiple of 4
   const int64_t kh = p.k >> 1, ks = p.k >> 4;
 
-  // Per-lane offsets; rows past m or n repeat the last valid row (never stored).
   PdSrc src;
+  if constexpr (G) {
+    const PdGroups gr = pd_groups(p);
+    if (mt >= gr.tile_off[p.experts]) return;  // uniform per workgroup
+    int lo = 0, hi = (int)p.experts;            // tile_off[lo] <= mt < tile_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (gr.tile_off[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int64_t base = gr.pair_off[lo] + (int64_t)(mt - gr.tile_off[lo]) * kPdBM;
+    const int64_t rows = (int64_t)gr.pair_off[lo + 1] - base < kPdBM ? (int64_t)gr.pair_off[lo + 1] - base : kPdBM;
+    if (tid < kPdBM) L.rowmap[tid] = gr.perm[base + (tid < rows ? tid : rows - 1)];  // read at the end
+    // Per-lane offsets from x itself; rows past the tile's end repeat its last row.
 #pragma unroll
-  for (int i = 0; i < kPdLX; ++i) {
-    const int q = w + 4 * i, r = 8 * q + (lane >> 3);
-    const int64_t gm = m0 + r < p.m ? r : p.m - 1 - m0;
-    src.x[i] = (uint32_t)(gm * p.k * 2 + 16 * ((lane & 7) ^ (r & 7)));
+    for (int i = 0; i < kPdLX; ++i) {
+      const int q = w + 4 * i, r = 8 * q + (lane >> 3);
+      const int64_t tok = gr.perm[base + (r < rows ? r : rows - 1)] / p.topk;
+      src.x[i] = (uint32_t)(tok * p.k * 2 + 16 * ((lane & 7) ^ (r & 7)));
+    }
+    p.m = rows;
+    p.packed += (int64_t)lo * p.w_stride;
+    p.scales += (int64_t)lo * (p.w_stride >> 3);
+    p.tscale += lo;
+    m0 = 0;
+  } else {
+    // Per-lane offsets; rows past m or n repeat the last valid row (never stored).
+#pragma unroll
+    for (int i = 0; i < kPdLX; ++i) {
+      const int q = w + 4 * i, r = 8 * q + (lane >> 3);
+      const int64_t gm = m0 + r < p.m ? r : p.m - 1 - m0;
+      src.x[i] = (uint32_t)(gm * p.k * 2 + 16 * ((lane & 7) ^ (r & 7)));
+    }
   }
   src.wscale = 0;
 #pragma unroll
@@ -526,10 +580,10 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   }
 
   switch (w) {
-    case 0: pd_body<0>(p, src, L, lane, m0, n0, nsteps); break;
-    case 1: pd_body<1>(p, src, L, lane, m0, n0, nsteps); break;
-    case 2: pd_body<2>(p, src, L, lane, m0, n0, nsteps); break;
-    default: pd_body<3>(p, src, L, lane, m0, n0, nsteps); break;
+    case 0: pd_body<0, G>(p, src, L, lane, m0, n0, nsteps); break;
+    case 1: pd_body<1, G>(p, src, L, lane, m0, n0, nsteps); break;
+    case 2: pd_body<2, G>(p, src, L, lane, m0, n0, nsteps); break;
+    default: pd_body<3, G>(p, src, L, lane, m0, n0, nsteps); break;
   }
 }
 
@@ -549,9 +603,31 @@ void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, cons
   for (int64_t t0 = 0; t0 < m_tiles; t0 += max_m_tiles) {
     const int64_t mt = m_tiles - t0 < max_m_tiles ? m_tiles - t0 : max_m_tiles;
     const int64_t mm = (m - t0 * kPdBM) < mt * kPdBM ? (m - t0 * kPdBM) : mt * kPdBM;
-    const PdArgs a{x + t0 * kPdBM * k, mm, n, k, packed, scales, tscale, y + t0 * kPdBM * n, (int)n_tiles, (int)mt};
-    prefill_dma_kernel<<<dim3((unsigned)(n_tiles * mt)), 256, 0, s>>>(a);
+    const PdArgs a{x + t0 * kPdBM * k, mm, n, k, packed, scales, tscale, y + t0 * kPdBM * n, (int)n_tiles, (int)mt,
+                   nullptr, 0, 0, 0};
+    prefill_dma_kernel<false><<<dim3((unsigned)(n_tiles * mt)), 256, 0, s>>>(a);
   }
+}
+
+int64_t prefill_grouped_tile_bound(int64_t pairs, int64_t experts) { return (pairs + kPdBM - 1) / kPdBM + experts; }
+
+// Activation offsets are 32-bit byte offsets from x; pair indices, tile
+// counts and the workgroup id are int32.
+bool prefill_grouped_supported(int64_t t_count, int64_t topk, int64_t experts, int64_t n, int64_t k) {
+  if (t_count <= 0 || topk <= 0 || experts <= 0 || n <= 0 || k <= 0 || k % kPdGroupK != 0) return false;
+  if (t_count > ((int64_t)1 << 31) / k || topk > ((int64_t)1 << 30) / t_count || experts > ((int64_t)1 << 28))
+    return false;
+  const int64_t n_tiles = (n + kPdBN - 1) / kPdBN;
+  return n_tiles <= ((int64_t)1 << 31) / (prefill_grouped_tile_bound(t_count * topk, experts) + 1);
+}
+
+void launch_prefill_grouped(const uint16_t* x, int64_t topk, const int32_t* groups, int64_t pairs, int64_t experts,
+                            int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                            uint16_t* y, hipStream_t s) {
+  const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = prefill_grouped_tile_bound(pairs, experts);
+  const PdArgs a{x, 0, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, groups, topk, experts,
+                 n * (k >> 1)};
+  prefill_dma_kernel<true><<<dim3((unsigned)(n_tiles * m_tiles)), 256, 0, s>>>(a);
 }
 
 }  // namespace nvfp4

@@ -29,6 +29,7 @@ SEED_W = 0          # weights
 SEED_X = 1          # activations
 SEED_OUTLIER = 2    # which input columns are outliers (decode workload)
 SEED_UP = 3         # the "up" half of the merged gate/up weight
+SEED_ROUTE = 4      # expert choices of the routed workloads
 
 W_STD = 0.02
 X_STD = 1.0
@@ -149,7 +150,7 @@ def workload_names() -> List[str]:
 
 @dataclasses.dataclass(frozen=True)
 class MoeWorkload:
-    """Synthetic routed decode over an expert stack: t tokens, each routed to topk of `experts` matrices [n, k].
+    """Synthetic routed linear over an expert stack: t tokens, each routed to topk of `experts` matrices [n, k].
 
     The stack is built from one seeded ~N(0, 0.02) matrix, expert i scaled by (1 + i / 64) (so every expert
     has its own tensor scale); route r of a rotation of `experts / topk` routes sends the token to experts
@@ -171,6 +172,22 @@ class MoeWorkload:
         r = np.arange(self.experts // self.topk, dtype=np.int32)[:, None, None] * self.topk
         return (r + np.arange(self.topk, dtype=np.int32)[None, None, :]).repeat(self.t, axis=1).astype(np.int32)
 
+    def expert_scale(self, i: int) -> float:
+        """Expert i's weight = BF16(base * (1 + i / 64)) (the factor is exact in FP32)."""
+        return 1.0 + i / 64.0
+
+    def expert_weight(self, i: int, base: np.ndarray = None) -> np.ndarray:
+        """BF16 bits of expert i: the FP32 product base * expert_scale(i), rounded to nearest even."""
+        base = self.base_weight() if base is None else base
+        return bf16_bits_from_f32(f32_from_bf16_bits(base) * np.float32(self.expert_scale(i)))
+
+    def random_routes(self, seed: int = SEED_ROUTE) -> np.ndarray:
+        """int32 [t, topk]: each token's topk distinct experts, uniform at random (a balanced router)."""
+        rng = np.random.default_rng(seed)
+        return np.argsort(rng.random((self.t, self.experts)), axis=1)[:, :self.topk].astype(np.int32)
+
 
 MOE_DECODE = MoeWorkload("moe_decode", "routed MoE decode: 128 experts of N=2048, K=4096, top-8, one token",
                          experts=128, n=2048, k=4096, topk=8)
+MOE_PREFILL = MoeWorkload("moe_prefill", "grouped MoE prefill: 2048 tokens, each routed to 8 of 128 experts "
+                          "of N=2048, K=4096", experts=128, n=2048, k=4096, topk=8, t=2048)

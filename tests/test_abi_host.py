@@ -121,3 +121,30 @@ def test_dequant_validation(L):
     assert dq(A, C, D, 4, 8, E, None) == B.ERR_SHAPE
     assert dq(A, C, D, 4, 64, E + 2, None) == B.ERR_ALIGN
     assert dq(A, C, D, 4, 64, A, None) == B.ERR_ALIAS
+
+
+def test_grouped_workspace_bytes(L):
+    wb = L.nvfp4_linear_grouped_workspace_bytes
+    # int32 counts[e], cursors[e], pair_off[e + 1], tile_off[e + 1], perm[t * topk], rounded up to 16 bytes
+    assert wb(10, 8, 128) == 2384           # (4 * 128 + 2 + 80) * 4 = 2376 -> 2384
+    assert wb(0, 1, 1) == 32
+    assert wb(4096, 8, 128) == 133136        # (4 * 128 + 2 + 32768) * 4 = 133128 -> 133136
+    assert wb(-1, 1, 1) == -1 and wb(1, 0, 1) == -1 and wb(1, 1, 0) == -1
+    assert wb(2 ** 62, 4, 1) == -1           # t * topk overflows
+
+
+def test_grouped_validation(L):
+    g = L.nvfp4_linear_grouped
+    R, W = 0x60000000, 0x70000000
+    need = L.nvfp4_linear_grouped_workspace_bytes(2, 2, 2)
+    args = lambda x=A, t=2, topk=2, e=2, y=E, ws=W, wsb=need: (x, t, topk, R, e, 64, 256, Bp, C, D, y, ws,  # noqa: E731
+                                                                 wsb, None)
+    assert g(*args(ws=None)) == B.ERR_NULL
+    assert g(*args(wsb=need - 16)) == B.ERR_SHAPE
+    assert g(*args(topk=0)) == B.ERR_SHAPE and g(*args(e=0)) == B.ERR_SHAPE
+    assert g(*args(ws=W + 8)) == B.ERR_ALIGN
+    assert g(*args(ws=A + 64)) == B.ERR_ALIAS      # workspace overlaps x
+    assert g(*args(ws=E + 16)) == B.ERR_ALIAS      # workspace overlaps y
+    assert g(*args(ws=R)) == B.ERR_ALIAS           # workspace overlaps route
+    assert g(*args(y=A + 32)) == B.ERR_ALIAS       # y overlaps x
+    assert g(*args(x=None, t=0, y=None, ws=None, wsb=0)) == B.OK    # t = 0 no-op

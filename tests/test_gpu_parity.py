@@ -414,3 +414,126 @@ def test_linear_routed_edges(nv):
     assert nv.lib().nvfp4_linear_routed(*args(2, 0, y.data_ptr())) == B.ERR_SHAPE
     assert nv.lib().nvfp4_linear_routed(*args(2, 2, x.data_ptr())) == B.ERR_ALIAS   # y overlaps x
     assert nv.lib().nvfp4_linear_routed(*args(2, 2, y.data_ptr() + 2)) == B.ERR_ALIGN
+
+
+# ---------------------------------------------------------------------------
+# Grouped (prefill) form over an expert stack: pairs sorted by expert on the
+# device, 128-row tiles per expert.  Same oracle as the routed decode.
+# ---------------------------------------------------------------------------
+def _routing(kind, t, topk, e, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "uniform":
+        r = rng.integers(0, e, size=(t, topk))
+    elif kind == "skew":        # geometric: expert 0 takes about half of the pairs, the last ones few or none
+        r = np.minimum(rng.geometric(0.5, size=(t, topk)) - 1, e - 1)
+    else:                       # "one": every pair on expert 1, the other experts empty
+        r = np.ones((t, topk), dtype=np.int64)
+    r = r.astype(np.int32)
+    if t * topk >= 6:
+        r.flat[2] = -1
+        r.flat[3] = e
+        r.flat[5] = 2 ** 31 - 1
+    return r
+
+
+GROUPED_CASES = [
+    (300, 4, 6, 300, 1024, "uniform"),   # ~200 pairs per expert: 2 tiles each, the second ragged; n = 272 + 28
+    (200, 8, 16, 545, 256, "skew"),      # one expert with 6+ tiles, experts with a few rows or none
+    (130, 2, 3, 64, 512, "one"),         # 257 pairs on one expert (3 tiles, the last 1 row); 2 empty experts
+    (1, 1, 1, 16, 256, "uniform"),       # one pair
+    (40, 3, 5, 100, 1040, "uniform"),    # k % 256 != 0: the routed GEMV runs instead
+]
+
+
+@pytest.mark.parametrize("t,topk,e,n,k,kind", GROUPED_CASES)
+def test_linear_grouped(nv, t, topk, e, n, k, kind):
+    w = _expert_stack(e, n, k, 1400 + k)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    rq = O.quantize_experts(w)
+    assert np.array_equal(u8_host(packed), rq[0]) and np.array_equal(u8_host(scales), rq[1])
+    x = WL.normal_bf16((t, k), 1.0, 1500 + t)
+    route = _routing(kind, t, topk, e, 1600 + e)
+    xd, rd = to_dev_bf16(x), torch.from_numpy(route).cuda()
+    y = nv.linear_grouped(xd, rd, packed, scales, tscale)
+    y_ref, bound = O.linear_routed_ref(x, route, *rq)
+    yb = bf16_host(y)
+    check_linear(yb.reshape(t * topk, n), y_ref.reshape(t * topk, n), bound.reshape(t * topk, n),
+                 f"grouped t={t} topk={topk} e={e} n={n} k={k} {kind}")
+    bad = (route < 0) | (route >= e)
+    assert np.all(yb[bad] == 0), "out-of-range expert ids must give zero rows"
+    # the sort order inside an expert varies between calls; the output does not
+    assert torch.equal(nv.linear_grouped(xd, rd, packed, scales, tscale), y)
+    if k % 256 == 0:
+        # each row is the dense prefill GEMM's row for that token and expert, bit for bit
+        for ei in np.unique(route[~bad])[:3]:
+            ts, js = np.nonzero(route == ei)
+            yd = nv.linear(to_dev_bf16(x[ts]), packed[ei], scales[ei], tscale[ei:ei + 1].clone(), kernel="prefill")
+            assert np.array_equal(bf16_host(yd), yb[ts, js]), f"expert {ei}"
+    else:
+        assert torch.equal(nv.linear_routed(xd, rd, packed, scales, tscale), y)
+
+
+def test_linear_grouped_workspace_reuse(nv):
+    """One workspace, two calls in a row (the second with fewer tokens and other ids): the counters restart."""
+    e, n, k = 4, 80, 512
+    w = _expert_stack(e, n, k, 1700)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    rq = O.quantize_experts(w)
+    ws = torch.full((nv.linear_grouped_workspace_bytes(300, 3, e),), 0xAB, dtype=torch.uint8, device="cuda")
+    for (t, topk, seed) in [(300, 3, 1701), (70, 2, 1702)]:
+        x = WL.normal_bf16((t, k), 1.0, seed)
+        route = _routing("uniform", t, topk, e, seed)
+        y = nv.linear_grouped(to_dev_bf16(x), torch.from_numpy(route).cuda(), packed, scales, tscale, workspace=ws)
+        y_ref, bound = O.linear_routed_ref(x, route, *rq)
+        check_linear(bf16_host(y).reshape(t * topk, n), y_ref.reshape(t * topk, n), bound.reshape(t * topk, n),
+                     f"grouped workspace reuse t={t} topk={topk}")
+
+
+def test_linear_grouped_edges(nv):
+    from nvfp4_weight_only_amd import binding as B
+    w = _expert_stack(2, 16, 512, 1800)
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    # t = 0 is a no-op
+    y = nv.linear_grouped(torch.empty((0, 512), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty((0, 3), dtype=torch.int32, device="cuda"), packed, scales, tscale)
+    assert y.shape == (0, 3, 16)
+    # every id out of range: all zeros (no tile is scheduled)
+    x = to_dev_bf16(WL.normal_bf16((2, 512), 1.0, 1801))
+    bad = torch.tensor([[-5, 2], [7, 2 ** 31 - 1]], dtype=torch.int32, device="cuda")
+    y = torch.full((2, 2, 16), 1.0, dtype=torch.bfloat16, device="cuda")
+    assert torch.count_nonzero(nv.linear_grouped(x, bad, packed, scales, tscale, out=y)) == 0
+    # argument errors are reported before anything is launched
+    ws = torch.empty(nv.linear_grouped_workspace_bytes(2, 2, 2), dtype=torch.uint8, device="cuda")
+    args = lambda yp, wp, wb: (x.data_ptr(), 2, 2, bad.data_ptr(), 2, 16, 512, packed.data_ptr(),  # noqa: E731
+                               scales.data_ptr(), tscale.data_ptr(), yp, wp, wb, 0)
+    L = nv.lib()
+    assert L.nvfp4_linear_grouped(*args(y.data_ptr(), None, ws.numel())) == B.ERR_NULL
+    assert L.nvfp4_linear_grouped(*args(y.data_ptr(), ws.data_ptr(), ws.numel() - 16)) == B.ERR_SHAPE
+    assert L.nvfp4_linear_grouped(*args(y.data_ptr(), ws.data_ptr() + 8, ws.numel())) == B.ERR_ALIGN
+    assert L.nvfp4_linear_grouped(*args(y.data_ptr(), y.data_ptr(), ws.numel())) == B.ERR_ALIAS
+    assert L.nvfp4_linear_grouped(*args(x.data_ptr(), ws.data_ptr(), ws.numel())) == B.ERR_ALIAS
+
+
+def test_linear_grouped_full_size_sampled(nv):
+    """2048 tokens routed top-8 over 128 experts of 2048 x 4096 (the grouped prefill workload, launched as
+    timed): sampled (pair, column) outputs against the oracle on those weight rows."""
+    mw = WL.MOE_PREFILL
+    base_bits = mw.base_weight()
+    base = to_dev_bf16(base_bits)
+    stack = torch.stack([(base.float() * mw.expert_scale(i)).to(torch.bfloat16) for i in range(mw.experts)])
+    del base
+    packed, scales, tscale = nv.quantize_experts(stack)
+    route = mw.random_routes()
+    x = WL.activations(mw.t, mw.k)
+    y = bf16_host(nv.linear_grouped(to_dev_bf16(x), torch.from_numpy(route).cuda(), packed, scales, tscale))
+    rng = np.random.default_rng(1900)
+    cols = np.sort(rng.choice(mw.n, 24, replace=False))
+    for ei in [0, 77, 127]:
+        wb = mw.expert_weight(ei, base_bits)
+        assert np.array_equal(bf16_host(stack[ei]), wb), "device-built expert differs from its definition"
+        amax = O.tensor_amax(wb)
+        q = O.quantize(wb[cols], amax=amax)
+        ts, js = np.nonzero(route == ei)
+        y_ref, bound = O.linear_ref(x[ts], *q)
+        check_linear(y[ts, js][:, cols], y_ref, bound, f"grouped full size, expert {ei} ({ts.size} pairs)")
+    del stack
