@@ -82,6 +82,16 @@ def graph_of(calls):
     return g
 
 
+def warm_graph(graph, seconds=0.1):
+    """Replay until `seconds` of wall time have passed: the clocks settle at their loaded state first."""
+    t_end = time.perf_counter() + seconds
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            return
+
+
 def time_graph_replays(graph, replays, launches_per_replay):
     """Average duration per launch (ms) over `replays` back-to-back graph replays, by HIP events."""
     torch.cuda.synchronize()
@@ -132,7 +142,7 @@ def bench_linear_row(wname, m, reps, kernel="auto"):
     x = dev_bf16(wl.activations(m))
     y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
     g = graph_of(linear_calls(x, rot, y, kernel))
-    time_graph_replays(g, 2, len(rot))
+    warm_graph(g)
     ms = time_graph_replays(g, reps, len(rot))
     nbytes = linear_bytes(m, wl.n, wl.k)
     flops = 2.0 * m * wl.n * wl.k
@@ -155,7 +165,7 @@ def bench_quant_rows(reps):
     ws = [w.clone() for _ in range(c)]
     outs = [nv.quantize(wi) for wi in ws]
     g = graph_of([(lambda wi=wi: nv.quantize(wi)) for wi in ws])
-    time_graph_replays(g, 1, c)
+    warm_graph(g)
     ms_q = time_graph_replays(g, reps, c)
     dq = [torch.empty((n, k), dtype=torch.bfloat16, device="cuda") for _ in range(c)]
     lib = nv.lib()
@@ -164,7 +174,7 @@ def bench_quant_rows(reps):
         return lambda: lib.nvfp4_dequant(o[0].data_ptr(), o[1].data_ptr(), o[2].data_ptr(), n, k, d.data_ptr(),
                                          torch.cuda.current_stream().cuda_stream)
     g2 = graph_of([dq_call(o, d) for o, d in zip(outs, dq)])
-    time_graph_replays(g2, 1, c)
+    warm_graph(g2)
     ms_d = time_graph_replays(g2, reps, c)
     e = n * k
     q_bytes = 2 * e + 2 * e + e // 2 + e // 16 + 4     # amax read, quantize read, packed + scales write
@@ -204,7 +214,7 @@ def bench_moe_rows(reps):
     y = torch.empty((mw.t, mw.topk, mw.n), dtype=torch.bfloat16, device="cuda")
     calls = [(lambda r=r: nv.linear_routed(x, r, packed, scales, tscale, out=y)) for r in routes]
     g = graph_of(calls)
-    time_graph_replays(g, 2, len(calls))
+    warm_graph(g)
     ms = time_graph_replays(g, reps, len(calls))
     nbytes = mw.t * mw.topk * (w_bytes + 2 * mw.n) + 2 * mw.t * mw.k + 4 * mw.t * mw.topk
     flops = 2.0 * mw.t * mw.topk * mw.n * mw.k
@@ -221,7 +231,7 @@ def bench_moe_rows(reps):
     y = torch.empty((pw.t, pw.topk, pw.n), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(nv.linear_grouped_workspace_bytes(pw.t, pw.topk, pw.experts), dtype=torch.uint8, device="cuda")
     g = graph_of([lambda: nv.linear_grouped(x, route, packed, scales, tscale, out=y, workspace=ws)])
-    time_graph_replays(g, 2, 1)
+    warm_graph(g)
     ms = time_graph_replays(g, max(reps // 3, 3), 1)
     pairs = pw.t * pw.topk
     flops = 2.0 * pairs * pw.n * pw.k

@@ -209,11 +209,12 @@ nvfp4_status nvfp4_linear_routed(const uint16_t* x, int64_t t_count, int64_t top
  * since a different kernel sums in a different order; an expert id outside
  * [0, e) gives a row of zeros), plus a caller-owned device workspace of at
  * least nvfp4_linear_grouped_workspace_bytes(t_count, topk, e) bytes,
- * 16-byte aligned, overlapping no argument.  On the stream, the (t, j) pairs
- * are counted and sorted by expert into the workspace, then one GEMM launch
- * multiplies each expert's matrix with its pairs' activation rows in 128-row
- * tiles, so an expert's weights are read once per 272 output columns however
- * many tokens chose it (the routed GEMV reads them once per pair).  The order
+ * 16-byte aligned, overlapping no argument.  On the stream, one workgroup
+ * counts and sorts the (t, j) pairs by expert into the workspace, then one
+ * GEMM launch multiplies each expert's matrix with its pairs' activation rows
+ * in 128-row tiles (and zeroes the rows of out-of-range ids), so an expert's
+ * weights are read once per 272 output columns however many tokens chose it
+ * (the routed GEMV reads them once per pair).  The order
  * of pairs within an expert is not deterministic; the output is, bit for bit.
  * Where the GEMM's limits are not met (k not a multiple of 256, t_count * k
  * above 2^31, or 32-bit pair and tile counts exceeded) the call runs

@@ -52,10 +52,11 @@ struct PdArgs {
   int64_t topk, experts, w_stride;  // w_stride: packed bytes per expert
 };
 
-// Layout of the grouping workspace (int32): counts[E], cursors[E],
-// pair_off[E + 1] (first sorted position of each expert's pairs),
-// tile_off[E + 1] (first 128-row tile of each expert), perm[pairs] (pair
-// indices, grouped by expert).
+// Layout of the grouping workspace (int32): cnt[E] (the sort's counters),
+// pair_off[E + 1] (first sorted position of each expert's pairs; pair_off[E]
+// = V, the pairs with a valid expert id), tile_off[E + 1] (first 128-row tile
+// of each expert), perm[pairs] (pair indices grouped by expert, then the V..
+// pairs - 1 invalid ones).
 struct PdGroups {
   const int32_t* pair_off;
   const int32_t* tile_off;
@@ -64,7 +65,7 @@ struct PdGroups {
 
 __device__ __forceinline__ PdGroups pd_groups(const PdArgs& p) {
   const int32_t* g = p.groups;
-  return PdGroups{g + 2 * p.experts, g + 3 * p.experts + 1, g + 4 * p.experts + 2};
+  return PdGroups{g + p.experts, g + 2 * p.experts + 1, g + 3 * p.experts + 2};
 }
 
 // LDS (16-byte slots):
@@ -517,7 +518,12 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
 // is tile mt of the sorted pair list: expert e with tile_off[e] <= mt <
 // tile_off[e + 1], its rows 128 (mt - tile_off[e]) .. of that expert's pairs.
 // Activation row of a pair = pair / topk, output row = pair; weights = matrix
-// e.  Tiles past the list's end exit at once.
+// e.  Workgroups past the list's end zero the output rows of the pairs whose
+// expert id is out of range (at least one m tile of them exists whenever such
+// pairs do: the launch has ceil(pairs / 128) + E m tiles and the valid pairs
+// use at most (V - nonempty experts) / 128 + nonempty experts of them), then
+// exit.  In the grouped form p.m holds the number of pairs until the tile's
+// row count replaces it.
 template <bool G>
 __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   __shared__ PdLds L;
@@ -539,7 +545,15 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   PdSrc src;
   if constexpr (G) {
     const PdGroups gr = pd_groups(p);
-    if (mt >= gr.tile_off[p.experts]) return;  // uniform per workgroup
+    const int used = gr.tile_off[p.experts];
+    if (mt >= used) {  // uniform per workgroup
+      const int64_t cols = p.n - n0 < kPdBN ? p.n - n0 : kPdBN;
+      for (int64_t i = gr.pair_off[p.experts] + (mt - used); i < p.m; i += p.m_tiles - used) {
+        uint16_t* dst = p.y + (int64_t)gr.perm[i] * p.n + n0;
+        for (int c = tid; c < cols; c += 256) dst[c] = 0;
+      }
+      return;
+    }
     int lo = 0, hi = (int)p.experts;            // tile_off[lo] <= mt < tile_off[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -625,7 +639,7 @@ void launch_prefill_grouped(const uint16_t* x, int64_t topk, const int32_t* grou
                             int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
                             uint16_t* y, hipStream_t s) {
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = prefill_grouped_tile_bound(pairs, experts);
-  const PdArgs a{x, 0, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, groups, topk, experts,
+  const PdArgs a{x, pairs, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, groups, topk, experts,
                  n * (k >> 1)};
   prefill_dma_kernel<true><<<dim3((unsigned)(n_tiles * m_tiles)), 256, 0, s>>>(a);
 }

@@ -125,10 +125,10 @@ def test_dequant_validation(L):
 
 def test_grouped_workspace_bytes(L):
     wb = L.nvfp4_linear_grouped_workspace_bytes
-    # int32 counts[e], cursors[e], pair_off[e + 1], tile_off[e + 1], perm[t * topk], rounded up to 16 bytes
-    assert wb(10, 8, 128) == 2384           # (4 * 128 + 2 + 80) * 4 = 2376 -> 2384
-    assert wb(0, 1, 1) == 32
-    assert wb(4096, 8, 128) == 133136        # (4 * 128 + 2 + 32768) * 4 = 133128 -> 133136
+    # int32 cnt[e], pair_off[e + 1], tile_off[e + 1], perm[t * topk], rounded up to 16 bytes
+    assert wb(10, 8, 128) == 1872           # (3 * 128 + 2 + 80) * 4 = 1864 -> 1872
+    assert wb(0, 1, 1) == 32                # (3 + 2) * 4 = 20 -> 32
+    assert wb(4096, 8, 128) == 132624        # (3 * 128 + 2 + 32768) * 4 = 132616 -> 132624
     assert wb(-1, 1, 1) == -1 and wb(1, 0, 1) == -1 and wb(1, 1, 0) == -1
     assert wb(2 ** 62, 4, 1) == -1           # t * topk overflows
 

@@ -442,6 +442,7 @@ GROUPED_CASES = [
     (130, 2, 3, 64, 512, "one"),         # 257 pairs on one expert (3 tiles, the last 1 row); 2 empty experts
     (1, 1, 1, 16, 256, "uniform"),       # one pair
     (40, 3, 5, 100, 1040, "uniform"),    # k % 256 != 0: the routed GEMV runs instead
+    (4200, 8, 4, 16, 256, "uniform"),    # 33600 pairs: more than the sort keeps in LDS
 ]
 
 
@@ -537,3 +538,31 @@ def test_linear_grouped_full_size_sampled(nv):
         y_ref, bound = O.linear_ref(x[ts], *q)
         check_linear(y[ts, js][:, cols], y_ref, bound, f"grouped full size, expert {ei} ({ts.size} pairs)")
     del stack
+
+
+@pytest.mark.parametrize("e", [2000, 9000])
+def test_linear_grouped_many_experts(nv, e):
+    """2000 experts: LDS counters, permutation stored straight to the workspace; 9000: more than the
+    sort's LDS counters hold, so its counters live in the workspace too."""
+    n, k, t, topk = 32, 256, 64, 4
+    rng = np.random.default_rng(2000)
+    w = WL.bf16_bits_from_f32((rng.standard_normal((e, n, k)) * 0.02 * (1.0 + rng.random((e, 1, 1)))).astype(np.float32))
+    packed, scales, tscale = nv.quantize_experts(to_dev_bf16(w))
+    x = WL.normal_bf16((t, k), 1.0, 2001)
+    route = rng.integers(0, e, size=(t, topk)).astype(np.int32)
+    route[0, :] = 17                   # several pairs on one expert
+    route.flat[5] = -3
+    route.flat[6] = e
+    y = bf16_host(nv.linear_grouped(to_dev_bf16(x), torch.from_numpy(route).cuda(), packed, scales, tscale))
+    ph, sh, th = u8_host(packed), u8_host(scales), tscale.cpu().numpy()
+    for ti in range(t):
+        for j in range(topk):
+            ei = int(route[ti, j])
+            if not 0 <= ei < e:
+                assert np.all(y[ti, j] == 0)
+                continue
+            q = O.quantize(w[ei])
+            assert np.array_equal(ph[ei], q[0]) and np.array_equal(sh[ei], q[1]) and th[ei] == q[2]
+            y_ref, bound = O.linear_ref(x[ti:ti + 1], *q)
+            bad = O.linear_violations(WL.f32_from_bf16_bits(y[ti, j][None]).astype(np.float64), y_ref, bound)
+            assert not bad.any(), f"pair ({ti}, {j}) on expert {ei}: {int(bad.sum())} outputs outside 2e-3*B"
