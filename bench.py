@@ -280,10 +280,26 @@ def profile_run(what, launches):
     prefill / prefill2048: nvfp4_linear on the prefill workload (N=17408, K=5120) at M=512 / 2048,
             rotated weight copies;
     copy:   a plain 256 MiB device-to-device copy (torch's copy kernel), the calibration for the
-            FETCH_SIZE / WRITE_SIZE counters (each launch moves exactly 256 MiB each way).
+            FETCH_SIZE / WRITE_SIZE counters (each launch moves exactly 256 MiB each way);
+    moe_prefill: nvfp4_linear_grouped on the grouped MoE prefill workload (2048 tokens, top-8 of 128
+            experts of N=2048, K=4096), one call per launch (the sort kernel and the grouped GEMM).
     """
     torch.cuda.set_device(0)
-    if what == "copy":
+    if what == "moe_prefill":
+        pw = WL.MOE_PREFILL
+        base = dev_bf16(pw.base_weight())
+        stack = torch.stack([(base.float() * pw.expert_scale(i)).to(torch.bfloat16) for i in range(pw.experts)])
+        packed, scales, tscale = nv.quantize_experts(stack)
+        del stack, base
+        route = torch.from_numpy(pw.random_routes()).cuda()
+        x = dev_bf16(WL.activations(pw.t, pw.k))
+        y = torch.empty((pw.t, pw.topk, pw.n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(nv.linear_grouped_workspace_bytes(pw.t, pw.topk, pw.experts), dtype=torch.uint8,
+                         device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            nv.linear_grouped(x, route, packed, scales, tscale, out=y, workspace=ws)
+    elif what == "copy":
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(launches):
@@ -311,7 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()
