@@ -13,6 +13,7 @@ The mutation tests at the end plant plausible mistakes in the oracle and
 check that some pin fails.
 """
 import itertools
+import math
 import os
 from fractions import Fraction
 
@@ -516,3 +517,184 @@ def test_linear_routed_brute_force():
                 assert abs(Fraction(y[t, j, n]) - exact) <= tol, (t, j, n)
                 assert abs(Fraction(bound[t, j, n]) - babs) <= tol, (t, j, n)
     assert np.array_equal(y[1, 0], y[1, 1])  # the same expert twice
+
+
+# ---------------------------------------------------------------------------
+# FP4 KV-cache gather (oracle/kv_oracle.py).
+# ---------------------------------------------------------------------------
+from oracle import kv_oracle as KV  # noqa: E402
+
+
+def test_ue8m0_table_matches_torch():
+    """UE8M0 (OCP MX scale byte) against torch's float8_e8m0fnu cast, all 256 codes."""
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(KV.UE8M0_TABLE[255]) and np.isnan(t[255])
+    assert np.array_equal(KV.UE8M0_TABLE[:255], t[:255])
+    assert KV.UE8M0_TABLE[127] == 1.0 and KV.UE8M0_TABLE[0] == 2.0 ** -127 and KV.UE8M0_TABLE[254] == 2.0 ** 127
+
+
+def _e2m1_signed(code, factor):
+    """E2M1 nibble times a non-negative Fraction, as a float64 with the nibble's sign (code 0x8 is -0, so its
+    products are -0): the bit layout written out, sign, exponent bias 1, one mantissa bit."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return math.copysign(float(mag * factor), -1.0 if s else 1.0)
+
+
+def test_kv_decode_nvfp4_against_exact_products():
+    """R15 (NVFP4): exact rational E2M1 * E4M3 * tscale, rounded once to float32 (exact in float64 first:
+    at most 6 + 24 significant bits), then to FP16 / BF16 by torch's casts."""
+    rng = np.random.default_rng(31)
+    codes = rng.integers(0, 256, size=(6, 2, 16), dtype=np.uint8)       # 6 rows x 2 heads x 32 elements
+    scales = rng.integers(0, 0x7F, size=(6, 2, 2), dtype=np.uint8)      # finite E4M3 codes
+    scales[0, 0, 0], scales[1, 1, 1] = 0x7E, 0x01                        # 448 and the smallest subnormal
+    ts = np.float32(0.0123)
+    e4m3 = torch.from_numpy(scales.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    exact = np.empty((6, 2, 32), dtype=np.float64)                       # exact: <= 30 significant bits
+    for idx in np.ndindex(6, 2):
+        for d in range(32):
+            byte = int(codes[idx][d // 2])
+            nib = byte & 0xF if d % 2 == 0 else byte >> 4
+            exact[idx + (d,)] = _e2m1_signed(nib, Fraction(float(e4m3[idx][d // 16])) * Fraction(float(ts)))
+    f32 = torch.from_numpy(exact).to(torch.float32)
+    for out, dt in ((KV.F16, torch.float16), (KV.BF16, torch.bfloat16)):
+        want = f32.to(dt).view(torch.int16).numpy().view(np.uint16)
+        got = KV.decode_rows(KV.NVFP4, out, codes, scales, ts)
+        assert np.array_equal(got, want), out
+
+
+def test_kv_decode_mxfp4_against_exact_products():
+    """R15 (MXFP4): E2M1 * 2^(e - 127) exactly, one rounding to FP16 / BF16 (torch's casts from float64, exact
+    through float32 for two significant bits), including FP16 overflow and underflow scales."""
+    rng = np.random.default_rng(32)
+    codes = rng.integers(0, 256, size=(5, 3, 32), dtype=np.uint8)       # 5 rows x 3 heads x 64 elements
+    scales = rng.integers(90, 160, size=(5, 3, 2), dtype=np.uint8)
+    scales[0, 0, 0], scales[0, 0, 1], scales[1, 0, 0], scales[1, 0, 1] = 0, 254, 140, 141
+    for out, dt in ((KV.F16, torch.float16), (KV.BF16, torch.bfloat16)):
+        want = np.empty((5, 3, 64), dtype=np.uint16)
+        for idx in np.ndindex(5, 3):
+            vals = []
+            for d in range(64):
+                byte = int(codes[idx][d // 2])
+                nib = byte & 0xF if d % 2 == 0 else byte >> 4
+                vals.append(_e2m1_signed(nib, Fraction(2) ** (int(scales[idx][d // 32]) - 127)))
+            want[idx] = torch.tensor(vals, dtype=torch.float64).to(dt).view(torch.int16).numpy().view(np.uint16)
+        got = KV.decode_rows(KV.MXFP4, out, codes, scales)
+        assert np.array_equal(got, want), out
+    # closed forms: scale 127 is the E2M1 table itself; FP16 overflows past 65504 (6 * 2^14 at e = 141)
+    c = np.full((1, 16), 0x77, dtype=np.uint8)                             # 6.0 everywhere
+    assert np.all(KV.decode_values(KV.MXFP4, c, np.array([[127]], dtype=np.uint8)) == 6.0)
+    assert np.all(KV.decode_rows(KV.MXFP4, KV.F16, c, np.array([[140]], dtype=np.uint8)) == 0x7A00)   # 49152
+    assert np.all(KV.decode_rows(KV.MXFP4, KV.F16, c, np.array([[141]], dtype=np.uint8)) == 0x7C00)   # +inf
+
+
+def test_kv_gather_indexing_brute_force():
+    """R16 on pages whose values name their source: every element of page p, slot i is 2^(p * 4 + i - 17)
+    (MXFP4, codes 1.0, scale byte 110 + 4p + i), so each output row says which page and slot it came from."""
+    nb, bs, heads, hd = 6, 4, 2, 32
+    codes = np.full((nb, bs, heads, hd // 2), 0x22, dtype=np.uint8)      # E2M1 1.0 in both nibbles
+    scales = np.empty((nb, bs, heads, 1), dtype=np.uint8)
+    for p in range(nb):
+        for i in range(bs):
+            scales[p, i] = 110 + 4 * p + i
+    block_table = np.array([[3, 0, 4, 5], [1, 7, 2, 0], [5, 2, 5, 1], [2, 2, 2, 2], [4, 3, 3, 3]], dtype=np.int32)
+    seq_lens = np.array([10, 7, 40, 3, 5], dtype=np.int32)              # seq 2 asks for more than its 4 pages hold
+    dst_start = np.array([1, 12, 20, -2, 38], dtype=np.int32)           # seq 3 starts before row 0, seq 4 runs past 39
+    out_rows = 40
+    sentinel = np.uint16(0x1234)
+    init = np.full((out_rows, heads, hd), sentinel, dtype=np.uint16)
+    # Expected sources, written out: (row, page, slot), rows that become zero; every other row is untouched.
+    src = [(1 + i, 3, i) for i in range(4)] + [(5 + i, 0, i) for i in range(4)] + [(9, 4, 0), (10, 4, 1)]
+    src += [(12 + i, 1, i) for i in range(4)]
+    zero = [16, 17, 18]                                                  # seq 1, page id 7 (out of range)
+    src += [(20 + i, 5, i) for i in range(4)] + [(24 + i, 2, i) for i in range(4)]
+    src += [(28 + i, 5, i) for i in range(4)] + [(32 + i, 1, i) for i in range(4)]   # 16 tokens, no more
+    src += [(0, 2, 2)]                                                   # seq 3: tokens 0, 1 fall before row 0
+    src += [(38, 4, 0), (39, 4, 1)]                                      # seq 4: tokens 2..4 fall past row 39
+    got = KV.kv_gather_ref(KV.MXFP4, KV.F16, codes, scales, None, block_table, seq_lens, dst_start, init)
+    want = init.copy()
+    for (r, p, i) in src:
+        want[r] = np.float16(2.0 ** (4 * p + i - 17)).view(np.uint16)
+    for r in zero:
+        want[r] = 0
+    assert np.array_equal(got, want)
+    for r in (11, 19, 36, 37):                                           # gaps between sequences untouched
+        assert np.all(got[r] == sentinel)
+
+
+def _expect_kv_pin_failure(monkeypatch, target, replacement, pins):
+    monkeypatch.setattr(KV, target, replacement)
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            return
+    raise AssertionError(f"planted mistake in kv_oracle.{target} went unnoticed")
+
+
+KV_DECODE_PINS = [test_kv_decode_nvfp4_against_exact_products, test_kv_decode_mxfp4_against_exact_products]
+
+
+def test_mutation_kv_swapped_nibbles(monkeypatch):
+    def swapped(p):
+        c = KV.unpack_nibbles.__wrapped__(p) if hasattr(KV.unpack_nibbles, "__wrapped__") else O.unpack_nibbles(p)
+        out = c.copy()
+        out[:, 0::2], out[:, 1::2] = c[:, 1::2], c[:, 0::2]
+        return out
+    _expect_kv_pin_failure(monkeypatch, "unpack_nibbles", swapped, KV_DECODE_PINS)
+
+
+def test_mutation_kv_dropped_tensor_scale(monkeypatch):
+    orig = KV.decode_values
+    _expect_kv_pin_failure(monkeypatch, "decode_values",
+                           lambda fmt, c, s, t=None: orig(fmt, c, s, None if fmt == KV.MXFP4 else 1.0), KV_DECODE_PINS)
+
+
+def test_mutation_kv_mx_group_16(monkeypatch):
+    _expect_kv_pin_failure(monkeypatch, "GROUP", {KV.NVFP4: 16, KV.MXFP4: 16}, KV_DECODE_PINS)
+
+
+def test_mutation_kv_ue8m0_bias(monkeypatch):
+    _expect_kv_pin_failure(monkeypatch, "UE8M0_TABLE", KV.UE8M0_TABLE * 2.0,
+                           [test_ue8m0_table_matches_torch] + KV_DECODE_PINS)
+
+
+def test_mutation_kv_rounding_toward_zero(monkeypatch):
+    def rtz(values, out):
+        v = np.asarray(values, dtype=np.float64)
+        if out == KV.F16:
+            r = v.astype(np.float16)
+            over = np.abs(r.astype(np.float64)) > np.abs(v)
+            r[over] = np.nextafter(r[over], np.float16(0))
+            return r.view(np.uint16)
+        b = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return b
+    _expect_kv_pin_failure(monkeypatch, "round_out", rtz, KV_DECODE_PINS)
+
+
+def test_mutation_kv_page_and_slot_swapped(monkeypatch):
+    def buggy(fmt, out, codes, scales, tscale, block_table, seq_lens, dst_start, out_init):
+        nb, bs = codes.shape[:2]
+        y = np.array(out_init, dtype=np.uint16, copy=True)
+        for s in range(block_table.shape[0]):
+            n = min(max(int(seq_lens[s]), 0), block_table.shape[1] * bs)
+            for i in range(n):
+                row = int(dst_start[s]) + i
+                if 0 <= row < y.shape[0]:
+                    page = int(block_table[s, i % block_table.shape[1]])      # planted: wrong table index
+                    y[row] = 0 if not 0 <= page < nb else KV.decode_rows(fmt, out, codes[page, i % bs],
+                                                                          scales[page, i % bs], tscale)
+        return y
+    _expect_kv_pin_failure(monkeypatch, "kv_gather_ref", buggy, [test_kv_gather_indexing_brute_force])
+
+
+def test_mutation_kv_length_not_clamped(monkeypatch):
+    orig = KV.kv_gather_ref
+
+    def unclamped(fmt, out, codes, scales, tscale, block_table, seq_lens, dst_start, out_init):
+        # planted: tokens past the block table's capacity reuse its last page instead of being dropped
+        cap = block_table.shape[1] * codes.shape[1]
+        bt = np.concatenate([block_table, np.repeat(block_table[:, -1:], 8, axis=1)], axis=1)
+        del cap
+        return orig(fmt, out, codes, scales, tscale, bt, seq_lens, dst_start, out_init)
+    _expect_kv_pin_failure(monkeypatch, "kv_gather_ref", unclamped, [test_kv_gather_indexing_brute_force])
