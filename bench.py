@@ -248,6 +248,39 @@ def bench_moe_rows(reps):
     return rows
 
 
+def bench_kv_rows(reps):
+    """Paged FP4 KV-cache gather (nvfp4_kv_gather) on the chunked-prefill workload: 16 sequences, 66,971 past
+    tokens of 8 heads x 128 in 16-token pages, to FP16; rotated cache + output copies."""
+    kw = WL.KV_PREFILL
+    table, lens, dst, nb, out_rows = kw.layout()
+    tokens = int(lens.sum())
+    elems = tokens * kw.heads * kw.head_dim
+    td, ld, dd = (torch.from_numpy(a).cuda() for a in (table, lens, dst))
+    rows = {}
+    for fmt in ("nvfp4", "mxfp4"):
+        codes, scales = kw.cache(fmt, nb)
+        cd, sd = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+        ts = torch.tensor([kw.KV_TSCALE], dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
+        per_copy = cd.numel() + sd.numel() + 2 * out_rows * kw.heads * kw.head_dim
+        c = copies_needed(per_copy)
+        items = [(cd.clone(), sd.clone(),
+                  torch.zeros((out_rows, kw.heads, kw.head_dim), dtype=torch.float16, device="cuda"))
+                 for _ in range(c)]
+        calls = [(lambda i=i: nv.kv_gather(i[0], i[1], ts, td, ld, dd, i[2], fmt=fmt)) for i in items]
+        g = graph_of(calls)
+        warm_graph(g)
+        ms = time_graph_replays(g, reps, len(calls))
+        nbytes = elems // 2 + elems // (16 if fmt == "nvfp4" else 32) + 2 * elems
+        row = {"format": fmt, "out": "f16", "seqs": kw.seqs, "tokens": tokens, "heads": kw.heads,
+               "head_dim": kw.head_dim, "block_size": kw.block_size, "copies": c,
+               "us_per_call": round(ms * 1e3, 3), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes}
+        row["hbm_frac"] = round(row["gb_s"] / HBM_PEAK_GBS, 4)
+        rows[f"kv_gather_{fmt}_f16"] = row
+        del g, items, cd, sd
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(budget_s=10.0):
     """The oracle's linear (float64) on the decode workload, single-threaded, for about budget_s seconds."""
     from threadpoolctl import threadpool_limits
@@ -394,6 +427,9 @@ def main():
         rows.update(bench_moe_rows(reps))
         log(f"  {rows['moe_routed_decode_top8']}")
         log(f"  {rows['moe_grouped_prefill_t2048_top8']}")
+        log("rows KV gather")
+        rows.update(bench_kv_rows(20))
+        log(f"  {rows['kv_gather_nvfp4_f16']} {rows['kv_gather_mxfp4_f16']}")
 
     log("cpu baseline (oracle)")
     cpu = cpu_baseline(args.cpu_budget)

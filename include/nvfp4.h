@@ -230,6 +230,49 @@ nvfp4_status nvfp4_linear_grouped(const uint16_t* x, int64_t t_count, int64_t to
                                   const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
                                   int64_t workspace_bytes, void* stream);
 
+/*
+ * Paged FP4 KV-cache gather.  imp "docs/quantization.md", KV-cache
+ * paragraphs: an NVFP4 KV cache keeps E2M1 values with UE4M3 micro-scales and
+ * an MXFP4 KV cache the same nibbles with UE8M0 micro-scales per 32 elements;
+ * for chunked prefill the past chunks' K/V are gathered from the paged cache
+ * into FP16 and joined with the current chunk before attention.
+ *
+ * One cache (one layer's K or V) in pages of block_size tokens:
+ *   codes  [num_blocks, block_size, heads, head_dim / 2] uint8, element 2j in
+ *          the low nibble of byte j;
+ *   scales [num_blocks, block_size, heads, head_dim / G] uint8: G = 16, E4M3
+ *          (format NVFP4_KV_NVFP4, with one FP32 tensor scale *tscale), or
+ *          G = 32, UE8M0 = 2^(byte - 127), 0xFF NaN (NVFP4_KV_MXFP4, no tensor
+ *          scale: tscale is ignored and may be NULL).
+ * For sequence s < seqs and token i < min(seq_lens[s], max_blocks * block_size):
+ *   out[dst_start[s] + i, :, :] = decode(page block_table[s, i / block_size],
+ *                                        slot i % block_size)
+ * with decode = RNE_out(fl32(fl32(E2M1 * E4M3) * tscale)) (NVFP4) or
+ * RNE_out(E2M1 * 2^(byte - 127)) (MXFP4), out [out_rows, heads, head_dim]
+ * FP16 (NVFP4_OUT_F16) or BF16 (NVFP4_OUT_BF16).  block_table [seqs,
+ * max_blocks], seq_lens [seqs] and dst_start [seqs] are int32 device data, so
+ * they are not validated on the host: a page id outside [0, num_blocks) gives
+ * zero rows, a negative length gathers nothing, and output rows outside
+ * [0, out_rows) are skipped.  Every other output row keeps its contents (the
+ * caller writes the current chunk's K/V around the gathered rows).
+ * Errors: an unknown format or out_type is NVFP4_ERR_UNSUPPORTED;
+ * head_dim % G != 0, non-positive num_blocks, block_size, heads, head_dim or
+ * max_blocks, negative seqs or out_rows, seqs * max_blocks > 2^31 - 1 or a
+ * byte size overflow is NVFP4_ERR_SHAPE; codes and out must be 16-byte
+ * aligned, tscale and the int32 arrays 4-byte aligned; out must not overlap
+ * an input.  seqs = 0 is a no-op.
+ */
+#define NVFP4_KV_NVFP4 0
+#define NVFP4_KV_MXFP4 1
+#define NVFP4_OUT_F16 0
+#define NVFP4_OUT_BF16 1
+
+nvfp4_status nvfp4_kv_gather(int format, int out_type, const uint8_t* codes, const uint8_t* scales,
+                             const float* tscale, int64_t num_blocks, int64_t block_size, int64_t heads,
+                             int64_t head_dim, const int32_t* block_table, int64_t max_blocks,
+                             const int32_t* seq_lens, const int32_t* dst_start, int64_t seqs, uint16_t* out,
+                             int64_t out_rows, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,10 +4,12 @@ The hot path runs in hand-written gfx950 HIP kernels behind the C ABI of
 libnvfp4.so (include/nvfp4.h).  This package holds the kernels (csrc/), the
 build script, the ctypes binding and the synthetic workload generators.
 """
-from .binding import (KERNEL_IDS, NVFP4Error, amax_accumulate, dequant, dequant_experts, lib, lib_path, linear,
+from .binding import (KERNEL_IDS, KV_FORMATS, NVFP4Error, amax_accumulate, dequant, dequant_experts, kv_gather, lib,
+                      lib_path, linear,
                       linear_grouped, linear_grouped_workspace_bytes, linear_routed, linear_workspace_bytes,
                       quantize, quantize_experts, quantize_shared, quantize_with_amax)
 
-__all__ = ["KERNEL_IDS", "NVFP4Error", "amax_accumulate", "dequant", "dequant_experts", "lib", "lib_path", "linear",
+__all__ = ["KERNEL_IDS", "KV_FORMATS", "NVFP4Error", "amax_accumulate", "dequant", "dequant_experts", "kv_gather",
+           "lib", "lib_path", "linear",
            "linear_grouped", "linear_grouped_workspace_bytes", "linear_routed", "linear_workspace_bytes", "quantize", "quantize_experts", "quantize_shared",
            "quantize_with_amax"]

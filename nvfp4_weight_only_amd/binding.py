@@ -25,7 +25,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = ran
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
             "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced",
             "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
-            "nvfp4_linear_grouped", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes")
+            "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_linear_workspace_bytes",
+            "nvfp4_linear_grouped_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
         L.nvfp4_linear_routed.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_kv_gather.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, i64, vp, i64, vp]
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
@@ -319,4 +321,46 @@ def linear_grouped(x: torch.Tensor, route: torch.Tensor, packed: torch.Tensor, s
                                       scales.data_ptr(), tscale.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel(), _stream(x)),
            "nvfp4_linear_grouped")
+    return out
+
+
+# KV-cache formats and output types (include/nvfp4.h).
+KV_FORMATS = {"nvfp4": 0, "mxfp4": 1}
+_KV_GROUP = {"nvfp4": 16, "mxfp4": 32}
+
+
+def kv_gather(codes: torch.Tensor, scales: torch.Tensor, tscale: Optional[torch.Tensor], block_table: torch.Tensor,
+              seq_lens: torch.Tensor, dst_start: torch.Tensor, out: torch.Tensor, fmt: str = "nvfp4") -> torch.Tensor:
+    """Gather a paged FP4 KV cache into `out` (FP16 or BF16 [out_rows, heads, head_dim]) in place.
+
+    codes uint8 [num_blocks, block_size, heads, head_dim/2]; scales uint8 [num_blocks, block_size, heads,
+    head_dim/G] (G = 16 for "nvfp4", with the FP32 tensor scale `tscale` [1]; G = 32 for "mxfp4", tscale None);
+    block_table int32 [seqs, max_blocks], seq_lens and dst_start int32 [seqs], all on the device.
+    """
+    if fmt not in KV_FORMATS:
+        raise ValueError(f"unknown KV format {fmt!r}")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    for t, name in ((block_table, "block_table"), (seq_lens, "seq_lens"), (dst_start, "dst_start")):
+        _need(t, torch.int32, name)
+    if fmt == "nvfp4":
+        _need(tscale, torch.float32, "tscale")
+    if out.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("out must be float16 or bfloat16")
+    _need(out, out.dtype, "out")
+    if codes.dim() != 4 or scales.dim() != 4:
+        raise ValueError("codes and scales must be [num_blocks, block_size, heads, *]")
+    nb, bs, heads, half = codes.shape
+    hd = 2 * half
+    if tuple(scales.shape) != (nb, bs, heads, hd // _KV_GROUP[fmt]):
+        raise ValueError("scales do not match codes")
+    if out.dim() != 3 or out.shape[1] != heads or out.shape[2] != hd:
+        raise ValueError("out must be [out_rows, heads, head_dim]")
+    if block_table.dim() != 2 or seq_lens.shape != (block_table.shape[0],) or dst_start.shape != seq_lens.shape:
+        raise ValueError("block_table must be [seqs, max_blocks], seq_lens and dst_start [seqs]")
+    _check(lib().nvfp4_kv_gather(KV_FORMATS[fmt], 1 if out.dtype == torch.bfloat16 else 0, codes.data_ptr(),
+                                 scales.data_ptr(), tscale.data_ptr() if tscale is not None else None, nb, bs, heads,
+                                 hd, block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(),
+                                 dst_start.data_ptr(), block_table.shape[0], out.data_ptr(), out.shape[0],
+                                 _stream(out)), "nvfp4_kv_gather")
     return out

@@ -60,4 +60,13 @@ void launch_linear_grouped(const uint16_t* x, int64_t t_count, int64_t topk, con
                            int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales, const float* tscale,
                            uint16_t* y, void* workspace, hipStream_t s);
 
+// Paged FP4 KV-cache gather (mx: UE8M0 scales per 32, else E4M3 per 16 and
+// one FP32 tensor scale; bf16: BF16 output, else FP16).  row_elems = heads *
+// head_dim, a multiple of 16 (32 when mx).  One workgroup per (sequence, block
+// table entry): seqs * max_blocks < 2^31.
+void launch_kv_gather(bool mx, bool bf16, const uint8_t* codes, const uint8_t* scales, const float* tscale,
+                      int64_t num_blocks, int64_t block_size, int64_t row_elems, const int32_t* block_table,
+                      int64_t max_blocks, const int32_t* seq_lens, const int32_t* dst_start, int64_t seqs,
+                      uint16_t* out, int64_t out_rows, hipStream_t s);
+
 }  // namespace nvfp4

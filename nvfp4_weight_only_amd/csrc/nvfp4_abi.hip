@@ -348,4 +348,42 @@ nvfp4_status nvfp4_linear_grouped(const uint16_t* x, int64_t t_count, int64_t to
   return launch_status();
 }
 
+nvfp4_status nvfp4_kv_gather(int format, int out_type, const uint8_t* codes, const uint8_t* scales,
+                             const float* tscale, int64_t num_blocks, int64_t block_size, int64_t heads,
+                             int64_t head_dim, const int32_t* block_table, int64_t max_blocks,
+                             const int32_t* seq_lens, const int32_t* dst_start, int64_t seqs, uint16_t* out,
+                             int64_t out_rows, void* stream) {
+  if ((format != NVFP4_KV_NVFP4 && format != NVFP4_KV_MXFP4) || (out_type != NVFP4_OUT_F16 && out_type != NVFP4_OUT_BF16))
+    return NVFP4_ERR_UNSUPPORTED;
+  const bool mx = format == NVFP4_KV_MXFP4;
+  if (!codes || !scales || (!mx && !tscale) || (seqs != 0 && (!block_table || !seq_lens || !dst_start || !out)))
+    return NVFP4_ERR_NULL;
+  const int64_t group = mx ? 32 : 16;
+  if (num_blocks < 1 || block_size < 1 || heads < 1 || head_dim < 1 || head_dim % group != 0 || max_blocks < 1 ||
+      seqs < 0 || out_rows < 0)
+    return NVFP4_ERR_SHAPE;
+  int64_t row_elems, page_elems, cache_elems, tab, ob;
+  if (!mul_ok(heads, head_dim, &row_elems) || !mul_ok(row_elems, block_size, &page_elems) ||
+      !mul_ok(page_elems, num_blocks, &cache_elems) || !mul_ok(seqs, max_blocks, &tab) || tab > INT32_MAX ||
+      tab > INT64_MAX / 4 || !mul_ok(out_rows, row_elems, &ob) || ob > INT64_MAX / 2 ||
+      max_blocks > INT64_MAX / block_size)
+    return NVFP4_ERR_SHAPE;
+  ob *= 2;
+  if (seqs == 0) return NVFP4_OK;
+  if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(tscale) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(dst_start) & 3u) != 0)
+    return NVFP4_ERR_ALIGN;
+  if (overlaps(out, ob, codes, cache_elems / 2) || overlaps(out, ob, scales, cache_elems / group) ||
+      (!mx && overlaps(out, ob, tscale, 4)) || overlaps(out, ob, block_table, 4 * tab) ||
+      overlaps(out, ob, seq_lens, 4 * seqs) || overlaps(out, ob, dst_start, 4 * seqs))
+    return NVFP4_ERR_ALIAS;
+  nvfp4_status st;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_kv_gather(mx, out_type == NVFP4_OUT_BF16, codes, scales, tscale, num_blocks, block_size, row_elems,
+                          block_table, max_blocks, seq_lens, dst_start, seqs, out, out_rows,
+                          static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 }  // extern "C"

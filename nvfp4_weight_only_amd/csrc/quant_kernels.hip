@@ -288,7 +288,12 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict
 #pragma unroll
     for (int u = 0; u < kDequantU; ++u) {
       const int64_t h = h0 + (int64_t)u * blockDim.x;
-      if (h < n_half) out[h] = dequant_half(p[u], sb[u], t);
+      if (h < n_half) {
+        // Nontemporal: the BF16 weight is written once and not read back here.
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const uint4 v = dequant_half(p[u], sb[u], t);
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(out) + h);
+      }
     }
   }
 }

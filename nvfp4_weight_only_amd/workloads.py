@@ -30,6 +30,7 @@ SEED_X = 1          # activations
 SEED_OUTLIER = 2    # which input columns are outliers (decode workload)
 SEED_UP = 3         # the "up" half of the merged gate/up weight
 SEED_ROUTE = 4      # expert choices of the routed workloads
+SEED_KV = 5         # KV-cache lengths (5), page order (6) and contents (7)
 
 W_STD = 0.02
 X_STD = 1.0
@@ -191,3 +192,64 @@ MOE_DECODE = MoeWorkload("moe_decode", "routed MoE decode: 128 experts of N=2048
                          experts=128, n=2048, k=4096, topk=8)
 MOE_PREFILL = MoeWorkload("moe_prefill", "grouped MoE prefill: 2048 tokens, each routed to 8 of 128 experts "
                           "of N=2048, K=4096", experts=128, n=2048, k=4096, topk=8, t=2048)
+
+
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    """Synthetic paged FP4 KV cache and the gather of a chunked-prefill step.
+
+    `seqs` sequences with seeded context lengths uniform in [min_len, max_len]; their pages are a random
+    permutation of the cache's pages (a fragmented cache) plus `spare_pages` unused ones; output rows of
+    sequence s start at dst_start[s], with `chunk` rows left free after each sequence for its current chunk.
+    Codes are uniform random bytes (every E2M1 nibble); scale bytes are E4M3 codes drawn around 1/8 .. 8
+    (0x28..0x48, NVFP4) or UE8M0 exponents 120..134 (MXFP4); the NVFP4 tensor scale is 1/64.
+    """
+    name: str
+    description: str
+    seqs: int
+    heads: int
+    head_dim: int
+    block_size: int
+    min_len: int
+    max_len: int
+    chunk: int
+    spare_pages: int = 64
+
+    def seq_lens(self) -> np.ndarray:
+        rng = np.random.default_rng(SEED_KV)
+        return rng.integers(self.min_len, self.max_len + 1, size=self.seqs).astype(np.int32)
+
+    def layout(self):
+        """(block_table int32 [seqs, max_blocks] (-1 past each sequence's pages), seq_lens, dst_start, num_blocks,
+        out_rows)."""
+        lens = self.seq_lens()
+        pages = (lens + self.block_size - 1) // self.block_size
+        max_blocks = int(pages.max())
+        num_blocks = int(pages.sum()) + self.spare_pages
+        perm = np.random.default_rng(SEED_KV + 1).permutation(num_blocks).astype(np.int32)
+        table = np.full((self.seqs, max_blocks), -1, dtype=np.int32)
+        at = 0
+        for s in range(self.seqs):
+            table[s, :pages[s]] = perm[at:at + pages[s]]
+            at += int(pages[s])
+        dst = np.concatenate([[0], np.cumsum(lens.astype(np.int64) + self.chunk)[:-1]]).astype(np.int32)
+        out_rows = int(dst[-1]) + int(lens[-1]) + self.chunk
+        return table, lens, dst, num_blocks, out_rows
+
+    def cache(self, fmt: str, num_blocks: int):
+        """(codes uint8 [num_blocks, block_size, heads, head_dim/2], scales uint8 [..., head_dim/G])."""
+        g = 16 if fmt == "nvfp4" else 32
+        rng = np.random.default_rng(SEED_KV + 2)
+        codes = rng.integers(0, 256, size=(num_blocks, self.block_size, self.heads, self.head_dim // 2),
+                             dtype=np.uint8)
+        lo, hi = (0x28, 0x48) if fmt == "nvfp4" else (120, 134)
+        scales = rng.integers(lo, hi + 1, size=(num_blocks, self.block_size, self.heads, self.head_dim // g),
+                              dtype=np.uint8)
+        return codes, scales
+
+    KV_TSCALE = 1.0 / 64.0
+
+
+KV_PREFILL = KvWorkload("kv_gather", "paged FP4 KV gather for chunked prefill: 16 sequences of 1024..8192 past "
+                        "tokens, 8 KV heads x 128, 16-token pages", seqs=16, heads=8, head_dim=128, block_size=16,
+                        min_len=1024, max_len=8192, chunk=512)

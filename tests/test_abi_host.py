@@ -148,3 +148,22 @@ def test_grouped_validation(L):
     assert g(*args(ws=R)) == B.ERR_ALIAS           # workspace overlaps route
     assert g(*args(y=A + 32)) == B.ERR_ALIAS       # y overlaps x
     assert g(*args(x=None, t=0, y=None, ws=None, wsb=0)) == B.OK    # t = 0 no-op
+
+
+def test_kv_gather_validation(L):
+    g = L.nvfp4_kv_gather
+    BT, SL, DS, O = 0x60000000, 0x61000000, 0x62000000, 0x70000000
+
+    def args(fmt=0, out=0, codes=A, scales=Bp, ts=D, nb=4, bs=16, heads=2, hd=64, mb=3, seqs=2, o=O, rows=100):
+        return (fmt, out, codes, scales, ts, nb, bs, heads, hd, BT, mb, SL, DS, seqs, o, rows, None)
+    assert g(*args(fmt=2)) == B.ERR_UNSUPPORTED and g(*args(out=2)) == B.ERR_UNSUPPORTED
+    assert g(*args(codes=None)) == B.ERR_NULL
+    assert g(*args(ts=None)) == B.ERR_NULL                        # NVFP4 needs its tensor scale
+    assert g(*args(hd=24)) == B.ERR_SHAPE                         # head_dim % 16 != 0
+    assert g(*args(fmt=1, hd=48, ts=None)) == B.ERR_SHAPE         # MXFP4: head_dim % 32 != 0
+    assert g(*args(bs=0)) == B.ERR_SHAPE and g(*args(nb=0)) == B.ERR_SHAPE and g(*args(mb=0)) == B.ERR_SHAPE
+    assert g(*args(seqs=-1)) == B.ERR_SHAPE and g(*args(rows=-1)) == B.ERR_SHAPE
+    assert g(*args(seqs=2 ** 20, mb=2 ** 12)) == B.ERR_SHAPE        # 2^32 workgroups
+    assert g(*args(codes=A + 8)) == B.ERR_ALIGN and g(*args(o=O + 8)) == B.ERR_ALIGN
+    assert g(*args(o=A)) == B.ERR_ALIAS                           # out overlaps the codes
+    assert g(*args(seqs=0)) == B.OK                               # no-op

@@ -566,3 +566,113 @@ def test_linear_grouped_many_experts(nv, e):
             y_ref, bound = O.linear_ref(x[ti:ti + 1], *q)
             bad = O.linear_violations(WL.f32_from_bf16_bits(y[ti, j][None]).astype(np.float64), y_ref, bound)
             assert not bad.any(), f"pair ({ti}, {j}) on expert {ei}: {int(bad.sum())} outputs outside 2e-3*B"
+
+
+# ---------------------------------------------------------------------------
+# Paged FP4 KV-cache gather: bit-exact against the oracle (R14-R16).
+# ---------------------------------------------------------------------------
+from oracle import kv_oracle as KV  # noqa: E402
+
+KV_OUT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _kv_random_cache(fmt, nb, bs, heads, hd, seed):
+    g = KV.GROUP[fmt]
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(nb, bs, heads, hd // 2), dtype=np.uint8)
+    if fmt == KV.NVFP4:
+        scales = rng.integers(0, 0x7F, size=(nb, bs, heads, hd // g), dtype=np.uint8)   # every finite E4M3
+    else:
+        scales = rng.integers(100, 155, size=(nb, bs, heads, hd // g), dtype=np.uint8)
+        scales.flat[:6] = [0, 1, 126, 127, 141, 254]    # subnormal products, FP16 overflow, FP32 overflow
+    return codes, scales
+
+
+def _kv_run(nv, fmt, out, codes, scales, ts, table, lens, dst, out_rows, init_bits):
+    od = KV_OUT[out]
+    y = torch.from_numpy(init_bits.view(np.int16)).cuda().view(od)
+    tsd = torch.tensor([ts], dtype=torch.float32, device="cuda") if fmt == KV.NVFP4 else None
+    nv.kv_gather(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), tsd,
+                 torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(), torch.from_numpy(dst).cuda(), y,
+                 fmt=fmt)
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _kv_equal(got, want, out):
+    """Bit equality, except that any NaN matches any NaN (payloads are not specified)."""
+    dt = np.float16 if out == "f16" else None
+    if dt is not None:
+        gn, wn = np.isnan(got.view(np.float16)), np.isnan(want.view(np.float16))
+    else:
+        f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+        gn, wn = np.isnan(f(got)), np.isnan(f(want))
+    return np.array_equal(gn, wn) and np.array_equal(got[~gn], want[~wn])
+
+
+KV_CASES = [   # nb, bs, heads, hd, lens, max_blocks
+    (40, 16, 8, 128, [1, 17, 100, 0, 250], 16),
+    (13, 7, 3, 64, [20, 49, 5], 7),
+    (9, 1, 1, 32, [3, 9, 1], 9),
+]
+
+
+@pytest.mark.parametrize("fmt", [KV.NVFP4, KV.MXFP4])
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("case", range(len(KV_CASES)))
+def test_kv_gather(nv, fmt, out, case):
+    nb, bs, heads, hd, lens, mb = KV_CASES[case]
+    codes, scales = _kv_random_cache(fmt, nb, bs, heads, hd, 2100 + case)
+    rng = np.random.default_rng(2200 + case)
+    seqs = len(lens)
+    table = rng.integers(0, nb, size=(seqs, mb)).astype(np.int32)      # pages shared and reused across sequences
+    lens = np.array(lens, dtype=np.int32)
+    dst = np.concatenate([[3], 3 + np.cumsum(lens + 5)[:-1]]).astype(np.int32)   # gaps for the current chunks
+    out_rows = int(dst[-1] + lens[-1] + 4)
+    init = rng.integers(0, 2 ** 16, size=(out_rows, heads, hd), dtype=np.uint16)
+    ts = np.float32(0.0123)
+    got = _kv_run(nv, fmt, out, codes, scales, ts, table, lens, dst, out_rows, init)
+    want = KV.kv_gather_ref(fmt, out, codes, scales, ts, table, lens, dst, init)
+    assert _kv_equal(got, want, out), f"{fmt} {out} case {case}: {int((got != want).sum())} elements differ"
+
+
+@pytest.mark.parametrize("fmt", [KV.NVFP4, KV.MXFP4])
+def test_kv_gather_edges(nv, fmt):
+    """Out-of-range page ids (zeros), negative and over-long lengths, rows before 0 and past the end, NaN scale
+    bytes; seqs = 0 is a no-op."""
+    nb, bs, heads, hd = 6, 4, 2, 64
+    codes, scales = _kv_random_cache(fmt, nb, bs, heads, hd, 2300)
+    scales[2, 1, 0, 0] = 0x7F if fmt == KV.NVFP4 else 0xFF          # a NaN scale
+    table = np.array([[3, -1, 2], [9, 2, 0], [2, 2, 2], [1, 0, 5], [4, 4, 4]], dtype=np.int32)
+    lens = np.array([12, 9, -4, 40, 7], dtype=np.int32)
+    dst = np.array([-3, 10, 30, 22, 38], dtype=np.int32)
+    out_rows = 42
+    for out in ("f16", "bf16"):
+        init = np.full((out_rows, heads, hd), 0x3C00 if out == "f16" else 0x3F80, dtype=np.uint16)
+        got = _kv_run(nv, fmt, out, codes, scales, np.float32(0.5), table, lens, dst, out_rows, init)
+        want = KV.kv_gather_ref(fmt, out, codes, scales, np.float32(0.5), table, lens, dst, init)
+        assert _kv_equal(got, want, out), out
+    y = torch.zeros((4, heads, hd), dtype=torch.float16, device="cuda")
+    e = torch.empty((0, 3), dtype=torch.int32, device="cuda")
+    nv.kv_gather(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                 torch.ones(1, device="cuda") if fmt == KV.NVFP4 else None, e,
+                 torch.empty(0, dtype=torch.int32, device="cuda"), torch.empty(0, dtype=torch.int32, device="cuda"),
+                 y, fmt=fmt)
+    assert torch.count_nonzero(y) == 0
+
+
+@pytest.mark.parametrize("fmt", [KV.NVFP4, KV.MXFP4])
+def test_kv_gather_full_size_sampled(nv, fmt):
+    """The chunked-prefill gather workload (16 sequences, 66,971 past tokens, 8 x 128, 16-token pages), launched
+    as timed; three whole sequences (short, long, last) against the oracle."""
+    kw = WL.KV_PREFILL
+    table, lens, dst, nb, out_rows = kw.layout()
+    codes, scales = kw.cache(fmt, nb)
+    init = np.zeros((out_rows, kw.heads, kw.head_dim), dtype=np.uint16)
+    got = _kv_run(nv, fmt, "f16", codes, scales, np.float32(kw.KV_TSCALE), table, lens, dst, out_rows, init)
+    for s in (int(np.argmin(lens)), int(np.argmax(lens)), kw.seqs - 1):
+        sel = slice(s, s + 1)
+        want = KV.kv_gather_ref(fmt, "f16", codes, scales, np.float32(kw.KV_TSCALE), table[sel], lens[sel], dst[sel],
+                                init)
+        rows = slice(int(dst[s]), int(dst[s] + lens[s]))
+        assert np.array_equal(got[rows], want[rows]), f"sequence {s}"
+        assert not np.any(got[int(dst[s] + lens[s]):int(dst[s] + lens[s]) + kw.chunk]), "chunk rows must stay zero"
