@@ -315,10 +315,26 @@ def profile_run(what, launches):
     copy:   a plain 256 MiB device-to-device copy (torch's copy kernel), the calibration for the
             FETCH_SIZE / WRITE_SIZE counters (each launch moves exactly 256 MiB each way);
     moe_prefill: nvfp4_linear_grouped on the grouped MoE prefill workload (2048 tokens, top-8 of 128
-            experts of N=2048, K=4096), one call per launch (the sort kernel and the grouped GEMM).
+            experts of N=2048, K=4096), one call per launch (the sort kernel and the grouped GEMM);
+    kv_gather: nvfp4_kv_gather (NVFP4 pages to FP16) on the chunked-prefill gather workload, cycling
+            through rotated cache + output copies.
     """
     torch.cuda.set_device(0)
-    if what == "moe_prefill":
+    if what == "kv_gather":
+        kw = WL.KV_PREFILL
+        table, lens, dst, nb, out_rows = kw.layout()
+        td, ld, dd = (torch.from_numpy(a).cuda() for a in (table, lens, dst))
+        codes, scales = kw.cache("nvfp4", nb)
+        ts = torch.tensor([kw.KV_TSCALE], dtype=torch.float32, device="cuda")
+        per_copy = codes.size + scales.size + 2 * out_rows * kw.heads * kw.head_dim
+        items = [(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                  torch.empty((out_rows, kw.heads, kw.head_dim), dtype=torch.float16, device="cuda"))
+                 for _ in range(copies_needed(per_copy))]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            c, s, o = items[i % len(items)]
+            nv.kv_gather(c, s, ts, td, ld, dd, o, fmt="nvfp4")
+    elif what == "moe_prefill":
         pw = WL.MOE_PREFILL
         base = dev_bf16(pw.base_weight())
         stack = torch.stack([(base.float() * pw.expert_scale(i)).to(torch.bfloat16) for i in range(pw.experts)])
@@ -360,7 +376,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()
