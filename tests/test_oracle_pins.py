@@ -698,3 +698,156 @@ def test_mutation_kv_length_not_clamped(monkeypatch):
         del cap
         return orig(fmt, out, codes, scales, tscale, bt, seq_lens, dst_start, out_init)
     _expect_kv_pin_failure(monkeypatch, "kv_gather_ref", unclamped, [test_kv_gather_indexing_brute_force])
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 tensors and the W4A4 linear (oracle/mxfp4_oracle.py).
+# ---------------------------------------------------------------------------
+from oracle import mxfp4_oracle as MX  # noqa: E402
+
+_E2M1_MAGS = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+              Fraction(6)]
+
+
+def _bf16_fraction(b):
+    """A BF16 bit pattern as an exact Fraction (sign, 8-bit exponent bias 127, 7-bit mantissa, subnormals)."""
+    s, e, m = (b >> 15) & 1, (b >> 7) & 0xFF, b & 0x7F
+    v = Fraction(m, 128) * Fraction(2) ** -126 if e == 0 else (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+    return -v if s else v
+
+
+def _mx_block_brute(bits):
+    """R17 by brute force on exact rationals: floor(log2(amax)) by walking powers of two, each element by an
+    exhaustive nearest search over the eight magnitudes (ties to the even code)."""
+    vals = [_bf16_fraction(int(b)) for b in bits]
+    amax = max(abs(v) for v in vals)
+    if amax == 0:
+        e = 0
+    else:
+        p = 0
+        while Fraction(2) ** (p + 1) <= amax:
+            p += 1
+        while Fraction(2) ** p > amax:
+            p -= 1
+        e = min(max(p - 2 + 127, 0), 254)
+    scale = Fraction(2) ** (e - 127)
+    codes = []
+    for b, v in zip(bits, vals):
+        q = abs(v) / scale
+        best = min(range(8), key=lambda c: (abs(q - _E2M1_MAGS[c]), c % 2))   # nearest, then the even code
+        codes.append(((int(b) >> 15) << 3) | best)
+    return e, codes
+
+
+def pin_mx_quantizer_brute_force():
+    rng = np.random.default_rng(41)
+    rows = []
+    for r in range(24):
+        f = rng.standard_normal(64).astype(np.float32) * np.float32(2.0 ** rng.integers(-20, 20))
+        rows.append(WL.bf16_bits_from_f32(f))
+    w = np.stack(rows)
+    w[0, :32] = 0                                            # an all-zero block
+    w[1, 3] = 0x8000                                          # -0
+    w[2, :32] = WL.bf16_bits_from_f32(np.full(32, 1e-39, dtype=np.float32))   # subnormal block: scale clamps at 0
+    w[3, 32:] = WL.bf16_bits_from_f32(np.array([4, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, 6.5, 7.9, -5, -0.75] + [0] * 20,
+                                               dtype=np.float32))                # midpoints and saturation
+    packed, scales = MX.quantize(w)
+    codes = O.unpack_nibbles(packed)
+    for r in range(w.shape[0]):
+        for b in range(2):
+            e, cs = _mx_block_brute(w[r, 32 * b:32 * b + 32])
+            assert scales[r, b] == e, (r, b)
+            assert list(codes[r, 32 * b:32 * b + 32]) == cs, (r, b)
+
+
+def pin_mx_closed_forms():
+    # amax 4 -> floor(log2) 2 -> scale byte 127 (2^0); the midpoints go to the even codes, 6.5 and 7.9 saturate
+    w = WL.bf16_bits_from_f32(np.array([[4, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, 6.5, 7.9, -5, -0.75] + [0] * 20],
+                                       dtype=np.float32))
+    packed, scales = MX.quantize(w)
+    assert scales[0, 0] == 127
+    assert list(O.unpack_nibbles(packed)[0, :12]) == [6, 0, 2, 2, 4, 4, 6, 6, 7, 7, 8 | 6, 8 | 2]
+    # idempotence: the block maximum quantizes to 4 or 6 times the scale, so dequant -> quantize is the identity
+    rng = np.random.default_rng(42)
+    x = WL.bf16_bits_from_f32((rng.standard_normal((8, 96)) * 3).astype(np.float32))
+    p1, s1 = MX.quantize(x)
+    back = O.f32_to_bf16_rne(MX.dequant_exact(p1, s1).astype(np.float32))
+    p2, s2 = MX.quantize(back)
+    assert np.array_equal(p1, p2) and np.array_equal(s1, s2)
+    # every block's largest magnitude code is 6 or 7
+    mags = O.unpack_nibbles(p1).reshape(8, 3, 32) & 7
+    assert np.all(mags.max(axis=2) >= 6)
+
+
+def pin_mx_linear():
+    rng = np.random.default_rng(43)
+    x = WL.bf16_bits_from_f32(rng.standard_normal((3, 64)).astype(np.float32))
+    w = WL.bf16_bits_from_f32((rng.standard_normal((5, 64)) * 0.05).astype(np.float32))
+    wp, ws = MX.quantize(w)
+    y, bound = MX.linear_w4a4_ref(x, wp, ws)
+    # exact rational sums of the brute-force-quantized operands
+    def deq(bits):
+        out = []
+        for b in range(0, 64, 32):
+            e, cs = _mx_block_brute(bits[b:b + 32])
+            out += [(-1 if c & 8 else 1) * _E2M1_MAGS[c & 7] * Fraction(2) ** (e - 127) for c in cs]
+        return out
+    xq = [deq(x[i]) for i in range(3)]
+    wq = [deq(w[j]) for j in range(5)]
+    for i in range(3):
+        for j in range(5):
+            assert y[i, j] == float(sum(a * b for a, b in zip(xq[i], wq[j])))
+            assert bound[i, j] == float(sum(abs(a * b) for a, b in zip(xq[i], wq[j])))
+    # one-hot activation: X = e_7 quantizes exactly (amax 1 -> scale 2^-2, code 4), so Y is column 7 of W's values
+    e7 = np.zeros((1, 64), dtype=np.uint16)
+    e7[0, 7] = 0x3F80
+    y1, _ = MX.linear_w4a4_ref(e7, wp, ws)
+    assert np.array_equal(y1[0], MX.dequant_exact(wp, ws)[:, 7])
+
+
+def test_mx_quantizer_brute_force():
+    pin_mx_quantizer_brute_force()
+
+
+def test_mx_closed_forms():
+    pin_mx_closed_forms()
+
+
+def test_mx_linear_exact():
+    pin_mx_linear()
+
+
+MX_PINS = [pin_mx_quantizer_brute_force, pin_mx_closed_forms, pin_mx_linear]
+
+
+def _expect_mx_pin_failure(monkeypatch, target, replacement):
+    monkeypatch.setattr(MX, target, replacement)
+    for pin in MX_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            return
+    raise AssertionError(f"planted mistake in mxfp4_oracle.{target} went unnoticed")
+
+
+def test_mutation_mx_scale_exponent(monkeypatch):
+    _expect_mx_pin_failure(monkeypatch, "E2M1_EMAX", 1)
+
+
+def test_mutation_mx_block_16(monkeypatch):
+    _expect_mx_pin_failure(monkeypatch, "MX_BLOCK", 16)
+
+
+def test_mutation_mx_ties_up(monkeypatch):
+    def ties_up(lhs, mids, rhs):
+        return sum((lhs >= u * rhs).astype(np.int64) for u in mids)
+    _expect_mx_pin_failure(monkeypatch, "_nearest_code_ties_even", ties_up)
+
+
+def test_mutation_mx_transposed_linear(monkeypatch):
+    orig = MX.dequant_exact
+
+    def swapped_halves(p, s):
+        v = orig(p, s)
+        return np.concatenate([v[:, 32:], v[:, :32]], axis=1) if v.shape[1] >= 64 else v
+    _expect_mx_pin_failure(monkeypatch, "dequant_exact", swapped_halves)
