@@ -281,6 +281,41 @@ def bench_kv_rows(reps):
     return rows
 
 
+FP4_MFMA_PEAK_TFLOPS = 10066.3  # MI355X dense FP4 / FP6 MFMA, published (no sparsity)
+
+
+def bench_mx_rows(reps):
+    """W4A4 MXFP4 linear (nvfp4_mx_linear_w4a4: X quantized to MXFP4 on the stream, then the FP4 GEMM) on the
+    prefill workload (N=17408, K=5120) at M=512 and 2048, rotated weight copies; also the GEMM alone."""
+    wl = WL.WORKLOADS["prefill"]
+    wq, wsc = nv.mx_quantize(dev_bf16(wl.weight()))
+    c = copies_needed(wq.numel() + wsc.numel())
+    rot = [(wq.clone(), wsc.clone()) for _ in range(c)]
+    rows = {}
+    for m in (512, 2048):
+        x = dev_bf16(wl.activations(m))
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
+        g = graph_of([(lambda r=r: nv.mx_linear_w4a4(x, r[0], r[1], out=y, workspace=ws)) for r in rot])
+        warm_graph(g)
+        ms = time_graph_replays(g, reps, len(rot))
+        xq, xs = nv.mx_quantize(x)
+        g2 = graph_of([(lambda r=r: nv.mx_gemm(xq, xs, r[0], r[1], out=y)) for r in rot])
+        warm_graph(g2)
+        ms_g = time_graph_replays(g2, reps, len(rot))
+        flops = 2.0 * m * wl.n * wl.k
+        row = {"m": m, "n": wl.n, "k": wl.k, "copies": c, "us_per_call": round(ms * 1e3, 3),
+               "tflop_s": round(flops / (ms * 1e-3) / 1e12, 1), "gemm_us": round(ms_g * 1e3, 3),
+               "gemm_tflop_s": round(flops / (ms_g * 1e-3) / 1e12, 1)}
+        row["fp4_frac"] = round(row["tflop_s"] / FP4_MFMA_PEAK_TFLOPS, 4)
+        row["gemm_fp4_frac"] = round(row["gemm_tflop_s"] / FP4_MFMA_PEAK_TFLOPS, 4)
+        rows[f"mx_w4a4_prefill_m{m}"] = row
+        del g, g2
+    del rot
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(budget_s=10.0):
     """The oracle's linear (float64) on the decode workload, single-threaded, for about budget_s seconds."""
     from threadpoolctl import threadpool_limits
@@ -446,6 +481,9 @@ def main():
         log("rows KV gather")
         rows.update(bench_kv_rows(20))
         log(f"  {rows['kv_gather_nvfp4_f16']} {rows['kv_gather_mxfp4_f16']}")
+        log("rows MXFP4 W4A4")
+        rows.update(bench_mx_rows(10))
+        log(f"  {rows['mx_w4a4_prefill_m512']} {rows['mx_w4a4_prefill_m2048']}")
 
     log("cpu baseline (oracle)")
     cpu = cpu_baseline(args.cpu_budget)

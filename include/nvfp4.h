@@ -273,6 +273,44 @@ nvfp4_status nvfp4_kv_gather(int format, int out_type, const uint8_t* codes, con
                              const int32_t* seq_lens, const int32_t* dst_start, int64_t seqs, uint16_t* out,
                              int64_t out_rows, void* stream);
 
+/*
+ * MXFP4 tensors and the W4A4 (FP4 x FP4) linear.  imp "docs/quantization.md",
+ * MXFP4 paragraph: the NVFP4 E2M1 nibble layout with a UE8M0 micro-scale per 32
+ * elements and no separate tensor scale, the format FP4 matrix cores take
+ * natively (an MXFP4 prefill runs at full FP4 rate); round-to-nearest MXFP4 is
+ * the page's quantizer.  Layout of a rows x k tensor (k a multiple of 32):
+ * packed [rows, k/2] (element 2j in the low nibble of byte j) and scales
+ * [rows, k/32], scale byte e meaning 2^(e - 127) (0xFF NaN).
+ *
+ * nvfp4_mx_quantize: BF16 [rows, k] -> MXFP4, round to nearest with the OCP
+ * MX shared scale: per block of 32, e = clamp(floor(log2(amax)) - 2 + 127, 0,
+ * 254) (0 for an all-zero block), code = sign | the E2M1 magnitude nearest to
+ * |v| / 2^(e - 127), ties to the even code, saturating at 6.  Bit for bit the
+ * same for weights and activations.  rows = 0 is a no-op.
+ * nvfp4_mx_dequant: MXFP4 -> BF16 [rows, k] (E2M1 * 2^(e - 127), RNE).
+ * nvfp4_mx_gemm: y [m, n] BF16 = xq [m, k] . wq [n, k]^T on the FP4 matrix
+ * cores (FP32 accumulation), from already quantized operands.
+ * nvfp4_mx_linear_w4a4: the same with x [m, k] BF16, quantized on the stream
+ * into a caller-owned workspace of nvfp4_mx_linear_w4a4_workspace_bytes(m, k)
+ * bytes (16-byte aligned, overlapping no argument) and then multiplied.
+ * Results are within 2e-3 of sum_k |xq * wq| of the exact product of the
+ * quantized operands, plus the BF16 output rounding.
+ * Errors: k % 32 != 0, n <= 0 or a size overflow is NVFP4_ERR_SHAPE (also a
+ * workspace below the size above); the GEMM needs k % 256 == 0 and
+ * m * k / 2, n * k / 2 < 2^32, else NVFP4_ERR_UNSUPPORTED; every pointer
+ * 16-byte aligned; outputs must not overlap inputs; m = 0 is a no-op.
+ */
+nvfp4_status nvfp4_mx_quantize(const uint16_t* w, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                               void* stream);
+nvfp4_status nvfp4_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k,
+                              uint16_t* out, void* stream);
+nvfp4_status nvfp4_mx_gemm(const uint8_t* xq, const uint8_t* xs, int64_t m, const uint8_t* wq, const uint8_t* ws,
+                           int64_t n, int64_t k, uint16_t* y, void* stream);
+int64_t nvfp4_mx_linear_w4a4_workspace_bytes(int64_t m, int64_t k);
+nvfp4_status nvfp4_mx_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* wq,
+                                  const uint8_t* ws, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,8 +25,9 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = ran
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
             "nvfp4_quantize_with_amax", "nvfp4_dequant", "nvfp4_linear", "nvfp4_linear_forced",
             "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
-            "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_linear_workspace_bytes",
-            "nvfp4_linear_grouped_workspace_bytes")
+            "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_mx_quantize", "nvfp4_mx_dequant", "nvfp4_mx_gemm",
+            "nvfp4_mx_linear_w4a4", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes",
+            "nvfp4_mx_linear_w4a4_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -63,6 +64,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_routed.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_grouped.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
         L.nvfp4_kv_gather.argtypes = [i32, i32, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, i64, vp, i64, vp]
+        L.nvfp4_mx_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.nvfp4_mx_dequant.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.nvfp4_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
+        L.nvfp4_mx_linear_w4a4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_mx_linear_w4a4_workspace_bytes.argtypes = [i64, i64]
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
@@ -363,4 +369,64 @@ def kv_gather(codes: torch.Tensor, scales: torch.Tensor, tscale: Optional[torch.
                                  hd, block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(),
                                  dst_start.data_ptr(), block_table.shape[0], out.data_ptr(), out.shape[0],
                                  _stream(out)), "nvfp4_kv_gather")
+    return out
+
+
+def mx_quantize(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """BF16 [rows, k] -> MXFP4 (packed uint8 [rows, k/2], UE8M0 scales uint8 [rows, k/32])."""
+    _need(w, torch.bfloat16, "w")
+    rows, k = w.shape
+    packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=w.device)
+    _check(lib().nvfp4_mx_quantize(w.data_ptr(), rows, k, packed.data_ptr(), scales.data_ptr(), _stream(w)),
+           "nvfp4_mx_quantize")
+    return packed, scales
+
+
+def mx_dequant(packed: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """MXFP4 -> BF16 [rows, k]."""
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    rows, k = packed.shape[0], packed.shape[1] * 2
+    if tuple(scales.shape) != (rows, k // 32):
+        raise ValueError("scales do not match packed")
+    out = torch.empty((rows, k), dtype=torch.bfloat16, device=packed.device)
+    _check(lib().nvfp4_mx_dequant(packed.data_ptr(), scales.data_ptr(), rows, k, out.data_ptr(), _stream(packed)),
+           "nvfp4_mx_dequant")
+    return out
+
+
+def mx_gemm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y [m, n] BF16 = Xq . Wq^T from MXFP4 operands (FP4 matrix cores)."""
+    for t, name in ((xq, "xq"), (xs, "xs"), (wq, "wq"), (ws, "ws")):
+        _need(t, torch.uint8, name)
+    m, k = xq.shape[0], xq.shape[1] * 2
+    n = wq.shape[0]
+    if wq.shape[1] * 2 != k or tuple(xs.shape) != (m, k // 32) or tuple(ws.shape) != (n, k // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=xq.device)
+    _check(lib().nvfp4_mx_gemm(xq.data_ptr(), xs.data_ptr(), m, wq.data_ptr(), ws.data_ptr(), n, k, out.data_ptr(),
+                               _stream(xq)), "nvfp4_mx_gemm")
+    return out
+
+
+def mx_linear_w4a4(x: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y [m, n] BF16 = MXFP4(X) . Wq^T: X quantized to MXFP4 on the stream, then the FP4 GEMM."""
+    _need(x, torch.bfloat16, "x")
+    _need(wq, torch.uint8, "wq")
+    _need(ws, torch.uint8, "ws")
+    m, k = x.shape
+    n = wq.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    need = lib().nvfp4_mx_linear_w4a4_workspace_bytes(m, k)
+    if need < 0:
+        raise ValueError(f"invalid shape m={m} k={k}")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_mx_linear_w4a4(x.data_ptr(), m, n, k, wq.data_ptr(), ws.data_ptr(), out.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream(x)), "nvfp4_mx_linear_w4a4")
     return out

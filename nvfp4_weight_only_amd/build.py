@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["nvfp4_abi.hip", "quant_kernels.hip", "gemv.hip", "gemm.hip", "skinny.hip", "prefill.hip", "grouped.hip", "kv_gather.hip"]
+SOURCES = ["nvfp4_abi.hip", "quant_kernels.hip", "gemv.hip", "gemm.hip", "skinny.hip", "prefill.hip", "grouped.hip", "kv_gather.hip", "mxfp4.hip"]
 
 
 def hipcc() -> str:

@@ -125,6 +125,17 @@ nvfp4_status validate_quantize_outputs(const uint16_t* w, const WeightSizes& ws,
   return NVFP4_OK;
 }
 
+// MXFP4 sizes of a rows x k tensor (k a multiple of 32; rows = 0 allowed).
+nvfp4_status mx_sizes(int64_t rows, int64_t k, WeightSizes* s) {
+  if (rows < 0 || k <= 0 || (k & 31) != 0) return NVFP4_ERR_SHAPE;
+  if (!mul_ok(rows, k, &s->elems) || !mul_ok(s->elems, 2, &s->w_bytes)) return NVFP4_ERR_SHAPE;
+  s->packed_bytes = s->elems / 2;
+  s->scale_bytes = s->elems / 32;
+  return NVFP4_OK;
+}
+
+int64_t mx_round16(int64_t b) { return (b + 15) / 16 * 16; }
+
 }  // namespace
 
 extern "C" {
@@ -383,6 +394,93 @@ nvfp4_status nvfp4_kv_gather(int format, int out_type, const uint8_t* codes, con
   nvfp4::launch_kv_gather(mx, out_type == NVFP4_OUT_BF16, codes, scales, tscale, num_blocks, block_size, row_elems,
                           block_table, max_blocks, seq_lens, dst_start, seqs, out, out_rows,
                           static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_mx_quantize(const uint16_t* w, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                               void* stream) {
+  WeightSizes ws;
+  nvfp4_status st = mx_sizes(rows, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (rows == 0) return NVFP4_OK;
+  if (!w || !packed || !scales) return NVFP4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
+  if (overlaps(packed, ws.packed_bytes, w, ws.w_bytes) || overlaps(scales, ws.scale_bytes, w, ws.w_bytes) ||
+      overlaps(packed, ws.packed_bytes, scales, ws.scale_bytes))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_mx_quantize(w, rows, k, packed, scales, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, uint16_t* out,
+                              void* stream) {
+  WeightSizes ws;
+  nvfp4_status st = mx_sizes(rows, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if (rows == 0) return NVFP4_OK;
+  if (!packed || !scales || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  if (overlaps(out, ws.w_bytes, packed, ws.packed_bytes) || overlaps(out, ws.w_bytes, scales, ws.scale_bytes))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_mx_dequant(packed, scales, rows, k, out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_mx_gemm(const uint8_t* xq, const uint8_t* xs, int64_t m, const uint8_t* wq, const uint8_t* ws,
+                           int64_t n, int64_t k, uint16_t* y, void* stream) {
+  WeightSizes xsz, wsz;
+  nvfp4_status st;
+  if ((st = mx_sizes(m, k, &xsz)) != NVFP4_OK || (st = mx_sizes(n, k, &wsz)) != NVFP4_OK) return st;
+  if (n == 0) return NVFP4_ERR_SHAPE;
+  int64_t ye, yb;
+  if (!mul_ok(m, n, &ye) || !mul_ok(ye, 2, &yb)) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!xq || !xs || !wq || !ws || !y) return NVFP4_ERR_NULL;
+  if (!nvfp4::mx_gemm_supported(m, n, k)) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return NVFP4_ERR_ALIGN;
+  if (overlaps(y, yb, xq, xsz.packed_bytes) || overlaps(y, yb, xs, xsz.scale_bytes) ||
+      overlaps(y, yb, wq, wsz.packed_bytes) || overlaps(y, yb, ws, wsz.scale_bytes))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_mx_gemm(xq, xs, m, wq, ws, n, k, y, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int64_t nvfp4_mx_linear_w4a4_workspace_bytes(int64_t m, int64_t k) {
+  WeightSizes xs;
+  if (mx_sizes(m, k, &xs) != NVFP4_OK || xs.packed_bytes > INT64_MAX / 4) return -1;
+  return mx_round16(xs.packed_bytes) + mx_round16(xs.scale_bytes);
+}
+
+nvfp4_status nvfp4_mx_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* wq,
+                                  const uint8_t* ws, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  WeightSizes xsz, wsz;
+  nvfp4_status st;
+  if ((st = mx_sizes(m, k, &xsz)) != NVFP4_OK || (st = mx_sizes(n, k, &wsz)) != NVFP4_OK) return st;
+  if (n == 0 || workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+  int64_t ye, yb;
+  if (!mul_ok(m, n, &ye) || !mul_ok(ye, 2, &yb) || xsz.packed_bytes > INT64_MAX / 4) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!x || !wq || !ws || !y || !workspace) return NVFP4_ERR_NULL;
+  const int64_t need = mx_round16(xsz.packed_bytes) + mx_round16(xsz.scale_bytes);
+  if (workspace_bytes < need) return NVFP4_ERR_SHAPE;
+  if (!nvfp4::mx_gemm_supported(m, n, k)) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(ws) || !aligned16(y) || !aligned16(workspace))
+    return NVFP4_ERR_ALIGN;
+  const void* ins[3] = {x, wq, ws};
+  const int64_t in_bytes[3] = {xsz.w_bytes, wsz.packed_bytes, wsz.scale_bytes};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(y, yb, ins[i], in_bytes[i]) || overlaps(workspace, need, ins[i], in_bytes[i])) return NVFP4_ERR_ALIAS;
+  if (overlaps(workspace, need, y, yb)) return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  uint8_t* xs = xq + mx_round16(xsz.packed_bytes);
+  nvfp4::launch_mx_quantize(x, m, k, xq, xs, s);
+  nvfp4::launch_mx_gemm(xq, xs, m, wq, ws, n, k, y, s);
   return launch_status();
 }
 

@@ -167,3 +167,24 @@ def test_kv_gather_validation(L):
     assert g(*args(codes=A + 8)) == B.ERR_ALIGN and g(*args(o=O + 8)) == B.ERR_ALIGN
     assert g(*args(o=A)) == B.ERR_ALIAS                           # out overlaps the codes
     assert g(*args(seqs=0)) == B.OK                               # no-op
+
+
+def test_mx_validation(L):
+    W = 0x70000000
+    q, d, g, lw, wb = L.nvfp4_mx_quantize, L.nvfp4_mx_dequant, L.nvfp4_mx_gemm, L.nvfp4_mx_linear_w4a4, \
+        L.nvfp4_mx_linear_w4a4_workspace_bytes
+    assert q(A, 4, 48, Bp, C, None) == B.ERR_SHAPE                      # k % 32 != 0
+    assert q(A, 0, 64, None, None, None) == B.OK                         # rows = 0 no-op
+    assert q(None, 4, 64, Bp, C, None) == B.ERR_NULL
+    assert q(A + 8, 4, 64, Bp, C, None) == B.ERR_ALIGN
+    assert q(A, 4, 64, A + 64, C, None) == B.ERR_ALIAS                   # packed overlaps w
+    assert d(Bp, C, 4, 64, Bp + 16, None) == B.ERR_ALIAS
+    assert g(A, Bp, 8, C, D, 64, 320, E, None) == B.ERR_UNSUPPORTED      # k % 256 != 0
+    assert g(A, Bp, 8, C, D, 0, 512, E, None) == B.ERR_SHAPE             # n = 0
+    assert g(A, Bp, 0, C, D, 64, 512, None, None) == B.OK                # m = 0 no-op
+    assert g(A, Bp, 8, C, D, 64, 512, A + 16, None) == B.ERR_ALIAS       # y overlaps xq
+    assert wb(8, 512) == 8 * 256 + 8 * 16 and wb(3, 32) == 48 + 16 and wb(8, 48) == -1
+    assert lw(A, 8, 64, 512, C, D, E, W, wb(8, 512) - 16, None) == B.ERR_SHAPE   # workspace too small
+    assert lw(A, 8, 64, 512, C, D, E, None, wb(8, 512), None) == B.ERR_NULL
+    assert lw(A, 8, 64, 512, C, D, E, A, wb(8, 512), None) == B.ERR_ALIAS       # workspace overlaps x
+    assert lw(A, 8, 64, 320, C, D, E, W, wb(8, 320), None) == B.ERR_UNSUPPORTED

@@ -676,3 +676,109 @@ def test_kv_gather_full_size_sampled(nv, fmt):
         rows = slice(int(dst[s]), int(dst[s] + lens[s]))
         assert np.array_equal(got[rows], want[rows]), f"sequence {s}"
         assert not np.any(got[int(dst[s] + lens[s]):int(dst[s] + lens[s]) + kw.chunk]), "chunk rows must stay zero"
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 tensors and the W4A4 GEMM (R17-R19).
+# ---------------------------------------------------------------------------
+from oracle import mxfp4_oracle as MXO  # noqa: E402
+
+
+def _mx_inputs(rows, k, seed, spread=16):
+    """BF16 rows whose 32-element blocks span 2^-spread .. 2^spread, with zero, negative-zero and subnormal
+    blocks and exact midpoints mixed in."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal((rows, k)).astype(np.float32)
+    f *= np.exp2(rng.integers(-spread, spread + 1, size=(rows, k // 32, 1))).repeat(32, axis=2).reshape(rows, k)
+    w = WL.bf16_bits_from_f32(f)
+    if rows >= 3 and k >= 64:
+        w[0, :32] = 0
+        w[1, 32:64] = 0x8000
+        w[2, :32] = WL.bf16_bits_from_f32((rng.random(32) * 2.0 ** -126).astype(np.float32))   # subnormal block
+        w[2, 32:44] = WL.bf16_bits_from_f32(np.array([4, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, 6.5, 7.9, -5, -.75],
+                                                     dtype=np.float32))
+    return w
+
+
+def _mx_dev(p, s):
+    return torch.from_numpy(np.ascontiguousarray(p)).cuda(), torch.from_numpy(np.ascontiguousarray(s)).cuda()
+
+
+@pytest.mark.parametrize("rows,k", [(64, 512), (37, 96), (1, 32), (300, 5120)])
+def test_mx_quantize_bit_exact(nv, rows, k):
+    w = _mx_inputs(rows, k, 3000 + k)
+    packed, scales = nv.mx_quantize(to_dev_bf16(w))
+    rp, rs = MXO.quantize(w)
+    assert np.array_equal(u8_host(scales), rs)
+    assert np.array_equal(u8_host(packed), rp)
+
+
+def test_mx_dequant_bit_exact(nv):
+    rng = np.random.default_rng(3100)
+    packed = rng.integers(0, 256, size=(40, 64), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(40, 4), dtype=np.uint8)
+    scales.flat[:5] = [0, 1, 127, 254, 255]
+    got = bf16_host(nv.mx_dequant(*_mx_dev(packed, scales)))
+    want = O.f32_to_bf16_rne(MXO.dequant_exact(packed, scales).astype(np.float32))
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    assert np.array_equal(np.isnan(f(got)), np.isnan(f(want)))
+    ok = ~np.isnan(f(want))
+    assert np.array_equal(got[ok], want[ok])
+
+
+MX_GEMM_SHAPES = [(1, 16, 256), (33, 300, 512), (256, 256, 256), (300, 520, 1024), (513, 257, 768), (40, 64, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", MX_GEMM_SHAPES)
+def test_mx_gemm(nv, m, n, k):
+    """FP4 x FP4 GEMM on operands the oracle quantized, against the exact product of their values."""
+    xp, xs = MXO.quantize(_mx_inputs(m, k, 3200 + m, spread=6))
+    wp, wsc = MXO.quantize(_mx_inputs(n, k, 3300 + n, spread=6))
+    y = bf16_host(nv.mx_gemm(*_mx_dev(xp, xs), *_mx_dev(wp, wsc)))
+    xq, wq = MXO.dequant_exact(xp, xs), MXO.dequant_exact(wp, wsc)
+    check_linear(y, xq @ wq.T, np.abs(xq) @ np.abs(wq).T, f"mx gemm {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(70, 300, 512), (2, 33, 256)])
+def test_mx_linear_w4a4(nv, m, n, k):
+    """BF16 X quantized on the GPU into the workspace (bit-exact against the oracle), then the GEMM."""
+    x = _mx_inputs(m, k, 3400 + m, spread=4)
+    wp, wsc = MXO.quantize(_mx_inputs(n, k, 3500 + n, spread=4))
+    ws = torch.zeros(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    y = bf16_host(nv.mx_linear_w4a4(to_dev_bf16(x), *_mx_dev(wp, wsc), workspace=ws))
+    rp, rs = MXO.quantize(x)
+    wsh = u8_host(ws)
+    pb = (m * k // 2 + 15) // 16 * 16
+    assert np.array_equal(wsh[:m * k // 2].reshape(m, k // 2), rp)
+    assert np.array_equal(wsh[pb:pb + m * k // 32].reshape(m, k // 32), rs)
+    y_ref, bound = MXO.linear_w4a4_ref(x, wp, wsc)
+    check_linear(y, y_ref, bound, f"mx w4a4 {m}x{n}x{k}")
+
+
+def test_mx_gemm_edges(nv):
+    from nvfp4_weight_only_amd import binding as B
+    xp, xs = _mx_dev(*MXO.quantize(_mx_inputs(4, 320, 3600)))
+    wp, wsc = _mx_dev(*MXO.quantize(_mx_inputs(8, 320, 3601)))
+    y = torch.empty((4, 8), dtype=torch.bfloat16, device="cuda")
+    assert nv.lib().nvfp4_mx_gemm(xp.data_ptr(), xs.data_ptr(), 4, wp.data_ptr(), wsc.data_ptr(), 8, 320,
+                                  y.data_ptr(), 0) == B.ERR_UNSUPPORTED          # k % 256 != 0
+    assert nv.lib().nvfp4_mx_gemm(xp.data_ptr(), xs.data_ptr(), 0, wp.data_ptr(), wsc.data_ptr(), 8, 320,
+                                  y.data_ptr(), 0) == B.OK                       # m = 0
+
+
+def test_mx_gemm_full_size_sampled(nv):
+    """The W4A4 prefill workload (M=2048, N=17408, K=5120), launched as timed; sampled rows and columns
+    against the oracle (MXFP4 blocks run along K, so a row's quantization does not depend on other rows)."""
+    wl = WL.WORKLOADS["prefill"]
+    m, n, k = 2048, wl.n, wl.k
+    w = wl.weight()
+    x = wl.activations(m)
+    wq, wsc = nv.mx_quantize(to_dev_bf16(w))
+    y = bf16_host(nv.mx_linear_w4a4(to_dev_bf16(x), wq, wsc))
+    rng = np.random.default_rng(3700)
+    rows = np.sort(rng.choice(m, 24, replace=False))
+    cols = np.sort(np.concatenate([rng.choice(n, 40, replace=False), [0, n - 1]]))
+    wp_s, ws_s = MXO.quantize(w[cols])
+    assert np.array_equal(u8_host(wq)[cols], wp_s) and np.array_equal(u8_host(wsc)[cols], ws_s)
+    y_ref, bound = MXO.linear_w4a4_ref(x[rows], wp_s, ws_s)
+    check_linear(y[np.ix_(rows, cols)], y_ref, bound, "mx w4a4 full size, sampled")
