@@ -260,54 +260,75 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(MxArgs p) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // Always issued (past the end: the last chunk again, into the stage nothing
+    // reads any more): loads under a branch would end in a full drain at the join.
+    const int cn = c + 1 < nchunks ? c + 1 : c;
+    issue(cn, (c + 1) & 1);
     uint32_t nsw[4], nsx[4];
-    if (c + 1 < nchunks) {
-      issue(c + 1, (c + 1) & 1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        nsw[t] = ws32[swo[t] + 2 * (c + 1)];
-        nsx[t] = xs32[sxo[t] + 2 * (c + 1)];
-      }
+    for (int t = 0; t < 4; ++t) {
+      nsw[t] = ws32[swo[t] + 2 * cn];
+      nsx[t] = xs32[sxo[t] + 2 * cn];
     }
     const MxStage& st = stage[c & 1];
     mx_kstep<0>(st, wn, wm, lane, sw, sx, acc);
     mx_kstep<1>(st, wn, wm, lane, sw, sx, acc);
     mx_kstep<2>(st, wn, wm, lane, sw, sx, acc);
     mx_kstep<3>(st, wn, wm, lane, sw, sx, acc);
-    if (c + 1 < nchunks) {
+    // The copy below uses the next chunk's scale loads: kept behind the MFMAs
+    // (hoisted above them, its wait would stall the chunk for a load latency).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        sw[t] = nsw[t];
-        sx[t] = nsx[t];
-      }
+    for (int t = 0; t < 4; ++t) {
+      sw[t] = nsw[t];
+      sx[t] = nsx[t];
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the repeat loads past the end have landed
 
-  // Epilogue: D of tile (i, j) is W-rows x X-rows: lane l holds X row
-  // 32 j + l % 32 and W rows 8 q + 4 h + 0..3 (items 4q .. 4q + 3), i.e. 4
-  // consecutive output columns of one output row.
+  // Epilogue: the BF16 tile goes through LDS (the stages, free now) so that
+  // the stores to Y are whole rows.  D of MFMA tile (i, j) is W-rows x X-rows:
+  // lane l holds X row 32 j + l % 32 and W rows 8 q + 4 h + 0..3 (items
+  // 4q .. 4q + 3), i.e. 4 consecutive output columns of one output row (one
+  // 8-byte LDS write).  LDS tile: [256 rows (m)][256 columns (n)] BF16, row
+  // stride 512 bytes, 16-byte pieces XOR-swizzled by the row's low 3 bits.
+  __syncthreads();
+  uint16_t* yt = reinterpret_cast<uint16_t*>(&stage[0]);
   const int l32 = lane & 31, h = lane >> 5;
-  const bool vec = (p.n & 3) == 0 && ((uintptr_t)p.y & 7) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t row = m0 + 128 * wm + 32 * j + l32;
-    if (row >= p.m) continue;
-    uint16_t* yr = p.y + row * p.n;
+    const int r = 128 * wm + 32 * j + l32;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + 128 * wn + 32 * i + 8 * q + 4 * h;
+        const int col = 128 * wn + 32 * i + 8 * q + 4 * h;            // multiple of 4
+        const int piece = (col >> 3) ^ (r & 7), half = (col >> 2) & 1;  // 16-byte piece, 8-byte half
         const f32x16_t& a = acc[i][j];
-        const uint32_t lo = mx_bf16x2(a[4 * q], a[4 * q + 1]), hi = mx_bf16x2(a[4 * q + 2], a[4 * q + 3]);
-        if (vec && col + 3 < p.n) {
-          *reinterpret_cast<uint2*>(yr + col) = make_uint2(lo, hi);
-        } else {
-          const uint16_t e4[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.n) yr[col + e] = e4[e];
-        }
+        *reinterpret_cast<uint2*>(yt + r * kMxTile + 8 * piece + 4 * half) =
+            make_uint2(mx_bf16x2(a[4 * q], a[4 * q + 1]), mx_bf16x2(a[4 * q + 2], a[4 * q + 3]));
       }
+  }
+  __syncthreads();
+  // 256 rows x 32 pieces of 16 bytes; thread t takes pieces t, t + 256, ...:
+  // consecutive threads write consecutive pieces of a row.  Nontemporal: Y is
+  // not read again by this kernel.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int64_t rows = p.m - m0 < kMxTile ? p.m - m0 : kMxTile;
+  const int64_t cols = p.n - n0 < kMxTile ? p.n - n0 : kMxTile;
+  const bool vec = (p.n & 7) == 0 && ((uintptr_t)p.y & 15) == 0;
+#pragma unroll 4
+  for (int pi = tid; pi < kMxTile * (kMxTile / 8); pi += 256) {
+    const int r = pi >> 5, c8 = 8 * (pi & 31);
+    if (r >= rows || c8 >= cols) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kMxTile + 8 * ((c8 >> 3) ^ (r & 7)));
+    uint16_t* dst = p.y + (m0 + r) * p.n + n0 + c8;
+    if (vec && c8 + 8 <= cols) {
+      __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst));
+    } else {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+      for (int t = 0; t < 8 && c8 + t < cols; ++t) dst[t] = e[t];
+    }
   }
 }
 
