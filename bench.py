@@ -352,10 +352,24 @@ def profile_run(what, launches):
     moe_prefill: nvfp4_linear_grouped on the grouped MoE prefill workload (2048 tokens, top-8 of 128
             experts of N=2048, K=4096), one call per launch (the sort kernel and the grouped GEMM);
     kv_gather: nvfp4_kv_gather (NVFP4 pages to FP16) on the chunked-prefill gather workload, cycling
-            through rotated cache + output copies.
+            through rotated cache + output copies;
+    mx_w4a4: nvfp4_mx_linear_w4a4 on the prefill workload at M=2048 (X quantized to MXFP4, then the FP4
+            GEMM), rotated MXFP4 weight copies.
     """
     torch.cuda.set_device(0)
-    if what == "kv_gather":
+    if what == "mx_w4a4":
+        wl = WL.WORKLOADS["prefill"]
+        m = 2048
+        wq, wsc = nv.mx_quantize(dev_bf16(wl.weight()))
+        rot = [(wq.clone(), wsc.clone()) for _ in range(copies_needed(wq.numel() + wsc.numel()))]
+        x = dev_bf16(wl.activations(m))
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            r = rot[i % len(rot)]
+            nv.mx_linear_w4a4(x, r[0], r[1], out=y, workspace=ws)
+    elif what == "kv_gather":
         kw = WL.KV_PREFILL
         table, lens, dst, nb, out_rows = kw.layout()
         td, ld, dd = (torch.from_numpy(a).cuda() for a in (table, lens, dst))
@@ -411,7 +425,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()
