@@ -296,7 +296,7 @@ nvfp4_status nvfp4_kv_gather(int format, int out_type, const uint8_t* codes, con
  * Results are within 2e-3 of sum_k |xq * wq| of the exact product of the
  * quantized operands, plus the BF16 output rounding.
  * Errors: k % 32 != 0, n <= 0 or a size overflow is NVFP4_ERR_SHAPE (also a
- * workspace below the size above); the GEMM needs k % 256 == 0 and
+ * workspace below the size above); the GEMM needs k % 128 == 0 and
  * m * k / 2, n * k / 2 < 2^32, else NVFP4_ERR_UNSUPPORTED; every pointer
  * 16-byte aligned; outputs must not overlap inputs; m = 0 is a no-op.
  */

@@ -52,7 +52,9 @@ def build(verbose: bool = False) -> str:
         subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
         objs.append(obj)
     tmp = LIB_PATH + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: every symbol the library uses must resolve at link time (a missing
+    # launcher would otherwise surface only when the library is loaded).
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -71,7 +71,7 @@ void launch_kv_gather(bool mx, bool bf16, const uint8_t* codes, const uint8_t* s
 
 // MXFP4 (UE8M0 scale per 32, no tensor scale).  Quantizer and dequantizer
 // over rows x k (k a multiple of 32); W4A4 GEMM y [m, n] = xq . wq^T for k a
-// multiple of 256 and m * k / 2, n * k / 2 < 2^32 (mx_gemm_supported).
+// multiple of 128 and m * k / 2, n * k / 2 < 2^32 (mx_gemm_supported).
 void launch_mx_quantize(const uint16_t* w, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales, hipStream_t s);
 void launch_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, uint16_t* out,
                        hipStream_t s);

@@ -15,17 +15,19 @@
 // consecutive K elements (16 bytes), with the scale byte of those 32 chosen by
 // opsel from a 32-bit register; the output is the usual 32 x 32 FP32 tile.
 // The weights are the A operand, so a lane ends up with 4 consecutive output
-// columns of one row.  A workgroup (4 wavefronts) computes a 256 (n) x 256 (m)
-// tile, each wavefront 128 x 128 (4 x 4 MFMA tiles, all 256 AGPRs).  Per K
-// chunk of 256 both operand tiles (256 rows x 128 bytes each) move from global
-// memory to LDS with global_load_lds_dwordx4, double-buffered (128 KB), in an
-// XOR-swizzled layout that makes every fragment read conflict-free.
+// columns of one row.  A workgroup (8 wavefronts, two per SIMD so that one
+// issues MFMAs while the other waits) computes a 256 (n) x 256 (m) tile, each
+// wavefront 128 (n) x 64 (m) (4 x 2 MFMA tiles, 128 accumulator registers).
+// Per K chunk of 128 both operand tiles (256 rows x 64 bytes each) and their
+// scale words (one 32-bit word per row: the chunk's four scale bytes) move from
+// global memory to LDS with global_load_lds_dwordx4 / _dword, in a ring of four
+// stages (three chunks in flight), in an XOR-swizzled layout that makes every
+// fragment read conflict-free.
 //
-// K order inside a chunk: lane half h in MFMA K-step s (0..3) takes elements
-// [128 h + 32 s, 128 h + 32 s + 32) of the chunk, i.e. 32-element block 4h + s,
-// for both operands (the dot product does not depend on the order of its
-// terms).  A lane's four scale bytes of a chunk are then one aligned 32-bit
-// word (blocks 4h .. 4h + 3), and K-step s selects byte s of it.
+// K order inside a chunk: lane half h in MFMA K-step s (0, 1) takes the
+// chunk's 32-element block 2s + h in both operands; its scale byte is byte
+// 2s + h of the row's word, i.e. byte 2s (opsel) once the word is shifted
+// right by 8h.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -45,42 +47,38 @@ __device__ __forceinline__ uint32_t mx_mag_code(float q) {
          (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) + (uint32_t)(q > 5.0f);
 }
 
-// One thread per 32-element block (64 input bytes in, 16 code bytes and one
-// scale byte out).
+// Four lanes per 32-element block: lane q of the four loads elements
+// [8q, 8q + 8) (16 bytes; a wavefront's load covers 1 KB of consecutive input),
+// the block maximum comes from two lane exchanges, and lane q writes the code
+// word of its 8 elements (a wavefront's store covers 256 consecutive bytes);
+// lane 0 of the four writes the scale byte.
 __global__ void __launch_bounds__(256) mx_quantize_kernel(const uint4* __restrict__ w, int64_t blocks,
-                                                          uint4* __restrict__ packed, uint8_t* __restrict__ scales) {
+                                                          uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  // groups is a multiple of 4 and the four lanes of a block are consecutive, so
+  // they always run the same iterations and the exchanges see four live lanes.
+  const int64_t groups = blocks * 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < blocks; b += stride) {
-    uint32_t v[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 q = w[4 * b + i];
-      v[4 * i] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
-    }
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const uint4 q = w[g];
+    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
     uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = max(amax, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+    for (int i = 0; i < 4; ++i) amax = max(amax, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
     // floor(log2(amax)) = exponent field - 127 for a normal amax; E = that - 2 + 127.
     const int ef = (int)(amax >> 7);
     const int e = ef <= 2 ? 0 : (ef - 2 > 254 ? 254 : ef - 2);
     const float inv = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), a normal float for e in [0, 252]
-    uint32_t out[4];
+    uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t bits = (v[4 * j + t / 2] >> (16 * (t & 1))) & 0xFFFFu;
-        const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;   // exact: a power-of-two scaling
-        word |= (((bits >> 15) << 3) | mx_mag_code(q)) << (4 * t);
-      }
-      out[j] = word;
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t bits = (v[t / 2] >> (16 * (t & 1))) & 0xFFFFu;
+      const float r = __uint_as_float((bits & 0x7FFFu) << 16) * inv;   // exact: a power-of-two scaling
+      word |= (((bits >> 15) << 3) | mx_mag_code(r)) << (4 * t);
     }
-    packed[b] = make_uint4(out[0], out[1], out[2], out[3]);
-    scales[b] = (uint8_t)e;
+    packed[g] = word;
+    if ((g & 3) == 0) scales[g >> 2] = (uint8_t)e;
   }
 }
 
@@ -120,12 +118,19 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) const void mx_lds_t;
 
 constexpr int kMxTile = 256;     // rows of W (n) and of X (m) per workgroup
-constexpr int kMxKC = 256;       // K elements per chunk (128 bytes per row)
-constexpr int kMxRowPieces = 8;  // 16-byte pieces per row and chunk
+constexpr int kMxKC = 128;       // K elements per chunk (64 bytes per row, 4 scale bytes per row)
+constexpr int kMxRowPieces = 4;  // 16-byte pieces per row and chunk
+constexpr int kMxStages = 4;     // the chunk in use and three in flight
 
+// One chunk of both operands and their scale words.  Row r's logical piece p
+// (elements [32 p, 32 p + 32) of the chunk) sits at physical piece
+// p ^ ((r >> 1) & 3): a 128-bit read by 8 consecutive rows at one logical piece
+// then covers all 32 banks.
 struct MxStage {
-  uint4 w[kMxTile * kMxRowPieces];  // 32 KB
-  uint4 x[kMxTile * kMxRowPieces];  // 32 KB
+  uint4 w[kMxTile * kMxRowPieces];  // 16 KB
+  uint4 x[kMxTile * kMxRowPieces];  // 16 KB
+  uint32_t sw[kMxTile];             // the chunk's 4 scale bytes of each weight row
+  uint32_t sx[kMxTile];             // ... of each activation row
 };
 
 struct MxArgs {
@@ -143,22 +148,40 @@ __device__ __forceinline__ uint32_t mx_lds_addr(const U* p) {
   return (uint32_t)(uintptr_t)(mx_lds_t*)p;
 }
 
-// One global_load_lds_dwordx4: 16 bytes per lane from base + off (uniform
-// 64-bit base, per-lane 32-bit offset) to LDS lds + 16 * lane.  No register
-// result; the kernel waits for it with an explicit vmcnt wait.
+__device__ __forceinline__ uint64_t mx_uniform_ptr(const void* base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+}
+
+// One global_load_lds_dwordx4 (16 bytes per lane) / global_load_lds_dword (4
+// bytes per lane) from base + off (uniform 64-bit base, per-lane 32-bit offset)
+// to LDS lds + 16 * lane / lds + 4 * lane.  No register result; the kernel
+// waits for them with explicit vmcnt waits (they are its only global loads in
+// the K loop).
 __device__ __forceinline__ void mx_lds_dma16(const void* base, uint32_t off, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(bs) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(mx_uniform_ptr(base))
+               : "memory");
+}
+__device__ __forceinline__ void mx_lds_dma4(const void* base, uint32_t off, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(off), "s"(mx_uniform_ptr(base))
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void mx_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 __device__ __forceinline__ i32x8_t mx_frag(uint4 v) { return i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
 
-template <int S>
+template <int OPSEL>
 __device__ __forceinline__ void mx_mfma(f32x16_t& acc, const uint4& a, const uint4& b, uint32_t sa, uint32_t sb) {
-  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx_frag(a), mx_frag(b), acc, 4, 4, S, (int)sa, S, (int)sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx_frag(a), mx_frag(b), acc, 4, 4, OPSEL, (int)sa, OPSEL,
+                                                        (int)sb);
 }
 
 __device__ __forceinline__ uint32_t mx_bf16x2(float a, float b) {
@@ -167,30 +190,43 @@ __device__ __forceinline__ uint32_t mx_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// The four K-steps of one chunk on stage `st`: fragments of row r, logical
-// piece 4h + s at physical piece (4h + s) ^ (r & 7).
+// MFMA K-step S (0, 1) of a chunk: lane half h takes the chunk's 32-element
+// block 2S + h in both operands (logical piece 2S + h); its scale byte is
+// byte 2S + h of the row's word, i.e. byte 2S once the word is shifted right
+// by 8h.
 template <int S>
 __device__ __forceinline__ void mx_kstep(const MxStage& st, int wn, int wm, int lane, const uint32_t (&sw)[4],
-                                         const uint32_t (&sx)[4], f32x16_t (&acc)[4][4]) {
+                                         const uint32_t (&sx)[2], f32x16_t (&acc)[4][2]) {
   const int l32 = lane & 31, h = lane >> 5;
-  uint4 a[4], b[4];
+  uint4 a[4], b[2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int rw = 128 * wn + 32 * t + l32, rx = 128 * wm + 32 * t + l32;
-    a[t] = st.w[rw * kMxRowPieces + ((4 * h + S) ^ (rw & 7))];
-    b[t] = st.x[rx * kMxRowPieces + ((4 * h + S) ^ (rx & 7))];
+    const int rw = 128 * wn + 32 * t + l32;
+    a[t] = st.w[rw * kMxRowPieces + ((2 * S + h) ^ ((rw >> 1) & 3))];
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int rx = 64 * wm + 32 * t + l32;
+    b[t] = st.x[rx * kMxRowPieces + ((2 * S + h) ^ ((rx >> 1) & 3))];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx_mfma<S>(acc[i][j], a[i], b[j], sw[i], sx[j]);
+    for (int j = 0; j < 2; ++j) mx_mfma<2 * S>(acc[i][j], a[i], b[j], sw[i], sx[j]);
 }
 
-__global__ void __launch_bounds__(256) mx_gemm_kernel(MxArgs p) {
-  __shared__ MxStage stage[2];
+// Per wavefront and chunk: 2 + 2 operand DMA instructions (16 rows x 64 bytes
+// each) and 1 scale-word instruction (64 rows x 4 bytes; wavefronts 0-3 the
+// weights', 4-7 the activations'), 5 in all.  Chunks 0..2 are issued before the
+// loop and chunk c + 3 at the top of chunk c (past the end: the last chunk
+// again, into the stage chunk c - 1 used, which nothing reads any more), so at
+// the top of chunk c exactly the newest 10 loads (chunks c + 1, c + 2) may
+// still be in flight: vmcnt(10).
+__global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
+  __shared__ MxStage stage[kMxStages];  // 4 x 34 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = w & 1, wm = w >> 1;
+  const int wn = w & 1, wm = w >> 1;  // wm 0..3: 64-row quarters of the m tile
   // Workgroups go to the 8 XCDs round-robin by id; when the count allows,
   // consecutive ids of one XCD take all m tiles of consecutive n tiles, so a
   // weight tile is fetched into that XCD's L2 once.
@@ -200,89 +236,69 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(MxArgs p) {
   const int nt = id / p.m_tiles, mt = id % p.m_tiles;
   const int64_t n0 = (int64_t)nt * kMxTile, m0 = (int64_t)mt * kMxTile;
   const int64_t kh = p.k >> 1, ks = p.k >> 5;
-  const int nchunks = (int)(p.k / kMxKC);
+  const int nchunks = (int)(p.k / kMxKC), last = nchunks - 1;
 
-  // DMA sources: instruction i (of 32 per operand) fills LDS rows 8i .. 8i + 7;
-  // this wavefront issues i = w + 4j.  Lane l: row 8i + l / 8, physical piece
-  // l % 8, which holds logical piece (l % 8) ^ (row & 7).  Rows past M or N
-  // repeat the last valid row (their results are not stored).
-  uint32_t offw[8], offx[8];
+  // Operand DMA: instruction i (of 16 per operand) fills LDS rows 16i .. 16i + 15;
+  // this wavefront issues i = w + 8j.  Lane l: row 16i + l / 4, physical piece
+  // l % 4, holding logical piece (l % 4) ^ ((row >> 1) & 3).  Rows past N or M
+  // repeat the last row (their results are not stored).
+  uint32_t offw[2], offx[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * (w + 4 * j) + (lane >> 3), q = lane & 7, pc = q ^ (r & 7);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (w + 8 * j) + (lane >> 2), pc = (lane & 3) ^ ((r >> 1) & 3);
     const int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1, gm = m0 + r < p.m ? m0 + r : p.m - 1;
     offw[j] = (uint32_t)(gn * kh + 16 * pc);
     offx[j] = (uint32_t)(gm * kh + 16 * pc);
   }
-  // Scale words: tile t of this wavefront, row 32 t + lane % 32, blocks 4h .. 4h + 3 of the chunk, as
-  // 32-bit word offsets from the scale arrays (a scale array is below 2^28 words when its packed array
-  // is below 2^32 bytes).
-  const uint32_t* ws32 = reinterpret_cast<const uint32_t*>(p.ws);
-  const uint32_t* xs32 = reinterpret_cast<const uint32_t*>(p.xs);
-  uint32_t swo[4], sxo[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t rn = n0 + 128 * wn + 32 * t + (lane & 31), rm = m0 + 128 * wm + 32 * t + (lane & 31);
-    swo[t] = (uint32_t)((rn < p.n ? rn : p.n - 1) * (ks >> 2) + (lane >> 5));
-    sxo[t] = (uint32_t)((rm < p.m ? rm : p.m - 1) * (ks >> 2) + (lane >> 5));
-  }
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  // Scale words: wavefront w fills rows 64 (w % 4) .. + 63 of the weights (w < 4)
+  // or of the activations (w >= 4).
+  const int w4 = w & 3;
+  const int64_t srn = n0 + 64 * w4 + lane < p.n ? n0 + 64 * w4 + lane : p.n - 1;
+  const int64_t srm = m0 + 64 * w4 + lane < p.m ? m0 + 64 * w4 + lane : p.m - 1;
+  const uint32_t soff = (uint32_t)((w < 4 ? srn : srm) * ks);
 
   auto issue = [&](int c, int sidx) {
     const uint8_t* bw = p.wq + (int64_t)c * (kMxKC / 2);
     const uint8_t* bx = p.xq + (int64_t)c * (kMxKC / 2);
-    const uint32_t lw = mx_lds_addr(&stage[sidx].w[0]), lx = mx_lds_addr(&stage[sidx].x[0]);
+    MxStage& sg = stage[sidx];
+    const uint32_t lw = mx_lds_addr(&sg.w[0]), lx = mx_lds_addr(&sg.x[0]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      mx_lds_dma16(bw, offw[j], lw + 1024 * (w + 4 * j));
-      mx_lds_dma16(bx, offx[j], lx + 1024 * (w + 4 * j));
+    for (int j = 0; j < 2; ++j) {
+      mx_lds_dma16(bw, offw[j], lw + 1024 * (w + 8 * j));
+      mx_lds_dma16(bx, offx[j], lx + 1024 * (w + 8 * j));
     }
+    if (w < 4) mx_lds_dma4(p.ws + 4 * c, soff, mx_lds_addr(&sg.sw[64 * w4]));
+    else mx_lds_dma4(p.xs + 4 * c, soff, mx_lds_addr(&sg.sx[64 * w4]));
   };
 
-  uint32_t sw[4], sx[4];
-  issue(0, 0);
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    sw[t] = ws32[swo[t]];
-    sx[t] = xs32[sxo[t]];
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  issue(0, 0);
+  issue(last < 1 ? last : 1, 1);
+  issue(last < 2 ? last : 2, 2);
+  const int l32 = lane & 31, h = lane >> 5;
   for (int c = 0; c < nchunks; ++c) {
-    // Chunk c's operands (and scale words) have landed in every wavefront;
-    // after the barrier every wavefront is done with chunk c - 1's stage.
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    // This wavefront's share of chunk c has landed; after the barrier every
+    // wavefront's has, and every wavefront is done with chunk c - 1's stage.
+    mx_wait_vmcnt<10>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // Always issued (past the end: the last chunk again, into the stage nothing
-    // reads any more): loads under a branch would end in a full drain at the join.
-    const int cn = c + 1 < nchunks ? c + 1 : c;
-    issue(cn, (c + 1) & 1);
-    uint32_t nsw[4], nsx[4];
+    issue(c + 3 <= last ? c + 3 : last, (c + 3) % kMxStages);
+    const MxStage& st = stage[c % kMxStages];
+    uint32_t sw[4], sx[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      nsw[t] = ws32[swo[t] + 2 * cn];
-      nsx[t] = xs32[sxo[t] + 2 * cn];
-    }
-    const MxStage& st = stage[c & 1];
+    for (int t = 0; t < 4; ++t) sw[t] = st.sw[128 * wn + 32 * t + l32] >> (8 * h);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sx[t] = st.sx[64 * wm + 32 * t + l32] >> (8 * h);
     mx_kstep<0>(st, wn, wm, lane, sw, sx, acc);
     mx_kstep<1>(st, wn, wm, lane, sw, sx, acc);
-    mx_kstep<2>(st, wn, wm, lane, sw, sx, acc);
-    mx_kstep<3>(st, wn, wm, lane, sw, sx, acc);
-    // The copy below uses the next chunk's scale loads: kept behind the MFMAs
-    // (hoisted above them, its wait would stall the chunk for a load latency).
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sw[t] = nsw[t];
-      sx[t] = nsx[t];
-    }
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the repeat loads past the end have landed
 
@@ -294,10 +310,9 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(MxArgs p) {
   // stride 512 bytes, 16-byte pieces XOR-swizzled by the row's low 3 bits.
   __syncthreads();
   uint16_t* yt = reinterpret_cast<uint16_t*>(&stage[0]);
-  const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 128 * wm + 32 * j + l32;
+  for (int j = 0; j < 2; ++j) {
+    const int r = 64 * wm + 32 * j + l32;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -318,7 +333,7 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(MxArgs p) {
   const int64_t cols = p.n - n0 < kMxTile ? p.n - n0 : kMxTile;
   const bool vec = (p.n & 7) == 0 && ((uintptr_t)p.y & 15) == 0;
 #pragma unroll 4
-  for (int pi = tid; pi < kMxTile * (kMxTile / 8); pi += 256) {
+  for (int pi = tid; pi < kMxTile * (kMxTile / 8); pi += 512) {
     const int r = pi >> 5, c8 = 8 * (pi & 31);
     if (r >= rows || c8 >= cols) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kMxTile + 8 * ((c8 >> 3) ^ (r & 7)));
@@ -341,8 +356,8 @@ unsigned mx_grid(int64_t items) {
 
 void launch_mx_quantize(const uint16_t* w, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales, hipStream_t s) {
   const int64_t blocks = rows * (k / 32);
-  mx_quantize_kernel<<<mx_grid(blocks), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), blocks,
-                                                     reinterpret_cast<uint4*>(packed), scales);
+  mx_quantize_kernel<<<mx_grid(4 * blocks), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), blocks,
+                                                         reinterpret_cast<uint32_t*>(packed), scales);
 }
 
 void launch_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, uint16_t* out,
@@ -361,7 +376,7 @@ void launch_mx_gemm(const uint8_t* xq, const uint8_t* xs, int64_t m, const uint8
                     int64_t k, uint16_t* y, hipStream_t s) {
   const int64_t n_tiles = (n + kMxTile - 1) / kMxTile, m_tiles = (m + kMxTile - 1) / kMxTile;
   const MxArgs a{xq, xs, wq, ws, y, m, n, k, (int)n_tiles, (int)m_tiles};
-  mx_gemm_kernel<<<dim3((unsigned)(n_tiles * m_tiles)), 256, 0, s>>>(a);
+  mx_gemm_kernel<<<dim3((unsigned)(n_tiles * m_tiles)), 512, 0, s>>>(a);
 }
 
 }  // namespace nvfp4

@@ -726,7 +726,8 @@ def test_mx_dequant_bit_exact(nv):
     assert np.array_equal(got[ok], want[ok])
 
 
-MX_GEMM_SHAPES = [(1, 16, 256), (33, 300, 512), (256, 256, 256), (300, 520, 1024), (513, 257, 768), (40, 64, 5120)]
+MX_GEMM_SHAPES = [(1, 16, 256), (33, 300, 512), (256, 256, 256), (300, 520, 1024), (513, 257, 768), (40, 64, 5120),
+                  (48, 200, 384), (7, 33, 128)]
 
 
 @pytest.mark.parametrize("m,n,k", MX_GEMM_SHAPES)
