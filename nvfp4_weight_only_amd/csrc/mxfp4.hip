@@ -54,31 +54,42 @@ __device__ __forceinline__ uint32_t mx_mag_code(float q) {
 // lane 0 of the four writes the scale byte.
 __global__ void __launch_bounds__(256) mx_quantize_kernel(const uint4* __restrict__ w, int64_t blocks,
                                                           uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
-  // groups is a multiple of 4 and the four lanes of a block are consecutive, so
-  // they always run the same iterations and the exchanges see four live lanes.
+  // groups and the stride are multiples of 4 and the four lanes of a block are
+  // consecutive, so they always take the same branches and the exchanges see
+  // four live lanes.  Each thread loads four groups before it converts any.
   const int64_t groups = blocks * 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
-    const uint4 q = w[g];
-    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
-    uint32_t amax = 0;
+  for (int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g0 < groups; g0 += 4 * stride) {
+    uint4 q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax = max(amax, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
-    // floor(log2(amax)) = exponent field - 127 for a normal amax; E = that - 2 + 127.
-    const int ef = (int)(amax >> 7);
-    const int e = ef <= 2 ? 0 : (ef - 2 > 254 ? 254 : ef - 2);
-    const float inv = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), a normal float for e in [0, 252]
-    uint32_t word = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t bits = (v[t / 2] >> (16 * (t & 1))) & 0xFFFFu;
-      const float r = __uint_as_float((bits & 0x7FFFu) << 16) * inv;   // exact: a power-of-two scaling
-      word |= (((bits >> 15) << 3) | mx_mag_code(r)) << (4 * t);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t g = g0 + u * stride;
+      q[u] = g < groups ? w[g] : make_uint4(0, 0, 0, 0);
     }
-    packed[g] = word;
-    if ((g & 3) == 0) scales[g >> 2] = (uint8_t)e;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t g = g0 + u * stride;
+      if (g >= groups) continue;
+      const uint32_t v[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = max(amax, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+      // floor(log2(amax)) = exponent field - 127 for a normal amax; E = that - 2 + 127.
+      const int ef = (int)(amax >> 7);
+      const int e = ef <= 2 ? 0 : (ef - 2 > 254 ? 254 : ef - 2);
+      const float inv = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), normal for e in [0, 252]
+      uint32_t word = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t bits = (v[t / 2] >> (16 * (t & 1))) & 0xFFFFu;
+        const float r = __uint_as_float((bits & 0x7FFFu) << 16) * inv;   // exact: a power-of-two scaling
+        word |= (((bits >> 15) << 3) | mx_mag_code(r)) << (4 * t);
+      }
+      packed[g] = word;
+      if ((g & 3) == 0) scales[g >> 2] = (uint8_t)e;
+    }
   }
 }
 
@@ -356,7 +367,7 @@ unsigned mx_grid(int64_t items) {
 
 void launch_mx_quantize(const uint16_t* w, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales, hipStream_t s) {
   const int64_t blocks = rows * (k / 32);
-  mx_quantize_kernel<<<mx_grid(4 * blocks), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), blocks,
+  mx_quantize_kernel<<<mx_grid(blocks), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), blocks,
                                                          reinterpret_cast<uint32_t*>(packed), scales);
 }
 
