@@ -205,14 +205,14 @@ __device__ __forceinline__ uint32_t mx_bf16x2(float a, float b) {
 // block 2S + h in both operands (logical piece 2S + h); its scale byte is
 // byte 2S + h of the row's word, i.e. byte 2S once the word is shifted right
 // by 8h.
-template <int S>
-__device__ __forceinline__ void mx_kstep(const MxStage& st, int wn, int wm, int lane, const uint32_t (&sw)[4],
-                                         const uint32_t (&sx)[2], f32x16_t (&acc)[4][2]) {
+template <int S, int NT>
+__device__ __forceinline__ void mx_kstep(const MxStage& st, int wn, int wm, int lane, const uint32_t (&sw)[NT],
+                                         const uint32_t (&sx)[2], f32x16_t (&acc)[NT][2]) {
   const int l32 = lane & 31, h = lane >> 5;
-  uint4 a[4], b[2];
+  uint4 a[NT], b[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int rw = 128 * wn + 32 * t + l32;
+  for (int t = 0; t < NT; ++t) {
+    const int rw = 32 * NT * wn + 32 * t + l32;
     a[t] = st.w[rw * kMxRowPieces + ((2 * S + h) ^ ((rw >> 1) & 3))];
   }
 #pragma unroll
@@ -221,7 +221,7 @@ __device__ __forceinline__ void mx_kstep(const MxStage& st, int wn, int wm, int 
     b[t] = st.x[rx * kMxRowPieces + ((2 * S + h) ^ ((rx >> 1) & 3))];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) mx_mfma<2 * S>(acc[i][j], a[i], b[j], sw[i], sx[j]);
 }
@@ -233,7 +233,13 @@ __device__ __forceinline__ void mx_kstep(const MxStage& st, int wn, int wm, int 
 // again, into the stage chunk c - 1 used, which nothing reads any more), so at
 // the top of chunk c exactly the newest 10 loads (chunks c + 1, c + 2) may
 // still be in flight: vmcnt(10).
+// TN: weight rows per workgroup tile, 256 or 192 (each wavefront TN / 2 of
+// them: NT = TN / 64 MFMA tiles); the host picks the one whose grid fills the
+// CUs best.  LDS stages always hold 256 weight rows; rows past TN repeat the
+// tile's last row and are not used.
+template <int TN>
 __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
+  constexpr int NT = TN / 64;
   __shared__ MxStage stage[kMxStages];  // 4 x 34 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,7 +251,7 @@ __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
   int id = (int)blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   const int nt = id / p.m_tiles, mt = id % p.m_tiles;
-  const int64_t n0 = (int64_t)nt * kMxTile, m0 = (int64_t)mt * kMxTile;
+  const int64_t n0 = (int64_t)nt * TN, m0 = (int64_t)mt * kMxTile;
   const int64_t kh = p.k >> 1, ks = p.k >> 5;
   const int nchunks = (int)(p.k / kMxKC), last = nchunks - 1;
 
@@ -257,14 +263,16 @@ __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 16 * (w + 8 * j) + (lane >> 2), pc = (lane & 3) ^ ((r >> 1) & 3);
-    const int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1, gm = m0 + r < p.m ? m0 + r : p.m - 1;
+    const int rn = r < TN ? r : TN - 1;
+    const int64_t gn = n0 + rn < p.n ? n0 + rn : p.n - 1, gm = m0 + r < p.m ? m0 + r : p.m - 1;
     offw[j] = (uint32_t)(gn * kh + 16 * pc);
     offx[j] = (uint32_t)(gm * kh + 16 * pc);
   }
   // Scale words: wavefront w fills rows 64 (w % 4) .. + 63 of the weights (w < 4)
   // or of the activations (w >= 4).
   const int w4 = w & 3;
-  const int64_t srn = n0 + 64 * w4 + lane < p.n ? n0 + 64 * w4 + lane : p.n - 1;
+  const int srt = 64 * w4 + lane < TN ? 64 * w4 + lane : TN - 1;
+  const int64_t srn = n0 + srt < p.n ? n0 + srt : p.n - 1;
   const int64_t srm = m0 + 64 * w4 + lane < p.m ? m0 + 64 * w4 + lane : p.m - 1;
   const uint32_t soff = (uint32_t)((w < 4 ? srn : srm) * ks);
 
@@ -282,9 +290,9 @@ __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
     else mx_lds_dma4(p.xs + 4 * c, soff, mx_lds_addr(&sg.sx[64 * w4]));
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[NT][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -303,13 +311,13 @@ __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
     asm volatile("" ::: "memory");
     issue(c + 3 <= last ? c + 3 : last, (c + 3) % kMxStages);
     const MxStage& st = stage[c % kMxStages];
-    uint32_t sw[4], sx[2];
+    uint32_t sw[NT], sx[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sw[t] = st.sw[128 * wn + 32 * t + l32] >> (8 * h);
+    for (int t = 0; t < NT; ++t) sw[t] = st.sw[32 * NT * wn + 32 * t + l32] >> (8 * h);
 #pragma unroll
     for (int t = 0; t < 2; ++t) sx[t] = st.sx[64 * wm + 32 * t + l32] >> (8 * h);
-    mx_kstep<0>(st, wn, wm, lane, sw, sx, acc);
-    mx_kstep<1>(st, wn, wm, lane, sw, sx, acc);
+    mx_kstep<0, NT>(st, wn, wm, lane, sw, sx, acc);
+    mx_kstep<1, NT>(st, wn, wm, lane, sw, sx, acc);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the repeat loads past the end have landed
 
@@ -317,37 +325,37 @@ __global__ void __launch_bounds__(512) mx_gemm_kernel(MxArgs p) {
   // the stores to Y are whole rows.  D of MFMA tile (i, j) is W-rows x X-rows:
   // lane l holds X row 32 j + l % 32 and W rows 8 q + 4 h + 0..3 (items
   // 4q .. 4q + 3), i.e. 4 consecutive output columns of one output row (one
-  // 8-byte LDS write).  LDS tile: [256 rows (m)][256 columns (n)] BF16, row
-  // stride 512 bytes, 16-byte pieces XOR-swizzled by the row's low 3 bits.
+  // 8-byte LDS write).  LDS tile: [256 rows (m)][TN columns (n)] BF16, 16-byte
+  // pieces XOR-swizzled by the row's low 3 bits (within aligned groups of 8).
   __syncthreads();
   uint16_t* yt = reinterpret_cast<uint16_t*>(&stage[0]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 64 * wm + 32 * j + l32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = 128 * wn + 32 * i + 8 * q + 4 * h;            // multiple of 4
+        const int col = 32 * NT * wn + 32 * i + 8 * q + 4 * h;         // multiple of 4
         const int piece = (col >> 3) ^ (r & 7), half = (col >> 2) & 1;  // 16-byte piece, 8-byte half
         const f32x16_t& a = acc[i][j];
-        *reinterpret_cast<uint2*>(yt + r * kMxTile + 8 * piece + 4 * half) =
+        *reinterpret_cast<uint2*>(yt + r * TN + 8 * piece + 4 * half) =
             make_uint2(mx_bf16x2(a[4 * q], a[4 * q + 1]), mx_bf16x2(a[4 * q + 2], a[4 * q + 3]));
       }
   }
   __syncthreads();
-  // 256 rows x 32 pieces of 16 bytes; thread t takes pieces t, t + 256, ...:
+  // 256 rows x TN / 8 pieces of 16 bytes; thread t takes pieces t, t + 512, ...:
   // consecutive threads write consecutive pieces of a row.  Nontemporal: Y is
   // not read again by this kernel.
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const int64_t rows = p.m - m0 < kMxTile ? p.m - m0 : kMxTile;
-  const int64_t cols = p.n - n0 < kMxTile ? p.n - n0 : kMxTile;
+  const int64_t cols = p.n - n0 < TN ? p.n - n0 : TN;
   const bool vec = (p.n & 7) == 0 && ((uintptr_t)p.y & 15) == 0;
 #pragma unroll 4
-  for (int pi = tid; pi < kMxTile * (kMxTile / 8); pi += 512) {
-    const int r = pi >> 5, c8 = 8 * (pi & 31);
+  for (int pi = tid; pi < kMxTile * (TN / 8); pi += 512) {
+    const int r = pi / (TN / 8), c8 = 8 * (pi - r * (TN / 8));
     if (r >= rows || c8 >= cols) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kMxTile + 8 * ((c8 >> 3) ^ (r & 7)));
+    const uint4 v = *reinterpret_cast<const uint4*>(yt + r * TN + 8 * ((c8 >> 3) ^ (r & 7)));
     uint16_t* dst = p.y + (m0 + r) * p.n + n0 + c8;
     if (vec && c8 + 8 <= cols) {
       __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst));
@@ -380,14 +388,45 @@ void launch_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t row
 
 bool mx_gemm_supported(int64_t m, int64_t n, int64_t k) {
   return m > 0 && n > 0 && k > 0 && k % kMxKC == 0 && m * (k / 2) < ((int64_t)1 << 32) &&
-         n * (k / 2) < ((int64_t)1 << 32) && ((n + kMxTile - 1) / kMxTile) * ((m + kMxTile - 1) / kMxTile) < (1 << 30);
+         n * (k / 2) < ((int64_t)1 << 32) && ((n + 191) / 192) * ((m + kMxTile - 1) / kMxTile) < (1 << 30);
+}
+
+// The tile width whose grid fills the CUs best: time ~ rounds of the grid over
+// the CUs x one tile's time (one workgroup per CU at a time).  Measured on the
+// 17408 x 5120 weight, a 192-row tile takes 0.86 of a 256-row tile's time (not
+// 0.75: the fixed costs per chunk stay), hence the weights 220 and 256.  The CU
+// count is read once (the library runs on gfx950 devices, which all report the
+// same).
+static int mx_pick_tn(int64_t m, int64_t n) {
+  static int cus = 0;
+  if (cus == 0) {
+    int d = 0, c = 0;
+    cus = (hipGetDevice(&d) == hipSuccess &&
+           hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, d) == hipSuccess && c > 0)
+              ? c
+              : 256;
+  }
+  const int64_t mt = (m + kMxTile - 1) / kMxTile;
+  int best = 256;
+  int64_t best_cost = INT64_MAX;
+  for (int tn : {256, 192}) {
+    const int64_t tiles = ((n + tn - 1) / tn) * mt, rounds = (tiles + cus - 1) / cus;
+    const int64_t cost = rounds * (tn == 192 ? 220 : 256);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = tn;
+    }
+  }
+  return best;
 }
 
 void launch_mx_gemm(const uint8_t* xq, const uint8_t* xs, int64_t m, const uint8_t* wq, const uint8_t* ws, int64_t n,
                     int64_t k, uint16_t* y, hipStream_t s) {
-  const int64_t n_tiles = (n + kMxTile - 1) / kMxTile, m_tiles = (m + kMxTile - 1) / kMxTile;
+  const int tn = mx_pick_tn(m, n);
+  const int64_t n_tiles = (n + tn - 1) / tn, m_tiles = (m + kMxTile - 1) / kMxTile;
   const MxArgs a{xq, xs, wq, ws, y, m, n, k, (int)n_tiles, (int)m_tiles};
-  mx_gemm_kernel<<<dim3((unsigned)(n_tiles * m_tiles)), 512, 0, s>>>(a);
+  if (tn == 192) mx_gemm_kernel<192><<<dim3((unsigned)(n_tiles * m_tiles)), 512, 0, s>>>(a);
+  else mx_gemm_kernel<256><<<dim3((unsigned)(n_tiles * m_tiles)), 512, 0, s>>>(a);
 }
 
 }  // namespace nvfp4

@@ -726,8 +726,10 @@ def test_mx_dequant_bit_exact(nv):
     assert np.array_equal(got[ok], want[ok])
 
 
+# 192-row weight tiles for most shapes; (16, 65536, 128) takes the 256-row tiles (one round of 256 of them
+# against two rounds of 192-row tiles).
 MX_GEMM_SHAPES = [(1, 16, 256), (33, 300, 512), (256, 256, 256), (300, 520, 1024), (513, 257, 768), (40, 64, 5120),
-                  (48, 200, 384), (7, 33, 128)]
+                  (48, 200, 384), (7, 33, 128), (16, 65536, 128)]
 
 
 @pytest.mark.parametrize("m,n,k", MX_GEMM_SHAPES)
