@@ -785,3 +785,90 @@ def test_mx_gemm_full_size_sampled(nv):
     assert np.array_equal(u8_host(wq)[cols], wp_s) and np.array_equal(u8_host(wsc)[cols], ws_s)
     y_ref, bound = MXO.linear_w4a4_ref(x[rows], wp_s, ws_s)
     check_linear(y[np.ix_(rows, cols)], y_ref, bound, "mx w4a4 full size, sampled")
+
+
+# ---------------------------------------------------------------------------
+# HIP-graph capture: every entry point captured once and replayed several
+# times, with eager work and synchronizations between the replays; each
+# replay must give the eager result bit for bit.
+# ---------------------------------------------------------------------------
+def test_graph_replays_match_eager(nv):
+    torch.manual_seed(0)
+    st = torch.cuda.Stream()
+    wd = to_dev_bf16(WL.normal_bf16((272, 1024), 0.02, 4000))
+    with torch.cuda.stream(st):
+        p, s, t = nv.quantize(wd)
+    torch.cuda.synchronize()
+    x1 = to_dev_bf16(WL.normal_bf16((1, 1024), 1.0, 4001))
+    x8 = to_dev_bf16(WL.normal_bf16((8, 1024), 1.0, 4002))
+    x300 = to_dev_bf16(WL.normal_bf16((300, 1024), 1.0, 4003))
+    stack = to_dev_bf16(_expert_stack(4, 80, 512, 4004))
+    route = torch.from_numpy(_routing("uniform", 150, 3, 4, 4005)).cuda()
+    xg = to_dev_bf16(WL.normal_bf16((150, 512), 1.0, 4006))
+    gws = torch.empty(nv.linear_grouped_workspace_bytes(150, 3, 4), dtype=torch.uint8, device="cuda")
+    codes, kscales = _kv_random_cache(KV.NVFP4, 12, 16, 2, 64, 4007)
+    kc, ks_ = torch.from_numpy(codes).cuda(), torch.from_numpy(kscales).cuda()
+    table = torch.from_numpy(np.random.default_rng(4008).integers(0, 12, size=(3, 4)).astype(np.int32)).cuda()
+    klen = torch.tensor([20, 64, 5], dtype=torch.int32, device="cuda")
+    kdst = torch.tensor([0, 24, 90], dtype=torch.int32, device="cuda")
+    kts = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+    mxw = nv.mx_quantize(to_dev_bf16(_mx_inputs(256, 512, 4009, spread=4)))
+    xm = to_dev_bf16(_mx_inputs(64, 512, 4010, spread=4))
+    mws = torch.empty(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(64, 512), dtype=torch.uint8, device="cuda")
+    ep, es, et = nv.quantize_experts(stack)
+    torch.cuda.synchronize()
+
+    outs = {
+        "gemv": torch.empty((1, 272), dtype=torch.bfloat16, device="cuda"),
+        "small_m": torch.empty((8, 272), dtype=torch.bfloat16, device="cuda"),
+        "prefill": torch.empty((300, 272), dtype=torch.bfloat16, device="cuda"),
+        "dequant": torch.empty((272, 1024), dtype=torch.bfloat16, device="cuda"),
+        "routed": torch.empty((150, 3, 80), dtype=torch.bfloat16, device="cuda"),
+        "grouped": torch.empty((150, 3, 80), dtype=torch.bfloat16, device="cuda"),
+        "kv": torch.empty((100, 2, 64), dtype=torch.float16, device="cuda"),
+        "w4a4": torch.empty((64, 256), dtype=torch.bfloat16, device="cuda"),
+    }
+    quant = {}
+
+    def step():
+        L = nv.lib()
+        sid = st.cuda_stream
+        nv.linear(x1, p, s, t, out=outs["gemv"])
+        nv.linear(x8, p, s, t, out=outs["small_m"])
+        nv.linear(x300, p, s, t, out=outs["prefill"])
+        assert L.nvfp4_dequant(p.data_ptr(), s.data_ptr(), t.data_ptr(), 272, 1024, outs["dequant"].data_ptr(),
+                               sid) == 0
+        if "p" not in quant:
+            quant["p"] = torch.empty_like(p)
+            quant["s"] = torch.empty_like(s)
+            quant["t"] = torch.empty_like(t)
+        assert L.nvfp4_quantize(wd.data_ptr(), 272, 1024, quant["p"].data_ptr(), quant["s"].data_ptr(),
+                                quant["t"].data_ptr(), sid) == 0
+        nv.linear_routed(xg, route, ep, es, et, out=outs["routed"])
+        nv.linear_grouped(xg, route, ep, es, et, out=outs["grouped"], workspace=gws)
+        nv.kv_gather(kc, ks_, kts, table, klen, kdst, outs["kv"], fmt="nvfp4")
+        nv.mx_linear_w4a4(xm, mxw[0], mxw[1], out=outs["w4a4"], workspace=mws)
+
+    with torch.cuda.stream(st):
+        for o in outs.values():
+            o.zero_()
+        step()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    eager.update({"q_" + k: v.clone() for k, v in quant.items()})
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in list(outs.values()) + list(quant.values()):
+            o.zero_()                                     # eager work between replays
+        nv.linear(x8, p, s, t)                            # an eager call on the default stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.int16), eager[k].view(torch.int16)), f"replay {rep}: {k}"
+        for k, v in quant.items():
+            assert torch.equal(v, eager["q_" + k]), f"replay {rep}: quantize {k}"
