@@ -43,6 +43,11 @@ Readings taken where the pages are silent or open:
                     quantize(W[i])).
   R13 routed        y[t, j] = X[t] . W_hat[route[t, j]]^T for top-k routing (each token's k chosen experts);
                     an expert id outside [0, ne) gives a zero row.
+  R20 NVFP4 x NVFP4 imp "docs/quantization.md", the Modelopt row of the loader table: a prefill in which
+                    the activations are NVFP4 too.  The pages do not say how the activation scales are
+                    chosen; the plain reading is this module's own quantizer applied to X [M, K] (one tensor
+                    scale from max |X| over the whole call, an E4M3 scale per 16 along K, R1-R8), then
+                    Y = X_hat . W_hat^T, accepted like R10/R11 with the bound sum_k |x_hat * w_hat|.
 
 Parity pins: every function here is checked by tests/test_oracle_pins.py
 against values the pages print, library routines (torch float8_e4m3fn),
@@ -231,6 +236,15 @@ def dequant_exact(packed: np.ndarray, scales: np.ndarray, tscale) -> np.ndarray:
 def linear_ref(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, tscale) -> Tuple[np.ndarray, np.ndarray]:
     """R10: (y_ref, bound) with y_ref = X . W_hat^T and bound = |X| . |W_hat|^T, both float64 [M, N]."""
     x = bf16_to_f64(x_bits)
+    w = dequant_exact(packed, scales, tscale)
+    return x @ w.T, np.abs(x) @ np.abs(w).T
+
+
+def linear_w4a4_ref(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray,
+                    tscale) -> Tuple[np.ndarray, np.ndarray]:
+    """R20: (y_ref, bound) float64 [M, N]; X is quantized to NVFP4 (its own tensor scale) before the product."""
+    xp, xs, xts = quantize(np.asarray(x_bits, dtype=np.uint16))
+    x = dequant_exact(xp, xs, xts)
     w = dequant_exact(packed, scales, tscale)
     return x @ w.T, np.abs(x) @ np.abs(w).T
 

@@ -472,6 +472,99 @@ def test_mutation_wrong_e4m3_bias(monkeypatch):
 
 
 # --------------------------------------------------------------------------
+# NVFP4 x NVFP4 linear (R20): activations quantized on the fly.
+# --------------------------------------------------------------------------
+def _brute_nvfp4_values(bits):
+    """NVFP4 values of a BF16 matrix as Fractions, by exhaustive exact-rational nearest search
+    (E4M3 grid from torch, E2M1 magnitudes from the page), one tensor scale for the whole matrix."""
+    mags = [Fraction(v) for v in _read_golden("e2m1_magnitudes.txt")]
+    rows = [[Fraction(float(a)) for a in row] for row in WL.f32_from_bf16_bits(bits)]
+    amax = max(abs(a) for row in rows for a in row)
+    if amax == 0:
+        return [[Fraction(0)] * len(r) for r in rows]
+    t = Fraction(float(np.float32(float(amax) / 2688.0)))
+    out = []
+    for row in rows:
+        vals = []
+        for b in range(0, len(row), 16):
+            blk = row[b:b + 16]
+            s = E4M3_GRID[_nearest_even(448 * max(abs(a) for a in blk) / amax, E4M3_GRID)]
+            for a in blk:
+                mag = 0 if s == 0 else mags[_nearest_even(2688 * abs(a) / (amax * s), mags)]
+                vals.append((mag if a >= 0 else -mag) * s * t)
+        out.append(vals)
+    return out
+
+
+def w4a4_inputs():
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((3, 48)) * np.array([[1.0], [0.07], [5.0]])   # rows of very different range
+    x[0, 5] = 9.0                                                          # one outlier sets the tensor scale
+    w = WL.normal_bf16((2, 48), 0.02, 61)
+    return _bits(x), w
+
+
+def pin_w4a4_brute_force():
+    x_bits, w_bits = w4a4_inputs()
+    packed, scales, tscale = O.quantize(w_bits)
+    y_ref, bound = O.linear_w4a4_ref(x_bits, packed, scales, tscale)
+    xv, wv = _brute_nvfp4_values(x_bits), _brute_nvfp4_values(w_bits)
+    assert y_ref.shape == (len(xv), len(wv))
+    for i in range(len(xv)):
+        for j in range(len(wv)):
+            exact = sum(a * b for a, b in zip(xv[i], wv[j]))
+            babs = sum(abs(a * b) for a, b in zip(xv[i], wv[j]))
+            tol = Fraction(1, 10 ** 12) * (babs + Fraction(1, 10 ** 30))
+            assert abs(Fraction(y_ref[i, j]) - exact) <= tol, (i, j)
+            assert abs(Fraction(bound[i, j]) - babs) <= tol, (i, j)
+
+
+def test_w4a4_brute_force():
+    pin_w4a4_brute_force()
+
+
+def test_w4a4_on_grid_activations_reduce_to_w4a16():
+    """X already on its own NVFP4 grid (a quantize-dequant fixed point) gives the weight-only result.
+
+    amax = 10.5 = 2688 * 2^-8 makes the tensor scale a power of two, so the grid values are exact in BF16."""
+    _, w_bits = w4a4_inputs()
+    x = np.random.default_rng(62).standard_normal((3, 48))
+    x[1, 7] = -10.5
+    xp, xs, xt = O.quantize(_bits(x))
+    assert float(xt) == 2.0 ** -8
+    x_grid = O.dequant_exact(xp, xs, xt)
+    xg_bits = O.f32_to_bf16_rne(x_grid.astype(np.float32))
+    assert np.array_equal(O.bf16_to_f64(xg_bits), x_grid)
+    q = O.quantize(w_bits)
+    a, _ = O.linear_w4a4_ref(xg_bits, *q)
+    b, _ = O.linear_ref(xg_bits, *q)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=0)
+
+
+def test_mutation_w4a4_activations_not_quantized(monkeypatch):
+    _expect_pin_failure(monkeypatch, "linear_w4a4_ref", lambda x, p, s, t: O.linear_ref(x, p, s, t),
+                        [pin_w4a4_brute_force])
+
+
+def test_mutation_w4a4_per_row_activation_scale(monkeypatch):
+    def per_row(x_bits, packed, scales, tscale):
+        rows = [O.quantize(x_bits[i:i + 1]) for i in range(x_bits.shape[0])]
+        x = np.concatenate([O.dequant_exact(*r) for r in rows])
+        w = O.dequant_exact(packed, scales, tscale)
+        return x @ w.T, np.abs(x) @ np.abs(w).T
+    _expect_pin_failure(monkeypatch, "linear_w4a4_ref", per_row, [pin_w4a4_brute_force])
+
+
+def test_mutation_w4a4_weight_scale_for_activations(monkeypatch):
+    def shared_scale(x_bits, packed, scales, tscale):
+        xp, xs, _ = O.quantize(x_bits)
+        x = O.dequant_exact(xp, xs, tscale)
+        w = O.dequant_exact(packed, scales, tscale)
+        return x @ w.T, np.abs(x) @ np.abs(w).T
+    _expect_pin_failure(monkeypatch, "linear_w4a4_ref", shared_scale, [pin_w4a4_brute_force])
+
+
+# --------------------------------------------------------------------------
 # Expert stacks (R12, R13).
 # --------------------------------------------------------------------------
 def test_quantize_experts_one_tensor_scale_per_expert():
