@@ -316,6 +316,27 @@ def bench_mx_rows(reps):
     return rows
 
 
+def bench_w4a4_nvfp4_row(m, reps):
+    """NVFP4 x NVFP4 linear (nvfp4_linear_w4a4: X quantized to NVFP4 on the stream, decoded exactly to BF16, then
+    the BF16-MFMA GEMM) on the prefill workload (N=17408, K=5120), rotated weight copies."""
+    wl = WL.WORKLOADS["prefill"]
+    packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+    rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
+    x = dev_bf16(wl.activations(m))
+    y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(nv.linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
+    g = graph_of([(lambda p=p, s=s, t=t: nv.linear_w4a4(x, p, s, t, out=y, workspace=ws)) for (p, s, t) in rot.items])
+    warm_graph(g)
+    ms = time_graph_replays(g, reps, len(rot))
+    flops = 2.0 * m * wl.n * wl.k
+    row = {"m": m, "n": wl.n, "k": wl.k, "copies": len(rot), "us_per_call": round(ms * 1e3, 3),
+           "tflop_s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    row["mfma_frac"] = round(row["tflop_s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    del rot, g
+    torch.cuda.empty_cache()
+    return {f"nvfp4_w4a4_prefill_m{m}": row}
+
+
 def cpu_baseline(budget_s=10.0):
     """The oracle's linear (float64) on the decode workload, single-threaded, for about budget_s seconds."""
     from threadpoolctl import threadpool_limits
@@ -498,6 +519,10 @@ def main():
         log("rows MXFP4 W4A4")
         rows.update(bench_mx_rows(10))
         log(f"  {rows['mx_w4a4_prefill_m512']} {rows['mx_w4a4_prefill_m2048']}")
+        log("rows NVFP4 W4A4")
+        for mm, reps_w in ((512, 10), (2048, 3)):
+            rows.update(bench_w4a4_nvfp4_row(mm, reps_w))
+        log(f"  {rows['nvfp4_w4a4_prefill_m512']} {rows['nvfp4_w4a4_prefill_m2048']}")
 
     log("cpu baseline (oracle)")
     cpu = cpu_baseline(args.cpu_budget)

@@ -311,6 +311,35 @@ nvfp4_status nvfp4_mx_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64
                                   const uint8_t* ws, uint16_t* y, void* workspace, int64_t workspace_bytes,
                                   void* stream);
 
+/*
+ * NVFP4 x NVFP4 linear (activations quantized too).  imp "docs/quantization.md",
+ * the Modelopt row of the loader table: an NVFP4 x NVFP4 prefill beside the
+ * weight-only path.  Each call quantizes x [m, k] BF16 to NVFP4 exactly as
+ * nvfp4_quantize quantizes a weight (one tensor scale from max |x| over the
+ * call, an E4M3 scale per 16 along k, E2M1 codes), then
+ *   y [m, n] BF16 = x_hat . w_hat^T,
+ * with FP32 accumulation.  The FP4 matrix cores of gfx950 take one power-of-two
+ * scale per 32 elements, not an E4M3 scale per 16, so the product runs on the
+ * BF16 matrix cores: each x_hat element without its tensor scale (E2M1 * E4M3,
+ * at most 6 significant bits) is exact in BF16, and the two tensor scales are
+ * applied once, as fl32(ts_w * ts_x), to the FP32 sums.  Results are within
+ * 2e-3 of sum_k |x_hat * w_hat| of the exact product, plus the BF16 output
+ * rounding.
+ *
+ * Workspace: nvfp4_linear_w4a4_workspace_bytes(m, k) bytes of device memory,
+ * 16-byte aligned, overlapping no argument, no clearing needed; -1 for an
+ * invalid shape, 0 for m = 0.  After the call it holds, each part starting on
+ * a 16-byte boundary: x's codes [m, k/2], x's E4M3 scales [m, k/16], the floats
+ * {ts_y, max |x|, ts_x, unused}, and x_hat / ts_x as BF16 [m, k].
+ * Errors: those of nvfp4_linear; a NULL workspace (m > 0) is NVFP4_ERR_NULL, a
+ * workspace below the size above NVFP4_ERR_SHAPE.  Concurrent calls need
+ * separate workspaces.
+ */
+int64_t nvfp4_linear_w4a4_workspace_bytes(int64_t m, int64_t k);
+nvfp4_status nvfp4_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                               const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

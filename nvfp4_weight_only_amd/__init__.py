@@ -5,11 +5,11 @@ libnvfp4.so (include/nvfp4.h).  This package holds the kernels (csrc/), the
 build script, the ctypes binding and the synthetic workload generators.
 """
 from .binding import (KERNEL_IDS, KV_FORMATS, NVFP4Error, amax_accumulate, dequant, dequant_experts, kv_gather, lib,
-                      lib_path, linear, mx_dequant, mx_gemm, mx_linear_w4a4, mx_quantize,
+                      lib_path, linear, linear_w4a4, linear_w4a4_workspace_bytes, mx_dequant, mx_gemm, mx_linear_w4a4, mx_quantize,
                       linear_grouped, linear_grouped_workspace_bytes, linear_routed, linear_workspace_bytes,
                       quantize, quantize_experts, quantize_shared, quantize_with_amax)
 
 __all__ = ["KERNEL_IDS", "KV_FORMATS", "NVFP4Error", "amax_accumulate", "dequant", "dequant_experts", "kv_gather",
-           "lib", "lib_path", "linear", "mx_dequant", "mx_gemm", "mx_linear_w4a4", "mx_quantize",
+           "lib", "lib_path", "linear", "linear_w4a4", "linear_w4a4_workspace_bytes", "mx_dequant", "mx_gemm", "mx_linear_w4a4", "mx_quantize",
            "linear_grouped", "linear_grouped_workspace_bytes", "linear_routed", "linear_workspace_bytes", "quantize", "quantize_experts", "quantize_shared",
            "quantize_with_amax"]

@@ -27,7 +27,7 @@ EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_ama
             "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
             "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_mx_quantize", "nvfp4_mx_dequant", "nvfp4_mx_gemm",
             "nvfp4_mx_linear_w4a4", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes",
-            "nvfp4_mx_linear_w4a4_workspace_bytes")
+            "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
         L.nvfp4_mx_linear_w4a4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, i64, vp]
         L.nvfp4_mx_linear_w4a4_workspace_bytes.argtypes = [i64, i64]
+        L.nvfp4_linear_w4a4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_linear_w4a4_workspace_bytes.argtypes = [i64, i64]
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
@@ -429,4 +431,30 @@ def mx_linear_w4a4(x: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor, out: Opt
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _check(lib().nvfp4_mx_linear_w4a4(x.data_ptr(), m, n, k, wq.data_ptr(), ws.data_ptr(), out.data_ptr(),
                                       workspace.data_ptr(), workspace.numel(), _stream(x)), "nvfp4_mx_linear_w4a4")
+    return out
+
+
+def linear_w4a4_workspace_bytes(m: int, k: int) -> int:
+    return int(lib().nvfp4_linear_w4a4_workspace_bytes(m, k))
+
+
+def linear_w4a4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y [m, n] BF16 = NVFP4(X) . W_hat^T: X quantized to NVFP4 on the stream (its own tensor scale)."""
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    m, k = x.shape
+    n = packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    need = linear_w4a4_workspace_bytes(m, k)
+    if need < 0:
+        raise ValueError(f"invalid shape m={m} k={k}")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_linear_w4a4(x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(),
+                                   out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(x)),
+           "nvfp4_linear_w4a4")
     return out

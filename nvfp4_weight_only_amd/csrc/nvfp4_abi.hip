@@ -484,4 +484,49 @@ nvfp4_status nvfp4_mx_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64
   return launch_status();
 }
 
+// NVFP4 x NVFP4: workspace = X codes [m, k/2] | X scales [m, k/16] | {ts_y, amax_x, ts_x, -} | X decoded BF16 [m, k],
+// each part starting on a 16-byte boundary.
+int64_t nvfp4_linear_w4a4_workspace_bytes(int64_t m, int64_t k) {
+  WeightSizes xs;
+  if (m < 0 || k <= 0 || (k & 15) != 0) return -1;
+  if (m == 0) return 0;
+  if (weight_sizes(m, k, &xs) != NVFP4_OK || xs.w_bytes > INT64_MAX / 2) return -1;
+  return mx_round16(xs.packed_bytes) + mx_round16(xs.scale_bytes) + 16 + xs.w_bytes;
+}
+
+nvfp4_status nvfp4_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                               const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
+  nvfp4_status st = validate_linear(x, m, n, k, packed, scales, tscale, y);
+  if (st != NVFP4_OK) return st;
+  if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  const int64_t need = nvfp4_linear_w4a4_workspace_bytes(m, k);
+  if (need < 0) return NVFP4_ERR_SHAPE;
+  if (!workspace) return NVFP4_ERR_NULL;
+  if (workspace_bytes < need) return NVFP4_ERR_SHAPE;
+  if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+  WeightSizes xs, wsz;
+  weight_sizes(m, k, &xs);
+  weight_sizes(n, k, &wsz);
+  const void* bufs[5] = {x, y, packed, scales, tscale};
+  const int64_t bytes[5] = {xs.w_bytes, 2 * m * n, wsz.packed_bytes, wsz.scale_bytes, 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, need, bufs[i], bytes[i])) return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  uint8_t* xsc = xq + mx_round16(xs.packed_bytes);
+  float* f = reinterpret_cast<float*>(xsc + mx_round16(xs.scale_bytes));
+  uint16_t* xd = reinterpret_cast<uint16_t*>(f + 4);
+  // amax_x (per-workgroup maxima in the code buffer first), codes + scales + decoded X, the two tensor scales,
+  // then the weight-only linear on the decoded X with ts_w * ts_x as its tensor scale.
+  // ts_y sits first so that it is 16-byte aligned like every tensor scale the linear takes.
+  nvfp4::launch_amax_set(x, xs.elems, reinterpret_cast<uint32_t*>(xq), f + 1, s);
+  nvfp4::launch_quantize_decode(x, xs.elems, f + 1, xq, xsc, xd, s);
+  nvfp4::launch_w4a4_tscale(f + 1, tscale, f + 2, f, s);
+  if (hipGetLastError() != hipSuccess) return NVFP4_ERR_DEVICE;
+  return run_linear(NVFP4_KERNEL_AUTO, xd, m, n, k, packed, scales, f, y, nullptr, 0, stream);
+}
+
 }  // extern "C"

@@ -95,6 +95,17 @@ __global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, 
   if (i < n) tscale[i] = __fdiv_rn(amax[i], 2688.0f);
 }
 
+// Activation tensor scale of an NVFP4 x NVFP4 linear and the output scale:
+// ts_x = fl32(amax_x / 2688), ts_y = fl32(ts_w * ts_x).
+__global__ void __launch_bounds__(64) w4a4_tscale_kernel(const float* amax_x, const float* ts_w, float* ts_x,
+                                                         float* ts_y) {
+  if (threadIdx.x == 0) {
+    const float tx = __fdiv_rn(amax_x[0], 2688.0f);
+    ts_x[0] = tx;
+    ts_y[0] = ts_w[0] * tx;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Quantize.
 // ---------------------------------------------------------------------------
@@ -189,8 +200,28 @@ __device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThreshold
 // encoding them, to keep several loads in flight.
 constexpr int kQuantU = 4;
 
+// The half block's decoded values E2M1 * E4M3 (no tensor scale) as 8 BF16.
+// Each product has at most 6 significant bits, so it is exact in FP32 and its
+// upper 16 bits are the exact BF16 value (signed zeros kept).
+__device__ __forceinline__ uint32_t decode_pair_bf16(float2 v, float s) {
+  return (__float_as_uint(v.x * s) >> 16) | (__float_as_uint(v.y * s) & 0xFFFF0000u);
+}
+
+template <int SEL>
+__device__ __forceinline__ float2 e2m1_pair(uint32_t word) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+  return make_float2(v[0], v[1]);
+}
+
+__device__ __forceinline__ uint4 decode_half_bf16(uint32_t word, uint32_t scode) {
+  const float s = e4m3_to_f32(scode);
+  return make_uint4(decode_pair_bf16(e2m1_pair<0>(word), s), decode_pair_bf16(e2m1_pair<1>(word), s),
+                    decode_pair_bf16(e2m1_pair<2>(word), s), decode_pair_bf16(e2m1_pair<3>(word), s));
+}
+
 __device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t amax_b, uint32_t sa, int ea,
-                                              uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+                                              uint32_t* __restrict__ packed, uint8_t* __restrict__ scales,
+                                              uint4* __restrict__ decoded) {
   {
     const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                            v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
@@ -206,6 +237,7 @@ __device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t
     for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
     packed[h] = word;
     if ((h & 1) == 0) scales[h >> 1] = (uint8_t)scode;
+    if (decoded) decoded[h] = decode_half_bf16(word, scode);
   }
 }
 
@@ -213,7 +245,8 @@ __device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t
 __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
                                                        const float* __restrict__ amax_p,
                                                        uint32_t* __restrict__ packed,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       uint4* __restrict__ decoded) {
   w += (int64_t)blockIdx.y * n_half;
   packed += (int64_t)blockIdx.y * n_half;
   scales += (int64_t)blockIdx.y * (n_half >> 1);
@@ -234,7 +267,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
 #pragma unroll
     for (int u = 0; u < kQuantU; ++u) {
       const int64_t h = h0 + (int64_t)u * blockDim.x;
-      if (h < n_half) quantize_half(v[u], h, amax_b, sa, ea, packed, scales);
+      if (h < n_half) quantize_half(v[u], h, amax_b, sa, ea, packed, scales, decoded);
     }
   }
 }
@@ -337,7 +370,19 @@ void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const fl
                      uint8_t* scales, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
   quantize_kernel<<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales);
+      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales, nullptr);
+}
+
+void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
+                            uint16_t* decoded, hipStream_t s) {
+  const int64_t n_half = n_elems / 8;
+  quantize_kernel<<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), 1u), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales,
+      reinterpret_cast<uint4*>(decoded));
+}
+
+void launch_w4a4_tscale(const float* amax_x, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s) {
+  w4a4_tscale_kernel<<<1, 64, 0, s>>>(amax_x, ts_w, ts_x, ts_y);
 }
 
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,

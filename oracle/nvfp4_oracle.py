@@ -240,10 +240,12 @@ def linear_ref(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, tscal
     return x @ w.T, np.abs(x) @ np.abs(w).T
 
 
-def linear_w4a4_ref(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray,
-                    tscale) -> Tuple[np.ndarray, np.ndarray]:
-    """R20: (y_ref, bound) float64 [M, N]; X is quantized to NVFP4 (its own tensor scale) before the product."""
-    xp, xs, xts = quantize(np.asarray(x_bits, dtype=np.uint16))
+def linear_w4a4_ref(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, tscale,
+                    x_amax: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """R20: (y_ref, bound) float64 [M, N]; X is quantized to NVFP4 (its own tensor scale) before the product.
+
+    x_amax: max |X| of the whole activation tensor when x_bits holds only some of its rows."""
+    xp, xs, xts = quantize(np.asarray(x_bits, dtype=np.uint16), amax=x_amax)
     x = dequant_exact(xp, xs, xts)
     w = dequant_exact(packed, scales, tscale)
     return x @ w.T, np.abs(x) @ np.abs(w).T

@@ -188,3 +188,23 @@ def test_mx_validation(L):
     assert lw(A, 8, 64, 512, C, D, E, None, wb(8, 512), None) == B.ERR_NULL
     assert lw(A, 8, 64, 512, C, D, E, A, wb(8, 512), None) == B.ERR_ALIAS       # workspace overlaps x
     assert lw(A, 8, 64, 320, C, D, E, W, wb(8, 320), None) == B.ERR_UNSUPPORTED
+
+
+def test_linear_w4a4_validation(L):
+    f, wb = L.nvfp4_linear_w4a4, L.nvfp4_linear_w4a4_workspace_bytes
+    W = 0x70000000
+    # codes 8*256 | scales 8*32 | 16 bytes of floats | decoded 8*512*2
+    assert wb(8, 512) == 8 * 256 + 8 * 32 + 16 + 8 * 512 * 2
+    assert wb(3, 48) == 80 + 16 + 16 + 3 * 48 * 2       # 72 and 9 bytes rounded up to 16
+    assert wb(0, 512) == 0 and wb(8, 40) == -1 and wb(-1, 512) == -1
+    n = 64
+    need = wb(8, 512)
+    assert f(A, 0, n, 512, C, D, E, None, None, 0, None) == B.OK                      # m = 0 no-op
+    assert f(A, 8, n, 40, C, D, E, E, W, need, None) == B.ERR_SHAPE                 # k % 16 != 0
+    assert f(A, 8, n, 512, C, D, E, E + 4096, None, need, None) == B.ERR_NULL
+    assert f(A, 8, n, 512, C, D, E, E + 4096, W, need - 16, None) == B.ERR_SHAPE   # workspace too small
+    assert f(A, 8, n, 512, C, D, E, E + 4096, W, -1, None) == B.ERR_SHAPE
+    assert f(A, 8, n, 512, C, D, E, E + 4096, W + 8, need, None) == B.ERR_ALIGN
+    assert f(A, 8, n, 512, C, D, E, E + 4096, A + 16, need, None) == B.ERR_ALIAS   # workspace overlaps x
+    assert f(A, 8, n, 512, C, D, E, E + 4096, C, need, None) == B.ERR_ALIAS        # overlaps packed
+    assert f(A, 8, n, 512, C, D, E, A, W, need, None) == B.ERR_ALIAS                # y overlaps x

@@ -788,6 +788,84 @@ def test_mx_gemm_full_size_sampled(nv):
 
 
 # ---------------------------------------------------------------------------
+# NVFP4 x NVFP4 linear: X quantized to NVFP4 on the stream, product on the
+# BF16 matrix cores from X's exact E2M1 * E4M3 values.
+# ---------------------------------------------------------------------------
+def _w4a4_workspace_check(ws, x, m, k, tscale_w=None):
+    """The workspace's X codes, scales, tensor amax / scale and decoded values against the oracle."""
+    rp, rs, rt = O.quantize(x)
+    h = u8_host(ws)
+    r16 = lambda b: (b + 15) // 16 * 16
+    o_s = r16(m * k // 2)
+    o_f = o_s + r16(m * k // 16)
+    assert np.array_equal(h[:m * k // 2].reshape(m, k // 2), rp), "X codes differ"
+    assert np.array_equal(h[o_s:o_s + m * k // 16].reshape(m, k // 16), rs), "X scales differ"
+    f = h[o_f:o_f + 16].view(np.float32)
+    assert f[1] == np.float32(O.tensor_amax(x)), "X amax differs"
+    assert f[2].view(np.uint32) == np.float32(rt).view(np.uint32), "X tensor scale differs"
+    if tscale_w is not None:   # the output scale fl32(ts_w * ts_x)
+        assert f[0].view(np.uint32) == (np.float32(tscale_w) * np.float32(rt)).view(np.uint32)
+    dec = h[o_f + 16:o_f + 16 + 2 * m * k].view(np.uint16).reshape(m, k)
+    want = O.f32_to_bf16_rne(O.decoded_products(rp, rs).astype(np.float32))   # exact: <= 6 significant bits
+    assert np.array_equal(dec, want), f"{int((dec != want).sum())} decoded X values differ"
+
+
+W4A4_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 272, 1024), (17, 130, 272), (33, 200, 512), (300, 272, 1024),
+               (130, 64, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", W4A4_SHAPES)
+def test_linear_w4a4(nv, m, n, k):
+    x = WL.normal_bf16((m, k), 1.0, 3800 + m)
+    w = WL.normal_bf16((n, k), 0.02, 3900 + n)
+    (packed, scales, tscale), (rp, rs, rt) = q_both(nv, w)
+    ws = torch.empty(nv.linear_w4a4_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    y = bf16_host(nv.linear_w4a4(to_dev_bf16(x), packed, scales, tscale, workspace=ws))
+    _w4a4_workspace_check(ws, x, m, k, rt)
+    y_ref, bound = O.linear_w4a4_ref(x, rp, rs, rt)
+    check_linear(y, y_ref, bound, f"nvfp4 w4a4 {m}x{n}x{k}")
+    y2 = bf16_host(nv.linear_w4a4(to_dev_bf16(x), packed, scales, tscale, workspace=ws))
+    assert np.array_equal(y, y2), "not deterministic"
+
+
+def test_linear_w4a4_edges(nv):
+    w = WL.normal_bf16((64, 512), 0.02, 3950)
+    (packed, scales, tscale), _ = q_both(nv, w)
+    # all-zero X: tensor scale 0, every code and value 0, Y = 0
+    x0 = np.zeros((5, 512), dtype=np.uint16)
+    ws = torch.empty(nv.linear_w4a4_workspace_bytes(5, 512), dtype=torch.uint8, device="cuda").fill_(0xAB)
+    y = bf16_host(nv.linear_w4a4(to_dev_bf16(x0), packed, scales, tscale, workspace=ws))
+    assert not y.any()
+    _w4a4_workspace_check(ws, x0, 5, 512)
+    # m = 0 is a no-op
+    e = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    assert nv.linear_w4a4(e, packed, scales, tscale).shape == (0, 64)
+    # one huge outlier: the rest of X rounds to small codes or zero, still within the bound of X_hat
+    x = WL.normal_bf16((4, 512), 1.0, 3951)
+    x[2, 100] = WL.bf16_bits_from_f32(np.array([3.0e4], dtype=np.float32))[0]
+    y = bf16_host(nv.linear_w4a4(to_dev_bf16(x), packed, scales, tscale))
+    y_ref, bound = O.linear_w4a4_ref(x, *O.quantize(w))
+    check_linear(y, y_ref, bound, "nvfp4 w4a4 outlier")
+
+
+def test_linear_w4a4_full_size_sampled(nv):
+    """The prefill workload (M=2048, N=17408, K=5120) with NVFP4 activations, launched as timed; sampled rows
+    and columns against the oracle, which quantizes the sampled rows against the whole X's amax."""
+    wl = WL.WORKLOADS["prefill"]
+    m, n, k = 2048, wl.n, wl.k
+    (packed, scales, tscale), w, amax = _quantized(nv, "prefill")
+    x = wl.activations(m)
+    y = bf16_host(nv.linear_w4a4(to_dev_bf16(x), packed, scales, tscale))
+    rng = np.random.default_rng(3960)
+    rows = np.sort(np.concatenate([rng.choice(m, 24, replace=False), [0, m - 1]]))
+    cols = sample_rows(n, 40, seed=3961)
+    rp, rs, rt = O.quantize(w[cols], amax=amax)
+    assert np.array_equal(u8_host(packed)[cols], rp) and np.array_equal(u8_host(scales)[cols], rs)
+    y_ref, bound = O.linear_w4a4_ref(x[rows], rp, rs, rt, x_amax=O.tensor_amax(x))
+    check_linear(y[np.ix_(rows, cols)], y_ref, bound, "nvfp4 w4a4 full size, sampled")
+
+
+# ---------------------------------------------------------------------------
 # HIP-graph capture: every entry point captured once and replayed several
 # times, with eager work and synchronizations between the replays; each
 # replay must give the eager result bit for bit.
@@ -827,7 +905,9 @@ def test_graph_replays_match_eager(nv):
         "grouped": torch.empty((150, 3, 80), dtype=torch.bfloat16, device="cuda"),
         "kv": torch.empty((100, 2, 64), dtype=torch.float16, device="cuda"),
         "w4a4": torch.empty((64, 256), dtype=torch.bfloat16, device="cuda"),
+        "nv_w4a4": torch.empty((300, 272), dtype=torch.bfloat16, device="cuda"),
     }
+    nws = torch.empty(nv.linear_w4a4_workspace_bytes(300, 1024), dtype=torch.uint8, device="cuda")
     quant = {}
 
     def step():
@@ -848,6 +928,7 @@ def test_graph_replays_match_eager(nv):
         nv.linear_grouped(xg, route, ep, es, et, out=outs["grouped"], workspace=gws)
         nv.kv_gather(kc, ks_, kts, table, klen, kdst, outs["kv"], fmt="nvfp4")
         nv.mx_linear_w4a4(xm, mxw[0], mxw[1], out=outs["w4a4"], workspace=mws)
+        nv.linear_w4a4(x300, p, s, t, out=outs["nv_w4a4"], workspace=nws)
 
     with torch.cuda.stream(st):
         for o in outs.values():
