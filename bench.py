@@ -375,10 +375,31 @@ def profile_run(what, launches):
     kv_gather: nvfp4_kv_gather (NVFP4 pages to FP16) on the chunked-prefill gather workload, cycling
             through rotated cache + output copies;
     mx_w4a4: nvfp4_mx_linear_w4a4 on the prefill workload at M=2048 (X quantized to MXFP4, then the FP4
-            GEMM), rotated MXFP4 weight copies.
+            GEMM), rotated MXFP4 weight copies;
+    nvfp4_w4a4: nvfp4_linear_w4a4 on the prefill workload at M=2048 (X quantized to NVFP4 and decoded, then
+            the BF16-MFMA GEMM), rotated weight copies;
+    quantize: nvfp4_quantize of the decode workload's BF16 weight (5120 x 5120), rotated input copies.
     """
     torch.cuda.set_device(0)
-    if what == "mx_w4a4":
+    if what == "quantize":
+        w = dev_bf16(WL.WORKLOADS["decode"].weight())
+        rot = [w.clone() for _ in range(copies_needed(w.numel() * 2))]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            nv.quantize(rot[i % len(rot)])
+    elif what == "nvfp4_w4a4":
+        wl = WL.WORKLOADS["prefill"]
+        m = 2048
+        packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+        rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
+        x = dev_bf16(wl.activations(m))
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(nv.linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p, s, t = rot.items[i % len(rot)]
+            nv.linear_w4a4(x, p, s, t, out=y, workspace=ws)
+    elif what == "mx_w4a4":
         wl = WL.WORKLOADS["prefill"]
         m = 2048
         wq, wsc = nv.mx_quantize(dev_bf16(wl.weight()))
@@ -446,7 +467,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4"], default=None,
+    ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4",
+                                              "nvfp4_w4a4", "quantize"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     args = ap.parse_args()

@@ -126,36 +126,44 @@ __device__ __forceinline__ void e4m3_split(uint32_t c, uint32_t& sig, int& ex) {
 
 // Round a non-negative float to an E4M3 code (RNE), clamped to 0..126.  Used
 // only for a first guess from an approximate quotient; the caller corrects it.
+// Branch-free (selects), so that several blocks' searches can interleave.
 __device__ __forceinline__ uint32_t e4m3_code_guess(float r) {
-  if (!(r < 448.0f)) return 126u;
-  if (r < 0x1p-6f) return (uint32_t)__builtin_rintf(r * 512.0f);
   uint32_t u = __float_as_uint(r);
   u += 0x7FFFFu + ((u >> 20) & 1u);
-  const uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
-  return c > 126u ? 126u : c;
+  uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);   // normal range [2^-6, 448)
+  c = c > 126u ? 126u : c;
+  const uint32_t sub = (uint32_t)__builtin_rintf(r * 512.0f);  // subnormal range: multiples of 2^-9
+  c = r < 0x1p-6f ? sub : c;
+  return r < 448.0f ? c : 126u;                                // also NaN
 }
 
 // The E4M3 code nearest to 448 * bam / amax (ties to the even code).
 // bam = sb * 2^eb, amax = sa * 2^ea.  With A = 448 sb 2^(eb-ea) and D = sa the
 // quotient is A / D; the comparisons A vs u * D against the midpoints u are
-// exact (u has <= 5 significant bits, D <= 8, A <= 17).
+// exact (u has <= 5 significant bits, D <= 8, A <= 17).  The guess is off by at
+// most one code; one step up, then one step down, settles it.
 __device__ __forceinline__ uint32_t e4m3_scale_code(uint32_t bam_b, uint32_t sa, int ea) {
-  if (bam_b == 0u) return 0u;
   uint32_t sb;
   int eb;
   bf16_split(bam_b, sb, eb);
   const float A = ldexpf((float)(448u * sb), eb - ea);
   const float D = (float)sa;
   uint32_t c = e4m3_code_guess(A * __builtin_amdgcn_rcpf(D));
-  if (c < 126u) {
-    const float rhs = 0.5f * (e4m3_to_f32(c) + e4m3_to_f32(c + 1u)) * D;
-    if ((c & 1u) ? (A >= rhs) : (A > rhs)) ++c;
-  }
-  if (c > 0u) {
-    const float rhs = 0.5f * (e4m3_to_f32(c - 1u) + e4m3_to_f32(c)) * D;
-    if (((c - 1u) & 1u) ? (A < rhs) : (A <= rhs)) --c;
-  }
-  return c;
+  // Neighbouring codes as one 16-bit pair, decoded by the hardware E4M3 conversion
+  // (exact for every code; codes here are at most 126, never NaN).
+  const uint32_t cu = c < 125u ? c : 125u;
+  const auto pu = __builtin_amdgcn_cvt_pk_f32_fp8((int)(cu | ((cu + 1u) << 8)), false);
+  const float up_rhs = 0.5f * (pu[0] + pu[1]) * D;
+  // Bitwise forms of the tie rule (an odd code's upper midpoint rounds up), so
+  // that no branch splits the block.
+  const uint32_t odd_u = c & 1u;
+  c += (uint32_t)(c < 126u) & ((odd_u & (uint32_t)(A >= up_rhs)) | ((odd_u ^ 1u) & (uint32_t)(A > up_rhs)));
+  const uint32_t cd = c > 1u ? c : 1u;
+  const auto pd = __builtin_amdgcn_cvt_pk_f32_fp8((int)((cd - 1u) | (cd << 8)), false);
+  const float dn_rhs = 0.5f * (pd[0] + pd[1]) * D;
+  const uint32_t odd_d = (c - 1u) & 1u;
+  c -= (uint32_t)(c > 0u) & ((odd_d & (uint32_t)(A < dn_rhs)) | ((odd_d ^ 1u) & (uint32_t)(A <= dn_rhs)));
+  return bam_b == 0u ? 0u : c;
 }
 
 // Per-block element thresholds.  With t_j = T_j / 4 the E2M1 midpoints
@@ -163,7 +171,8 @@ __device__ __forceinline__ uint32_t e4m3_scale_code(uint32_t bam_b, uint32_t sa,
 // becomes  L = 21 |w| 2^(9 - ea - es)  vs  R_j = T_j sa ss  (2688 = 21 * 2^7).
 struct ElemThresholds {
   float r[7];
-  int shift;  // 9 - ea - es
+  uint32_t u[7];  // bits of r
+  int shift;      // 9 - ea - es
 };
 
 __device__ __forceinline__ ElemThresholds element_thresholds(uint32_t scode, uint32_t sa, int ea) {
@@ -180,16 +189,28 @@ __device__ __forceinline__ ElemThresholds element_thresholds(uint32_t scode, uin
   t.r[4] = 10.0f * S;
   t.r[5] = 14.0f * S;
   t.r[6] = 20.0f * S;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) t.u[j] = __float_as_uint(t.r[j]);
   t.shift = 9 - ea - es;
   return t;
 }
 
 // 4-bit code of one BF16 element (bits in the low 16 bits of b).
+// The magnitude code is the number of midpoints L passes (ties to the even
+// code: L must reach an odd code's upper midpoint R_1, R_3, R_5 and exceed an
+// even code's R_0, R_2, R_4, R_6).  The R_j increase with j, so a binary search
+// takes three of the seven exact comparisons: R_3, then R_5 or R_1, then the
+// even midpoint just below.
 __device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThresholds& t) {
+  // Selects are written as bit masks so that they stay v_cndmask / v_bfi and
+  // never become branches.
   const float L = 21.0f * ldexpf(__uint_as_float((b & 0x7FFFu) << 16), t.shift);
-  uint32_t mag = (uint32_t)(L > t.r[0]) + (uint32_t)(L >= t.r[1]) + (uint32_t)(L > t.r[2]) +
-                 (uint32_t)(L >= t.r[3]) + (uint32_t)(L > t.r[4]) + (uint32_t)(L >= t.r[5]) +
-                 (uint32_t)(L > t.r[6]);
+  const uint32_t hi = 0u - (uint32_t)(L >= t.r[3]);                             // code >= 4
+  const uint32_t m = (t.u[5] & hi) | (t.u[1] & ~hi);
+  const uint32_t mid = 0u - (uint32_t)(L >= __uint_as_float(m));               // code >= 6, or >= 2
+  const uint32_t lo_hi = (t.u[6] & mid) | (t.u[4] & ~mid), lo_lo = (t.u[2] & mid) | (t.u[0] & ~mid);
+  const float lo = __uint_as_float((lo_hi & hi) | (lo_lo & ~hi));
+  const uint32_t mag = (hi & 4u) | (mid & 2u) | (uint32_t)(L > lo);
   return mag | ((b >> 12) & 8u);
 }
 
@@ -214,34 +235,49 @@ __device__ __forceinline__ float2 e2m1_pair(uint32_t word) {
 }
 
 __device__ __forceinline__ uint4 decode_half_bf16(uint32_t word, uint32_t scode) {
-  const float s = e4m3_to_f32(scode);
+  const float s = e4m3x2_to_f32<false>(scode).x;
   return make_uint4(decode_pair_bf16(e2m1_pair<0>(word), s), decode_pair_bf16(e2m1_pair<1>(word), s),
                     decode_pair_bf16(e2m1_pair<2>(word), s), decode_pair_bf16(e2m1_pair<3>(word), s));
 }
 
-__device__ __forceinline__ void quantize_half(const uint4 v, int64_t h, uint32_t amax_b, uint32_t sa, int ea,
-                                              uint32_t* __restrict__ packed, uint8_t* __restrict__ scales,
-                                              uint4* __restrict__ decoded) {
-  {
-    const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-    uint32_t lm = 0;
+// Codes and scale code of one half block (8 BF16 in v); the partner lane
+// (lane ^ 1) holds the other half of the 16-element block.
+struct HalfCodes {
+  uint32_t word, scode;
+};
+
+__device__ __forceinline__ HalfCodes quantize_half(const uint4 v, uint32_t amax_b, uint32_t sa, int ea) {
+  const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  uint32_t lm = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lm = max(lm, e[i] & 0x7FFFu);
-    const uint32_t pm = (uint32_t)__shfl_xor((int)lm, 1, 64);
-    const uint32_t bam = max(lm, pm);
-    const uint32_t scode = (amax_b & 0x7FFFu) ? e4m3_scale_code(bam, sa, ea) : 0u;
-    const ElemThresholds t = element_thresholds(scode, sa, ea);
-    uint32_t word = 0;
+  for (int i = 0; i < 8; ++i) lm = max(lm, e[i] & 0x7FFFu);
+  const uint32_t pm = (uint32_t)__shfl_xor((int)lm, 1, 64);
+  const uint32_t bam = max(lm, pm);
+  const uint32_t sc = e4m3_scale_code(bam, sa, ea);   // evaluated always: a select, not a branch
+  const uint32_t scode = (amax_b & 0x7FFFu) ? sc : 0u;
+  const ElemThresholds t = element_thresholds(scode, sa, ea);
+  uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
-    packed[h] = word;
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)scode;
-    if (decoded) decoded[h] = decode_half_bf16(word, scode);
-  }
+  for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
+  return HalfCodes{word, scode};
+}
+
+template <bool DECODE>
+__device__ __forceinline__ void store_half(int64_t h, HalfCodes q, uint32_t* __restrict__ packed,
+                                           uint8_t* __restrict__ scales, uint4* __restrict__ decoded) {
+  packed[h] = q.word;
+  if constexpr (DECODE) decoded[h] = decode_half_bf16(q.word, q.scode);
+  // Both lanes of a pair hold the block's scale code and write the same byte
+  // to the same address: no branch.
+  scales[h >> 1] = (uint8_t)q.scode;
 }
 
 // Over a stack, blockIdx.y picks the matrix (n_half half blocks each).
+// Iterations whose kQuantU half blocks all exist run without a branch between
+// loads, codes and stores, so the compiler interleaves the half blocks; only
+// the last iteration of the grid takes the guarded path.
+template <bool DECODE>
 __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
                                                        const float* __restrict__ amax_p,
                                                        uint32_t* __restrict__ packed,
@@ -256,18 +292,29 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
   bf16_split(amax_b & 0x7FFFu, sa, ea);
   // The stride and blockDim are even, and n_half is even (k % 16 == 0), so both
   // lanes of a pair take the same branches.
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x * kQuantU;
-  for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x * kQuantU + threadIdx.x; h0 < n_half; h0 += stride) {
+  const int64_t B = blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * B * kQuantU;
+  for (int64_t h0 = (int64_t)blockIdx.x * B * kQuantU + threadIdx.x; h0 < n_half; h0 += stride) {
     uint4 v[kQuantU];
+    HalfCodes q[kQuantU];
+    if (h0 + (kQuantU - 1) * B < n_half) {
 #pragma unroll
-    for (int u = 0; u < kQuantU; ++u) {
-      const int64_t h = h0 + (int64_t)u * blockDim.x;
-      v[u] = h < n_half ? w[h] : make_uint4(0u, 0u, 0u, 0u);
-    }
+      for (int u = 0; u < kQuantU; ++u) v[u] = w[h0 + u * B];
 #pragma unroll
-    for (int u = 0; u < kQuantU; ++u) {
-      const int64_t h = h0 + (int64_t)u * blockDim.x;
-      if (h < n_half) quantize_half(v[u], h, amax_b, sa, ea, packed, scales, decoded);
+      for (int u = 0; u < kQuantU; ++u) q[u] = quantize_half(v[u], amax_b, sa, ea);
+#pragma unroll
+      for (int u = 0; u < kQuantU; ++u) store_half<DECODE>(h0 + u * B, q[u], packed, scales, decoded);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kQuantU; ++u) {
+        const int64_t h = h0 + u * B;
+        v[u] = h < n_half ? w[h] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kQuantU; ++u) {
+        const int64_t h = h0 + u * B;
+        if (h < n_half) store_half<DECODE>(h, quantize_half(v[u], amax_b, sa, ea), packed, scales, decoded);
+      }
     }
   }
 }
@@ -369,14 +416,14 @@ void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hip
 void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
                      uint8_t* scales, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  quantize_kernel<<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
+  quantize_kernel<false><<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
       reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales, nullptr);
 }
 
 void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
                             uint16_t* decoded, hipStream_t s) {
   const int64_t n_half = n_elems / 8;
-  quantize_kernel<<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), 1u), 256, 0, s>>>(
+  quantize_kernel<true><<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), 1u), 256, 0, s>>>(
       reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales,
       reinterpret_cast<uint4*>(decoded));
 }
