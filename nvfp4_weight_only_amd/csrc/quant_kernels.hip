@@ -214,14 +214,7 @@ __device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThreshold
   return mag | ((b >> 12) & 8u);
 }
 
-// One thread per 8 consecutive elements (a half block) at a time; lanes 2i and
-// 2i+1 hold the two halves of one 16-element block.  w is read as uint4 (8
-// BF16), packed is written as one 32-bit word per half block, the scale byte by
-// the even lane.  Each thread loads kQuantU half blocks (blockDim apart) before
-// encoding them, to keep several loads in flight.
-constexpr int kQuantU = 4;
-
-// The half block's decoded values E2M1 * E4M3 (no tensor scale) as 8 BF16.
+// 8 codes (one 32-bit word) decoded to E2M1 * E4M3 (no tensor scale) as 8 BF16.
 // Each product has at most 6 significant bits, so it is exact in FP32 and its
 // upper 16 bits are the exact BF16 value (signed zeros kept).
 __device__ __forceinline__ uint32_t decode_pair_bf16(float2 v, float s) {
@@ -240,80 +233,95 @@ __device__ __forceinline__ uint4 decode_half_bf16(uint32_t word, uint32_t scode)
                     decode_pair_bf16(e2m1_pair<2>(word), s), decode_pair_bf16(e2m1_pair<3>(word), s));
 }
 
-// Codes and scale code of one half block (8 BF16 in v); the partner lane
-// (lane ^ 1) holds the other half of the 16-element block.
-struct HalfCodes {
-  uint32_t word, scode;
+// One thread per 16-element block at a time: two 16-byte loads (8 BF16 each),
+// one 64-bit store of the 16 codes, one scale byte.  Each thread loads
+// kQuantB blocks (blockDim apart) before it encodes any of them.
+constexpr int kQuantB = 2;
+
+struct BlockCodes {
+  uint32_t lo, hi, scode;  // codes of elements 0..7 and 8..15, scale code
 };
 
-__device__ __forceinline__ HalfCodes quantize_half(const uint4 v, uint32_t amax_b, uint32_t sa, int ea) {
+__device__ __forceinline__ uint32_t half_codes(const uint4 v, const ElemThresholds& t) {
   const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                          v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-  uint32_t lm = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) lm = max(lm, e[i] & 0x7FFFu);
-  const uint32_t pm = (uint32_t)__shfl_xor((int)lm, 1, 64);
-  const uint32_t bam = max(lm, pm);
-  const uint32_t sc = e4m3_scale_code(bam, sa, ea);   // evaluated always: a select, not a branch
-  const uint32_t scode = (amax_b & 0x7FFFu) ? sc : 0u;
-  const ElemThresholds t = element_thresholds(scode, sa, ea);
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
-  return HalfCodes{word, scode};
+  return word;
+}
+
+// Largest magnitude (bits & 0x7FFF) of 8 BF16, by lane-wise 16-bit maxima.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2_t mag2(uint32_t x) { return __builtin_bit_cast(u16x2_t, x & 0x7FFF7FFFu); }
+
+__device__ __forceinline__ uint32_t half_max(const uint4 v) {
+  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(mag2(v.x), mag2(v.y)),
+                                              __builtin_elementwise_max(mag2(v.z), mag2(v.w)));
+  return max((uint32_t)a[0], (uint32_t)a[1]);
+}
+
+__device__ __forceinline__ BlockCodes quantize_block(const uint4 v0, const uint4 v1, uint32_t amax_b, uint32_t sa,
+                                                     int ea) {
+  const uint32_t bam = max(half_max(v0), half_max(v1));
+  const uint32_t sc = e4m3_scale_code(bam, sa, ea);   // evaluated always: a select, not a branch
+  const uint32_t scode = (amax_b & 0x7FFFu) ? sc : 0u;
+  const ElemThresholds t = element_thresholds(scode, sa, ea);
+  return BlockCodes{half_codes(v0, t), half_codes(v1, t), scode};
 }
 
 template <bool DECODE>
-__device__ __forceinline__ void store_half(int64_t h, HalfCodes q, uint32_t* __restrict__ packed,
-                                           uint8_t* __restrict__ scales, uint4* __restrict__ decoded) {
-  packed[h] = q.word;
-  if constexpr (DECODE) decoded[h] = decode_half_bf16(q.word, q.scode);
-  // Both lanes of a pair hold the block's scale code and write the same byte
-  // to the same address: no branch.
-  scales[h >> 1] = (uint8_t)q.scode;
+__device__ __forceinline__ void store_block(int64_t blk, BlockCodes q, uint2* __restrict__ packed,
+                                            uint8_t* __restrict__ scales, uint4* __restrict__ decoded) {
+  packed[blk] = make_uint2(q.lo, q.hi);
+  scales[blk] = (uint8_t)q.scode;
+  if constexpr (DECODE) {
+    decoded[2 * blk] = decode_half_bf16(q.lo, q.scode);
+    decoded[2 * blk + 1] = decode_half_bf16(q.hi, q.scode);
+  }
 }
 
-// Over a stack, blockIdx.y picks the matrix (n_half half blocks each).
-// Iterations whose kQuantU half blocks all exist run without a branch between
-// loads, codes and stores, so the compiler interleaves the half blocks; only
-// the last iteration of the grid takes the guarded path.
+// Over a stack, blockIdx.y picks the matrix (n_blk blocks each).  Iterations
+// whose kQuantB blocks all exist run without a branch between loads, codes and
+// stores, so the compiler interleaves the blocks; only the grid's last
+// iteration takes the guarded path.
 template <bool DECODE>
-__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_half,
+__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_blk,
                                                        const float* __restrict__ amax_p,
-                                                       uint32_t* __restrict__ packed,
+                                                       uint2* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
                                                        uint4* __restrict__ decoded) {
-  w += (int64_t)blockIdx.y * n_half;
-  packed += (int64_t)blockIdx.y * n_half;
-  scales += (int64_t)blockIdx.y * (n_half >> 1);
+  w += (int64_t)blockIdx.y * 2 * n_blk;
+  packed += (int64_t)blockIdx.y * n_blk;
+  scales += (int64_t)blockIdx.y * n_blk;
   const uint32_t amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;  // amax is a BF16 value held in FP32
   uint32_t sa;
   int ea;
   bf16_split(amax_b & 0x7FFFu, sa, ea);
-  // The stride and blockDim are even, and n_half is even (k % 16 == 0), so both
-  // lanes of a pair take the same branches.
   const int64_t B = blockDim.x;
-  const int64_t stride = (int64_t)gridDim.x * B * kQuantU;
-  for (int64_t h0 = (int64_t)blockIdx.x * B * kQuantU + threadIdx.x; h0 < n_half; h0 += stride) {
-    uint4 v[kQuantU];
-    HalfCodes q[kQuantU];
-    if (h0 + (kQuantU - 1) * B < n_half) {
+  const int64_t stride = (int64_t)gridDim.x * B * kQuantB;
+  for (int64_t b0 = (int64_t)blockIdx.x * B * kQuantB + threadIdx.x; b0 < n_blk; b0 += stride) {
+    uint4 v[2 * kQuantB];
+    if (b0 + (kQuantB - 1) * B < n_blk) {
 #pragma unroll
-      for (int u = 0; u < kQuantU; ++u) v[u] = w[h0 + u * B];
+      for (int u = 0; u < kQuantB; ++u) {
+        v[2 * u] = w[2 * (b0 + u * B)];
+        v[2 * u + 1] = w[2 * (b0 + u * B) + 1];
+      }
+      BlockCodes q[kQuantB];
 #pragma unroll
-      for (int u = 0; u < kQuantU; ++u) q[u] = quantize_half(v[u], amax_b, sa, ea);
+      for (int u = 0; u < kQuantB; ++u) q[u] = quantize_block(v[2 * u], v[2 * u + 1], amax_b, sa, ea);
 #pragma unroll
-      for (int u = 0; u < kQuantU; ++u) store_half<DECODE>(h0 + u * B, q[u], packed, scales, decoded);
+      for (int u = 0; u < kQuantB; ++u) store_block<DECODE>(b0 + u * B, q[u], packed, scales, decoded);
     } else {
 #pragma unroll
-      for (int u = 0; u < kQuantU; ++u) {
-        const int64_t h = h0 + u * B;
-        v[u] = h < n_half ? w[h] : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < kQuantU; ++u) {
-        const int64_t h = h0 + u * B;
-        if (h < n_half) store_half<DECODE>(h, quantize_half(v[u], amax_b, sa, ea), packed, scales, decoded);
+      for (int u = 0; u < kQuantB; ++u) {
+        const int64_t blk = b0 + u * B;
+        if (blk < n_blk) {
+          store_block<DECODE>(blk, quantize_block(w[2 * blk], w[2 * blk + 1], amax_b, sa, ea), packed, scales,
+                              decoded);
+        }
       }
     }
   }
@@ -415,16 +423,16 @@ void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hip
 
 void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
                      uint8_t* scales, hipStream_t s) {
-  const int64_t n_half = n_elems / 8;
-  quantize_kernel<false><<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), (unsigned)count), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales, nullptr);
+  const int64_t n_blk = n_elems / 16;
+  quantize_kernel<false><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales, nullptr);
 }
 
 void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
                             uint16_t* decoded, hipStream_t s) {
-  const int64_t n_half = n_elems / 8;
-  quantize_kernel<true><<<dim3(grid_for(n_half, 256 * kQuantU, 1 << 20), 1u), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_half, amax, reinterpret_cast<uint32_t*>(packed), scales,
+  const int64_t n_blk = n_elems / 16;
+  quantize_kernel<true><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales,
       reinterpret_cast<uint4*>(decoded));
 }
 
