@@ -366,19 +366,23 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint32_t* __restrict
   const float t = tscale_p[blockIdx.y];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * kDequantU;
   for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x * kDequantU + threadIdx.x; h0 < n_half; h0 += stride) {
+    // Loads never branch: an index past the end reads the last half block
+    // again (its result is not stored), so every load is issued before any
+    // wait.  Nontemporal stores: the BF16 weight is written once and not read
+    // back here.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     uint32_t p[kDequantU], sb[kDequantU];
 #pragma unroll
     for (int u = 0; u < kDequantU; ++u) {
       const int64_t h = h0 + (int64_t)u * blockDim.x;
-      p[u] = h < n_half ? packed[h] : 0u;
-      sb[u] = h < n_half ? scales[h >> 1] : 0u;
+      const int64_t hc = h < n_half ? h : n_half - 1;
+      p[u] = packed[hc];
+      sb[u] = scales[hc >> 1];
     }
 #pragma unroll
     for (int u = 0; u < kDequantU; ++u) {
       const int64_t h = h0 + (int64_t)u * blockDim.x;
       if (h < n_half) {
-        // Nontemporal: the BF16 weight is written once and not read back here.
-        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
         const uint4 v = dequant_half(p[u], sb[u], t);
         __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(out) + h);
       }
