@@ -136,6 +136,26 @@ def test_quantize_dequant_bit_exact_crafted(nv):
         _quant_compare(nv, w, name)
 
 
+def test_quantize_crafted_ties_tiled(nv):
+    """The crafted tie rows tiled to 640 x 1024, so that most blocks take the quantize kernel's whole-iteration
+    path (the small crafted cases above take only its guarded tail); also as NVFP4 x NVFP4 activations, with
+    the decoded BF16 values checked bit for bit."""
+    cw = crafted_weights()
+    for name, reps in (("e2m1 ties", (640, 32)), ("e4m3 ties", (10, 32))):
+        w = np.ascontiguousarray(np.tile(cw[name], reps))
+        log(f"quantize/dequant tiled {name}: {w.shape}")
+        _quant_compare(nv, w, f"tiled {name}")
+    x = np.ascontiguousarray(np.tile(cw["e2m1 ties"], (640, 32)))
+    m, k = x.shape
+    wq = WL.normal_bf16((48, k), 0.02, 3970)
+    (packed, scales, tscale), (rp, rs, rt) = q_both(nv, wq)
+    ws = torch.empty(nv.linear_w4a4_workspace_bytes(m, k), dtype=torch.uint8, device="cuda")
+    y = bf16_host(nv.linear_w4a4(to_dev_bf16(x), packed, scales, tscale, workspace=ws))
+    _w4a4_workspace_check(ws, x, m, k, rt)
+    y_ref, bound = O.linear_w4a4_ref(x, rp, rs, rt)
+    check_linear(y, y_ref, bound, "nvfp4 w4a4 tiled ties")
+
+
 # ---------------------------------------------------------------------------
 # Full-size weights: exact on sampled rows (the quantizer is row-local once amax is known).
 # ---------------------------------------------------------------------------
