@@ -447,8 +447,14 @@ def linear_w4a4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tsc
     _need(tscale, torch.float32, "tscale")
     m, k = x.shape
     n = packed.shape[0]
+    if packed.shape != (n, k // 2) or scales.shape != (n, k // 16):
+        raise ValueError("packed/scales do not match x's k")
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (m, n):
+            raise ValueError("out must be [m, n]")
     need = linear_w4a4_workspace_bytes(m, k)
     if need < 0:
         raise ValueError(f"invalid shape m={m} k={k}")
