@@ -22,11 +22,10 @@ void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const fl
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,
                     uint16_t* out, hipStream_t s);
 // launch_quantize of one matrix that also writes, per element, the exact BF16
-// value E2M1 * E4M3 (the tensor scale left out) to decoded [n_elems].
+// value E2M1 * E4M3 (the tensor scale left out) to decoded [n_elems], and the
+// scalars ts_x = fl32(amax / 2688), ts_y = fl32(ts_w * ts_x) (NVFP4 x NVFP4).
 void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
-                            uint16_t* decoded, hipStream_t s);
-// ts_x = fl32(amax_x / 2688), ts_y = fl32(ts_w * ts_x) (one value each).
-void launch_w4a4_tscale(const float* amax_x, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s);
+                            uint16_t* decoded, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s);
 
 void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                  const float* tscale, uint16_t* y, hipStream_t s);

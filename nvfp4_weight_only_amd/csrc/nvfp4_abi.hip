@@ -519,12 +519,11 @@ nvfp4_status nvfp4_linear_w4a4(const uint16_t* x, int64_t m, int64_t n, int64_t 
   uint8_t* xsc = xq + mx_round16(xs.packed_bytes);
   float* f = reinterpret_cast<float*>(xsc + mx_round16(xs.scale_bytes));
   uint16_t* xd = reinterpret_cast<uint16_t*>(f + 4);
-  // amax_x (per-workgroup maxima in the code buffer first), codes + scales + decoded X, the two tensor scales,
-  // then the weight-only linear on the decoded X with ts_w * ts_x as its tensor scale.
+  // amax_x (per-workgroup maxima in the code buffer first), then codes + scales + decoded X and the two tensor
+  // scales in one kernel, then the weight-only linear on the decoded X with ts_w * ts_x as its tensor scale.
   // ts_y sits first so that it is 16-byte aligned like every tensor scale the linear takes.
   nvfp4::launch_amax_set(x, xs.elems, reinterpret_cast<uint32_t*>(xq), f + 1, s);
-  nvfp4::launch_quantize_decode(x, xs.elems, f + 1, xq, xsc, xd, s);
-  nvfp4::launch_w4a4_tscale(f + 1, tscale, f + 2, f, s);
+  nvfp4::launch_quantize_decode(x, xs.elems, f + 1, xq, xsc, xd, tscale, f + 2, f, s);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_DEVICE;
   return run_linear(NVFP4_KERNEL_AUTO, xd, m, n, k, packed, scales, f, y, nullptr, 0, stream);
 }

@@ -95,17 +95,6 @@ __global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, 
   if (i < n) tscale[i] = __fdiv_rn(amax[i], 2688.0f);
 }
 
-// Activation tensor scale of an NVFP4 x NVFP4 linear and the output scale:
-// ts_x = fl32(amax_x / 2688), ts_y = fl32(ts_w * ts_x).
-__global__ void __launch_bounds__(64) w4a4_tscale_kernel(const float* amax_x, const float* ts_w, float* ts_x,
-                                                         float* ts_y) {
-  if (threadIdx.x == 0) {
-    const float tx = __fdiv_rn(amax_x[0], 2688.0f);
-    ts_x[0] = tx;
-    ts_y[0] = ts_w[0] * tx;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Quantize.
 // ---------------------------------------------------------------------------
@@ -291,7 +280,17 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
                                                        const float* __restrict__ amax_p,
                                                        uint2* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
-                                                       uint4* __restrict__ decoded) {
+                                                       uint4* __restrict__ decoded, const float* ts_w = nullptr,
+                                                       float* ts_x = nullptr, float* ts_y = nullptr) {
+  if constexpr (DECODE) {
+    // NVFP4 x NVFP4: one thread also writes ts_x = fl32(amax / 2688) and ts_y = fl32(ts_w * ts_x).  Every
+    // workgroup reads only amax_p, which is neither of them; the linear that follows reads ts_y.
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const float tx = __fdiv_rn(amax_p[0], 2688.0f);
+      ts_x[0] = tx;
+      ts_y[0] = ts_w[0] * tx;
+    }
+  }
   w += (int64_t)blockIdx.y * 2 * n_blk;
   packed += (int64_t)blockIdx.y * n_blk;
   scales += (int64_t)blockIdx.y * n_blk;
@@ -433,15 +432,11 @@ void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const fl
 }
 
 void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
-                            uint16_t* decoded, hipStream_t s) {
+                            uint16_t* decoded, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s) {
   const int64_t n_blk = n_elems / 16;
   quantize_kernel<true><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
       reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales,
-      reinterpret_cast<uint4*>(decoded));
-}
-
-void launch_w4a4_tscale(const float* amax_x, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s) {
-  w4a4_tscale_kernel<<<1, 64, 0, s>>>(amax_x, ts_w, ts_x, ts_y);
+      reinterpret_cast<uint4*>(decoded), ts_w, ts_x, ts_y);
 }
 
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,
