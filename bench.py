@@ -361,7 +361,7 @@ def cpu_baseline(budget_s=10.0):
                       f"(M=1, K=5120), {calls} calls in {el:.1f} s, single thread"}
 
 
-def profile_run(what, launches):
+def profile_run(what, launches, wname="decode", m=1):
     """A short, untimed run for hardware-counter passes (rocprofv3 --pmc): `launches` launches of one kernel.
 
     decode: nvfp4_linear on the decode workload, cycling through rotated weight copies so that every
@@ -378,10 +378,32 @@ def profile_run(what, launches):
             GEMM), rotated MXFP4 weight copies;
     nvfp4_w4a4: nvfp4_linear_w4a4 on the prefill workload at M=2048 (X quantized to NVFP4 and decoded, then
             the BF16-MFMA GEMM), rotated weight copies;
-    quantize: nvfp4_quantize of the decode workload's BF16 weight (5120 x 5120), rotated input copies.
+    quantize: nvfp4_quantize of the decode workload's BF16 weight (5120 x 5120), rotated input copies;
+    dequant: nvfp4_dequant of the decode workload's quantized weight (5120 x 5120), rotated copies;
+    linear: nvfp4_linear on workload `wname` at M = `m` (e.g. small_m_up / small_m_down at M = 8 or 32,
+            gate_up at M = 1), rotated weight copies, the workspace-backed call as the bench rows make it.
     """
     torch.cuda.set_device(0)
-    if what == "quantize":
+    if what == "dequant":
+        packed, scales, tscale = nv.quantize(dev_bf16(WL.WORKLOADS["decode"].weight()))
+        rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() * 5))
+        outs = [torch.empty((packed.shape[0], packed.shape[1] * 2), dtype=torch.bfloat16, device="cuda")
+                for _ in range(2)]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p, s, t = rot.items[i % len(rot)]
+            nv.dequant(p, s, t, out=outs[i % 2])
+    elif what == "linear":
+        wl = WL.WORKLOADS[wname]
+        packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+        rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
+        x = dev_bf16(wl.activations(m))
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p, s, t = rot.items[i % len(rot)]
+            nv.linear(x, p, s, t, out=y)
+    elif what == "quantize":
         w = dev_bf16(WL.WORKLOADS["decode"].weight())
         rot = [w.clone() for _ in range(copies_needed(w.numel() * 2))]
         torch.cuda.synchronize()
@@ -468,9 +490,11 @@ def main():
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4",
-                                              "nvfp4_w4a4", "quantize"], default=None,
+                                              "nvfp4_w4a4", "quantize", "dequant", "linear"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
+    ap.add_argument("--workload", default="small_m_up", help="workload of a --profile linear run")
+    ap.add_argument("--m", type=int, default=8, help="activation rows of a --profile linear run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The library runs the linear on "
@@ -479,7 +503,7 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile:
-        profile_run(args.profile, args.launches)
+        profile_run(args.profile, args.launches, args.workload, args.m)
         return
     torch.cuda.set_device(0)
     nv.lib()
@@ -503,6 +527,7 @@ def main():
     for _ in range(max(1, args.warmup // c)):
         full.replay()
     torch.cuda.synchronize()
+    warm_graph(full)   # the same 0.1 s of loaded clock as every row below
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()

@@ -48,9 +48,10 @@ typedef enum {
   NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
   NVFP4_ERR_SHAPE = 2,       /* m < 0, n <= 0, k <= 0, k % 16 != 0, or a byte size overflows int64 */
   NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
-  NVFP4_ERR_ALIAS = 4,       /* an output buffer overlaps an input buffer */
-  NVFP4_ERR_DEVICE = 5,      /* HIP reported an error (no device, launch failure) */
-  NVFP4_ERR_UNSUPPORTED = 6, /* the current device is not gfx950, or an unknown kernel id */
+  NVFP4_ERR_DEVICE = 4,      /* HIP reported an error (no device, launch failure) */
+  NVFP4_ERR_UNSUPPORTED = 5, /* the current device is not gfx950, or an unknown kernel id */
+  NVFP4_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer (appended after the five
+                                codes above so that their values stay fixed) */
 } nvfp4_status;
 
 /* Human-readable name of a status code (static string, never NULL). */

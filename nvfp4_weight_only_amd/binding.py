@@ -19,7 +19,7 @@ KERNEL_AUTO, KERNEL_GEMV, KERNEL_SMALL_M, KERNEL_PREFILL = 0, 1, 2, 3
 KERNEL_IDS = {"auto": KERNEL_AUTO, "gemv": KERNEL_GEMV, "small_m": KERNEL_SMALL_M, "prefill": KERNEL_PREFILL}
 
 # Status codes (include/nvfp4.h).
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_DEVICE, ERR_UNSUPPORTED = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_UNSUPPORTED, ERR_ALIAS = range(7)
 
 # Every symbol include/nvfp4.h declares.
 EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_amax_accumulate",
@@ -139,8 +139,9 @@ def quantize_shared(members) -> Tuple[list, torch.Tensor]:
     return [(p, s) for p, s, _ in outs], outs[0][2]
 
 
-def dequant(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor) -> torch.Tensor:
-    """NVFP4 -> BF16 [n, k]."""
+def dequant(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NVFP4 -> BF16 [n, k] (into `out` when given)."""
     _need(packed, torch.uint8, "packed")
     _need(scales, torch.uint8, "scales")
     _need(tscale, torch.float32, "tscale")
@@ -148,7 +149,12 @@ def dequant(packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor) ->
     k = 2 * kh
     if scales.shape != (n, k // 16):
         raise ValueError("scales must be [n, k/16]")
-    out = torch.empty((n, k), dtype=torch.bfloat16, device=packed.device)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=packed.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (n, k):
+            raise ValueError("out must be [n, k]")
     _check(lib().nvfp4_dequant(packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(), n, k, out.data_ptr(),
                                _stream(packed)), "nvfp4_dequant")
     return out
@@ -164,15 +170,28 @@ def linear_workspace_bytes(m: int, n: int, k: int) -> int:
 
 # Workspaces owned by the binding, one per (device, stream): zero-filled when
 # allocated, and left with zero counters by every call, so they are reused as is.
+# A workspace that a larger shape supersedes is kept alive, never freed: a HIP
+# graph captured earlier may still hold its address, and if the allocator handed
+# that memory to another tensor, replays would write partial sums into it and
+# start from counters that are not zero.
 _workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+_superseded: list = []
 
 
 def _workspace_for(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            # The zero fill would only be recorded in the graph, not run, and the graph would own memory the
+            # binding cannot keep zeroed: the workspace must exist before capture.
+            raise RuntimeError(
+                f"nvfp4: no workspace of {nbytes} bytes for this stream during graph capture: call linear() with "
+                f"this shape once before capturing, or pass workspace= (a zero-filled uint8 device tensor)")
         # 256-byte aligned by the caching allocator; grown geometrically.
         size = max(nbytes, 2 * ws.numel() if ws is not None else 0)
+        if ws is not None:
+            _superseded.append(ws)
         ws = torch.zeros(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws

@@ -8,6 +8,7 @@ instructions disabled.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -43,14 +44,19 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
+    objs = [os.path.join(objdir, src + ".o") for src in SOURCES]
+    cmds = [[cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    if verbose:
+        for cmd in cmds:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
-        objs.append(obj)
+    # The sources compile independently: run the compiler processes side by side.
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        results = list(pool.map(lambda c: subprocess.run(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), cmds))
+    for cmd, r in zip(cmds, results):
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout.decode(errors="replace"))
+            raise subprocess.CalledProcessError(r.returncode, cmd)
     tmp = LIB_PATH + ".tmp"
     # -z defs: every symbol the library uses must resolve at link time (a missing
     # launcher would otherwise surface only when the library is loaded).

@@ -172,13 +172,11 @@ __device__ __forceinline__ uint64_t mx_uniform_ptr(const void* base) {
 // the K loop).
 __device__ __forceinline__ void mx_lds_dma16(const void* base, uint32_t off, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(mx_uniform_ptr(base))
-               : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(mx_uniform_ptr(base)), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void mx_lds_dma4(const void* base, uint32_t off, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(off), "s"(mx_uniform_ptr(base))
-               : "memory");
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(mx_uniform_ptr(base)), "{m0}"(m0) : "memory");
 }
 
 template <int N>

@@ -95,7 +95,7 @@ struct PdLds {
 // loads mix the packed and the scale arrays in one instruction).
 __device__ __forceinline__ void pd_lds_dma16_ptr(const void* src, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
 // One global_load_lds_dwordx4: 16 bytes per lane from base + off (a
@@ -104,14 +104,14 @@ __device__ __forceinline__ void pd_lds_dma16_ptr(const void* src, uint32_t lds) 
 // wait insertion loses track of which buffer a pending load writes at a loop
 // head and drains every load in flight; the instruction has no register
 // result, and the kernel orders LDS reads after it with explicit vmcnt waits.
-// M0 is not used by anything else in this kernel.
+// M0 is declared clobbered, so the compiler keeps nothing of its own there.
 __device__ __forceinline__ void pd_lds_dma16(const void* base, uint32_t off, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   const uint64_t b = (uint64_t)(uintptr_t)base;
   // readfirstlane returns int: widen through uint32_t, never by sign extension.
   const uint64_t bs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(bs) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(bs), "{m0}"(m0) : "memory");
 }
 
 template <typename U>

@@ -363,11 +363,11 @@ typedef __attribute__((address_space(3))) const void sk_lds_t;
 // for every load in flight (vmcnt(0)) once per ring turn, which drains the
 // pipeline.  The instruction has no register result, so nothing the compiler
 // allocates can be overwritten by the load in flight; the kernel's explicit
-// vmcnt waits order the LDS reads after it, and the kernel uses M0 for nothing
-// else.
+// vmcnt waits order the LDS reads after it.  M0 is declared clobbered, so the
+// compiler keeps nothing of its own there across the statement.
 __device__ __forceinline__ void sk_lds_dma16(const void* src, uint32_t lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);  // uniform per wavefront by construction
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
 
 template <typename U>

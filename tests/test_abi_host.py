@@ -208,3 +208,26 @@ def test_linear_w4a4_validation(L):
     assert f(A, 8, n, 512, C, D, E, E + 4096, A + 16, need, None) == B.ERR_ALIAS   # workspace overlaps x
     assert f(A, 8, n, 512, C, D, E, E + 4096, C, need, None) == B.ERR_ALIAS        # overlaps packed
     assert f(A, 8, n, 512, C, D, E, A, W, need, None) == B.ERR_ALIAS                # y overlaps x
+
+
+def test_binding_workspace_kept_when_superseded_and_refused_under_capture(monkeypatch):
+    """The binding's per-stream split-K workspace: a larger shape replaces it without freeing the old one
+    (a captured graph may still point at it), and no workspace is created while a capture is running."""
+    import torch
+
+    monkeypatch.setattr(B, "_workspaces", {})
+    monkeypatch.setattr(B, "_superseded", [])
+    capturing = {"on": False}
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: capturing["on"])
+    dev = torch.device("cpu", 0)
+    a = B._workspace_for(dev, 7, 1000)
+    assert a.numel() == 1000 and not a.any()
+    assert B._workspace_for(dev, 7, 800) is a                   # big enough: reused as is
+    b = B._workspace_for(dev, 7, 1500)                          # grows geometrically
+    assert b.numel() == 2000 and B._superseded == [a]           # the old one stays referenced
+    capturing["on"] = True
+    assert B._workspace_for(dev, 7, 2000) is b                  # an existing one may be used in a capture
+    with pytest.raises(RuntimeError, match="graph capture"):
+        B._workspace_for(dev, 7, 4000)                          # but none is allocated there
+    with pytest.raises(RuntimeError, match="graph capture"):
+        B._workspace_for(dev, 8, 16)                            # nor for a new stream

@@ -739,7 +739,8 @@ def test_mx_dequant_bit_exact(nv):
     scales = rng.integers(0, 256, size=(40, 4), dtype=np.uint8)
     scales.flat[:5] = [0, 1, 127, 254, 255]
     got = bf16_host(nv.mx_dequant(*_mx_dev(packed, scales)))
-    want = O.f32_to_bf16_rne(MXO.dequant_exact(packed, scales).astype(np.float32))
+    with np.errstate(over="ignore"):   # scale byte 254 times 6 overflows FP32 to inf, as the format says
+        want = O.f32_to_bf16_rne(MXO.dequant_exact(packed, scales).astype(np.float32))
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
     assert np.array_equal(np.isnan(f(got)), np.isnan(f(want)))
     ok = ~np.isnan(f(want))
@@ -973,3 +974,43 @@ def test_graph_replays_match_eager(nv):
             assert torch.equal(v.view(torch.int16), eager[k].view(torch.int16)), f"replay {rep}: {k}"
         for k, v in quant.items():
             assert torch.equal(v, eager["q_" + k]), f"replay {rep}: quantize {k}"
+
+
+def test_graph_keeps_binding_workspace_after_growth(nv):
+    """A graph captured with the binding's split-K workspace stays correct after a larger shape on the same
+    stream grows that workspace: the old one is kept, so a tensor allocated afterwards cannot take its memory."""
+    st = torch.cuda.Stream()
+    m, n, k = 8, 300, 2048
+    q, rq = q_both(nv, WL.normal_bf16((n, k), 0.02, 4100))
+    x = WL.normal_bf16((m, k), 1.0, 4101)
+    xd = to_dev_bf16(x)
+    y_ref, bound = O.linear_ref(x, *rq)
+    assert nv.linear_workspace_bytes(m, n, k) > 0, "shape expected to split K"
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(st):
+        nv.linear(xd, *q, out=out)                       # allocates the stream's workspace eagerly
+    torch.cuda.synchronize()
+    eager = out.clone()
+    check_linear(bf16_host(eager), y_ref, bound, "split-K before capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            nv.linear(xd, *q, out=out)
+    torch.cuda.synchronize()
+    # A larger split shape on the same stream grows the binding's workspace.
+    m2, n2, k2 = 32, 5120, 4096
+    big = nv.linear_workspace_bytes(m2, n2, k2)
+    assert big > nv.linear_workspace_bytes(m, n, k)
+    q2, _ = q_both(nv, WL.normal_bf16((n2, k2), 0.02, 4102))
+    x2 = to_dev_bf16(WL.normal_bf16((m2, k2), 1.0, 4103))
+    with torch.cuda.stream(st):
+        nv.linear(x2, *q2)
+    torch.cuda.synchronize()
+    sentinel = torch.full((1 << 20,), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert bool((sentinel == 0x5A).all()), f"replay {rep} wrote into a later allocation"
