@@ -337,28 +337,105 @@ def bench_w4a4_nvfp4_row(m, reps):
     return {f"nvfp4_w4a4_prefill_m{m}": row}
 
 
-def cpu_baseline(budget_s=10.0):
-    """The oracle's linear (float64) on the decode workload, single-threaded, for about budget_s seconds."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands (numpy, float64), timed on the host
+# cores in a child process (fork after the data are built, no GPU there).
+# ---------------------------------------------------------------------------
+_CPU = {}   # the data of the configuration being timed, inherited by the forked workers
+
+# (name, k, weight kind, activation rows of the linear calls); the weight rows are a bounded sample:
+# the first rows of the workload's weight (plain ~N(0, 0.02), with the outlier columns for decode; for the
+# merged gate/up weight a plain ~N(0, 0.02) stand-in, since its two halves are rescaled over the whole tensor).
+CPU_CONFIGS = [("tiny", 256, 512, "plain", (1,)), ("decode", 5120, 5120, "outliers", (1,)),
+               ("gate_up", 34816, 5120, "plain", (1,)), ("small_m_up", 17408, 5120, "plain", (8, 32)),
+               ("small_m_down", 5120, 17408, "plain", (8, 32)), ("prefill", 17408, 5120, "plain", (512, 2048))]
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
+    _CPU["limits"] = threadpool_limits(limits=1)   # one thread per worker: the pool is the parallelism
+
+
+def _cpu_task(args):
     from oracle import nvfp4_oracle as O
-    wl = WL.WORKLOADS["decode"]
-    w = wl.weight()
-    x = wl.activations(1)
-    rows = 1024   # bounded sample: 1024 of the 5120 weight rows
-    p, s, t = O.quantize(w[:rows], amax=O.tensor_amax(w))
-    with threadpool_limits(limits=1):
-        calls = 0
-        t0 = time.perf_counter()
-        while True:
-            O.linear_ref(x, p, s, t)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s:
+    op, r0, r1 = args
+    d = _CPU
+    if op == "quantize":
+        O.quantize(d["w"][r0:r1])
+    elif op == "dequant":
+        O.dequant(d["p"][r0:r1], d["s"][r0:r1], d["t"])
+    else:
+        O.linear_ref(d["x"][op], d["p"][r0:r1], d["s"][r0:r1], d["t"])
+    return r1 - r0
+
+
+def _cpu_time_op(pool, op, rows_per_task, cores, budget_s):
+    """Rounds of one task per worker until budget_s of wall time; returns (rows processed, seconds)."""
+    tasks = [(op, i * rows_per_task, (i + 1) * rows_per_task) for i in range(cores)]
+    rows, t0 = 0, time.perf_counter()
+    while True:
+        rows += sum(pool.map(_cpu_task, tasks))
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return rows, el
+
+
+def cpu_baseline_run(budget_s=20.0):
+    """The oracle's quantize, dequant and float64 linear per configuration on all usable host cores."""
+    import multiprocessing
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    model = "unknown"
+    with open("/proc/cpuinfo") as f:
+        for line in f:
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
                 break
-    nbytes = linear_bytes(1, rows, wl.k) * calls
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle linear_ref (float64) on rows 0..{rows - 1} of the decode weight "
-                      f"(M=1, K=5120), {calls} calls in {el:.1f} s, single thread"}
+    ops = sum(2 + len(ms) for *_, ms in CPU_CONFIGS)
+    per_op = budget_s / ops
+    ctx = multiprocessing.get_context("fork")
+    out = {}
+    for name, n, k, kind, ms in CPU_CONFIGS:
+        # rows per task: about 0.15 s of work each (quantize ~370 ns, dequant ~11 ns per element on one core)
+        rq = max(1, min(-(-n // cores), 400_000 // k))
+        rd = max(1, min(-(-n // cores), 15_000_000 // k))
+        rl = {m: max(1, min(-(-n // cores), int(0.15 / (k * (10 + 0.5 * m) * 1e-9)))) for m in ms}
+        wrows, rows = cores * rq, cores * max([rd, *rl.values()])
+        w = WL.weight_with_outlier_columns(wrows, k) if kind == "outliers" else WL.weight_plain(wrows, k)
+        # Dequant and linear inputs: uniform random codes and E4M3 scale bytes 0x28..0x48 (1/8 .. 8); the
+        # oracle's cost does not depend on the values, and quantizing this many rows first would take minutes.
+        rng = np.random.default_rng(8)
+        p = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+        sc = rng.integers(0x28, 0x49, size=(rows, k // 16), dtype=np.uint8)
+        _CPU.clear()
+        _CPU.update(w=w, p=p, s=sc, t=np.float32(1.0 / 64), x={m: WL.activations(m, k) for m in ms})
+        res = {"n": n, "k": k}
+        with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+            r, el = _cpu_time_op(pool, "quantize", rq, cores, per_op)
+            res["quantize_gb_s"] = round(r * k * (2 + 2 + 0.5625) / el / 1e9, 4)
+            r, el = _cpu_time_op(pool, "dequant", rd, cores, per_op)
+            res["dequant_gb_s"] = round(r * k * 2.5625 / el / 1e9, 4)
+            for m in ms:
+                r, el = _cpu_time_op(pool, m, rl[m], cores, per_op)
+                nb = r * (k // 2 + k // 16 + 2 * m) + 2 * m * k + 4
+                res[f"linear_m{m}_gb_s"] = round(nb / el / 1e9, 4)
+                res[f"linear_m{m}_gflop_s"] = round(2.0 * m * r * k / el / 1e9, 3)
+        out[name] = res
+    head = out["decode"]["linear_m1_gb_s"]
+    return {"value": head, "unit": "GB/s", "cores": cores, "kind": "oracle", "cpu_model": model,
+            "sample": (f"oracle (numpy float64) on {cores} host cores (one worker process each, one BLAS thread): "
+                       f"value = linear_ref at M=1 on the decode shape (K=5120); per_config times quantize "
+                       f"(amax + codes of the first weight rows; GB/s on 4.5625 B/element), dequant (2.5625 B/element) and "
+                       f"linear_ref (random codes, scales 1/8..8) on row samples of every configuration, about "
+                       f"{per_op:.1f} s each"),
+            "per_config": out}
+
+
+def cpu_baseline(budget_s=20.0):
+    """Runs cpu_baseline_run in a child process (this process has initialised the GPU, so it forks nothing)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--cpu-budget",
+                        str(budget_s)], capture_output=True, text=True, check=True)
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def profile_run(what, launches, wname="decode", m=1):
@@ -488,7 +565,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3700)
     ap.add_argument("--warmup", type=int, default=370)
     ap.add_argument("--rows", default="all", help="'all' or 'none': also measure the other rows of the hot path")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4",
                                               "nvfp4_w4a4", "quantize", "dequant", "linear"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
@@ -496,6 +574,9 @@ def main():
     ap.add_argument("--workload", default="small_m_up", help="workload of a --profile linear run")
     ap.add_argument("--m", type=int, default=8, help="activation rows of a --profile linear run")
     args = ap.parse_args()
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline_run(args.cpu_budget)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The library runs the linear on "
               f"one MI355X; a multi-GPU layer would shard the weight rows (N) or whole 16-element K blocks "

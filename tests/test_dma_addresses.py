@@ -1,0 +1,87 @@
+"""CPU replay of the prefill GEMM's LDS-DMA source addresses (csrc/prefill.hip,
+prefill_dma_kernel, dense form): for every workgroup, wavefront, load
+instruction, lane and step -- including the loads issued past the last step,
+which repeat the last step or group -- the 16 bytes each lane reads must lie
+inside its buffer (x, packed or scales), the activation offsets must fit the
+32-bit lane offsets the kernel uses, and every LDS destination must lie inside
+its stage or group buffer.  The formulas are written out from the kernel's
+source; no GPU is involved."""
+import numpy as np
+import pytest
+
+BM, BN, BK, GK, WSLOTS = 128, 272, 64, 256, 9
+LX, LW = 4, 10
+WLAST = BN * WSLOTS - 64
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def prefill_dma_check(m, n, k, clamp=True):
+    assert k % GK == 0
+    n_tiles, m_tiles = _cdiv(n, BN), _cdiv(m, BM)
+    nsteps = k // BK
+    kh, ks = k // 2, k // 16
+    lane = np.arange(64)
+    w = np.arange(4)[:, None]
+    # Steps issued: 0..3 before the loop, then t + 4 for t < nsteps (up to nsteps + 3), clamped to nsteps - 1.
+    tc = np.minimum(np.arange(nsteps + 4), nsteps - 1)
+    gc = np.unique(tc >> 2)
+    worst_x32 = 0
+    for mt in range(m_tiles):
+        m0 = mt * BM
+        for i in range(LX):
+            q = w + 4 * i
+            r = 8 * q + (lane >> 3)                               # [4, 64]
+            gm = np.where(m0 + r < m, r, m - 1 - m0) if clamp else r
+            off = gm * k * 2 + 16 * ((lane & 7) ^ (r & 7))        # 32-bit lane offset from x + m0 k + tc * 128
+            assert off.min() >= 0 and off.max() < 2 ** 32
+            worst_x32 = max(worst_x32, int(off.max()))
+            base = m0 * k * 2 + tc[:, None, None] * (2 * BK)
+            addr = base + off[None]
+            assert addr.min() >= 0 and (addr + 16).max() <= m * k * 2, (m, n, k, mt, i)
+            dst = 1024 * (w + 4 * i) + 16 * lane                  # bytes into the 16 KiB X stage
+            assert dst.min() >= 0 and (dst + 16).max() <= BM * 8 * 16
+    for nt in range(n_tiles):
+        n0 = nt * BN
+        for i in range(LW):
+            q0 = 64 * (w + 4 * i)
+            qs = np.minimum(q0, WLAST)
+            slot = qs + lane                                      # [4, 64]
+            r, piece = slot // WSLOTS, slot % WSLOTS
+            gn = np.where(n0 + r < n, n0 + r, n - 1) if clamp else n0 + r
+            is_scale = piece == 8
+            # Each instruction's scale lanes step 16 bytes per group, packed lanes 128.
+            for g in gc:
+                pa = gn * kh + 16 * piece + g * (GK // 2)
+                sa = gn * ks + g * (GK // 16)
+                assert (pa[~is_scale] >= 0).all() and (pa[~is_scale] + 16 <= n * kh).all(), (m, n, k, nt, i, g)
+                assert (sa[is_scale] >= 0).all() and (sa[is_scale] + 16 <= n * ks).all(), (m, n, k, nt, i, g)
+            dst = 16 * slot
+            assert dst.min() >= 0 and (dst + 16).max() <= BN * WSLOTS * 16
+    return worst_x32
+
+
+# The down projection (N=5120, K=17408) and the prefill shape at the timed M, and the ragged test shapes.
+SHAPES = [(512, 5120, 17408), (2048, 5120, 17408), (512, 17408, 5120), (2048, 17408, 5120),
+          (200, 560, 768), (129, 545, 256), (300, 300, 2560), (130, 257, 2304), (65, 17, 256), (1, 1, 256)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_prefill_dma_sources_in_bounds(m, n, k):
+    prefill_dma_check(m, n, k)
+
+
+def test_prefill_dma_largest_supported_k_offsets_fit_32_bits():
+    # prefill_dma_supported admits k < 2^24: the largest activation lane offset must still fit 32 bits.
+    k = (1 << 24) - GK
+    r = 127
+    assert r * k * 2 + 16 * 7 < 2 ** 32
+
+
+def test_replay_catches_a_planted_overrun():
+    # The checker itself: without the kernel's clamps of rows past m and n, a ragged tile reads past the end.
+    with pytest.raises(AssertionError):
+        prefill_dma_check(129, 545, 256, clamp=False)
+    prefill_dma_check(129, 545, 256, clamp=True)
