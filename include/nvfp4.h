@@ -133,9 +133,11 @@ nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
  *
  * Workspace contract:
  *   - a device pointer, 16-byte aligned, not overlapping any argument buffer;
+ *   - layout: the arrival counters in the first 16 KiB (the same bytes for
+ *     every shape), then the FP32 partial sums;
  *   - zero-filled once before its first use; every call leaves the bytes that
- *     must start at zero (the arrival counters) at zero again, so later calls
- *     need no clearing;
+ *     must start at zero (the arrival counters) at zero again, so later calls,
+ *     of any shape, need no clearing;
  *   - calls that may run at the same time (other streams) need separate
  *     workspaces;
  *   - NULL, or workspace_bytes below the size returned above, runs the unsplit
@@ -147,6 +149,28 @@ int64_t nvfp4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 nvfp4_status nvfp4_linear_ws(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* packed, const uint8_t* scales, const float* tscale,
                              uint16_t* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_linear_ws without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The split-K
+ * workspace is a library-owned device array of nvfp4_linear_noalloc_max_bytes()
+ * bytes (8 MiB, enough for every split the small-M kernel plans), one copy per
+ * GPU, held until the process ends; its address is looked up once per device,
+ * on the first call with that device current, which also clears its counter
+ * region with a kernel on `stream`.  No call allocates or frees memory.
+ * Same arguments, results (bit for bit those of nvfp4_linear_ws with a
+ * workspace of at least nvfp4_linear_workspace_bytes(m, n, k) bytes) and
+ * errors as nvfp4_linear; a shape whose workspace would exceed the array
+ * returns NVFP4_ERR_SHAPE, and a failed address lookup NVFP4_ERR_DEVICE.
+ * Every call on one GPU shares that GPU's array and leaves its counters at
+ * zero: calls that may overlap on one GPU (other streams, other threads)
+ * race and must not be issued.
+ */
+int64_t nvfp4_linear_noalloc_max_bytes(void);
+nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                                  const uint8_t* packed, const uint8_t* scales, const float* tscale,
+                                  uint16_t* y, void* stream);
 
 /* Kernel ids for nvfp4_linear_forced. */
 #define NVFP4_KERNEL_AUTO 0

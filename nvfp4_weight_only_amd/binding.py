@@ -27,7 +27,8 @@ EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_ama
             "nvfp4_linear_ws", "nvfp4_quantize_experts", "nvfp4_dequant_experts", "nvfp4_linear_routed",
             "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_mx_quantize", "nvfp4_mx_dequant", "nvfp4_mx_gemm",
             "nvfp4_mx_linear_w4a4", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes",
-            "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes")
+            "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes",
+            "nvfp4_linear_noalloc", "nvfp4_linear_noalloc_max_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -58,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
         L.nvfp4_linear.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_forced.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.nvfp4_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.nvfp4_linear_noalloc_max_bytes.argtypes = []
+        L.nvfp4_linear_noalloc_max_bytes.restype = i64
         L.nvfp4_linear_ws.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
         L.nvfp4_quantize_experts.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
@@ -74,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
-            getattr(L, name).restype = i64 if name.endswith("_workspace_bytes") else i32
+            getattr(L, name).restype = i64 if name.endswith(("_workspace_bytes", "_max_bytes")) else i32
         _lib = L
     return _lib
 
@@ -239,6 +243,24 @@ def linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: 
             ws = workspace
         wptr, wbytes = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
         _check(lib().nvfp4_linear_ws(*head, wptr, wbytes, stream), "nvfp4_linear_ws")
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+                   out: torch.Tensor) -> torch.Tensor:
+    """The linear through nvfp4_linear_noalloc: the split-K workspace is the library's own device array, so the
+    call allocates nothing (`out` is required for the same reason)."""
+    _need(x, torch.bfloat16, "x")
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    _need(tscale, torch.float32, "tscale")
+    _need(out, torch.bfloat16, "out")
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape != (n, k // 2) or scales.shape != (n, k // 16) or out.shape != (m, n):
+        raise ValueError("packed/scales/out do not match x")
+    _check(lib().nvfp4_linear_noalloc(x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(),
+                                      tscale.data_ptr(), out.data_ptr(), _stream(x)), "nvfp4_linear_noalloc")
     return out
 
 

@@ -39,6 +39,9 @@ void launch_gemv_routed(const uint16_t* x, int64_t t_count, int64_t topk, const 
 // Small-M kernel.  With a workspace of at least skinny_workspace_bytes(m, n, k)
 // bytes (zero-filled before its first use; left that way by every launch) it may
 // split K across workgroups; with none it runs unsplit.
+// The workspace starts with kSkinnyCounterBytes of arrival counters (the same
+// region for every shape), followed by the FP32 partial sums.
+constexpr int64_t kSkinnyCounterBytes = 16384;
 int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                    const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes, hipStream_t s);

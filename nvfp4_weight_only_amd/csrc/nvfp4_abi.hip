@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "launch.hpp"
 #include "nvfp4.h"
@@ -136,6 +137,45 @@ nvfp4_status mx_sizes(int64_t rows, int64_t k, WeightSizes* s) {
 
 int64_t mx_round16(int64_t b) { return (b + 15) / 16 * 16; }
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch for nvfp4_linear_noalloc: the split-K workspace of the
+// small-M kernel (arrival counters, then FP32 partial sums) in a file-scope
+// device array, so that the call allocates nothing.  Every GPU the library
+// runs on holds its own copy of the array until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: host code uses
+// only the device address that hipGetSymbolAddress returns for the current
+// device (kept per device below).
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = 8 << 20;   // covers every split the small-M kernel plans (at most 6.7 MiB)
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_scratch_ready[kMaxDevices];  // 0 not set up, 1 set up
+std::mutex g_scratch_mutex;
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The current device's copy of `scratch` (set up once per device: its address,
+// and the arrival-counter region cleared by a kernel on `s`, which the caller's
+// first call then follows in stream order).  NULL on a HIP error.
+void* scratch_for_current_device(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (g_scratch_ready[dev].load(std::memory_order_acquire) == 1) return g_scratch_ptr[dev];
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ready[dev].load(std::memory_order_relaxed) == 1) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+  zero_words_kernel<<<16, 256, 0, s>>>(static_cast<uint32_t*>(ptr), nvfp4::kSkinnyCounterBytes / 4);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  g_scratch_ptr[dev] = ptr;
+  g_scratch_ready[dev].store(1, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +276,22 @@ nvfp4_status nvfp4_linear_ws(const uint16_t* x, int64_t m, int64_t n, int64_t k,
                              const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
                              int64_t workspace_bytes, void* stream) {
   return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, workspace, workspace_bytes, stream);
+}
+
+int64_t nvfp4_linear_noalloc_max_bytes(void) { return kScratchBytes; }
+
+nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                                  const uint8_t* scales, const float* tscale, uint16_t* y, void* stream) {
+  nvfp4_status st = validate_linear(x, m, n, k, packed, scales, tscale, y);
+  if (st != NVFP4_OK) return st;
+  if (m == 0) return NVFP4_OK;
+  const int64_t need = nvfp4_linear_workspace_bytes(m, n, k);
+  if (need < 0 || need > kScratchBytes) return NVFP4_ERR_SHAPE;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  if (need == 0) return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, nullptr, 0, stream);
+  void* ws = scratch_for_current_device(static_cast<hipStream_t>(stream));
+  if (ws == nullptr) return NVFP4_ERR_DEVICE;
+  return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, ws, kScratchBytes, stream);
 }
 
 nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,

@@ -697,7 +697,12 @@ SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k, bool split) {
   pl.row_blocks = ceil_div(n, rows);
   pl.npad = round_up(n, 4);
   if (pl.slices > 1) {
-    pl.count_bytes = round_up(pl.row_blocks * pl.gy * 4, 256);
+    // The arrival counters sit in a region of fixed size at the start of the
+    // workspace, the same for every shape, so that a workspace shared by
+    // several shapes never finds one shape's partial sums where another keeps
+    // its counters (every call leaves the counters it used at zero).
+    if (pl.row_blocks * pl.gy * 4 > kSkinnyCounterBytes) return skinny_plan(m, n, k, false);
+    pl.count_bytes = kSkinnyCounterBytes;
     pl.ws_bytes = pl.count_bytes + (int64_t)pl.slices * m * pl.npad * 4;
   }
   return pl;

@@ -78,9 +78,10 @@ def test_linear_workspace_bytes(L):
     assert wb(1, 5120, 5120) == 0            # GEMV: no workspace
     assert wb(65, 17408, 5120) == 0          # prefill GEMM: no workspace
     assert wb(8, 17408, 5120) == 0           # small-M, 68 rows x 1 K slice per workgroup
-    # small-M down projection: 64 blocks of 80 rows x 4 K slices; 256 B of counters + 4 * m * n FP32 partials
-    assert wb(8, 5120, 17408) == 256 + 4 * 8 * 5120 * 4
-    assert wb(32, 5120, 17408) == 256 + 4 * 32 * 5120 * 4
+    # small-M down projection: 64 blocks of 80 rows x 4 K slices; the fixed 16 KiB counter region + 4 * m * n
+    # FP32 partials
+    assert wb(8, 5120, 17408) == 16384 + 4 * 8 * 5120 * 4
+    assert wb(32, 5120, 17408) == 16384 + 4 * 32 * 5120 * 4
     assert wb(-1, 64, 64) == -1 and wb(8, 64, 24) == -1 and wb(8, 0, 64) == -1
 
 
@@ -231,3 +232,19 @@ def test_binding_workspace_kept_when_superseded_and_refused_under_capture(monkey
         B._workspace_for(dev, 7, 4000)                          # but none is allocated there
     with pytest.raises(RuntimeError, match="graph capture"):
         B._workspace_for(dev, 8, 16)                            # nor for a new stream
+
+
+def test_linear_noalloc_validation(L):
+    f = L.nvfp4_linear_noalloc
+    assert L.nvfp4_linear_noalloc_max_bytes() == 8 << 20
+    # every split the small-M kernel plans for m <= 64 fits the library's scratch
+    for m in (2, 8, 32, 64):
+        for n in (16, 300, 1280, 5120, 13651, 17408):
+            for k in (256, 4096, 17408):
+                assert 0 <= L.nvfp4_linear_workspace_bytes(m, n, k) <= L.nvfp4_linear_noalloc_max_bytes()
+    assert f(None, 8, 64, 64, Bp, C, D, E, None) == B.ERR_NULL
+    assert f(A, 8, 64, 24, Bp, C, D, E, None) == B.ERR_SHAPE          # k % 16 != 0
+    assert f(A, -1, 64, 64, Bp, C, D, E, None) == B.ERR_SHAPE         # m < 0
+    assert f(A + 8, 8, 64, 64, Bp, C, D, E, None) == B.ERR_ALIGN
+    assert f(A, 8, 64, 64, Bp, C, D, A + 16, None) == B.ERR_ALIAS     # y overlaps x
+    assert f(None, 0, 64, 64, Bp, C, D, None, None) == B.OK           # m = 0 no-op
