@@ -944,3 +944,93 @@ def test_mutation_mx_transposed_linear(monkeypatch):
         v = orig(p, s)
         return np.concatenate([v[:, 32:], v[:, :32]], axis=1) if v.shape[1] >= 64 else v
     _expect_mx_pin_failure(monkeypatch, "dequant_exact", swapped_halves)
+
+
+# ---------------------------------------------------------------------------
+# The library's kernel-native layout (oracle/layout_oracle.py): pinned by the
+# hand-derived positions of tests/golden/kernel_native_layout.txt, an
+# element-level check of every nibble and scale, the round trip and padding.
+# ---------------------------------------------------------------------------
+from oracle import layout_oracle as LO  # noqa: E402
+
+
+def _golden_layout_lines():
+    path = os.path.join(os.path.dirname(__file__), "golden", "kernel_native_layout.txt")
+    with open(path) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def test_kernel_native_layout_golden_positions():
+    rng = np.random.default_rng(7100)
+    packed = rng.integers(0, 256, size=(16, 128), dtype=np.uint8)
+    scales = rng.integers(0, 127, size=(16, 16), dtype=np.uint8)
+    prep = LO.prepare(packed, scales)
+    assert prep.size == 2 * 1152
+    lines = _golden_layout_lines()
+    assert len(lines) == 18
+    for ln in lines:
+        if ln[0] == "packed":
+            blk, slot, word = int(ln[1]), int(ln[2]), int(ln[3].rstrip(":"))
+            row, src = int(ln[4]), [int(v) for v in ln[5:9]]
+            off = blk * 1152 + 16 * slot + 4 * word
+            assert list(prep[off:off + 4]) == list(packed[row, src]), ln
+        else:
+            blk, word = int(ln[1]), int(ln[2].rstrip(":"))
+            row, src = int(ln[3]), [int(v) for v in ln[4:8]]
+            off = blk * 1152 + 1024 + 4 * word
+            assert list(prep[off:off + 4]) == list(scales[row, src]), ln
+
+
+def test_kernel_native_layout_every_element_and_scale():
+    """Each element k of row n sits at block (n // 16, k // 128), slot 16 g + n % 16, word i, nibble e with
+    k % 128 = 32 i + 8 g + e, and its scale in byte i of word 16 (g // 2) + n % 16 of the same block."""
+    rng = np.random.default_rng(7101)
+    n, k = 37, 384
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 127, size=(n, k // 16), dtype=np.uint8)
+    prep = LO.prepare(packed, scales)
+    codes = np.empty((n, k), dtype=np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = packed & 0xF, packed >> 4
+    quads = k // 128
+    for row in range(n):
+        t, r = divmod(row, 16)
+        for kk in range(k):
+            q, rem = divmod(kk, 128)
+            i, rem = divmod(rem, 32)
+            g, e = divmod(rem, 8)
+            base = (t * quads + q) * 1152
+            byte = prep[base + 16 * (16 * g + r) + 4 * i + e // 2]
+            assert ((byte >> (4 * (e % 2))) & 0xF) == codes[row, kk]
+            assert prep[base + 1024 + 4 * (16 * (g // 2) + r) + i] == scales[row, kk // 16]
+
+
+def test_kernel_native_layout_round_trip_and_padding():
+    rng = np.random.default_rng(7102)
+    for n, k in [(16, 128), (33, 256), (5, 640), (48, 128)]:
+        packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        scales = rng.integers(0, 127, size=(n, k // 16), dtype=np.uint8)
+        prep = LO.prepare(packed, scales)
+        assert prep.size == LO.prepared_bytes(n, k) == -(-n // 16) * 16 * k * 9 // 16
+        p2, s2 = LO.unprepare(prep, n, k)
+        assert np.array_equal(p2, packed) and np.array_equal(s2, scales)
+        assert LO.padding_is_zero(prep, n, k)
+    with pytest.raises(ValueError):
+        LO.prepared_bytes(16, 96)
+
+
+def test_mutation_kernel_native_swapped_lane_groups(monkeypatch):
+    """A planted mistake (slots of lane groups 1 and 2 exchanged) fails the golden positions."""
+    orig = LO.prepare
+
+    def bad(packed, scales):
+        out = orig(packed, scales).copy()
+        for blk in range(out.size // 1152):
+            b = blk * 1152
+            s1 = out[b + 256:b + 512].copy()
+            out[b + 256:b + 512] = out[b + 512:b + 768]
+            out[b + 512:b + 768] = s1
+        return out
+
+    monkeypatch.setattr(LO, "prepare", bad)
+    with pytest.raises(AssertionError):
+        test_kernel_native_layout_golden_positions()
