@@ -156,6 +156,55 @@ def bench_linear_row(wname, m, reps, kernel="auto"):
     return out
 
 
+def bench_prepared_row(wname, m, reps):
+    """nvfp4_linear_prepared on the kernel-native layout of the workload's weight, rotated copies (the same
+    algorithmic bytes as the checkpoint layout: the layout is a permutation of them)."""
+    wl = WL.WORKLOADS[wname]
+    packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+    prep = nv.prepare(packed, scales)
+    del packed, scales
+    c = copies_needed(prep.numel())
+    items = [(prep.clone(), tscale.clone()) for _ in range(c)]
+    del prep
+    x = dev_bf16(wl.activations(m))
+    y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+    calls = [(lambda p=p, t=t: nv.linear_prepared(x, p, t, wl.n, out=y)) for (p, t) in items]
+    g = graph_of(calls)
+    warm_graph(g)
+    ms = time_graph_replays(g, reps, len(items))
+    nbytes = linear_bytes(m, wl.n, wl.k)
+    flops = 2.0 * m * wl.n * wl.k
+    out = {"m": m, "n": wl.n, "k": wl.k, "copies": c, "layout": "kernel-native (nvfp4_prepare)",
+           "us_per_call": round(ms * 1e3, 3), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "tflop_s": round(flops / (ms * 1e-3) / 1e12, 2), "weight_streams_per_s": round(1.0 / (ms * 1e-3), 1)}
+    out["hbm_frac"] = round(out["gb_s"] / HBM_PEAK_GBS, 4)
+    out["mfma_frac"] = round(out["tflop_s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    del items, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_prepare_row(reps):
+    """nvfp4_prepare (checkpoint -> kernel-native layout) of the small-M up weight: read and write 0.5625 B per
+    element each."""
+    wl = WL.WORKLOADS["small_m_up"]
+    packed, scales, _ = nv.quantize(dev_bf16(wl.weight()))
+    c = copies_needed(2 * (packed.numel() + scales.numel()))
+    items = [(packed.clone(), scales.clone(), torch.empty(nv.prepared_bytes(wl.n, wl.k), dtype=torch.uint8,
+                                                           device="cuda")) for _ in range(c)]
+    L = nv.lib()
+
+    def call(p, s, o):
+        L.nvfp4_prepare(p.data_ptr(), s.data_ptr(), wl.n, wl.k, o.data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    g = graph_of([(lambda it=it: call(*it)) for it in items])
+    warm_graph(g)
+    ms = time_graph_replays(g, reps, len(items))
+    nbytes = 2 * (packed.numel() + scales.numel())
+    return {"n": wl.n, "k": wl.k, "copies": c, "us_per_call": round(ms * 1e3, 3),
+            "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def bench_quant_rows(reps):
     """Quantizer (amax + quantize passes) and dequantizer on the decode weight, rotated."""
     wl = WL.WORKLOADS["decode"]
@@ -458,7 +507,8 @@ def profile_run(what, launches, wname="decode", m=1):
     quantize: nvfp4_quantize of the decode workload's BF16 weight (5120 x 5120), rotated input copies;
     dequant: nvfp4_dequant of the decode workload's quantized weight (5120 x 5120), rotated copies;
     linear: nvfp4_linear on workload `wname` at M = `m` (e.g. small_m_up / small_m_down at M = 8 or 32,
-            gate_up at M = 1), rotated weight copies, the workspace-backed call as the bench rows make it.
+            gate_up at M = 1), rotated weight copies, the workspace-backed call as the bench rows make it;
+    prepared: nvfp4_linear_prepared on the kernel-native layout of workload `wname` at M = `m`, rotated copies.
     """
     torch.cuda.set_device(0)
     if what == "dequant":
@@ -480,6 +530,18 @@ def profile_run(what, launches, wname="decode", m=1):
         for i in range(launches):
             p, s, t = rot.items[i % len(rot)]
             nv.linear(x, p, s, t, out=y)
+    elif what == "prepared":
+        wl = WL.WORKLOADS[wname]
+        packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
+        prep = nv.prepare(packed, scales)
+        del packed, scales
+        items = [(prep.clone(), tscale.clone()) for _ in range(copies_needed(prep.numel()))]
+        x = dev_bf16(wl.activations(m))
+        y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p, t = items[i % len(items)]
+            nv.linear_prepared(x, p, t, wl.n, out=y)
     elif what == "quantize":
         w = dev_bf16(WL.WORKLOADS["decode"].weight())
         rot = [w.clone() for _ in range(copies_needed(w.numel() * 2))]
@@ -568,7 +630,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4",
-                                              "nvfp4_w4a4", "quantize", "dequant", "linear"], default=None,
+                                              "nvfp4_w4a4", "quantize", "dequant", "linear", "prepared"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
     ap.add_argument("--workload", default="small_m_up", help="workload of a --profile linear run")
@@ -634,6 +696,14 @@ def main():
             log(f"row {key}")
             rows[key] = bench_linear_row(wname, mm, reps)
             log(f"  {rows[key]}")
+        for wname, mm, reps in [("small_m_up", 8, 30), ("small_m_up", 32, 30), ("small_m_down", 8, 30),
+                                ("small_m_down", 32, 30), ("gate_up", 1, 30), ("decode", 1, 30)]:
+            key = f"prepared_{wname}_m{mm}"
+            log(f"row {key}")
+            rows[key] = bench_prepared_row(wname, mm, reps)
+            log(f"  {rows[key]}")
+        rows["prepare_small_m_up_17408x5120"] = bench_prepare_row(20)
+        log(f"  prepare: {rows['prepare_small_m_up_17408x5120']}")
         log("rows quantize/dequant")
         rows.update(bench_quant_rows(20))
         log(f"  {rows['quantize_decode_5120x5120']} {rows['dequant_decode_5120x5120']}")

@@ -172,6 +172,50 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
                                   const uint8_t* packed, const uint8_t* scales, const float* tscale,
                                   uint16_t* y, void* stream);
 
+/*
+ * Kernel-native weight layout.  imp "docs/quantization.md", "NVFP4 kernel
+ * pipeline" (Dense layers): the loader keeps the checkpoint's packed weights
+ * and re-lays scale factors once for its prefill GEMM.  Here the same bytes
+ * (values unchanged) are re-laid once, for k a multiple of 128, into the order
+ * the gfx950 decode kernels read them:
+ *   - rows in tiles of 16 (n padded with zero rows to a multiple of 16), k in
+ *     quads of 128 elements; block (tile t, quad q) is 1152 bytes at offset
+ *     (t * k/128 + q) * 1152;
+ *   - its first 1024 bytes are 64 slots of 16 bytes: slot 16 g + r (g = 0..3,
+ *     r = 0..15) holds, as 4-byte words i = 0..3, the elements
+ *     128 q + 32 i + 8 g .. + 8 of row 16 t + r (low nibble first, as in
+ *     packed);
+ *   - its last 128 bytes are 32 words: word 16 h + r (h = 0, 1) holds, as
+ *     byte i, the E4M3 scale of block 8 q + 2 i + h of row 16 t + r.
+ * A wavefront then loads the weights of one (tile, quad) as one contiguous
+ * kilobyte and their scales as one 128-byte line.  The tensor scale is
+ * unchanged and passed separately.
+ *
+ * nvfp4_prepared_bytes(n, k): size of the layout, -1 when n <= 0, k <= 0,
+ * k % 128 != 0 or the size overflows (no HIP call).
+ * nvfp4_prepare: packed [n, k/2] + scales [n, k/16] -> prepared (16-byte
+ * aligned, nvfp4_prepared_bytes(n, k) bytes, overlapping neither input).
+ * nvfp4_dequant_prepared: prepared + tscale -> w_out [n, k] BF16, bit for bit
+ * the nvfp4_dequant of the weight it was prepared from.
+ * nvfp4_linear_prepared: y [m, n] = x [m, k] . W_hat^T from the prepared
+ * weight, for 1 <= m <= 32 (the decode and batched-decode shapes; larger m is
+ * NVFP4_ERR_UNSUPPORTED: the prefill GEMM reads the checkpoint layout); m = 0
+ * is a no-op.  Accumulation in FP32 in a different order than nvfp4_linear,
+ * so within the same tolerance, not bit-identical to it.  Workspace: as for
+ * nvfp4_linear_ws, with nvfp4_linear_prepared_workspace_bytes(m, n, k) bytes
+ * (0: none needed; NULL or too small runs without a K split).
+ * Errors as nvfp4_linear; a k that is not a multiple of 128 is NVFP4_ERR_SHAPE.
+ */
+int64_t nvfp4_prepared_bytes(int64_t n, int64_t k);
+nvfp4_status nvfp4_prepare(const uint8_t* packed, const uint8_t* scales, int64_t n, int64_t k, uint8_t* prepared,
+                           void* stream);
+nvfp4_status nvfp4_dequant_prepared(const uint8_t* prepared, const float* tscale, int64_t n, int64_t k,
+                                    uint16_t* w_out, void* stream);
+int64_t nvfp4_linear_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k);
+nvfp4_status nvfp4_linear_prepared(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prepared,
+                                   const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                                   void* stream);
+
 /* Kernel ids for nvfp4_linear_forced. */
 #define NVFP4_KERNEL_AUTO 0
 #define NVFP4_KERNEL_GEMV 1     /* VALU dot-product GEMV; any m (rows handled independently) */

@@ -28,7 +28,8 @@ EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_ama
             "nvfp4_linear_grouped", "nvfp4_kv_gather", "nvfp4_mx_quantize", "nvfp4_mx_dequant", "nvfp4_mx_gemm",
             "nvfp4_mx_linear_w4a4", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes",
             "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes",
-            "nvfp4_linear_noalloc", "nvfp4_linear_noalloc_max_bytes")
+            "nvfp4_linear_noalloc", "nvfp4_linear_noalloc_max_bytes", "nvfp4_prepared_bytes", "nvfp4_prepare",
+            "nvfp4_dequant_prepared", "nvfp4_linear_prepared_workspace_bytes", "nvfp4_linear_prepared")
 
 
 class NVFP4Error(RuntimeError):
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_linear_noalloc_max_bytes.argtypes = []
         L.nvfp4_linear_noalloc_max_bytes.restype = i64
+        L.nvfp4_prepared_bytes.argtypes = [i64, i64]
+        L.nvfp4_prepare.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.nvfp4_dequant_prepared.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.nvfp4_linear_prepared_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_linear_prepared.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, i64, vp]
         L.nvfp4_linear_ws.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
         L.nvfp4_quantize_experts.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
@@ -78,7 +84,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
-            getattr(L, name).restype = i64 if name.endswith(("_workspace_bytes", "_max_bytes")) else i32
+            getattr(L, name).restype = i64 if name.endswith(("_workspace_bytes", "_max_bytes", "_prepared_bytes")) \
+                else i32
         _lib = L
     return _lib
 
@@ -261,6 +268,74 @@ def linear_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, 
         raise ValueError("packed/scales/out do not match x")
     _check(lib().nvfp4_linear_noalloc(x.data_ptr(), m, n, k, packed.data_ptr(), scales.data_ptr(),
                                       tscale.data_ptr(), out.data_ptr(), _stream(x)), "nvfp4_linear_noalloc")
+    return out
+
+
+def prepared_bytes(n: int, k: int) -> int:
+    b = lib().nvfp4_prepared_bytes(n, k)
+    if b < 0:
+        raise ValueError(f"no kernel-native layout for n={n} k={k} (k must be a positive multiple of 128)")
+    return b
+
+
+def prepare(packed: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """Checkpoint layout (packed [n, k/2], scales [n, k/16]) -> the kernel-native layout (uint8, flat)."""
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.uint8, "scales")
+    n, kh = packed.shape
+    k = 2 * kh
+    if scales.shape != (n, k // 16):
+        raise ValueError("scales must be [n, k/16]")
+    out = torch.empty(prepared_bytes(n, k), dtype=torch.uint8, device=packed.device)
+    _check(lib().nvfp4_prepare(packed.data_ptr(), scales.data_ptr(), n, k, out.data_ptr(), _stream(packed)),
+           "nvfp4_prepare")
+    return out
+
+
+def dequant_prepared(prepared: torch.Tensor, tscale: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Kernel-native layout -> BF16 [n, k]."""
+    _need(prepared, torch.uint8, "prepared")
+    _need(tscale, torch.float32, "tscale")
+    if prepared.numel() != prepared_bytes(n, k):
+        raise ValueError("prepared does not match n, k")
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=prepared.device)
+    _check(lib().nvfp4_dequant_prepared(prepared.data_ptr(), tscale.data_ptr(), n, k, out.data_ptr(),
+                                        _stream(prepared)), "nvfp4_dequant_prepared")
+    return out
+
+
+def linear_prepared(x: torch.Tensor, prepared: torch.Tensor, tscale: torch.Tensor, n: int,
+                    out: Optional[torch.Tensor] = None,
+                    workspace: Union[str, None, torch.Tensor] = "auto") -> torch.Tensor:
+    """Y[m, n] = X[m, k] . W_hat^T from the kernel-native layout (1 <= m <= 32).  workspace as for linear()."""
+    _need(x, torch.bfloat16, "x")
+    _need(prepared, torch.uint8, "prepared")
+    _need(tscale, torch.float32, "tscale")
+    m, k = x.shape
+    if prepared.numel() != prepared_bytes(n, k):
+        raise ValueError("prepared does not match n and x's k")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if out.shape != (m, n):
+            raise ValueError("out must be [m, n]")
+    stream = _stream(x)
+    need = lib().nvfp4_linear_prepared_workspace_bytes(m, n, k)
+    if need < 0:
+        raise ValueError(f"invalid shape m={m} n={n} k={k}")
+    if workspace is None or need == 0:
+        ws = None
+    elif isinstance(workspace, torch.Tensor):
+        _need(workspace, torch.uint8, "workspace")
+        ws = workspace
+    else:
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        ws = _workspace_for(x.device, stream, need)
+    wptr, wbytes = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    _check(lib().nvfp4_linear_prepared(x.data_ptr(), m, n, k, prepared.data_ptr(), tscale.data_ptr(),
+                                       out.data_ptr(), wptr, wbytes, stream), "nvfp4_linear_prepared")
     return out
 
 

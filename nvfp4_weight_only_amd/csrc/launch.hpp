@@ -45,6 +45,24 @@ constexpr int64_t kSkinnyCounterBytes = 16384;
 int64_t skinny_workspace_bytes(int64_t m, int64_t n, int64_t k);
 void launch_skinny(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed, const uint8_t* scales,
                    const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes, hipStream_t s);
+// The kernel-native weight layout (16-row tiles x 128-element quads, 1152
+// bytes per (tile, quad); k a multiple of 128): its size, the conversion from
+// the checkpoint layout, and its dequantizer.
+int64_t prepared_bytes(int64_t n, int64_t k);
+void launch_prepare(const uint8_t* packed, const uint8_t* scales, int64_t n, int64_t k, uint8_t* out, hipStream_t s);
+void launch_dequant_prepared(const uint8_t* prep, const float* tscale, int64_t n, int64_t k, uint16_t* out,
+                             hipStream_t s);
+// Small-M MFMA kernel on the kernel-native layout, 1 <= m <= 32.  With a plan
+// that splits K (slices > 1) it needs a workspace of plan.ws_bytes laid out as
+// for launch_skinny.
+struct SmallMPlan {
+  int rows = 16, tiles = 1, slices = 1, quads = 1;
+  int64_t row_blocks = 1, npad = 0, ws_bytes = 0;
+};
+bool small_m_supported(int64_t m, int64_t n, int64_t k);
+SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split);
+void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,
+                    const float* tscale, uint16_t* y, void* workspace, hipStream_t s);
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                          const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
 // Streaming prefill GEMM (K a multiple of 256); launch_gemm_prefill uses it when supported.

@@ -294,6 +294,83 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
   return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, ws, kScratchBytes, stream);
 }
 
+int64_t nvfp4_prepared_bytes(int64_t n, int64_t k) {
+  WeightSizes ws;
+  if (weight_sizes(n, k, &ws) != NVFP4_OK || k % 128 != 0) return -1;
+  const int64_t tiles = (n + 15) / 16;
+  int64_t b;
+  if (!mul_ok(tiles, k / 128, &b) || !mul_ok(b, 1152, &b)) return -1;
+  return b;
+}
+
+nvfp4_status nvfp4_prepare(const uint8_t* packed, const uint8_t* scales, int64_t n, int64_t k, uint8_t* prepared,
+                           void* stream) {
+  if (!packed || !scales || !prepared) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  const int64_t pb = nvfp4_prepared_bytes(n, k);
+  if (pb < 0) return NVFP4_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(prepared)) return NVFP4_ERR_ALIGN;
+  if (overlaps(prepared, pb, packed, ws.packed_bytes) || overlaps(prepared, pb, scales, ws.scale_bytes))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_prepare(packed, scales, n, k, prepared, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+nvfp4_status nvfp4_dequant_prepared(const uint8_t* prepared, const float* tscale, int64_t n, int64_t k,
+                                    uint16_t* w_out, void* stream) {
+  if (!prepared || !tscale || !w_out) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  const int64_t pb = nvfp4_prepared_bytes(n, k);
+  if (pb < 0) return NVFP4_ERR_SHAPE;
+  if (!aligned16(prepared) || !aligned16(tscale) || !aligned16(w_out)) return NVFP4_ERR_ALIGN;
+  if (overlaps(w_out, ws.w_bytes, prepared, pb) || overlaps(w_out, ws.w_bytes, tscale, 4)) return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_dequant_prepared(prepared, tscale, n, k, w_out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int64_t nvfp4_linear_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || nvfp4_prepared_bytes(n, k) < 0) return -1;
+  int64_t ye;
+  if (!mul_ok(m, n, &ye) || ye > INT64_MAX / 32) return -1;
+  if (m == 0 || !nvfp4::small_m_supported(m, n, k)) return 0;
+  return nvfp4::small_m_plan(m, n, k, true).ws_bytes;
+}
+
+nvfp4_status nvfp4_linear_prepared(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prepared,
+                                   const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+  if (!prepared || !tscale || (m != 0 && (!x || !y))) return NVFP4_ERR_NULL;
+  if (m < 0 || workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  const int64_t pb = nvfp4_prepared_bytes(n, k);
+  if (pb < 0) return NVFP4_ERR_SHAPE;
+  int64_t xe, ye, xb, yb;
+  if (!mul_ok(m, k, &xe) || !mul_ok(xe, 2, &xb) || !mul_ok(m, n, &ye) || !mul_ok(ye, 2, &yb)) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!nvfp4::small_m_supported(m, n, k)) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(prepared) || !aligned16(tscale) || !aligned16(y)) return NVFP4_ERR_ALIGN;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, prepared, pb) || overlaps(y, yb, tscale, 4)) return NVFP4_ERR_ALIAS;
+  nvfp4::SmallMPlan pl = nvfp4::small_m_plan(m, n, k, true);
+  if (pl.slices > 1 && (workspace == nullptr || workspace_bytes < pl.ws_bytes)) pl = nvfp4::small_m_plan(m, n, k, false);
+  if (pl.slices > 1) {
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    if (overlaps(workspace, workspace_bytes, x, xb) || overlaps(workspace, workspace_bytes, y, yb) ||
+        overlaps(workspace, workspace_bytes, prepared, pb) || overlaps(workspace, workspace_bytes, tscale, 4))
+      return NVFP4_ERR_ALIAS;
+  }
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_small_m(pl, x, m, n, k, prepared, tscale, y, workspace, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                  const uint8_t* packed, const uint8_t* scales, const float* tscale, uint16_t* y,
                                  void* stream) {

@@ -1,0 +1,482 @@
+// Small-M (batched decode, M <= 32) W4A16 linear on the kernel-native weight
+// layout (nvfp4_prepare), gfx950.
+//
+// With a handful of activation rows the linear is bound by the one pass over
+// the packed weights (0.5625 B per weight element; model card
+// "Qwen3.8-27B-NVFP4 (compressed-tensors)": weights NVFP4, activations BF16;
+// imp "docs/quantization.md", NVFP4 kernel pipeline: the decode path streams
+// the packed weights once).  Every weight element is loaded from HBM once,
+// straight into registers, decoded there to the exact BF16 value E2M1 x E4M3,
+// and used as the A operand of v_mfma_f32_16x16x32_bf16 for all M activation
+// rows at once (the activations are the B operand, 16 rows per MFMA tile).
+//
+// Kernel-native layout: 16-row tiles x 128-element quads, 1152 bytes per
+// (tile, quad): 64 slots of 16 bytes, slot 16 g + r holding the elements
+// 32 i + 8 g .. + 8 (word i) of the quad in row r, then 32 scale words, word
+// 16 h + r holding the scales of blocks 2 i + h (byte i) of row r.  A lane
+// (r, g) of MFMA step 4 q + i takes word i of slot 16 g + r as its A operand
+// (K order: step j covers [32 j, 32 j + 32), lane group g takes [32 j + 8 g,
+// + 8) of both operands), and byte i of scale word 16 (g / 2) + r as its
+// scale.  So a wavefront's weights of one (tile, quad) are one contiguous
+// 1 KB load (whole cache lines) and its scales one 128-byte line; in the
+// checkpoint layout the same data are 16 rows x 64 bytes and 16 rows x 8 bytes,
+// twice and sixteen times the cache lines per byte.
+//
+// Work split.  A workgroup of eight wavefronts (two per SIMD) owns the output
+// rows [row0, row0 + rows) (rows a multiple of 4) and one K slice of whole
+// quads.  It reads the T tiles that cover its rows (a tile shared with the
+// neighbouring block is read by both; their ids are consecutive on one XCD, so
+// the second read is an L2 hit) and stores only its own rows.  The slice's
+// quads are shared out among the eight wavefronts, and every wavefront runs its
+// quads for all T tiles, so the activation fragments of a quad are loaded once
+// per wavefront and serve T tiles.  There is no barrier in the K loop: each
+// wavefront double-buffers one quad of activation fragments and one quad of
+// weights for all its tiles in registers, and issues the next quad's loads
+// before the current quad's products.  At the end the eight wavefronts' FP32
+// sums meet in LDS and are added in wavefront order.  With several K slices (a
+// caller workspace), the workgroups of a row block exchange FP32 partial sums
+// in the workspace and the last one to arrive adds them in slice order, so the
+// result is the same bits on every run.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kSmWaves = 8;
+constexpr int kSmQuadK = 128;
+constexpr int kSmBlock = 1152;  // bytes per (tile, quad) of the kernel-native layout
+
+struct SmArgs {
+  const uint16_t* x;     // [m, k]
+  int64_t m, n, k;
+  const uint8_t* prep;   // kernel-native weight
+  const float* tscale;
+  uint16_t* y;           // [m, n]
+  float* part;           // [slices, m, npad] FP32 partial sums (slices > 1)
+  uint32_t* count;       // [row blocks] arrival counters (slices > 1)
+  int64_t npad;          // n rounded up to a multiple of 4
+  int rows;              // output rows per workgroup (a multiple of 4)
+  int slices;            // K slices
+  int quads;             // k / 128
+  int xcd_order;         // 1: consecutive row blocks on one XCD (grid size a multiple of 8)
+};
+
+// One (tile, quad) as a lane holds it: its 16 packed bytes and its scale word.
+struct SmW {
+  uint4 w;
+  uint32_t s;
+};
+
+// Activation fragments of one quad: step i, m tile mt.
+template <int NMT>
+struct SmX {
+  uint4 v[4][NMT];
+};
+
+__device__ __forceinline__ void sm_load_w(SmW& r, const uint8_t* tile, int q, int lane) {
+  const uint8_t* b = tile + (int64_t)q * kSmBlock;
+  r.w = *reinterpret_cast<const uint4*>(b + 16 * lane);
+  r.s = *reinterpret_cast<const uint32_t*>(b + 1024 + 4 * (16 * ((lane >> 5) & 1) + (lane & 15)));
+}
+
+// Activation fragments of quad q: step i, m tile mt is row xr[mt] at elements
+// [128 q + 32 i + 8 g, + 8).
+template <int NMT>
+__device__ __forceinline__ void sm_load_x(SmX<NMT>& r, const uint16_t* const* xr, int q, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      r.v[i][mt] = *reinterpret_cast<const uint4*>(xr[mt] + (int64_t)q * kSmQuadK + 32 * i + 8 * g);
+}
+
+// Products of one quad of one row tile.
+template <int NMT>
+__device__ __forceinline__ void sm_quad(const SmW& r, const SmX<NMT>& xq, f32x4_t* acc) {
+  const float2 s01 = e4m3x2_to_f32<false>(r.s), s23 = e4m3x2_to_f32<true>(r.s);
+  const uint32_t wd[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+  const float sc[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, e2m1x8_scaled_to_bf16_hw(wd[i], sc[i]));
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, xq.v[i][mt]), acc[mt], 0, 0,
+                                                        0);
+  }
+}
+
+// Y of one (row tile, m tile) of the block: D layout of a 16x16 MFMA tile,
+// item v of lane l is weight row tile_row + 4 (l / 16) + v and activation row
+// gm = 16 mt + l % 16.  Only rows in [row0, row_end) belong to this block.
+__device__ __forceinline__ void sm_store_y(const SmArgs& p, f32x4_t v, int64_t tile_row, int64_t row0,
+                                           int64_t row_end, int64_t gm, int lane) {
+  const int64_t n0 = tile_row + 4 * (lane >> 4);  // row0 and n0 are multiples of 4
+  if (gm >= p.m || n0 < row0 || n0 >= row_end) return;
+  const float t = *p.tscale;
+  uint16_t* yp = p.y + gm * p.n + n0;
+  const uint32_t b0 = f32_to_bf16_rne(v[0] * t), b1 = f32_to_bf16_rne(v[1] * t);
+  const uint32_t b2 = f32_to_bf16_rne(v[2] * t), b3 = f32_to_bf16_rne(v[3] * t);
+  if ((p.n & 3) == 0 && n0 + 3 < row_end) {
+    *reinterpret_cast<uint2*>(yp) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  } else {
+    const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n0 + r < row_end) yp[r] = (uint16_t)bb[r];
+  }
+}
+
+// NMT: MFMA m tiles (16 activation rows each; rows past m repeat the last one
+// and are never stored); T: tiles read per workgroup.
+template <int NMT, int T>
+__global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
+  constexpr int NP = T * NMT;  // (row tile, m tile) pairs
+  __shared__ f32x4_t red[kSmWaves * NP * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups are dispatched to the XCDs round-robin by id: with xcd_order,
+  // logical block L of XCD x is x * (grid / 8) + id / 8, so consecutive row
+  // blocks (which share a tile) run on one XCD.
+  const unsigned id = blockIdx.x;
+  const unsigned lid = p.xcd_order ? (id & 7u) * (gridDim.x >> 3) + (id >> 3) : id;
+  const int rb = (int)(lid / (unsigned)p.slices), sl = (int)(lid % (unsigned)p.slices);
+  const int64_t row0 = (int64_t)rb * p.rows;
+  const int64_t row_end = row0 + p.rows < p.n ? row0 + p.rows : p.n;
+  const int64_t tile0 = row0 >> 4;
+  const int64_t tiles = (p.n + 15) >> 4;
+  // This workgroup's quads, then this wavefront's share of them.
+  const int Q0 = (int)((int64_t)sl * p.quads / p.slices), Q1 = (int)((int64_t)(sl + 1) * p.quads / p.slices);
+  const int q0 = Q0 + (Q1 - Q0) * w / kSmWaves, q1 = Q0 + (Q1 - Q0) * (w + 1) / kSmWaves;
+
+  // Tiles past the weight's last tile repeat it (their rows are never stored).
+  const uint8_t* tb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t ti = tile0 + t < tiles ? tile0 + t : tiles - 1;
+    tb[t] = p.prep + ti * (int64_t)p.quads * kSmBlock;
+  }
+  const uint16_t* xr[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int64_t mr = 16 * mt + (lane & 15);
+    xr[mt] = p.x + (mr < p.m ? mr : p.m - 1) * p.k;
+  }
+
+  f32x4_t acc[T][NMT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (q1 > q0) {
+    // Double buffer: while quad q's products run, quad q + 1 is in flight.
+    // Past the last quad the loads repeat it (in bounds; never used).  The
+    // scheduling barrier keeps a quad's loads ahead of the previous quad's
+    // products (the scheduler would otherwise sink them next to their uses to
+    // save registers, and each quad would wait out a full load latency).
+    SmX<NMT> xa, xb;
+    SmW wa[T], wb[T];
+    auto load = [&](SmX<NMT>& xq, SmW* wq, int q) {
+      sm_load_x<NMT>(xq, xr, q, g);
+#pragma unroll
+      for (int t = 0; t < T; ++t) sm_load_w(wq[t], tb[t], q, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](const SmX<NMT>& xq, const SmW* wq) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) sm_quad<NMT>(wq[t], xq, acc[t]);
+    };
+    load(xa, wa, q0);
+    int q = q0;
+    for (; q + 1 < q1; q += 2) {
+      load(xb, wb, q + 1);
+      compute(xa, wa);
+      load(xa, wa, q + 2 < q1 ? q + 2 : q1 - 1);
+      compute(xb, wb);
+    }
+    if (q < q1) compute(xa, wa);
+  }
+
+  // The eight wavefronts' sums of each (row tile, m tile) pair, added in
+  // wavefront order by wavefront pair % 8.
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) red[((w * T + t) * NMT + mt) * 64 + lane] = acc[t][mt];
+  __syncthreads();
+  constexpr int PPW = (NP + kSmWaves - 1) / kSmWaves;  // pairs per wavefront (1 or 2)
+  f32x4_t sum[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    sum[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (pi < NP) {
+#pragma unroll
+      for (int ww = 0; ww < kSmWaves; ++ww) sum[i] += red[(ww * NP + pi) * 64 + lane];
+    }
+  }
+  auto pair_rows = [&](int pi, int64_t& tile_row, int64_t& gm) {
+    tile_row = (tile0 + pi / NMT) * 16;
+    gm = 16 * (pi % NMT) + (lane & 15);
+  };
+  if (p.slices == 1) {
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int pi = w + kSmWaves * i;
+      if (pi < NP) {
+        int64_t tr, gm;
+        pair_rows(pi, tr, gm);
+        sm_store_y(p, sum[i], tr, row0, row_end, gm, lane);
+      }
+    }
+    return;
+  }
+
+  // Several K slices.  The partial sums are exchanged with device-scope
+  // relaxed atomic stores and loads, which gfx950 performs at the device's
+  // coherence point (the L2s of the eight XCDs are not coherent with each other
+  // for ordinary accesses).  Every thread waits for its stores to complete
+  // (vmcnt(0)) before the barrier, and only then is the arrival counter bumped,
+  // so a workgroup that sees the count reach `slices - 1` finds every other
+  // slice's sums complete.
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    if (pi < NP) {
+      int64_t tr, gm;
+      pair_rows(pi, tr, gm);
+      const int64_t n0 = tr + 4 * (lane >> 4);
+      if (gm < p.m && n0 >= row0 && n0 < row_end) {
+        float* dst = p.part + ((int64_t)sl * p.m + gm) * p.npad + n0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, sum[i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial-sum stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* cnt = p.count + rb;
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(p.slices - 1);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    is_last = last;
+  }
+  __syncthreads();
+  if (!is_last) return;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    if (pi < NP) {
+      int64_t tr, gm;
+      pair_rows(pi, tr, gm);
+      const int64_t n0 = tr + 4 * (lane >> 4);
+      f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (gm < p.m && n0 >= row0 && n0 < row_end) {
+        for (int s = 0; s < p.slices; ++s) {
+          f32x4_t ps = sum[i];
+          if (s != sl) {
+            const float* src = p.part + ((int64_t)s * p.m + gm) * p.npad + n0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ps[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          v += ps;
+        }
+      }
+      sm_store_y(p, v, tr, row0, row_end, gm, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel-native layout: conversion from the checkpoint layout and the
+// dequantizer that reads it.  One thread per 16 output bytes of a 1152-byte
+// (tile, quad) block: units 0..63 are the packed slots, 64..71 four scale
+// words each.  Rows past n are zero.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prepare_kernel(const uint8_t* __restrict__ packed,
+                                                      const uint8_t* __restrict__ scales, int64_t n, int64_t k,
+                                                      int64_t blocks, uint8_t* __restrict__ out) {
+  const int64_t quads = k / kSmQuadK, kh = k >> 1, ks = k >> 4;
+  const int64_t units = blocks * 72;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < units;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = id / 72, t = b / quads, q = b - t * quads;
+    const int u = (int)(id - b * 72);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (u < 64) {
+      const int g = u >> 4, r = u & 15;
+      const int64_t row = t * 16 + r;
+      if (row < n) {
+        const uint8_t* src = packed + row * kh + q * 64 + 4 * g;
+        v = make_uint4(*reinterpret_cast<const uint32_t*>(src), *reinterpret_cast<const uint32_t*>(src + 16),
+                       *reinterpret_cast<const uint32_t*>(src + 32), *reinterpret_cast<const uint32_t*>(src + 48));
+      }
+    } else {
+      uint32_t wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int word = 4 * (u - 64) + j, h = word >> 4, r = word & 15;
+        const int64_t row = t * 16 + r;
+        wv[j] = 0u;
+        if (row < n) {
+          const uint2 s8 = *reinterpret_cast<const uint2*>(scales + row * ks + q * 8);
+          wv[j] = __builtin_amdgcn_perm(s8.y, s8.x, h ? 0x07050301u : 0x06040200u);
+        }
+      }
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    *reinterpret_cast<uint4*>(out + b * kSmBlock + 16 * u) = v;
+  }
+}
+
+// w = RNE_bf16(fl32(fl32(E2M1 * E4M3) * tscale)) for the 8 elements of one
+// packed word and its E4M3 scale byte, as 8 BF16 in natural order.
+__device__ __forceinline__ uint4 sm_dequant8(uint32_t p, uint32_t sbyte, float t) {
+  const float s = e4m3_to_f32(sbyte);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (p >> (8 * j + 4 * h)) & 0xFu;
+      float v = e2m1_mag_to_f32(c & 7u) * s;  // exact
+      v = v * t;                              // one FP32 rounding
+      if (c & 8u) v = -v;
+      pair |= f32_to_bf16_rne(v) << (16 * h);
+    }
+    o[j] = pair;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// One thread per packed slot: 32 elements of one row, four 16-byte stores.
+__global__ void __launch_bounds__(256) dequant_prepared_kernel(const uint8_t* __restrict__ prep,
+                                                               const float* __restrict__ tscale_p, int64_t n,
+                                                               int64_t k, int64_t blocks, uint16_t* __restrict__ out) {
+  const int64_t quads = k / kSmQuadK;
+  const int64_t slots = blocks * 64;
+  const float ts = *tscale_p;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < slots;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = id >> 6, t = b / quads, q = b - t * quads;
+    const int s = (int)(id & 63), g = s >> 4, r = s & 15;
+    const int64_t row = t * 16 + r;
+    if (row >= n) continue;
+    const uint8_t* blk = prep + b * kSmBlock;
+    const uint4 wv = *reinterpret_cast<const uint4*>(blk + 16 * s);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(blk + 1024 + 4 * (16 * (g >> 1) + r));
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint16_t* dst = out + row * k + q * kSmQuadK + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(dst + 32 * i) = sm_dequant8(wd[i], (sw >> (8 * i)) & 0xFFu, ts);
+  }
+}
+
+template <int NMT>
+void launch_nmt(const SmallMPlan& pl, const SmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(pl.row_blocks * pl.slices));
+  switch (pl.tiles) {
+    case 1: small_m_kernel<NMT, 1><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 2: small_m_kernel<NMT, 2><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 3: small_m_kernel<NMT, 3><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 4: small_m_kernel<NMT, 4><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    default: small_m_kernel<NMT, 5><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+  }
+}
+
+int64_t sm_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t sm_round_up(int64_t a, int64_t b) { return sm_ceil_div(a, b) * b; }
+
+unsigned sm_grid(int64_t items, int64_t max_blocks) {
+  int64_t b = sm_ceil_div(items, 256);
+  b = b > max_blocks ? max_blocks : b;
+  return (unsigned)(b < 1 ? 1 : b);
+}
+
+// Most tiles any block of `rows` rows (a multiple of 4) covers: a block that
+// starts r0 % 16 rows into a tile reaches ceil((r0 % 16 + rows) / 16) tiles, and
+// r0 % 16 takes the values 0, 4, 8, 12 in a repeating pattern.
+int64_t sm_max_tiles(int64_t n, int64_t rows) {
+  int64_t worst = 0;
+  for (int64_t b = 0; b < 4 && b * rows < n; ++b) {
+    const int64_t r0 = b * rows, r1 = (r0 + rows < n ? r0 + rows : n) - 1;
+    const int64_t t = r1 / 16 - r0 / 16 + 1;
+    worst = t > worst ? t : worst;
+  }
+  return worst;
+}
+
+}  // namespace
+
+int64_t prepared_bytes(int64_t n, int64_t k) { return sm_ceil_div(n, 16) * (k / kSmQuadK) * kSmBlock; }
+
+void launch_prepare(const uint8_t* packed, const uint8_t* scales, int64_t n, int64_t k, uint8_t* out, hipStream_t s) {
+  const int64_t blocks = sm_ceil_div(n, 16) * (k / kSmQuadK);
+  prepare_kernel<<<sm_grid(blocks * 72, 1 << 20), 256, 0, s>>>(packed, scales, n, k, blocks, out);
+}
+
+void launch_dequant_prepared(const uint8_t* prep, const float* tscale, int64_t n, int64_t k, uint16_t* out,
+                             hipStream_t s) {
+  const int64_t blocks = sm_ceil_div(n, 16) * (k / kSmQuadK);
+  dequant_prepared_kernel<<<sm_grid(blocks * 64, 1 << 20), 256, 0, s>>>(prep, tscale, n, k, blocks, out);
+}
+
+bool small_m_supported(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && m <= 32 && n >= 1 && k >= kSmQuadK && k % kSmQuadK == 0 && k / kSmQuadK < (1 << 24);
+}
+
+SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
+  SmallMPlan pl;
+  pl.quads = (int)(k / kSmQuadK);
+  // K slices: about 80 weight rows per workgroup and 256 workgroups (one per
+  // CU), each slice at least eight quads (one per wavefront), at most 16.
+  int64_t s = 1;
+  if (split) {
+    s = (80 * 256 + n / 2) / n;
+    int64_t cap = pl.quads / kSmWaves;
+    cap = cap < 16 ? cap : 16;
+    s = s > cap ? cap : s;
+    s = s < 1 ? 1 : s;
+  }
+  pl.slices = (int)s;
+  // Rows per workgroup: one workgroup per CU (or per half CU, ... when that
+  // needs more), a multiple of 4, covering at most five tiles.
+  int64_t rows = 0;
+  for (int64_t per_cu = 1;; ++per_cu) {
+    rows = sm_round_up(sm_ceil_div(n * s, 256 * per_cu), 4);
+    if (sm_max_tiles(n, rows) <= 5) break;
+  }
+  pl.rows = (int)rows;
+  pl.tiles = (int)sm_max_tiles(n, rows);
+  pl.row_blocks = sm_ceil_div(n, rows);
+  pl.npad = sm_round_up(n, 4);
+  if (pl.slices > 1) {
+    if (pl.row_blocks * 4 > kSkinnyCounterBytes) return small_m_plan(m, n, k, false);
+    pl.ws_bytes = kSkinnyCounterBytes + (int64_t)pl.slices * m * pl.npad * 4;
+  }
+  return pl;
+}
+
+void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,
+                    const float* tscale, uint16_t* y, void* workspace, hipStream_t s) {
+  const int64_t grid = pl.row_blocks * pl.slices;
+  SmArgs a{x, m, n, k, prep, tscale, y, nullptr, nullptr, pl.npad, pl.rows, pl.slices, pl.quads, (grid & 7) == 0};
+  if (pl.slices > 1) {
+    a.count = static_cast<uint32_t*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes);
+  }
+  if (m <= 16)
+    launch_nmt<1>(pl, a, s);
+  else
+    launch_nmt<2>(pl, a, s);
+}
+
+}  // namespace nvfp4

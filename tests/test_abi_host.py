@@ -248,3 +248,27 @@ def test_linear_noalloc_validation(L):
     assert f(A + 8, 8, 64, 64, Bp, C, D, E, None) == B.ERR_ALIGN
     assert f(A, 8, 64, 64, Bp, C, D, A + 16, None) == B.ERR_ALIAS     # y overlaps x
     assert f(None, 0, 64, 64, Bp, C, D, None, None) == B.OK           # m = 0 no-op
+
+
+def test_prepared_layout_validation(L):
+    pb = L.nvfp4_prepared_bytes
+    assert pb(16, 128) == 1152 and pb(17, 256) == 2 * 2 * 1152 and pb(17408, 5120) == 17408 * 5120 * 9 // 16
+    assert pb(16, 96) == -1 and pb(0, 128) == -1 and pb(16, 0) == -1
+    p = L.nvfp4_prepare
+    assert p(None, C, 16, 128, E, None) == B.ERR_NULL
+    assert p(Bp, C, 16, 96, E, None) == B.ERR_SHAPE            # k % 128 != 0
+    assert p(Bp + 8, C, 16, 128, E, None) == B.ERR_ALIGN
+    assert p(Bp, C, 16, 128, Bp + 512, None) == B.ERR_ALIAS     # output overlaps packed
+    d = L.nvfp4_dequant_prepared
+    assert d(None, D, 16, 128, E, None) == B.ERR_NULL
+    assert d(Bp, D, 16, 64, E, None) == B.ERR_SHAPE
+    assert d(Bp, D, 16, 128, Bp + 16, None) == B.ERR_ALIAS
+    wb = L.nvfp4_linear_prepared_workspace_bytes
+    assert wb(8, 64, 96) == -1 and wb(-1, 64, 128) == -1 and wb(0, 64, 128) == 0 and wb(33, 64, 128) == 0
+    lp = L.nvfp4_linear_prepared
+    assert lp(None, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_NULL
+    assert lp(A, 8, 64, 96, Bp, D, E, None, 0, None) == B.ERR_SHAPE
+    assert lp(A, 33, 64, 128, Bp, D, E, None, 0, None) == B.ERR_UNSUPPORTED   # prefill m
+    assert lp(A + 8, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_ALIGN
+    assert lp(A, 8, 64, 128, Bp, D, A + 16, None, 0, None) == B.ERR_ALIAS    # y overlaps x
+    assert lp(None, 0, 64, 128, Bp, D, None, None, 0, None) == B.OK          # m = 0 no-op

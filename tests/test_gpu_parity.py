@@ -226,7 +226,9 @@ LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 6
               (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (2, 70, 6144), (1, 100, 1056),
               (1, 33, 4640), (1, 16400, 6144), (1, 40, 17408),
               # prefill with K a multiple of 256: several 128 x 272 tiles with ragged edges, one K group
-              (200, 560, 768), (129, 545, 256), (300, 300, 2560)]
+              (200, 560, 768), (129, 545, 256), (300, 300, 2560),
+              # more small-M shapes: k = 128 and 384, 4-row workgroups, ragged n with two m tiles, large n
+              (2, 100, 128), (5, 1000, 384), (31, 77, 640), (8, 10240, 512), (17, 4352, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", LIN_SHAPES)
@@ -273,7 +275,7 @@ def test_linear_edge_cases(nv):
 # Small-M kernel with K split across workgroups (caller workspace).
 # ---------------------------------------------------------------------------
 SPLIT_SHAPES = [(8, 300, 1040), (17, 130, 272), (32, 64, 5120), (33, 200, 512), (64, 5120, 5120), (16, 33, 4608),
-                (64, 257, 2064), (9, 513, 784), (2, 5120, 2048)]
+                (64, 257, 2064), (9, 513, 784), (2, 5120, 2048), (24, 700, 3072), (3, 2000, 8192)]
 
 
 @pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
@@ -1014,3 +1016,83 @@ def test_graph_keeps_binding_workspace_after_growth(nv):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert bool((sentinel == 0x5A).all()), f"replay {rep} wrote into a later allocation"
+
+
+# ---------------------------------------------------------------------------
+# Kernel-native layout (nvfp4_prepare): conversion bit-exact against the layout
+# oracle, dequant bit-exact against the weight oracle, and the small-M linear
+# on the prepared weight within the linear's tolerance.
+# ---------------------------------------------------------------------------
+from oracle import layout_oracle as LO  # noqa: E402
+
+PREP_SHAPES = [(16, 128), (37, 384), (300, 1024), (5, 640), (64, 5120)]
+
+
+@pytest.mark.parametrize("n,k", PREP_SHAPES)
+def test_prepare_and_dequant_prepared_bit_exact(nv, n, k):
+    w = WL.normal_bf16((n, k), 0.02, 7200 + n)
+    (packed, scales, tscale), (rp, rs, rt) = q_both(nv, w)
+    prep = nv.prepare(packed, scales)
+    assert prep.numel() == LO.prepared_bytes(n, k)
+    assert np.array_equal(u8_host(prep), LO.prepare(rp, rs)), "prepared layout differs from the oracle"
+    dq = bf16_host(nv.dequant_prepared(prep, tscale, n, k))
+    assert np.array_equal(dq, O.dequant(rp, rs, rt)), "dequant of the prepared layout differs from the oracle"
+
+
+PREP_LINEAR = [(1, 16, 128), (2, 100, 128), (8, 300, 1024), (16, 37, 384), (17, 64, 5120), (32, 300, 640),
+               (5, 1000, 384), (8, 10240, 512), (3, 2000, 8192), (32, 68, 1280), (24, 700, 3072)]
+
+
+@pytest.mark.parametrize("m,n,k", PREP_LINEAR)
+def test_linear_prepared(nv, m, n, k):
+    w = WL.normal_bf16((n, k), 0.02, 7300 + n)
+    x = WL.normal_bf16((m, k), 1.0, 7400 + m)
+    (packed, scales, tscale), rq = q_both(nv, w)
+    prep = nv.prepare(packed, scales)
+    y_ref, bound = O.linear_ref(x, *rq)
+    xd = to_dev_bf16(x)
+    y0 = bf16_host(nv.linear_prepared(xd, prep, tscale, n, workspace=None))
+    check_linear(y0, y_ref, bound, f"prepared unsplit m={m} n={n} k={k}")
+    need = nv.lib().nvfp4_linear_prepared_workspace_bytes(m, n, k)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+    y1 = bf16_host(nv.linear_prepared(xd, prep, tscale, n, workspace=ws))
+    check_linear(y1, y_ref, bound, f"prepared split m={m} n={n} k={k} (workspace {need} B)")
+    for _ in range(2):   # counters back at zero; bitwise reproducible
+        assert np.array_equal(bf16_host(nv.linear_prepared(xd, prep, tscale, n, workspace=ws)), y1)
+        assert np.array_equal(bf16_host(nv.linear_prepared(xd, prep, tscale, n, workspace=None)), y0)
+
+
+def test_linear_prepared_rejects_prefill_m(nv):
+    w = WL.normal_bf16((32, 256), 0.02, 7500)
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
+    prep = nv.prepare(packed, scales)
+    with pytest.raises(nv.NVFP4Error):
+        nv.linear_prepared(to_dev_bf16(WL.normal_bf16((33, 256), 1.0, 7501)), prep, tscale, 32)
+
+
+PREP_FULL = [("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8), ("small_m_down", 32), ("gate_up", 1),
+             ("decode", 1)]
+
+
+@pytest.mark.parametrize("wname,m", PREP_FULL, ids=[f"{a}-m{b}" for a, b in PREP_FULL])
+def test_linear_prepared_full_size_sampled(nv, wname, m):
+    """The timed workloads on the prepared weight, launched as the benchmark does (binding workspace):
+    sampled output columns against the oracle, and the prepared bytes of sampled tiles against the layout
+    oracle."""
+    wl = WL.WORKLOADS[wname]
+    w = wl.weight()
+    x = wl.activations(m)
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
+    prep = nv.prepare(packed, scales)
+    y = bf16_host(nv.linear_prepared(to_dev_bf16(x), prep, tscale, wl.n))
+    amax = O.tensor_amax(w)
+    tiles = np.unique(np.concatenate([sample_rows(wl.n // 16, 6, seed=7600), [0, wl.n // 16 - 1]]))
+    rows = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles])
+    rp, rs, rt = O.quantize(w[rows], amax=amax)
+    ph = u8_host(prep)
+    blk = 1152 * (wl.k // 128)
+    for j, t in enumerate(tiles):
+        want = LO.prepare(rp[16 * j:16 * j + 16], rs[16 * j:16 * j + 16])
+        assert np.array_equal(ph[t * blk:(t + 1) * blk], want), f"tile {t}"
+    y_ref, bound = O.linear_ref(x, rp, rs, rt)
+    check_linear(y[:, rows], y_ref, bound, f"{wname} prepared m={m} full size, sampled")
