@@ -205,6 +205,31 @@ def bench_prepare_row(reps):
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_stream_rows(reps):
+    """Plain streaming reads (nvfp4_stream_read) of the weight sizes the linear streams: the measured HBM read
+    rate the other rows are also reported against."""
+    out = {}
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    L = nv.lib()
+    for name, nbytes in (("decode", 14_766_080), ("small_m", 50_495_488), ("gate_up", 100_352_000)):
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies_needed(nbytes))]
+        for b in bufs:
+            b.fill_(1)
+
+        def call(b):
+            L.nvfp4_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+        g = graph_of([(lambda b=b: call(b)) for b in bufs])
+        warm_graph(g)
+        ms = time_graph_replays(g, reps, len(bufs))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"stream_read_{name}_{nbytes}B"] = {"bytes": nbytes, "copies": len(bufs), "us_per_call": round(ms * 1e3, 3),
+                                                "gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del bufs, g
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_quant_rows(reps):
     """Quantizer (amax + quantize passes) and dequantizer on the decode weight, rotated."""
     wl = WL.WORKLOADS["decode"]
@@ -487,7 +512,7 @@ def cpu_baseline(budget_s=20.0):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-def profile_run(what, launches, wname="decode", m=1):
+def profile_run(what, launches, wname="decode", m=1, graph=False):
     """A short, untimed run for hardware-counter passes (rocprofv3 --pmc): `launches` launches of one kernel.
 
     decode: nvfp4_linear on the decode workload, cycling through rotated weight copies so that every
@@ -508,28 +533,28 @@ def profile_run(what, launches, wname="decode", m=1):
     dequant: nvfp4_dequant of the decode workload's quantized weight (5120 x 5120), rotated copies;
     linear: nvfp4_linear on workload `wname` at M = `m` (e.g. small_m_up / small_m_down at M = 8 or 32,
             gate_up at M = 1), rotated weight copies, the workspace-backed call as the bench rows make it;
-    prepared: nvfp4_linear_prepared on the kernel-native layout of workload `wname` at M = `m`, rotated copies.
+    prepared: nvfp4_linear_prepared on the kernel-native layout of workload `wname` at M = `m`, rotated copies;
+    stream: nvfp4_stream_read of the byte count the linear of workload `wname` streams (packed + scales),
+            rotated buffers.
+    With `graph`, the launches are the rotated sequence captured in one HIP graph and replayed (after the 0.1 s
+    warm-up the bench rows get), as the bench rows time them; otherwise one host launch each.
     """
     torch.cuda.set_device(0)
+    calls = []               # one zero-argument launch per rotated copy
     if what == "dequant":
         packed, scales, tscale = nv.quantize(dev_bf16(WL.WORKLOADS["decode"].weight()))
         rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() * 5))
         outs = [torch.empty((packed.shape[0], packed.shape[1] * 2), dtype=torch.bfloat16, device="cuda")
                 for _ in range(2)]
-        torch.cuda.synchronize()
-        for i in range(launches):
-            p, s, t = rot.items[i % len(rot)]
-            nv.dequant(p, s, t, out=outs[i % 2])
+        calls = [(lambda p=p, s=s, t=t, o=outs[i % 2]: nv.dequant(p, s, t, out=o))
+                 for i, (p, s, t) in enumerate(rot.items)]
     elif what == "linear":
         wl = WL.WORKLOADS[wname]
         packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
         rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
         x = dev_bf16(wl.activations(m))
         y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
-        torch.cuda.synchronize()
-        for i in range(launches):
-            p, s, t = rot.items[i % len(rot)]
-            nv.linear(x, p, s, t, out=y)
+        calls = linear_calls(x, rot, y)
     elif what == "prepared":
         wl = WL.WORKLOADS[wname]
         packed, scales, tscale = nv.quantize(dev_bf16(wl.weight()))
@@ -538,16 +563,19 @@ def profile_run(what, launches, wname="decode", m=1):
         items = [(prep.clone(), tscale.clone()) for _ in range(copies_needed(prep.numel()))]
         x = dev_bf16(wl.activations(m))
         y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
-        torch.cuda.synchronize()
-        for i in range(launches):
-            p, t = items[i % len(items)]
-            nv.linear_prepared(x, p, t, wl.n, out=y)
+        calls = [(lambda p=p, t=t: nv.linear_prepared(x, p, t, wl.n, out=y)) for (p, t) in items]
+    elif what == "stream":
+        wl = WL.WORKLOADS[wname]
+        nbytes = wl.n * wl.k // 2 + wl.n * wl.k // 16
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies_needed(nbytes))]
+        sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+        L = nv.lib()
+        calls = [(lambda b=b: L.nvfp4_stream_read(b.data_ptr(), nbytes, sink.data_ptr(),
+                                                  torch.cuda.current_stream().cuda_stream)) for b in bufs]
     elif what == "quantize":
         w = dev_bf16(WL.WORKLOADS["decode"].weight())
         rot = [w.clone() for _ in range(copies_needed(w.numel() * 2))]
-        torch.cuda.synchronize()
-        for i in range(launches):
-            nv.quantize(rot[i % len(rot)])
+        calls = [(lambda w=w: nv.quantize(w)) for w in rot]
     elif what == "nvfp4_w4a4":
         wl = WL.WORKLOADS["prefill"]
         m = 2048
@@ -556,10 +584,7 @@ def profile_run(what, launches, wname="decode", m=1):
         x = dev_bf16(wl.activations(m))
         y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(nv.linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
-        torch.cuda.synchronize()
-        for i in range(launches):
-            p, s, t = rot.items[i % len(rot)]
-            nv.linear_w4a4(x, p, s, t, out=y, workspace=ws)
+        calls = [(lambda p=p, s=s, t=t: nv.linear_w4a4(x, p, s, t, out=y, workspace=ws)) for (p, s, t) in rot.items]
     elif what == "mx_w4a4":
         wl = WL.WORKLOADS["prefill"]
         m = 2048
@@ -568,10 +593,7 @@ def profile_run(what, launches, wname="decode", m=1):
         x = dev_bf16(wl.activations(m))
         y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(m, wl.k), dtype=torch.uint8, device="cuda")
-        torch.cuda.synchronize()
-        for i in range(launches):
-            r = rot[i % len(rot)]
-            nv.mx_linear_w4a4(x, r[0], r[1], out=y, workspace=ws)
+        calls = [(lambda r=r: nv.mx_linear_w4a4(x, r[0], r[1], out=y, workspace=ws)) for r in rot]
     elif what == "kv_gather":
         kw = WL.KV_PREFILL
         table, lens, dst, nb, out_rows = kw.layout()
@@ -582,10 +604,7 @@ def profile_run(what, launches, wname="decode", m=1):
         items = [(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
                   torch.empty((out_rows, kw.heads, kw.head_dim), dtype=torch.float16, device="cuda"))
                  for _ in range(copies_needed(per_copy))]
-        torch.cuda.synchronize()
-        for i in range(launches):
-            c, s, o = items[i % len(items)]
-            nv.kv_gather(c, s, ts, td, ld, dd, o, fmt="nvfp4")
+        calls = [(lambda c=c, s=s, o=o: nv.kv_gather(c, s, ts, td, ld, dd, o, fmt="nvfp4")) for (c, s, o) in items]
     elif what == "moe_prefill":
         pw = WL.MOE_PREFILL
         base = dev_bf16(pw.base_weight())
@@ -597,14 +616,11 @@ def profile_run(what, launches, wname="decode", m=1):
         y = torch.empty((pw.t, pw.topk, pw.n), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(nv.linear_grouped_workspace_bytes(pw.t, pw.topk, pw.experts), dtype=torch.uint8,
                          device="cuda")
-        torch.cuda.synchronize()
-        for _ in range(launches):
-            nv.linear_grouped(x, route, packed, scales, tscale, out=y, workspace=ws)
+        calls = [lambda: nv.linear_grouped(x, route, packed, scales, tscale, out=y, workspace=ws)]
     elif what == "copy":
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(launches):
-            dst.copy_(src)
+        calls = [lambda: dst.copy_(src)]
     else:
         nv.lib()
         wl = WL.WORKLOADS["decode" if what == "decode" else "prefill"]
@@ -613,12 +629,18 @@ def profile_run(what, launches, wname="decode", m=1):
         x = dev_bf16(wl.activations(m))
         rot = Rotated(packed, scales, tscale, copies_needed(packed.numel() + scales.numel()))
         y = torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda")
-        torch.cuda.synchronize()
-        for i in range(launches):
-            p, s, t = rot.items[i % len(rot)]
-            nv.linear(x, p, s, t, out=y)
+        calls = linear_calls(x, rot, y)
     torch.cuda.synchronize()
-    print(f"profile run done: {what} x{launches}", flush=True)
+    if graph:
+        g = graph_of(calls)
+        warm_graph(g)
+        for _ in range(-(-launches // len(calls))):
+            g.replay()
+    else:
+        for i in range(launches):
+            calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    print(f"profile run done: {what} x{launches}{' (graph replays)' if graph else ''}", flush=True)
 
 
 def main():
@@ -630,9 +652,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--cpu-baseline-only", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--profile", choices=["decode", "prefill", "prefill2048", "copy", "moe_prefill", "kv_gather", "mx_w4a4",
-                                              "nvfp4_w4a4", "quantize", "dequant", "linear", "prepared"], default=None,
+                                              "nvfp4_w4a4", "quantize", "dequant", "linear", "prepared", "stream"], default=None,
                     help="short untimed run of one kernel for hardware-counter passes; prints no JSON")
     ap.add_argument("--launches", type=int, default=40, help="launches in a --profile run")
+    ap.add_argument("--graph", action="store_true", help="--profile run: replay the rotated launches as one HIP graph")
     ap.add_argument("--workload", default="small_m_up", help="workload of a --profile linear run")
     ap.add_argument("--m", type=int, default=8, help="activation rows of a --profile linear run")
     args = ap.parse_args()
@@ -646,7 +669,7 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.profile:
-        profile_run(args.profile, args.launches, args.workload, args.m)
+        profile_run(args.profile, args.launches, args.workload, args.m, args.graph)
         return
     torch.cuda.set_device(0)
     nv.lib()
@@ -704,6 +727,9 @@ def main():
             log(f"  {rows[key]}")
         rows["prepare_small_m_up_17408x5120"] = bench_prepare_row(20)
         log(f"  prepare: {rows['prepare_small_m_up_17408x5120']}")
+        log("rows streaming read")
+        rows.update(bench_stream_rows(30))
+        log(f"  {[(k, v['us_per_call'], v['gb_s']) for k, v in rows.items() if k.startswith('stream_read')]}")
         log("rows quantize/dequant")
         rows.update(bench_quant_rows(20))
         log(f"  {rows['quantize_decode_5120x5120']} {rows['dequant_decode_5120x5120']}")
@@ -722,6 +748,16 @@ def main():
             rows.update(bench_w4a4_nvfp4_row(mm, reps_w))
         log(f"  {rows['nvfp4_w4a4_prefill_m512']} {rows['nvfp4_w4a4_prefill_m2048']}")
 
+    # Every HBM-bound row also as a fraction of the measured streaming-read rate of the nearest size.
+    streams = sorted((v["bytes"], v["gb_s"]) for k, v in rows.items() if k.startswith("stream_read"))
+    if streams:
+        for key, r in rows.items():
+            if "gb_s" in r and "hbm_frac" in r and not key.startswith("stream_read"):
+                nb = r.get("bytes") or linear_bytes(r.get("m", 1), r.get("n", 1), r.get("k", 1))
+                ref = min(streams, key=lambda sv: abs(sv[0] - nb))[1]
+                r["measured_read_gb_s"] = ref
+                r["measured_read_frac"] = round(r["gb_s"] / ref, 4)
+    head_read = min(streams, key=lambda sv: abs(sv[0] - linear_bytes(m, n, k)))[1] if streams else None
     log("cpu baseline (oracle)")
     cpu = cpu_baseline(args.cpu_budget)
     result = {
@@ -745,7 +781,9 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemv_decode_5120x5120", digest),
                      "kernel": "gemv_ks_kernel<5, 1>", "bytes_per_launch": nbytes,
-                     "avg_launch_us": round(ms * 1e3, 3)},
+                     "avg_launch_us": round(ms * 1e3, 3),
+                     "measured_read_gb_s": head_read,
+                     "measured_read_frac": round(gbs / head_read, 4) if head_read else None},
         "cpu_baseline": cpu,
         "rows": rows,
     }

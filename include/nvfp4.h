@@ -73,8 +73,10 @@ const char* nvfp4_version(void);
  *             ties to the even code, saturating at 6; 0 when s = 0
  * Every rounding decision is taken on the exact real quotient.
  * w: [n, k] BF16.  Outputs packed [n, k/2], scales [n, k/16], tscale [1].
- * The tscale slot is used as scratch for amax, and packed for per-workgroup
- * maxima, during the call.
+ * Three kernels on the stream: per-workgroup maxima of |W| (held in packed
+ * until the encode pass overwrites it), their reduction straight to tscale,
+ * and the encode pass, which recovers amax from tscale exactly (the BF16 value
+ * nearest to fl32(2688 * tscale) is amax for every finite BF16 amax).
  */
 nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k,
                             uint8_t* packed, uint8_t* scales, float* tscale, void* stream);
@@ -216,6 +218,19 @@ nvfp4_status nvfp4_linear_prepared(const uint16_t* x, int64_t m, int64_t n, int6
                                    const float* tscale, uint16_t* y, void* workspace, int64_t workspace_bytes,
                                    void* stream);
 
+/*
+ * Measurement aid (not a step of the linear): reads `bytes` bytes (a positive
+ * multiple of 16) of device memory at `src` once, with 16-byte loads, in
+ * nvfp4_stream_read_sink_words(bytes) <= 8192 workgroups; workgroup b stores
+ * the XOR of the 32-bit words it read to sink[b] (caller-owned device memory
+ * of that many words, 4-byte aligned, not overlapping src), so the XOR of
+ * those words is the XOR of the whole buffer.  Its rate is the plain HBM read
+ * rate on the device, against which the streaming kernels above are measured.
+ * src 16-byte aligned.  nvfp4_stream_read_sink_words returns -1 for a bad size.
+ */
+int64_t nvfp4_stream_read_sink_words(int64_t bytes);
+nvfp4_status nvfp4_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Kernel ids for nvfp4_linear_forced. */
 #define NVFP4_KERNEL_AUTO 0
 #define NVFP4_KERNEL_GEMV 1     /* VALU dot-product GEMV; any m (rows handled independently) */
@@ -240,7 +255,7 @@ nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, in
  *   w [e, n, k] BF16 -> packed [e, n, k/2], scales [e, n, k/16], tscale [e]
  * where matrix i of the outputs equals nvfp4_quantize applied to w[i], bit
  * for bit.  e = 0 is a no-op.  The same scratch use as nvfp4_quantize:
- * tscale[i] holds expert i's amax and its packed matrix holds per-workgroup
+ * tscale[i] is written first and its packed matrix holds per-workgroup
  * maxima until the last kernels overwrite them.
  */
 nvfp4_status nvfp4_quantize_experts(const uint16_t* w, int64_t e, int64_t n, int64_t k,

@@ -29,7 +29,8 @@ EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_ama
             "nvfp4_mx_linear_w4a4", "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped_workspace_bytes",
             "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes",
             "nvfp4_linear_noalloc", "nvfp4_linear_noalloc_max_bytes", "nvfp4_prepared_bytes", "nvfp4_prepare",
-            "nvfp4_dequant_prepared", "nvfp4_linear_prepared_workspace_bytes", "nvfp4_linear_prepared")
+            "nvfp4_dequant_prepared", "nvfp4_linear_prepared_workspace_bytes", "nvfp4_linear_prepared",
+            "nvfp4_stream_read", "nvfp4_stream_read_sink_words")
 
 
 class NVFP4Error(RuntimeError):
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequant_prepared.argtypes = [vp, vp, i64, i64, vp, vp]
         L.nvfp4_linear_prepared_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_prepared.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_stream_read.argtypes = [vp, i64, vp, vp]
+        L.nvfp4_stream_read_sink_words.argtypes = [i64]
         L.nvfp4_linear_ws.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
         L.nvfp4_quantize_experts.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.nvfp4_dequant_experts.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
@@ -84,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_linear_workspace_bytes.argtypes = [i64, i64, i64]
         L.nvfp4_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64]
         for name in EXPORTED[2:]:
-            getattr(L, name).restype = i64 if name.endswith(("_workspace_bytes", "_max_bytes", "_prepared_bytes")) \
+            getattr(L, name).restype = i64 if name.endswith(("_workspace_bytes", "_max_bytes", "_prepared_bytes", "_sink_words")) \
                 else i32
         _lib = L
     return _lib

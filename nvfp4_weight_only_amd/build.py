@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["nvfp4_abi.hip", "quant_kernels.hip", "gemv.hip", "gemm.hip", "skinny.hip", "small_m.hip", "prefill.hip", "grouped.hip", "kv_gather.hip", "mxfp4.hip"]
+SOURCES = ["nvfp4_abi.hip", "quant_kernels.hip", "gemv.hip", "gemm.hip", "skinny.hip", "small_m.hip", "prefill.hip", "grouped.hip", "kv_gather.hip", "mxfp4.hip", "stream.hip"]
 
 
 def hipcc() -> str:

@@ -17,6 +17,12 @@ void launch_amax_set(const uint16_t* w, int64_t n_elems, uint32_t* part, float* 
 void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* amax,
                            hipStream_t s);
 void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hipStream_t s);
+// tscale[i] = fl32(max |w_i| / 2688) (partial maxima in part as for launch_amax_set_stack), and the
+// quantize pass that recovers amax from it: the quantizer in three launches.
+void launch_tscale_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* tscale,
+                             hipStream_t s);
+void launch_quantize_from_tscale(const uint16_t* w, int64_t count, int64_t n_elems, const float* tscale,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s);
 void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
                      uint8_t* scales, hipStream_t s);
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,
@@ -104,5 +110,12 @@ void launch_mx_dequant(const uint8_t* packed, const uint8_t* scales, int64_t row
 bool mx_gemm_supported(int64_t m, int64_t n, int64_t k);
 void launch_mx_gemm(const uint8_t* xq, const uint8_t* xs, int64_t m, const uint8_t* wq, const uint8_t* ws, int64_t n,
                     int64_t k, uint16_t* y, hipStream_t s);
+
+// Plain streaming read of `bytes` bytes (a multiple of 16) of device memory by
+// stream_read_blocks(bytes) <= kStreamSinkWords workgroups; workgroup b stores the
+// XOR of the 32-bit words it read to sink[b].
+constexpr int64_t kStreamSinkWords = 8192;
+int64_t stream_read_blocks(int64_t bytes);
+void launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace nvfp4

@@ -204,12 +204,11 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* pa
   if ((st = validate_quantize_outputs(w, ws, packed, scales, tscale)) != NVFP4_OK) return st;
   if ((st = check_device()) != NVFP4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The tscale slot holds amax until the last kernel turns it into amax / 2688;
-  // the packed output (n k / 2 bytes) holds the per-workgroup maxima until the
-  // quantize pass overwrites it.
-  nvfp4::launch_amax_set(w, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
-  nvfp4::launch_quantize(w, 1, ws.elems, tscale, packed, scales, s);
-  nvfp4::launch_finalize_tscale(tscale, tscale, 1, s);
+  // The packed output (n k / 2 bytes) holds the per-workgroup maxima until the
+  // quantize pass overwrites it; the reduction writes the tensor scale, from
+  // which the quantize pass recovers amax exactly.
+  nvfp4::launch_tscale_set_stack(w, 1, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
+  nvfp4::launch_quantize_from_tscale(w, 1, ws.elems, tscale, packed, scales, s);
   return launch_status();
 }
 
@@ -371,6 +370,22 @@ nvfp4_status nvfp4_linear_prepared(const uint16_t* x, int64_t m, int64_t n, int6
   return launch_status();
 }
 
+int64_t nvfp4_stream_read_sink_words(int64_t bytes) {
+  if (bytes <= 0 || bytes % 16 != 0) return -1;
+  return nvfp4::stream_read_blocks(bytes);
+}
+
+nvfp4_status nvfp4_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return NVFP4_ERR_NULL;
+  if (bytes <= 0 || bytes % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return NVFP4_ERR_ALIGN;
+  if (overlaps(sink, 4 * nvfp4::stream_read_blocks(bytes), src, bytes)) return NVFP4_ERR_ALIAS;
+  nvfp4_status st;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  nvfp4::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 nvfp4_status nvfp4_linear_forced(int kernel_id, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                                  const uint8_t* packed, const uint8_t* scales, const float* tscale, uint16_t* y,
                                  void* stream) {
@@ -399,9 +414,8 @@ nvfp4_status nvfp4_quantize_experts(const uint16_t* w, int64_t e, int64_t n, int
   if (e == 0) return NVFP4_OK;
   if ((st = check_device()) != NVFP4_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  nvfp4::launch_amax_set_stack(w, e, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
-  nvfp4::launch_quantize(w, e, ws.elems, tscale, packed, scales, s);
-  nvfp4::launch_finalize_tscale(tscale, tscale, e, s);
+  nvfp4::launch_tscale_set_stack(w, e, ws.elems, reinterpret_cast<uint32_t*>(packed), tscale, s);
+  nvfp4::launch_quantize_from_tscale(w, e, ws.elems, tscale, packed, scales, s);
   return launch_status();
 }
 

@@ -68,7 +68,10 @@ __global__ void __launch_bounds__(256) amax_partial_kernel(const uint4* __restri
 }
 
 // amax[y] = max of part[y][0 .. nb) as an FP32 value (the BF16 magnitude
-// widened); y = blockIdx.y over a stack.
+// widened); y = blockIdx.y over a stack.  With TSCALE the value written is the
+// tensor scale fl32(amax / 2688) instead (the quantize pass then recovers amax
+// from it exactly, see amax_bits_from_tscale).
+template <bool TSCALE>
 __global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __restrict__ part, int nb, float* amax,
                                                           int64_t part_stride) {
   part += (int64_t)blockIdx.y * part_stride;
@@ -79,7 +82,10 @@ __global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __rest
   __shared__ uint32_t pw[4];
   if ((threadIdx.x & 63) == 0) pw[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) *amax = __uint_as_float(max(max(pw[0], pw[1]), max(pw[2], pw[3])) << 16);
+  if (threadIdx.x == 0) {
+    const float a = __uint_as_float(max(max(pw[0], pw[1]), max(pw[2], pw[3])) << 16);
+    *amax = TSCALE ? __fdiv_rn(a, 2688.0f) : a;
+  }
 }
 
 // *amax = max(*amax, max |w|) through an atomic max on the FP32 bits.
@@ -98,6 +104,12 @@ __global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, 
 // ---------------------------------------------------------------------------
 // Quantize.
 // ---------------------------------------------------------------------------
+
+// BF16 bits of amax from its tensor scale t = fl32(amax / 2688): the BF16
+// value nearest to fl32(2688 t) is amax again, for every finite non-negative
+// BF16 amax (FP32 subnormal t included; 2688 t is within a relative 2^-23 of
+// amax, far closer than half a BF16 step).
+__device__ __forceinline__ uint32_t amax_bits_from_tscale(float t) { return f32_to_bf16_rne(2688.0f * t); }
 
 // A finite BF16 magnitude b (bits & 0x7FFF) as sig * 2^ex with an integer sig < 256.
 __device__ __forceinline__ void bf16_split(uint32_t b, uint32_t& sig, int& ex) {
@@ -275,7 +287,8 @@ __device__ __forceinline__ void store_block(int64_t blk, BlockCodes q, uint2* __
 // whose kQuantB blocks all exist run without a branch between loads, codes and
 // stores, so the compiler interleaves the blocks; only the grid's last
 // iteration takes the guarded path.
-template <bool DECODE>
+// FROM_TSCALE: amax_p holds the tensor scale (amax recovered from it), else amax.
+template <bool DECODE, bool FROM_TSCALE = false>
 __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_blk,
                                                        const float* __restrict__ amax_p,
                                                        uint2* __restrict__ packed,
@@ -294,7 +307,9 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
   w += (int64_t)blockIdx.y * 2 * n_blk;
   packed += (int64_t)blockIdx.y * n_blk;
   scales += (int64_t)blockIdx.y * n_blk;
-  const uint32_t amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;  // amax is a BF16 value held in FP32
+  // amax is a BF16 value held in FP32 (or recovered from the tensor scale)
+  const uint32_t amax_b = FROM_TSCALE ? amax_bits_from_tscale(amax_p[blockIdx.y])
+                                      : __float_as_uint(amax_p[blockIdx.y]) >> 16;
   uint32_t sa;
   int ea;
   bf16_split(amax_b & 0x7FFFu, sa, ea);
@@ -417,7 +432,23 @@ void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, ui
   const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
   amax_partial_kernel<<<dim3(nb, (unsigned)count), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part, n_vec,
                                                                 n_vec);
-  amax_reduce_kernel<<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, amax, n_vec);
+  amax_reduce_kernel<false><<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, amax, n_vec);
+}
+
+void launch_tscale_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* tscale,
+                             hipStream_t s) {
+  const int64_t n_vec = n_elems / 8;
+  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
+  amax_partial_kernel<<<dim3(nb, (unsigned)count), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part, n_vec,
+                                                                n_vec);
+  amax_reduce_kernel<true><<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, tscale, n_vec);
+}
+
+void launch_quantize_from_tscale(const uint16_t* w, int64_t count, int64_t n_elems, const float* tscale,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  const int64_t n_blk = n_elems / 16;
+  quantize_kernel<false, true><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, tscale, reinterpret_cast<uint2*>(packed), scales, nullptr);
 }
 
 void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hipStream_t s) {

@@ -272,3 +272,15 @@ def test_prepared_layout_validation(L):
     assert lp(A + 8, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_ALIGN
     assert lp(A, 8, 64, 128, Bp, D, A + 16, None, 0, None) == B.ERR_ALIAS    # y overlaps x
     assert lp(None, 0, 64, 128, Bp, D, None, None, 0, None) == B.OK          # m = 0 no-op
+
+
+def test_stream_read_validation(L):
+    f = L.nvfp4_stream_read
+    assert f(None, 1024, E, None) == B.ERR_NULL
+    assert f(A, 1000, E, None) == B.ERR_SHAPE and f(A, 0, E, None) == B.ERR_SHAPE
+    assert f(A + 8, 1024, E, None) == B.ERR_ALIGN
+    assert f(A, 1024, A + 16, None) == B.ERR_ALIAS
+    w = L.nvfp4_stream_read_sink_words
+    assert w(0) == -1 and w(1000) == -1
+    assert w(16) == 1 and w(16 * 2048) == 1 and w(16 * 2048 + 16) == 2      # 2048 16-byte loads per workgroup
+    assert w(1 << 40) == 8192

@@ -1096,3 +1096,23 @@ def test_linear_prepared_full_size_sampled(nv, wname, m):
         assert np.array_equal(ph[t * blk:(t + 1) * blk], want), f"tile {t}"
     y_ref, bound = O.linear_ref(x, rp, rs, rt)
     check_linear(y[:, rows], y_ref, bound, f"{wname} prepared m={m} full size, sampled")
+
+
+def test_stream_read_reads_every_byte(nv):
+    """The streaming-read measurement kernel folds every byte: the XOR of its per-workgroup sink words is the
+    XOR of the whole buffer (computed on the host), at sizes with a ragged last workgroup and with more data
+    than the grid covers in one pass."""
+    rng = np.random.default_rng(7700)
+    L = nv.lib()
+    for nbytes in (16, 4096, 16 * 2049 * 256 + 48, 16 * 8192 * 2048 + 16 * 300):
+        data = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+        want = int(np.bitwise_xor.reduce(data))
+        src = torch.from_numpy(data.view(np.int32)).cuda()
+        words = L.nvfp4_stream_read_sink_words(nbytes)
+        assert 1 <= words <= 8192
+        sink = torch.zeros(words + 4, dtype=torch.int32, device="cuda")
+        assert L.nvfp4_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        assert int(np.bitwise_xor.reduce(got[:words])) == want, nbytes
+        assert not got[words:].any(), "wrote past its sink words"
