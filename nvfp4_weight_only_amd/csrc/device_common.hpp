@@ -129,6 +129,28 @@ __device__ __forceinline__ uint32_t e2m1x2_scaled_to_bf16(uint32_t p, float s) {
   return __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
 }
 
+// Dequantized BF16 pair: byte SEL of `p` (elements 2*SEL, 2*SEL+1) as
+// RNE_bf16(fl32(fl32(E2M1 * s) * t)).  E2M1 from the conversion instruction
+// (exact, -0 kept), E2M1 * s exact, one FP32 rounding by t, then the
+// nearest-even BF16 conversion (v_cvt_pk_bf16_f32).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_dequant_bf16(uint32_t p, float s, float t) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, SEL);
+  const f32x2_t a = {(v[0] * s) * t, (v[1] * s) * t};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2v_t));
+}
+
+// Eight elements (one packed word) dequantized to BF16 with block scale s and
+// tensor scale t (finite): four natural-order pairs.  A NaN scale (E4M3 0x7F /
+// 0xFF) gives the canonical quiet NaN 0x7FC0 in every element.
+__device__ __forceinline__ uint4 e2m1x8_dequant_bf16(uint32_t p, float s, float t) {
+  const uint4 r = make_uint4(e2m1x2_dequant_bf16<0>(p, s, t), e2m1x2_dequant_bf16<1>(p, s, t),
+                             e2m1x2_dequant_bf16<2>(p, s, t), e2m1x2_dequant_bf16<3>(p, s, t));
+  return s == s ? r : make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+}
+
 // Eight elements of `p` times `s` as four natural-order BF16 pairs.
 __device__ __forceinline__ uint4 e2m1x8_scaled_to_bf16_hw(uint32_t p, float s) {
   return make_uint4(e2m1x2_scaled_to_bf16<0>(p, s), e2m1x2_scaled_to_bf16<1>(p, s), e2m1x2_scaled_to_bf16<2>(p, s),

@@ -7,9 +7,10 @@
 //   tscale = fl32(amax / 2688)
 //   scale  = E4M3 code nearest to 448 * bam / amax           (ties to even)
 //   code   = sign(w) | E2M1 code nearest to 2688 |w| / (amax s)   (ties to even, saturating)
-// Every decision compares two exact products in FP32 (operands are rescaled
-// by powers of two so that both sides stay in range), so the result equals
-// the decision on the exact real quotients.
+// Each rounding is the hardware's nearest-even conversion of an FP32 value
+// that equals the exact quotient at a midpoint and lies on the exact
+// quotient's side of every midpoint otherwise, so the result is the decision
+// on the exact real quotients.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -25,28 +26,34 @@ namespace nvfp4 {
 // address atomics serialise, so the atomic form uses few workgroups.
 // ---------------------------------------------------------------------------
 constexpr int kAmaxU = 8;
-constexpr int kAmaxBlocks = 512;
+constexpr int kAmaxBlocks = 512;          // atomic form
+constexpr int kAmaxPartialBlocks = 8192;  // partial-slot form: one pass over the data per thread
 
-__device__ __forceinline__ uint32_t bf16x8_absmax_bits(uint4 v) {
-  const uint32_t a = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-  const uint32_t b = max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-  return max(a, b);
+typedef unsigned short amax_u16x2_t __attribute__((ext_vector_type(2)));
+
+// Lane-wise 16-bit maxima of the magnitude bits of 8 BF16 (two per 32 bits).
+__device__ __forceinline__ amax_u16x2_t bf16x8_absmax_pair(uint4 v) {
+  const auto m = [](uint32_t x) { return __builtin_bit_cast(amax_u16x2_t, x & 0x7FFF7FFFu); };
+  return __builtin_elementwise_max(__builtin_elementwise_max(m(v.x), m(v.y)), __builtin_elementwise_max(m(v.z), m(v.w)));
 }
 
 // The workgroup's maximum |w| (BF16 magnitude bits), valid in thread 0.
+// Loads never branch: an index past the end loads the last vector again, which
+// cannot change the maximum.
 __device__ __forceinline__ uint32_t amax_block(const uint4* __restrict__ w, int64_t n_vec) {
-  uint32_t m = 0;
+  amax_u16x2_t mp = {0, 0};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * kAmaxU;
   for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x * kAmaxU + threadIdx.x; i0 < n_vec; i0 += stride) {
     uint4 v[kAmaxU];
 #pragma unroll
     for (int u = 0; u < kAmaxU; ++u) {
       const int64_t i = i0 + (int64_t)u * blockDim.x;
-      v[u] = i < n_vec ? w[i] : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = w[i < n_vec ? i : n_vec - 1];
     }
 #pragma unroll
-    for (int u = 0; u < kAmaxU; ++u) m = max(m, bf16x8_absmax_bits(v[u]));
+    for (int u = 0; u < kAmaxU; ++u) mp = __builtin_elementwise_max(mp, bf16x8_absmax_pair(v[u]));
   }
+  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
   m = wave_max_u32(m);
   __shared__ uint32_t part[4];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -76,8 +83,16 @@ __global__ void __launch_bounds__(256) amax_reduce_kernel(const uint32_t* __rest
                                                           int64_t part_stride) {
   part += (int64_t)blockIdx.y * part_stride;
   amax += blockIdx.y;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nb; i += blockDim.x) m = max(m, part[i]);
+  // Eight independent loads per thread in flight (one pass for nb <= 2048).
+  uint32_t mv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  for (int i0 = threadIdx.x; i0 < nb; i0 += blockDim.x * 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * (int)blockDim.x;
+      mv[u] = max(mv[u], part[i < nb ? i : nb - 1]);  // a repeated slot cannot change the maximum
+    }
+  }
+  uint32_t m = max(max(max(mv[0], mv[1]), max(mv[2], mv[3])), max(max(mv[4], mv[5]), max(mv[6], mv[7])));
   m = wave_max_u32(m);
   __shared__ uint32_t pw[4];
   if ((threadIdx.x & 63) == 0) pw[threadIdx.x >> 6] = m;
@@ -111,108 +126,89 @@ __global__ void __launch_bounds__(64) finalize_tscale_kernel(const float* amax, 
 // amax, far closer than half a BF16 step).
 __device__ __forceinline__ uint32_t amax_bits_from_tscale(float t) { return f32_to_bf16_rne(2688.0f * t); }
 
-// A finite BF16 magnitude b (bits & 0x7FFF) as sig * 2^ex with an integer sig < 256.
-__device__ __forceinline__ void bf16_split(uint32_t b, uint32_t& sig, int& ex) {
-  const uint32_t f = b >> 7;
-  sig = (b & 0x7Fu) | (f ? 0x80u : 0u);
-  ex = (f ? (int)f : 1) - 134;
+// Rounding decisions through FP64 and the gfx950 conversion instructions.
+//
+// Both roundings of the quantizer are "nearest grid point of an exact
+// quotient, ties to the even code": the E4M3 scale of 448 bam / amax and the
+// E2M1 magnitude of 2688 |w| / (amax s).  Every operand is a BF16 or E4M3
+// value (at most 8 significant bits), so when such a quotient is not exactly a
+// midpoint of its grid it lies at least a relative 2^-17 away from every
+// midpoint (numerator and denominator are small integers times powers of two:
+// a nonzero difference is at least the smaller power of two).  The quotient is
+// formed in FP64 from one correctly rounded division and one product (relative
+// error below 2^-51), then rounded to FP32: a midpoint (a short FP32 value)
+// comes out exactly, and every other quotient stays on its side of every
+// midpoint.  The hardware FP32 -> E4M3 / E2M1 conversions round to nearest
+// even on the exact FP32 input, which is then the decision on the exact real
+// quotient.  E2M1 saturates at 6 (code 7), as the nearest-code rule does.
+
+// The E4M3 code nearest to r, 0 <= r <= 448 (hardware conversion, round to
+// nearest even, OCP E4M3FN).
+__device__ __forceinline__ uint32_t e4m3_code_rne(float r) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false) & 0xFFu;
 }
 
-// E4M3 value of a code as sig * 2^ex (sig <= 15).
-__device__ __forceinline__ void e4m3_split(uint32_t c, uint32_t& sig, int& ex) {
-  const uint32_t e = c >> 3, m = c & 7u;
-  sig = e ? (8u + m) : m;
-  ex = e ? (int)e - 10 : -9;
-}
-
-// Round a non-negative float to an E4M3 code (RNE), clamped to 0..126.  Used
-// only for a first guess from an approximate quotient; the caller corrects it.
-// Branch-free (selects), so that several blocks' searches can interleave.
-__device__ __forceinline__ uint32_t e4m3_code_guess(float r) {
-  uint32_t u = __float_as_uint(r);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  uint32_t c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);   // normal range [2^-6, 448)
-  c = c > 126u ? 126u : c;
-  const uint32_t sub = (uint32_t)__builtin_rintf(r * 512.0f);  // subnormal range: multiples of 2^-9
-  c = r < 0x1p-6f ? sub : c;
-  return r < 448.0f ? c : 126u;                                // also NaN
-}
-
-// The E4M3 code nearest to 448 * bam / amax (ties to the even code).
-// bam = sb * 2^eb, amax = sa * 2^ea.  With A = 448 sb 2^(eb-ea) and D = sa the
-// quotient is A / D; the comparisons A vs u * D against the midpoints u are
-// exact (u has <= 5 significant bits, D <= 8, A <= 17).  The guess is off by at
-// most one code; one step up, then one step down, settles it.
-__device__ __forceinline__ uint32_t e4m3_scale_code(uint32_t bam_b, uint32_t sa, int ea) {
-  uint32_t sb;
-  int eb;
-  bf16_split(bam_b, sb, eb);
-  const float A = ldexpf((float)(448u * sb), eb - ea);
-  const float D = (float)sa;
-  uint32_t c = e4m3_code_guess(A * __builtin_amdgcn_rcpf(D));
-  // Neighbouring codes as one 16-bit pair, decoded by the hardware E4M3 conversion
-  // (exact for every code; codes here are at most 126, never NaN).
-  const uint32_t cu = c < 125u ? c : 125u;
-  const auto pu = __builtin_amdgcn_cvt_pk_f32_fp8((int)(cu | ((cu + 1u) << 8)), false);
-  const float up_rhs = 0.5f * (pu[0] + pu[1]) * D;
-  // Bitwise forms of the tie rule (an odd code's upper midpoint rounds up), so
-  // that no branch splits the block.
-  const uint32_t odd_u = c & 1u;
-  c += (uint32_t)(c < 126u) & ((odd_u & (uint32_t)(A >= up_rhs)) | ((odd_u ^ 1u) & (uint32_t)(A > up_rhs)));
-  const uint32_t cd = c > 1u ? c : 1u;
-  const auto pd = __builtin_amdgcn_cvt_pk_f32_fp8((int)((cd - 1u) | (cd << 8)), false);
-  const float dn_rhs = 0.5f * (pd[0] + pd[1]) * D;
-  const uint32_t odd_d = (c - 1u) & 1u;
-  c -= (uint32_t)(c > 0u) & ((odd_d & (uint32_t)(A < dn_rhs)) | ((odd_d ^ 1u) & (uint32_t)(A <= dn_rhs)));
-  return bam_b == 0u ? 0u : c;
-}
-
-// Per-block element thresholds.  With t_j = T_j / 4 the E2M1 midpoints
-// (T = 1, 3, 5, 7, 10, 14, 20), the element decision 2688 |w| vs t_j amax s
-// becomes  L = 21 |w| 2^(9 - ea - es)  vs  R_j = T_j sa ss  (2688 = 21 * 2^7).
-struct ElemThresholds {
-  float r[7];
-  uint32_t u[7];  // bits of r
-  int shift;      // 9 - ea - es
+// Per-tensor constants: k448 = 448 / amax and k2688 = 2688 / amax in FP64
+// (correctly rounded divisions); zero when amax is 0 (then every scale and code
+// is 0).
+struct QuantConsts {
+  double k448, k2688;
 };
 
-__device__ __forceinline__ ElemThresholds element_thresholds(uint32_t scode, uint32_t sa, int ea) {
-  ElemThresholds t;
-  uint32_t ss;
-  int es;
-  e4m3_split(scode, ss, es);
-  // scale 0: every magnitude is 0 (compare against +inf)
-  const float S = scode ? (float)(sa * ss) : __builtin_huge_valf();
-  t.r[0] = 1.0f * S;
-  t.r[1] = 3.0f * S;
-  t.r[2] = 5.0f * S;
-  t.r[3] = 7.0f * S;
-  t.r[4] = 10.0f * S;
-  t.r[5] = 14.0f * S;
-  t.r[6] = 20.0f * S;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) t.u[j] = __float_as_uint(t.r[j]);
-  t.shift = 9 - ea - es;
-  return t;
+__device__ __forceinline__ QuantConsts quant_consts(uint32_t amax_b) {
+  const double a = (double)__uint_as_float((amax_b & 0x7FFFu) << 16);
+  QuantConsts c;
+  c.k448 = a > 0.0 ? 448.0 / a : 0.0;
+  c.k2688 = a > 0.0 ? 2688.0 / a : 0.0;
+  return c;
 }
 
-// 4-bit code of one BF16 element (bits in the low 16 bits of b).
-// The magnitude code is the number of midpoints L passes (ties to the even
-// code: L must reach an odd code's upper midpoint R_1, R_3, R_5 and exceed an
-// even code's R_0, R_2, R_4, R_6).  The R_j increase with j, so a binary search
-// takes three of the seven exact comparisons: R_3, then R_5 or R_1, then the
-// even midpoint just below.
-__device__ __forceinline__ uint32_t element_code(uint32_t b, const ElemThresholds& t) {
-  // Selects are written as bit masks so that they stay v_cndmask / v_bfi and
-  // never become branches.
-  const float L = 21.0f * ldexpf(__uint_as_float((b & 0x7FFFu) << 16), t.shift);
-  const uint32_t hi = 0u - (uint32_t)(L >= t.r[3]);                             // code >= 4
-  const uint32_t m = (t.u[5] & hi) | (t.u[1] & ~hi);
-  const uint32_t mid = 0u - (uint32_t)(L >= __uint_as_float(m));               // code >= 6, or >= 2
-  const uint32_t lo_hi = (t.u[6] & mid) | (t.u[4] & ~mid), lo_lo = (t.u[2] & mid) | (t.u[0] & ~mid);
-  const float lo = __uint_as_float((lo_hi & hi) | (lo_lo & ~hi));
-  const uint32_t mag = (hi & 4u) | (mid & 2u) | (uint32_t)(L > lo);
-  return mag | ((b >> 12) & 8u);
+// Eight elements (one uint4 of BF16) to eight 4-bit codes in one word (element
+// i in nibble i): code = E2M1 nearest to w * cq with the sign of w, where
+// cq = 2688 / (amax s) in FP64 (0 for a zero scale: every magnitude code 0).
+template <int J>
+__device__ __forceinline__ uint32_t pair_codes(uint32_t word, uint32_t e, double cq) {
+  const float lo = (float)((double)__uint_as_float(e << 16) * cq);
+  const float hi = (float)((double)__uint_as_float(e & 0xFFFF0000u) * cq);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lo, hi, 1.0f, J);
+}
+
+__device__ __forceinline__ uint32_t half_codes(const uint4 v, double cq) {
+  uint32_t word = pair_codes<0>(0u, v.x, cq);
+  word = pair_codes<1>(word, v.y, cq);
+  word = pair_codes<2>(word, v.z, cq);
+  return pair_codes<3>(word, v.w, cq);
+}
+
+// One thread per 16-element block at a time: two 16-byte loads (8 BF16 each),
+// one 64-bit store of the 16 codes, one scale byte.  Each thread loads
+// kQuantB blocks (blockDim apart) before it encodes any of them.
+constexpr int kQuantB = 2;
+
+struct BlockCodes {
+  uint32_t lo, hi, scode;  // codes of elements 0..7 and 8..15, scale code
+};
+
+// Largest magnitude (bits & 0x7FFF) of 8 BF16, by lane-wise 16-bit maxima.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2_t mag2(uint32_t x) { return __builtin_bit_cast(u16x2_t, x & 0x7FFF7FFFu); }
+
+__device__ __forceinline__ uint32_t half_max(const uint4 v) {
+  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(mag2(v.x), mag2(v.y)),
+                                              __builtin_elementwise_max(mag2(v.z), mag2(v.w)));
+  return max((uint32_t)a[0], (uint32_t)a[1]);
+}
+
+__device__ __forceinline__ BlockCodes quantize_block(const uint4 v0, const uint4 v1, const QuantConsts& c) {
+  const uint32_t bam = max(half_max(v0), half_max(v1));
+  // Scale: E4M3 nearest to 448 bam / amax (at most 448: bam <= amax).
+  const float r = (float)((double)__uint_as_float(bam << 16) * c.k448);
+  const uint32_t scode = e4m3_code_rne(fminf(r, 448.0f));
+  // Elements: E2M1 nearest to 2688 |w| / (amax s), s the E4M3 value of scode.
+  const double s = (double)e4m3x2_to_f32<false>(scode).x;
+  const double cq = scode ? c.k2688 / s : 0.0;
+  return BlockCodes{half_codes(v0, cq), half_codes(v1, cq), scode};
 }
 
 // 8 codes (one 32-bit word) decoded to E2M1 * E4M3 (no tensor scale) as 8 BF16.
@@ -232,44 +228,6 @@ __device__ __forceinline__ uint4 decode_half_bf16(uint32_t word, uint32_t scode)
   const float s = e4m3x2_to_f32<false>(scode).x;
   return make_uint4(decode_pair_bf16(e2m1_pair<0>(word), s), decode_pair_bf16(e2m1_pair<1>(word), s),
                     decode_pair_bf16(e2m1_pair<2>(word), s), decode_pair_bf16(e2m1_pair<3>(word), s));
-}
-
-// One thread per 16-element block at a time: two 16-byte loads (8 BF16 each),
-// one 64-bit store of the 16 codes, one scale byte.  Each thread loads
-// kQuantB blocks (blockDim apart) before it encodes any of them.
-constexpr int kQuantB = 2;
-
-struct BlockCodes {
-  uint32_t lo, hi, scode;  // codes of elements 0..7 and 8..15, scale code
-};
-
-__device__ __forceinline__ uint32_t half_codes(const uint4 v, const ElemThresholds& t) {
-  const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) word |= element_code(e[i], t) << (4 * i);
-  return word;
-}
-
-// Largest magnitude (bits & 0x7FFF) of 8 BF16, by lane-wise 16-bit maxima.
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ u16x2_t mag2(uint32_t x) { return __builtin_bit_cast(u16x2_t, x & 0x7FFF7FFFu); }
-
-__device__ __forceinline__ uint32_t half_max(const uint4 v) {
-  const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(mag2(v.x), mag2(v.y)),
-                                              __builtin_elementwise_max(mag2(v.z), mag2(v.w)));
-  return max((uint32_t)a[0], (uint32_t)a[1]);
-}
-
-__device__ __forceinline__ BlockCodes quantize_block(const uint4 v0, const uint4 v1, uint32_t amax_b, uint32_t sa,
-                                                     int ea) {
-  const uint32_t bam = max(half_max(v0), half_max(v1));
-  const uint32_t sc = e4m3_scale_code(bam, sa, ea);   // evaluated always: a select, not a branch
-  const uint32_t scode = (amax_b & 0x7FFFu) ? sc : 0u;
-  const ElemThresholds t = element_thresholds(scode, sa, ea);
-  return BlockCodes{half_codes(v0, t), half_codes(v1, t), scode};
 }
 
 template <bool DECODE>
@@ -310,9 +268,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
   // amax is a BF16 value held in FP32 (or recovered from the tensor scale)
   const uint32_t amax_b = FROM_TSCALE ? amax_bits_from_tscale(amax_p[blockIdx.y])
                                       : __float_as_uint(amax_p[blockIdx.y]) >> 16;
-  uint32_t sa;
-  int ea;
-  bf16_split(amax_b & 0x7FFFu, sa, ea);
+  const QuantConsts qc = quant_consts(amax_b);
   const int64_t B = blockDim.x;
   const int64_t stride = (int64_t)gridDim.x * B * kQuantB;
   for (int64_t b0 = (int64_t)blockIdx.x * B * kQuantB + threadIdx.x; b0 < n_blk; b0 += stride) {
@@ -325,7 +281,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
       }
       BlockCodes q[kQuantB];
 #pragma unroll
-      for (int u = 0; u < kQuantB; ++u) q[u] = quantize_block(v[2 * u], v[2 * u + 1], amax_b, sa, ea);
+      for (int u = 0; u < kQuantB; ++u) q[u] = quantize_block(v[2 * u], v[2 * u + 1], qc);
 #pragma unroll
       for (int u = 0; u < kQuantB; ++u) store_block<DECODE>(b0 + u * B, q[u], packed, scales, decoded);
     } else {
@@ -333,8 +289,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
       for (int u = 0; u < kQuantB; ++u) {
         const int64_t blk = b0 + u * B;
         if (blk < n_blk) {
-          store_block<DECODE>(blk, quantize_block(w[2 * blk], w[2 * blk + 1], amax_b, sa, ea), packed, scales,
-                              decoded);
+          store_block<DECODE>(blk, quantize_block(w[2 * blk], w[2 * blk + 1], qc), packed, scales, decoded);
         }
       }
     }
@@ -349,24 +304,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
 constexpr int kDequantU = 4;
 
 __device__ __forceinline__ uint4 dequant_half(uint32_t p, uint32_t sbyte, float t) {
-  {
-    const float s = e4m3_to_f32(sbyte);
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t pair = 0;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t c = (p >> (8 * j + 4 * q)) & 0xFu;
-        float v = e2m1_mag_to_f32(c & 7u) * s;  // exact
-        v = v * t;                              // one FP32 rounding
-        if (c & 8u) v = -v;
-        pair |= f32_to_bf16_rne(v) << (16 * q);
-      }
-      o[j] = pair;
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-  }
+  return e2m1x8_dequant_bf16(p, e4m3x2_to_f32<false>(sbyte).x, t);
 }
 
 // Over a stack, blockIdx.y picks the matrix (n_half half blocks each).
@@ -429,7 +367,7 @@ void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, ui
   // Matrix i's partial maxima go to part + i * n_elems / 8: the packed output of matrix i (n_elems / 8 words), and
   // the grid never exceeds n_elems / 8 workgroups.
   const int64_t n_vec = n_elems / 8;
-  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
+  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxPartialBlocks);
   amax_partial_kernel<<<dim3(nb, (unsigned)count), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part, n_vec,
                                                                 n_vec);
   amax_reduce_kernel<false><<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, amax, n_vec);
@@ -438,7 +376,7 @@ void launch_amax_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, ui
 void launch_tscale_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, uint32_t* part, float* tscale,
                              hipStream_t s) {
   const int64_t n_vec = n_elems / 8;
-  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxBlocks);
+  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxPartialBlocks);
   amax_partial_kernel<<<dim3(nb, (unsigned)count), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, part, n_vec,
                                                                 n_vec);
   amax_reduce_kernel<true><<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, tscale, n_vec);

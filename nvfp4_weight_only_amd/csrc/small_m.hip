@@ -338,22 +338,7 @@ __global__ void __launch_bounds__(256) prepare_kernel(const uint8_t* __restrict_
 // w = RNE_bf16(fl32(fl32(E2M1 * E4M3) * tscale)) for the 8 elements of one
 // packed word and its E4M3 scale byte, as 8 BF16 in natural order.
 __device__ __forceinline__ uint4 sm_dequant8(uint32_t p, uint32_t sbyte, float t) {
-  const float s = e4m3_to_f32(sbyte);
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t pair = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t c = (p >> (8 * j + 4 * h)) & 0xFu;
-      float v = e2m1_mag_to_f32(c & 7u) * s;  // exact
-      v = v * t;                              // one FP32 rounding
-      if (c & 8u) v = -v;
-      pair |= f32_to_bf16_rne(v) << (16 * h);
-    }
-    o[j] = pair;
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  return e2m1x8_dequant_bf16(p, e4m3x2_to_f32<false>(sbyte).x, t);
 }
 
 // One thread per packed slot: 32 elements of one row, four 16-byte stores.
