@@ -180,9 +180,10 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
  * and re-lays scale factors once for its prefill GEMM.  Here the same bytes
  * (values unchanged) are re-laid once, for k a multiple of 128, into the order
  * the gfx950 decode kernels read them:
- *   - rows in tiles of 16 (n padded with zero rows to a multiple of 16), k in
- *     quads of 128 elements; block (tile t, quad q) is 1152 bytes at offset
- *     (t * k/128 + q) * 1152;
+ *   - rows in tiles of 16 (n padded with zero rows to a multiple of 16,
+ *     tiles = ceil(n / 16)), k in quads of 128 elements; block (tile t,
+ *     quad q) is 1152 bytes at offset (q * tiles + t) * 1152 (quad-major: the
+ *     blocks of consecutive tiles for one quad lie side by side);
  *   - its first 1024 bytes are 64 slots of 16 bytes: slot 16 g + r (g = 0..3,
  *     r = 0..15) holds, as 4-byte words i = 0..3, the elements
  *     128 q + 32 i + 8 g .. + 8 of row 16 t + r (low nibble first, as in
@@ -190,8 +191,9 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
  *   - its last 128 bytes are 32 words: word 16 h + r (h = 0, 1) holds, as
  *     byte i, the E4M3 scale of block 8 q + 2 i + h of row 16 t + r.
  * A wavefront then loads the weights of one (tile, quad) as one contiguous
- * kilobyte and their scales as one 128-byte line.  The tensor scale is
- * unchanged and passed separately.
+ * kilobyte and their scales as one 128-byte line, and the tiles a workgroup
+ * reads for one quad are one contiguous run.  The tensor scale is unchanged
+ * and passed separately.
  *
  * nvfp4_prepared_bytes(n, k): size of the layout, -1 when n <= 0, k <= 0,
  * k % 128 != 0 or the size overflows (no HIP call).

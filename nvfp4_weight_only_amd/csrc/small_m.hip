@@ -11,7 +11,10 @@
 // rows at once (the activations are the B operand, 16 rows per MFMA tile).
 //
 // Kernel-native layout: 16-row tiles x 128-element quads, 1152 bytes per
-// (tile, quad): 64 slots of 16 bytes, slot 16 g + r holding the elements
+// (tile, quad), quad-major (block (t, q) at (q * tiles + t) * 1152, so the
+// tiles a workgroup reads for one quad are one contiguous run, and the eight
+// wavefronts, on neighbouring quads, read neighbouring runs): 64 slots of 16
+// bytes, slot 16 g + r holding the elements
 // 32 i + 8 g .. + 8 (word i) of the quad in row r, then 32 scale words, word
 // 16 h + r holding the scales of blocks 2 i + h (byte i) of row r.  A lane
 // (r, g) of MFMA step 4 q + i takes word i of slot 16 g + r as its A operand
@@ -27,9 +30,10 @@
 // quads.  It reads the T tiles that cover its rows (a tile shared with the
 // neighbouring block is read by both; their ids are consecutive on one XCD, so
 // the second read is an L2 hit) and stores only its own rows.  The slice's
-// quads are shared out among the eight wavefronts, and every wavefront runs its
-// quads for all T tiles, so the activation fragments of a quad are loaded once
-// per wavefront and serve T tiles.  There is no barrier in the K loop: each
+// quads are dealt out to the eight wavefronts in turn (wavefront w takes quads
+// w, w + 8, ...), and every wavefront runs its quads for all T tiles, so the
+// activation fragments of a quad are loaded once per wavefront and serve T
+// tiles.  There is no barrier in the K loop: each
 // wavefront double-buffers one quad of activation fragments and one quad of
 // weights for all its tiles in registers, and issues the next quad's loads
 // before the current quad's products.  At the end the eight wavefronts' FP32
@@ -75,8 +79,10 @@ struct SmX {
   uint4 v[4][NMT];
 };
 
-__device__ __forceinline__ void sm_load_w(SmW& r, const uint8_t* tile, int q, int lane) {
-  const uint8_t* b = tile + (int64_t)q * kSmBlock;
+// tile: the tile's block of quad 0; qstride: bytes from one quad's blocks to
+// the next (tiles * 1152, quad-major layout).
+__device__ __forceinline__ void sm_load_w(SmW& r, const uint8_t* tile, int64_t qstride, int q, int lane) {
+  const uint8_t* b = tile + (int64_t)q * qstride;
   r.w = *reinterpret_cast<const uint4*>(b + 16 * lane);
   r.s = *reinterpret_cast<const uint32_t*>(b + 1024 + 4 * (16 * ((lane >> 5) & 1) + (lane & 15)));
 }
@@ -148,16 +154,20 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
   const int64_t row_end = row0 + p.rows < p.n ? row0 + p.rows : p.n;
   const int64_t tile0 = row0 >> 4;
   const int64_t tiles = (p.n + 15) >> 4;
-  // This workgroup's quads, then this wavefront's share of them.
+  const int64_t qstride = tiles * kSmBlock;
+  // This workgroup's quads [Q0, Q1); wavefront w takes every eighth of them,
+  // Q0 + w, Q0 + w + 8, ..., so that the eight wavefronts read neighbouring
+  // quads at any one time.
   const int Q0 = (int)((int64_t)sl * p.quads / p.slices), Q1 = (int)((int64_t)(sl + 1) * p.quads / p.slices);
-  const int q0 = Q0 + (Q1 - Q0) * w / kSmWaves, q1 = Q0 + (Q1 - Q0) * (w + 1) / kSmWaves;
+  const int qw = Q0 + w;
+  const int nq = Q1 > qw ? (Q1 - qw + kSmWaves - 1) / kSmWaves : 0;  // this wavefront's quads
 
   // Tiles past the weight's last tile repeat it (their rows are never stored).
   const uint8_t* tb[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t ti = tile0 + t < tiles ? tile0 + t : tiles - 1;
-    tb[t] = p.prep + ti * (int64_t)p.quads * kSmBlock;
+    tb[t] = p.prep + ti * (int64_t)kSmBlock;
   }
   const uint16_t* xr[NMT];
 #pragma unroll
@@ -172,33 +182,34 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (q1 > q0) {
-    // Double buffer: while quad q's products run, quad q + 1 is in flight.
+  if (nq > 0) {
+    // Double buffer: while quad j's products run, quad j + 1 is in flight.
     // Past the last quad the loads repeat it (in bounds; never used).  The
     // scheduling barrier keeps a quad's loads ahead of the previous quad's
     // products (the scheduler would otherwise sink them next to their uses to
     // save registers, and each quad would wait out a full load latency).
     SmX<NMT> xa, xb;
     SmW wa[T], wb[T];
-    auto load = [&](SmX<NMT>& xq, SmW* wq, int q) {
+    auto load = [&](SmX<NMT>& xq, SmW* wq, int j) {
+      const int q = qw + kSmWaves * j;
       sm_load_x<NMT>(xq, xr, q, g);
 #pragma unroll
-      for (int t = 0; t < T; ++t) sm_load_w(wq[t], tb[t], q, lane);
+      for (int t = 0; t < T; ++t) sm_load_w(wq[t], tb[t], qstride, q, lane);
       __builtin_amdgcn_sched_barrier(0);
     };
     auto compute = [&](const SmX<NMT>& xq, const SmW* wq) {
 #pragma unroll
       for (int t = 0; t < T; ++t) sm_quad<NMT>(wq[t], xq, acc[t]);
     };
-    load(xa, wa, q0);
-    int q = q0;
-    for (; q + 1 < q1; q += 2) {
-      load(xb, wb, q + 1);
+    load(xa, wa, 0);
+    int j = 0;
+    for (; j + 1 < nq; j += 2) {
+      load(xb, wb, j + 1);
       compute(xa, wa);
-      load(xa, wa, q + 2 < q1 ? q + 2 : q1 - 1);
+      load(xa, wa, j + 2 < nq ? j + 2 : nq - 1);
       compute(xb, wb);
     }
-    if (q < q1) compute(xa, wa);
+    if (j < nq) compute(xa, wa);
   }
 
   // The eight wavefronts' sums of each (row tile, m tile) pair, added in
@@ -302,11 +313,11 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
 __global__ void __launch_bounds__(256) prepare_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales, int64_t n, int64_t k,
                                                       int64_t blocks, uint8_t* __restrict__ out) {
-  const int64_t quads = k / kSmQuadK, kh = k >> 1, ks = k >> 4;
+  const int64_t tiles = (n + 15) >> 4, kh = k >> 1, ks = k >> 4;
   const int64_t units = blocks * 72;
   for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < units;
        id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = id / 72, t = b / quads, q = b - t * quads;
+    const int64_t b = id / 72, q = b / tiles, t = b - q * tiles;  // block b = q * tiles + t
     const int u = (int)(id - b * 72);
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (u < 64) {
@@ -345,12 +356,12 @@ __device__ __forceinline__ uint4 sm_dequant8(uint32_t p, uint32_t sbyte, float t
 __global__ void __launch_bounds__(256) dequant_prepared_kernel(const uint8_t* __restrict__ prep,
                                                                const float* __restrict__ tscale_p, int64_t n,
                                                                int64_t k, int64_t blocks, uint16_t* __restrict__ out) {
-  const int64_t quads = k / kSmQuadK;
+  const int64_t tiles = (n + 15) >> 4;
   const int64_t slots = blocks * 64;
   const float ts = *tscale_p;
   for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < slots;
        id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = id >> 6, t = b / quads, q = b - t * quads;
+    const int64_t b = id >> 6, q = b / tiles, t = b - q * tiles;  // block b = q * tiles + t
     const int s = (int)(id & 63), g = s >> 4, r = s & 15;
     const int64_t row = t * 16 + r;
     if (row >= n) continue;
@@ -421,11 +432,15 @@ bool small_m_supported(int64_t m, int64_t n, int64_t k) {
 SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
   SmallMPlan pl;
   pl.quads = (int)(k / kSmQuadK);
-  // K slices: about 80 weight rows per workgroup and 256 workgroups (one per
+  // K slices: about 40 weight rows per workgroup and 256 workgroups (one per
   // CU), each slice at least eight quads (one per wavefront), at most 16.
+  // (Fewer rows per workgroup would mean more slices, whose partial-sum
+  // exchange at the end costs more than the shorter K loop saves; at the down
+  // projection 5120 x 17408, M = 8, 40 rows x 2 slices measured 15.5 us against
+  // 16.6 us for 80 x 4 and 17.8 us for 20 x 1.)
   int64_t s = 1;
   if (split) {
-    s = (80 * 256 + n / 2) / n;
+    s = (40 * 256 + n / 2) / n;
     int64_t cap = pl.quads / kSmWaves;
     cap = cap < 16 ? cap : 16;
     s = s > cap ? cap : s;

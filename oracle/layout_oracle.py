@@ -16,8 +16,9 @@ hand-written fixture (tests/golden/kernel_native_layout.txt).
 Definition, for a weight [N, K] with K a multiple of 128 (packed [N, K/2],
 scales [N, K/16], element 2j of a row in the low nibble of packed byte j):
   * rows are grouped in tiles of 16 (N padded with zero rows to a multiple of
-    16), K in quads of 128 elements;
-  * block (tile t, quad q) is 1152 bytes at offset (t * K/128 + q) * 1152;
+    16; tiles = ceil(N / 16)), K in quads of 128 elements;
+  * block (tile t, quad q) is 1152 bytes at offset (q * tiles + t) * 1152
+    (quad-major: all tiles of quad 0, then all tiles of quad 1, ...);
   * its first 1024 bytes are 64 slots of 16 bytes; slot s = 16 g + r
     (g = 0..3, r = 0..15) holds, as four 4-byte words i = 0..3, the elements
         k = 128 q + 32 i + 8 g + e,  e = 0..7,
@@ -63,11 +64,11 @@ def prepare(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     n, k = packed.shape[0], 2 * packed.shape[1]
     out = np.zeros(prepared_bytes(n, k), dtype=np.uint8)
     codes = _codes(packed)
-    quads = k // QUAD_K
+    quads, tiles = k // QUAD_K, -(-n // TILE_ROWS)
     for row in range(n):
         t, r = divmod(row, TILE_ROWS)
         for q in range(quads):
-            base = (t * quads + q) * BLOCK_BYTES
+            base = (q * tiles + t) * BLOCK_BYTES
             for g in range(4):
                 for i in range(4):
                     k0 = QUAD_K * q + 32 * i + 8 * g
@@ -87,13 +88,13 @@ def unprepare(prep: np.ndarray, n: int, k: int) -> Tuple[np.ndarray, np.ndarray]
     prep = np.asarray(prep, dtype=np.uint8)
     if prep.size != prepared_bytes(n, k):
         raise ValueError("size does not match n, k")
-    quads = k // QUAD_K
+    quads, tiles = k // QUAD_K, -(-n // TILE_ROWS)
     codes = np.zeros((n, k), dtype=np.uint8)
     scales = np.zeros((n, k // 16), dtype=np.uint8)
     for row in range(n):
         t, r = divmod(row, TILE_ROWS)
         for q in range(quads):
-            base = (t * quads + q) * BLOCK_BYTES
+            base = (q * tiles + t) * BLOCK_BYTES
             for g in range(4):
                 for i in range(4):
                     off = base + 16 * (16 * g + r) + 4 * i
@@ -111,12 +112,12 @@ def unprepare(prep: np.ndarray, n: int, k: int) -> Tuple[np.ndarray, np.ndarray]
 def padding_is_zero(prep: np.ndarray, n: int, k: int) -> bool:
     """Rows n .. 16 * ceil(n / 16) - 1 of the last tile hold zero codes and zero scales."""
     prep = np.asarray(prep, dtype=np.uint8)
-    quads = k // QUAD_K
+    quads, tiles = k // QUAD_K, -(-n // TILE_ROWS)
     t = (n - 1) // TILE_ROWS
     for row in range(n, (t + 1) * TILE_ROWS):
         r = row - t * TILE_ROWS
         for q in range(quads):
-            base = (t * quads + q) * BLOCK_BYTES
+            base = (q * tiles + t) * BLOCK_BYTES
             for g in range(4):
                 off = base + 16 * (16 * g + r)
                 if prep[off:off + 16].any():

@@ -265,6 +265,9 @@ def test_prepared_layout_validation(L):
     assert d(Bp, D, 16, 128, Bp + 16, None) == B.ERR_ALIAS
     wb = L.nvfp4_linear_prepared_workspace_bytes
     assert wb(8, 64, 96) == -1 and wb(-1, 64, 128) == -1 and wb(0, 64, 128) == 0 and wb(33, 64, 128) == 0
+    # down projection: 128 blocks of 40 rows x 2 K slices (the fixed 16 KiB counter region + 2 * m * n FP32
+    # partials); up projection: 68 rows x 1 slice, no workspace
+    assert wb(8, 5120, 17408) == 16384 + 2 * 8 * 5120 * 4 and wb(8, 17408, 5120) == 0
     lp = L.nvfp4_linear_prepared
     assert lp(None, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_NULL
     assert lp(A, 8, 64, 96, Bp, D, E, None, 0, None) == B.ERR_SHAPE

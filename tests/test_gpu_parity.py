@@ -1089,11 +1089,10 @@ def test_linear_prepared_full_size_sampled(nv, wname, m):
     tiles = np.unique(np.concatenate([sample_rows(wl.n // 16, 6, seed=7600), [0, wl.n // 16 - 1]]))
     rows = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles])
     rp, rs, rt = O.quantize(w[rows], amax=amax)
-    ph = u8_host(prep)
-    blk = 1152 * (wl.k // 128)
+    ph = u8_host(prep).reshape(wl.k // 128, wl.n // 16, 1152)      # quad-major: [quad, tile, block]
     for j, t in enumerate(tiles):
-        want = LO.prepare(rp[16 * j:16 * j + 16], rs[16 * j:16 * j + 16])
-        assert np.array_equal(ph[t * blk:(t + 1) * blk], want), f"tile {t}"
+        want = LO.prepare(rp[16 * j:16 * j + 16], rs[16 * j:16 * j + 16])   # one tile: its quads in order
+        assert np.array_equal(ph[:, t, :].reshape(-1), want), f"tile {t}"
     y_ref, bound = O.linear_ref(x, rp, rs, rt)
     check_linear(y[:, rows], y_ref, bound, f"{wname} prepared m={m} full size, sampled")
 

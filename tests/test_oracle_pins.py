@@ -962,12 +962,12 @@ def _golden_layout_lines():
 
 def test_kernel_native_layout_golden_positions():
     rng = np.random.default_rng(7100)
-    packed = rng.integers(0, 256, size=(16, 128), dtype=np.uint8)
-    scales = rng.integers(0, 127, size=(16, 16), dtype=np.uint8)
+    packed = rng.integers(0, 256, size=(32, 128), dtype=np.uint8)
+    scales = rng.integers(0, 127, size=(32, 16), dtype=np.uint8)
     prep = LO.prepare(packed, scales)
-    assert prep.size == 2 * 1152
+    assert prep.size == 4 * 1152
     lines = _golden_layout_lines()
-    assert len(lines) == 18
+    assert len(lines) == 24
     for ln in lines:
         if ln[0] == "packed":
             blk, slot, word = int(ln[1]), int(ln[2]), int(ln[3].rstrip(":"))
@@ -982,8 +982,9 @@ def test_kernel_native_layout_golden_positions():
 
 
 def test_kernel_native_layout_every_element_and_scale():
-    """Each element k of row n sits at block (n // 16, k // 128), slot 16 g + n % 16, word i, nibble e with
-    k % 128 = 32 i + 8 g + e, and its scale in byte i of word 16 (g // 2) + n % 16 of the same block."""
+    """Each element k of row n sits in the block of tile n // 16 and quad k // 128 (block index
+    quad * tiles + tile), slot 16 g + n % 16, word i, nibble e with k % 128 = 32 i + 8 g + e, and its scale in
+    byte i of word 16 (g // 2) + n % 16 of the same block."""
     rng = np.random.default_rng(7101)
     n, k = 37, 384
     packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
@@ -991,14 +992,14 @@ def test_kernel_native_layout_every_element_and_scale():
     prep = LO.prepare(packed, scales)
     codes = np.empty((n, k), dtype=np.uint8)
     codes[:, 0::2], codes[:, 1::2] = packed & 0xF, packed >> 4
-    quads = k // 128
+    tiles = -(-n // 16)
     for row in range(n):
         t, r = divmod(row, 16)
         for kk in range(k):
             q, rem = divmod(kk, 128)
             i, rem = divmod(rem, 32)
             g, e = divmod(rem, 8)
-            base = (t * quads + q) * 1152
+            base = (q * tiles + t) * 1152
             byte = prep[base + 16 * (16 * g + r) + 4 * i + e // 2]
             assert ((byte >> (4 * (e % 2))) & 0xF) == codes[row, kk]
             assert prep[base + 1024 + 4 * (16 * (g // 2) + r) + i] == scales[row, kk // 16]
@@ -1030,6 +1031,22 @@ def test_mutation_kernel_native_swapped_lane_groups(monkeypatch):
             out[b + 256:b + 512] = out[b + 512:b + 768]
             out[b + 512:b + 768] = s1
         return out
+
+    monkeypatch.setattr(LO, "prepare", bad)
+    with pytest.raises(AssertionError):
+        test_kernel_native_layout_golden_positions()
+
+
+def test_mutation_kernel_native_tile_major(monkeypatch):
+    """A planted mistake (blocks in tile-major order, tile t's quads side by side) fails the golden positions."""
+    orig = LO.prepare
+
+    def bad(packed, scales):
+        out = orig(packed, scales)
+        n, k = packed.shape[0], 2 * packed.shape[1]
+        tiles, quads = -(-n // 16), k // 128
+        blocks = out.reshape(quads, tiles, 1152)          # quad-major as written
+        return np.ascontiguousarray(blocks.transpose(1, 0, 2)).reshape(-1)
 
     monkeypatch.setattr(LO, "prepare", bad)
     with pytest.raises(AssertionError):
