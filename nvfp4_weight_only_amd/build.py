@@ -68,5 +68,34 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_host_sanitized(outdir: str, verbose: bool = False) -> str:
+    """The library with its host code (argument checks, plans, launchers) compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer, into outdir/libnvfp4_hostsan.so, for sweeping the C ABI's validation on a
+    machine without a GPU.  The device code is built as usual (no sanitizer reaches it)."""
+    cc = hipcc()
+    os.makedirs(outdir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    flags = [*compile_flags(), *san]
+    objs = [os.path.join(outdir, src + ".host.o") for src in SOURCES]
+    cmds = [[cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        results = list(pool.map(lambda c: subprocess.run(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), cmds))
+    for cmd, r in zip(cmds, results):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout.decode(errors="replace"))
+            raise subprocess.CalledProcessError(r.returncode, cmd)
+    lib = os.path.join(outdir, "libnvfp4_hostsan.so")
+    link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+            "-fsanitize=undefined", "-o", lib, *objs]
+    if verbose:
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -196,4 +196,52 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Partial sums of a split-K exchange: device-scope relaxed atomic stores and
+// loads of FP32 (written through to the device's coherence point, so the
+// release below finds no dirty L2 lines of them to write back).
+__device__ __forceinline__ void splitk_store4(float* dst, f32x4_t v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4_t splitk_load4(const float* src) {
+  f32x4_t v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K hand-off between the workgroups that share one block of outputs,
+// each having stored its FP32 partial sums (splitk_store4).  In HIP's
+// memory model: the first barrier orders every thread's stores before thread
+// 0's release read-modify-write of the block's arrival counter (device
+// scope); the workgroup whose increment completes the count performs a
+// device-scope acquire fence, and the second barrier orders that before its
+// threads' loads of the other slices' sums, so those loads see the stores
+// (release sequence on the counter, then barrier transitivity).  On
+// gfx950 the release writes back the XCD's L2 and the acquire invalidates the
+// CU's L1 and the XCD's L2 lines from other agents, because the eight XCDs'
+// L2s are not coherent with each other; only the last workgroup of a block
+// pays for the invalidation.  The explicit vmcnt(0) before the first barrier
+// also makes every thread's stores complete to L2 before thread 0 releases.
+// Returns true in every thread of the last workgroup, which also resets the
+// counter to zero for the next launch (the launch boundary orders that).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool splitk_arrive(uint32_t* count, int slices) {
+  __shared__ int last_flag;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(slices - 1);
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    last_flag = last;
+  }
+  __syncthreads();
+  return last_flag != 0;
+}
+
 }  // namespace nvfp4

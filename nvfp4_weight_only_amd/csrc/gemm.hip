@@ -262,8 +262,10 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PrefillArgs p) {
 }
 
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
-  if (prefill_dma_supported(m, n, k)) return launch_prefill_dma(x, m, n, k, packed, scales, tscale, y, s);
+                         const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                         int64_t workspace_bytes, hipStream_t s) {
+  if (prefill_dma_supported(m, n, k))
+    return launch_prefill_dma(x, m, n, k, packed, scales, tscale, y, workspace, workspace_bytes, s);
   const unsigned gx = (unsigned)((n + kPfBN - 1) / kPfBN);
   const int64_t tiles_m = (m + kPfBM - 1) / kPfBM;
   const int64_t max_y = 65535;

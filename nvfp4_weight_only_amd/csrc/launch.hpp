@@ -69,12 +69,21 @@ bool small_m_supported(int64_t m, int64_t n, int64_t k);
 SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split);
 void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,
                     const float* tscale, uint16_t* y, void* workspace, hipStream_t s);
+// Prefill GEMM.  With a workspace of at least prefill_workspace_bytes(m, n, k)
+// bytes (zero-filled before its first use; left that way by every launch), a
+// tile count that leaves CUs idle is split along K (prefill_split_slices
+// workgroups per tile); with none it runs unsplit.  The workspace starts with
+// kSkinnyCounterBytes of arrival counters, then the FP32 partial tiles.
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                         const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+                         const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                         int64_t workspace_bytes, hipStream_t s);
 // Streaming prefill GEMM (K a multiple of 256); launch_gemm_prefill uses it when supported.
 bool prefill_dma_supported(int64_t m, int64_t n, int64_t k);
+int prefill_split_slices(int64_t m, int64_t n, int64_t k);
+int64_t prefill_workspace_bytes(int64_t m, int64_t n, int64_t k);
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                        const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s);
+                        const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                        int64_t workspace_bytes, hipStream_t s);
 
 // Grouped prefill over an expert stack (K a multiple of 256, t_count * k <= 2^31,
 // int32 pair indices and workgroup ids):

@@ -81,7 +81,7 @@ int auto_kernel(int64_t m) {
   return m == 1 ? NVFP4_KERNEL_GEMV : (m <= 64 ? NVFP4_KERNEL_SMALL_M : NVFP4_KERNEL_PREFILL);
 }
 
-// A workspace is used only by the small-M kernel (K split across workgroups).
+// A workspace is used by the small-M kernel and the prefill GEMM (K split across workgroups).
 nvfp4_status run_linear(int kernel, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                         const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
                         int64_t workspace_bytes, void* stream) {
@@ -108,7 +108,9 @@ nvfp4_status run_linear(int kernel, const uint16_t* x, int64_t m, int64_t n, int
     case NVFP4_KERNEL_SMALL_M:
       nvfp4::launch_skinny(x, m, n, k, packed, scales, tscale, y, workspace, workspace ? workspace_bytes : 0, s);
       break;
-    default: nvfp4::launch_gemm_prefill(x, m, n, k, packed, scales, tscale, y, s); break;
+    default:
+      nvfp4::launch_gemm_prefill(x, m, n, k, packed, scales, tscale, y, workspace, workspace ? workspace_bytes : 0, s);
+      break;
   }
   return launch_status();
 }
@@ -267,7 +269,9 @@ int64_t nvfp4_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || weight_sizes(n, k, &ws) != NVFP4_OK) return -1;
   int64_t ye;
   if (!mul_ok(m, n, &ye) || ye > INT64_MAX / 32) return -1;
-  if (auto_kernel(m) != NVFP4_KERNEL_SMALL_M) return 0;
+  const int kernel = auto_kernel(m);
+  if (kernel == NVFP4_KERNEL_PREFILL) return nvfp4::prefill_workspace_bytes(m, n, k);
+  if (kernel != NVFP4_KERNEL_SMALL_M) return 0;
   return nvfp4::skinny_workspace_bytes(m, n, k);
 }
 
@@ -284,7 +288,9 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
   nvfp4_status st = validate_linear(x, m, n, k, packed, scales, tscale, y);
   if (st != NVFP4_OK) return st;
   if (m == 0) return NVFP4_OK;
-  const int64_t need = nvfp4_linear_workspace_bytes(m, n, k);
+  // The scratch array serves the small-M kernel's K split; the prefill GEMM
+  // runs unsplit here (its split needs more than the array holds).
+  const int64_t need = auto_kernel(m) == NVFP4_KERNEL_PREFILL ? 0 : nvfp4_linear_workspace_bytes(m, n, k);
   if (need < 0 || need > kScratchBytes) return NVFP4_ERR_SHAPE;
   if ((st = check_device()) != NVFP4_OK) return st;
   if (need == 0) return run_linear(NVFP4_KERNEL_AUTO, x, m, n, k, packed, scales, tscale, y, nullptr, 0, stream);

@@ -50,7 +50,18 @@ struct PdArgs {
   // built by the grouping kernels (see PdGroups), and the stack's layout.
   const int32_t* groups;
   int64_t topk, experts, w_stride;  // w_stride: packed bytes per expert
+  // Split K (plain form only): `slices` workgroups per tile, each over a range
+  // of whole 256-element groups, exchange FP32 partial tiles in `part` and meet
+  // at the tile's arrival counter in `count` (see pd_exchange).
+  int slices;
+  float* part;
+  uint32_t* count;
 };
+
+// FP32 partial tile of one (tile, slice): per wavefront 34 float4 per lane
+// (its 8 accumulator tiles of 16 items, then the fifth tile's 8 items).
+constexpr int kPdPartVec = 34;
+constexpr int64_t kPdPartBytes = 4 * kPdPartVec * 64 * 16;  // 139,264 = 128 x 272 x 4
 
 // Layout of the grouping workspace (int32): cnt[E] (the sort's counters),
 // pair_off[E + 1] (first sorted position of each expert's pairs; pair_off[E]
@@ -411,11 +422,68 @@ __device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* y
   }
 }
 
+// Split-K exchange of one wavefront's sums (its accumulators and its row
+// tile of the fifth column tile, already summed over the wavefronts): the
+// slice's partial tile goes to the workspace, the tile's workgroups meet at
+// its arrival counter (splitk_arrive: release / acquire at device scope), and
+// the last one replaces its sums by the sum over all slices in slice order
+// (the same bits whichever workgroup arrives last).  Returns false in the
+// others, which are done.
+template <int W>
+__device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][2], float4& t5a, float4& t5b, int tile,
+                                            int sl, int lane) {
+  auto slot = [&](int s, int j) {
+    return p.part + ((((int64_t)tile * p.slices + s) * 4 + W) * kPdPartVec + j) * 256 + 4 * lane;
+  };
+  auto get = [&](int j) -> f32x4_t {
+    if (j < 32) {
+      const f32x16_t& a = acc[j >> 3][(j >> 2) & 1];
+      const int q = 4 * (j & 3);
+      return f32x4_t{a[q], a[q + 1], a[q + 2], a[q + 3]};
+    }
+    const float4 t = j == 32 ? t5a : t5b;
+    return f32x4_t{t.x, t.y, t.z, t.w};
+  };
+  auto put = [&](int j, f32x4_t v) {
+    if (j < 32) {
+      f32x16_t& a = acc[j >> 3][(j >> 2) & 1];
+      const int q = 4 * (j & 3);
+      a[q] = v[0]; a[q + 1] = v[1]; a[q + 2] = v[2]; a[q + 3] = v[3];
+    } else if (j == 32) {
+      t5a = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      t5b = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // Ordinary 16-byte stores and loads (whole kilobytes per instruction): the
+  // release of splitk_arrive writes the partial tile back from L2, the
+  // acquire makes the last workgroup read it from memory.
+#pragma unroll
+  for (int j = 0; j < kPdPartVec; ++j) *reinterpret_cast<f32x4_t*>(slot(sl, j)) = get(j);
+  if (!splitk_arrive(p.count + tile, p.slices)) return false;
+  // Two halves of 17 vectors: each half's loads of every other slice are in
+  // flight together.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x4_t sum[17];
+#pragma unroll
+    for (int i = 0; i < 17; ++i) sum[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < p.slices; ++s) {
+#pragma unroll
+      for (int i = 0; i < 17; ++i)
+        sum[i] += s == sl ? get(17 * h + i) : *reinterpret_cast<const f32x4_t*>(slot(s, 17 * h + i));
+    }
+#pragma unroll
+    for (int i = 0; i < 17; ++i) put(17 * h + i, sum[i]);
+  }
+  return true;
+}
+
 // Wavefront W's whole K loop and epilogue (a template, so that the fifth
 // tile's operand choice is static and every accumulator stays in place).
 template <int W, bool G>
 __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds& L, int lane, int64_t m0,
-                                        int64_t n0, int nsteps) {
+                                        int64_t n0, int nsteps, int tile, int sl) {
   f32x16_t acc[4][2], acc5[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -489,6 +557,10 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
     t5b.x += b.x; t5b.y += b.y; t5b.z += b.z; t5b.w += b.w;
   }
 
+  if constexpr (!G) {
+    if (p.slices > 1 && !pd_exchange<W>(p, acc, t5a, t5b, tile, sl, lane)) return;
+  }
+
   // Epilogue: the BF16 tile goes through LDS (the X stages, free now) so that
   // the stores to Y are whole 16-byte pieces of rows.  Transposed 32x32 D
   // layout: item v of lane l is row l % 32 of Y's row tile and column
@@ -533,14 +605,22 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   // Tile order: workgroups are dispatched to the 8 XCDs round-robin by id, so
   // when the tile count allows, consecutive ids of one XCD cover all m tiles of
   // consecutive n tiles (the weight tile is then fetched into that XCD's L2 once).
-  const int nwg = p.n_tiles * p.m_tiles;
+  // With split K the slices of a tile are consecutive ids (one XCD).
+  const int nwg = p.n_tiles * p.m_tiles * p.slices;
   int id = (int)blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
-  const int nt = id / p.m_tiles, mt = id % p.m_tiles;
+  const int sl = id % p.slices, tile = id / p.slices;
+  const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
   int64_t m0 = (int64_t)mt * kPdBM;
   const int64_t n0 = (int64_t)nt * kPdBN;
-  const int nsteps = (int)(p.k / kPdBK);  // a multiple of 4
-  const int64_t kh = p.k >> 1, ks = p.k >> 4;
+  const int64_t kh = p.k >> 1, ks = p.k >> 4;  // row strides (the whole K)
+  // This slice's groups [g0, g1) of 256 K elements: the sources start there.
+  const int groups = (int)(p.k / kPdGroupK);
+  const int g0 = (int)((int64_t)sl * groups / p.slices), g1 = (int)((int64_t)(sl + 1) * groups / p.slices);
+  const int nsteps = 4 * (g1 - g0);
+  p.x += (int64_t)g0 * kPdGroupK;
+  p.packed += (int64_t)g0 * (kPdGroupK / 2);
+  p.scales += (int64_t)g0 * (kPdGroupK / 16);
 
   PdSrc src;
   if constexpr (G) {
@@ -594,10 +674,10 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   }
 
   switch (w) {
-    case 0: pd_body<0, G>(p, src, L, lane, m0, n0, nsteps); break;
-    case 1: pd_body<1, G>(p, src, L, lane, m0, n0, nsteps); break;
-    case 2: pd_body<2, G>(p, src, L, lane, m0, n0, nsteps); break;
-    default: pd_body<3, G>(p, src, L, lane, m0, n0, nsteps); break;
+    case 0: pd_body<0, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
+    case 1: pd_body<1, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
+    case 2: pd_body<2, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
+    default: pd_body<3, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
   }
 }
 
@@ -609,16 +689,48 @@ bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) {
   return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0 && k < ((int64_t)1 << 24);
 }
 
+// K slices for a tile count that leaves CUs idle: as many as keep the
+// workgroups within one round of 256 (at most 4, at least one 256-element group
+// each); 1 when the tiles alone fill the chip.
+int prefill_split_slices(int64_t m, int64_t n, int64_t k) {
+  if (!prefill_dma_supported(m, n, k)) return 1;
+  const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM);
+  if (tiles > 128 || tiles > 4096) return 1;
+  int64_t s = 256 / tiles;
+  s = s > 4 ? 4 : s;
+  const int64_t groups = k / kPdGroupK;
+  return (int)(s > groups ? groups : s);
+}
+
+int64_t prefill_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int s = prefill_split_slices(m, n, k);
+  if (s <= 1) return 0;
+  const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM);
+  return kSkinnyCounterBytes + s * tiles * kPdPartBytes;
+}
+
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
-                        const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+                        const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
+                        int64_t workspace_bytes, hipStream_t s) {
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = (m + kPdBM - 1) / kPdBM;
+  const int64_t need = prefill_workspace_bytes(m, n, k);
+  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+    // Split K (fewer than 129 tiles: one launch).  The workspace starts with the
+    // arrival counters (zero, and left zero by every launch), then the partial tiles.
+    const int sl = prefill_split_slices(m, n, k);
+    const PdArgs a{x, m, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, nullptr, 0, 0, 0, sl,
+                   reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes),
+                   static_cast<uint32_t*>(workspace)};
+    prefill_dma_kernel<false><<<dim3((unsigned)(n_tiles * m_tiles * sl)), 256, 0, s>>>(a);
+    return;
+  }
   // One launch covers up to 2^31 - 1 workgroups; larger m is split by row.
   const int64_t max_m_tiles = ((int64_t)1 << 30) / n_tiles;
   for (int64_t t0 = 0; t0 < m_tiles; t0 += max_m_tiles) {
     const int64_t mt = m_tiles - t0 < max_m_tiles ? m_tiles - t0 : max_m_tiles;
     const int64_t mm = (m - t0 * kPdBM) < mt * kPdBM ? (m - t0 * kPdBM) : mt * kPdBM;
     const PdArgs a{x + t0 * kPdBM * k, mm, n, k, packed, scales, tscale, y + t0 * kPdBM * n, (int)n_tiles, (int)mt,
-                   nullptr, 0, 0, 0};
+                   nullptr, 0, 0, 0, 1, nullptr, nullptr};
     prefill_dma_kernel<false><<<dim3((unsigned)(n_tiles * mt)), 256, 0, s>>>(a);
   }
 }
@@ -640,7 +752,7 @@ void launch_prefill_grouped(const uint16_t* x, int64_t topk, const int32_t* grou
                             uint16_t* y, hipStream_t s) {
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = prefill_grouped_tile_bound(pairs, experts);
   const PdArgs a{x, pairs, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, groups, topk, experts,
-                 n * (k >> 1)};
+                 n * (k >> 1), 1, nullptr, nullptr};
   prefill_dma_kernel<true><<<dim3((unsigned)(n_tiles * m_tiles)), 256, 0, s>>>(a);
 }
 

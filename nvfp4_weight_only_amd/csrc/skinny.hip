@@ -146,16 +146,8 @@ __device__ __forceinline__ void sk_store_y(const SkinnyArgs& p, const f32x4_t* a
 // With several K slices: this slice's FP32 sums of one tile go to the
 // workspace.  rows and row_start are multiples of 4, so a 4-row group is
 // either wholly inside the block or starts past its end (the last block's
-// padding columns n .. npad-1 are written and never read).
-//
-// The partial sums are exchanged with device-scope (agent) relaxed atomic
-// stores and loads, which gfx950 performs at the device's coherence point (the
-// L2s of the 8 XCDs are not coherent with each other for ordinary accesses).
-// sk_arrive makes every thread wait for its stores to complete (vmcnt(0))
-// before the workgroup barrier, and only then bumps the arrival counter, so a
-// workgroup that sees the count reach `slices - 1` finds every other slice's
-// sums complete.  This avoids a device-scope release fence, which writes back
-// the whole L2 of the XCD once per workgroup.
+// padding columns n .. npad-1 are written and never read).  sk_arrive
+// (splitk_arrive) orders these stores before the other slices' loads.
 template <int NMT>
 __device__ __forceinline__ void sk_publish(const SkinnyArgs& p, const f32x4_t* acc, int sl, int64_t tile_row,
                                            int64_t row_end, int64_t m0, int lane) {
@@ -163,29 +155,15 @@ __device__ __forceinline__ void sk_publish(const SkinnyArgs& p, const f32x4_t* a
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int64_t gm = m0 + 16 * mt + (lane & 15);
-    if (gm < p.m && n0 < row_end) {
-      float* dst = p.part + ((int64_t)sl * p.m + gm) * p.npad + n0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, acc[mt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (gm < p.m && n0 < row_end) splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, acc[mt]);
   }
 }
 
 // After every tile of the workgroup is published: true (in every thread) in the
 // last workgroup of the row block to arrive, which then owns the reduction.
 __device__ __forceinline__ bool sk_arrive(const SkinnyArgs& p, int rb, int tid) {
-  __shared__ int is_last;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial-sum stores have completed
-  __syncthreads();
-  uint32_t* cnt = p.count + (int64_t)rb * gridDim.y + blockIdx.y;
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == (uint32_t)(p.slices - 1);
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    is_last = last;
-  }
-  __syncthreads();
-  return is_last != 0;
+  (void)tid;
+  return splitk_arrive(p.count + (int64_t)rb * gridDim.y + blockIdx.y, p.slices);
 }
 
 // In the last workgroup: one tile's slices added in slice order (this
@@ -202,12 +180,7 @@ __device__ __forceinline__ void sk_reduce_tile(const SkinnyArgs& p, const f32x4_
     if (gm >= p.m || n0 >= row_end) continue;
     for (int s = 0; s < p.slices; ++s) {
       const float* src = p.part + ((int64_t)s * p.m + gm) * p.npad + n0;
-      f32x4_t ps = acc[mt];
-      if (s != sl) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ps[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      v[mt] += ps;
+      v[mt] += s == sl ? acc[mt] : splitk_load4(src);
     }
   }
   sk_store_y<NMT>(p, v, tile_row, row_end, m0, lane);

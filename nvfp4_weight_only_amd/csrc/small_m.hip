@@ -247,13 +247,9 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
     return;
   }
 
-  // Several K slices.  The partial sums are exchanged with device-scope
-  // relaxed atomic stores and loads, which gfx950 performs at the device's
-  // coherence point (the L2s of the eight XCDs are not coherent with each other
-  // for ordinary accesses).  Every thread waits for its stores to complete
-  // (vmcnt(0)) before the barrier, and only then is the arrival counter bumped,
-  // so a workgroup that sees the count reach `slices - 1` finds every other
-  // slice's sums complete.
+  // Several K slices: this slice's sums go to the workspace, then the
+  // workgroups of the row block meet at the arrival counter (splitk_arrive);
+  // the last one adds the slices in slice order and stores y.
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int pi = w + kSmWaves * i;
@@ -261,25 +257,11 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
       int64_t tr, gm;
       pair_rows(pi, tr, gm);
       const int64_t n0 = tr + 4 * (lane >> 4);
-      if (gm < p.m && n0 >= row0 && n0 < row_end) {
-        float* dst = p.part + ((int64_t)sl * p.m + gm) * p.npad + n0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, sum[i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (gm < p.m && n0 >= row0 && n0 < row_end)
+        splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, sum[i]);
     }
   }
-  __shared__ int is_last;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial-sum stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* cnt = p.count + rb;
-    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == (uint32_t)(p.slices - 1);
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-    is_last = last;
-  }
-  __syncthreads();
-  if (!is_last) return;
+  if (!splitk_arrive(p.count + rb, p.slices)) return;
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int pi = w + kSmWaves * i;
@@ -289,15 +271,8 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
       const int64_t n0 = tr + 4 * (lane >> 4);
       f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       if (gm < p.m && n0 >= row0 && n0 < row_end) {
-        for (int s = 0; s < p.slices; ++s) {
-          f32x4_t ps = sum[i];
-          if (s != sl) {
-            const float* src = p.part + ((int64_t)s * p.m + gm) * p.npad + n0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ps[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          v += ps;
-        }
+        for (int s = 0; s < p.slices; ++s)
+          v += s == sl ? sum[i] : splitk_load4(p.part + ((int64_t)s * p.m + gm) * p.npad + n0);
       }
       sm_store_y(p, v, tr, row0, row_end, gm, lane);
     }

@@ -141,6 +141,8 @@ WORKLOADS: Dict[str, Workload] = {
                  5120, 17408, (8, 32), "plain"),
         Workload("prefill", "prefill GEMM: M in {512,2048}, N=17408, K=5120",
                  17408, 5120, (512, 2048), "plain"),
+        Workload("prefill_down", "prefill GEMM, down projection: M in {512,2048}, N=5120, K=17408",
+                 5120, 17408, (512, 2048), "plain"),
     ]
 }
 

@@ -76,7 +76,12 @@ def test_linear_validation(L):
 def test_linear_workspace_bytes(L):
     wb = L.nvfp4_linear_workspace_bytes
     assert wb(1, 5120, 5120) == 0            # GEMV: no workspace
-    assert wb(65, 17408, 5120) == 0          # prefill GEMM: no workspace
+    # prefill GEMM: K split only while the 128 x 272 tiles leave CUs idle (at most 128 tiles): the counter
+    # region + slices x tiles x 139,264-byte FP32 partial tiles
+    assert wb(65, 17408, 5120) == 16384 + 4 * 64 * 139264        # 64 tiles, 4 slices
+    assert wb(512, 5120, 17408) == 16384 + 3 * 76 * 139264       # 76 tiles, 3 slices
+    assert wb(512, 17408, 5120) == 0 and wb(2048, 5120, 17408) == 0   # 256 and 304 tiles
+    assert wb(65, 17408, 5136) == 0                               # K not a multiple of 256: other kernel
     assert wb(8, 17408, 5120) == 0           # small-M, 68 rows x 1 K slice per workgroup
     # small-M down projection: 64 blocks of 80 rows x 4 K slices; the fixed 16 KiB counter region + 4 * m * n
     # FP32 partials
