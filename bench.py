@@ -231,16 +231,21 @@ def bench_stream_rows(reps):
 
 
 def bench_quant_rows(reps):
-    """Quantizer (amax + quantize passes) and dequantizer on the decode weight, rotated."""
+    """Quantizer (amax + encode passes; with and without a workspace) and dequantizer on the decode weight,
+    rotated."""
     wl = WL.WORKLOADS["decode"]
     w = dev_bf16(wl.weight())
     n, k = wl.n, wl.k
     c = copies_needed(2 * n * k)
     ws = [w.clone() for _ in range(c)]
     outs = [nv.quantize(wi) for wi in ws]
-    g = graph_of([(lambda wi=wi: nv.quantize(wi)) for wi in ws])
+    g = graph_of([(lambda wi=wi: nv.quantize(wi)) for wi in ws])          # nvfp4_quantize_ws: 2 launches
     warm_graph(g)
     ms_q = time_graph_replays(g, reps, c)
+    g3 = graph_of([(lambda wi=wi: nv.quantize(wi, workspace=None)) for wi in ws])   # nvfp4_quantize: 3 launches
+    warm_graph(g3)
+    ms_q3 = time_graph_replays(g3, reps, c)
+    del g3
     dq = [torch.empty((n, k), dtype=torch.bfloat16, device="cuda") for _ in range(c)]
     lib = nv.lib()
 
@@ -257,7 +262,15 @@ def bench_quant_rows(reps):
         "quantize_decode_5120x5120": {"us_per_call": round(ms_q * 1e3, 2),
                                       "gb_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
                                       "hbm_frac": round(q_bytes / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "bytes": q_bytes, "note": "4 launches: amax partial maxima, amax reduce, quantize pass, tscale"},
+                                      "bytes": q_bytes,
+                                      "note": "nvfp4_quantize_ws, 2 launches: per-workgroup amax (at most 1024 "
+                                              "partial maxima), then the encode pass, each workgroup of which "
+                                              "reduces the partial maxima itself"},
+        "quantize_3launch_decode_5120x5120": {"us_per_call": round(ms_q3 * 1e3, 2),
+                                              "gb_s": round(q_bytes / (ms_q3 * 1e-3) / 1e9, 1),
+                                              "hbm_frac": round(q_bytes / (ms_q3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                              "bytes": q_bytes,
+                                              "note": "nvfp4_quantize (no workspace): amax, tensor scale, encode"},
         "dequant_decode_5120x5120": {"us_per_call": round(ms_d * 1e3, 2),
                                      "gb_s": round(d_bytes / (ms_d * 1e-3) / 1e9, 1),
                                      "hbm_frac": round(d_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -781,7 +794,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemv_decode_5120x5120", digest),
-                     "kernel": "gemv_ks_kernel<5, 1>", "bytes_per_launch": nbytes,
+                     "kernel": "gemv_ks_kernel<3, 1>", "bytes_per_launch": nbytes,
                      "avg_launch_us": round(ms * 1e3, 3),
                      "measured_read_gb_s": head_read,
                      "measured_read_frac": round(gbs / head_read, 4) if head_read else None},

@@ -82,6 +82,23 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k,
                             uint8_t* packed, uint8_t* scales, float* tscale, void* stream);
 
 /*
+ * nvfp4_quantize in two launches instead of three, for a caller that has a
+ * workspace: at least nvfp4_quantize_workspace_bytes() bytes (4096) of device
+ * memory, 16-byte aligned, overlapping no argument; its contents before the
+ * call do not matter (calls that overlap on one workspace race).  The amax pass
+ * writes at most 1024 per-workgroup maxima of |W| to the workspace and every
+ * workgroup of the encode pass reduces them itself (workgroup 0 also writes
+ * tscale), so no reduction launch sits between the two.  The outputs are those
+ * of nvfp4_quantize bit for bit.  A NULL or too small workspace runs
+ * nvfp4_quantize.  Errors as nvfp4_quantize, plus NVFP4_ERR_SHAPE for a
+ * negative workspace_bytes and NVFP4_ERR_ALIGN / NVFP4_ERR_ALIAS for the
+ * workspace.
+ */
+int64_t nvfp4_quantize_workspace_bytes(void);
+nvfp4_status nvfp4_quantize_ws(const uint16_t* w, int64_t n, int64_t k, uint8_t* packed, uint8_t* scales,
+                               float* tscale, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Merged linears (model card "Qwen3.8-27B-NVFP4", "What is quantized": q/k/v
  * and gate/up members share one tensor scale; the amax spread inside a group
  * reaches 3.7x).  To quantize members held as separate tensors:

@@ -30,7 +30,8 @@ EXPORTED = ("nvfp4_status_string", "nvfp4_version", "nvfp4_quantize", "nvfp4_ama
             "nvfp4_mx_linear_w4a4_workspace_bytes", "nvfp4_linear_w4a4", "nvfp4_linear_w4a4_workspace_bytes",
             "nvfp4_linear_noalloc", "nvfp4_linear_noalloc_max_bytes", "nvfp4_prepared_bytes", "nvfp4_prepare",
             "nvfp4_dequant_prepared", "nvfp4_linear_prepared_workspace_bytes", "nvfp4_linear_prepared",
-            "nvfp4_stream_read", "nvfp4_stream_read_sink_words")
+            "nvfp4_stream_read", "nvfp4_stream_read_sink_words", "nvfp4_quantize_ws",
+            "nvfp4_quantize_workspace_bytes")
 
 
 class NVFP4Error(RuntimeError):
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_version.argtypes = []
         L.nvfp4_version.restype = ctypes.c_char_p
         L.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.nvfp4_quantize_ws.argtypes = [vp, i64, i64, vp, vp, vp, vp, i64, vp]
+        L.nvfp4_quantize_workspace_bytes.argtypes = []
         L.nvfp4_amax_accumulate.argtypes = [vp, i64, i64, vp, vp]
         L.nvfp4_quantize_with_amax.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.nvfp4_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
@@ -111,15 +114,31 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def quantize(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """BF16 [n, k] -> (packed uint8 [n, k/2], scales uint8 [n, k/16], tscale float32 [1])."""
+def quantize(w: torch.Tensor, workspace: Union[str, None, torch.Tensor] = "auto"
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """BF16 [n, k] -> (packed uint8 [n, k/2], scales uint8 [n, k/16], tscale float32 [1]).
+
+    workspace: "auto" runs nvfp4_quantize_ws (two launches) on the binding-owned workspace of the current
+    device and stream; None runs nvfp4_quantize (three launches); a uint8 device tensor is passed through.
+    The outputs are the same bits either way."""
     _need(w, torch.bfloat16, "w")
     n, k = w.shape
     packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     scales = torch.empty((n, k // 16), dtype=torch.uint8, device=w.device)
     tscale = torch.empty((1,), dtype=torch.float32, device=w.device)
-    _check(lib().nvfp4_quantize(w.data_ptr(), n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr(),
-                                _stream(w)), "nvfp4_quantize")
+    stream = _stream(w)
+    head = (w.data_ptr(), n, k, packed.data_ptr(), scales.data_ptr(), tscale.data_ptr())
+    if workspace is None:
+        _check(lib().nvfp4_quantize(*head, stream), "nvfp4_quantize")
+        return packed, scales, tscale
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
+        ws = _workspace_for(w.device, stream, lib().nvfp4_quantize_workspace_bytes())
+    else:
+        _need(workspace, torch.uint8, "workspace")
+        ws = workspace
+    _check(lib().nvfp4_quantize_ws(*head, ws.data_ptr(), ws.numel(), stream), "nvfp4_quantize_ws")
     return packed, scales, tscale
 
 

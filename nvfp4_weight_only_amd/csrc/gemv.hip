@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(64 * W) gemv_lds_kernel(const uint16_t* __rest
 //     wavefronts in wavefront order through LDS.
 // Rows past n repeat row n - 1 and are not stored.
 constexpr int kGemvKsMaxWaves = 10;
-constexpr int kGemvKsI = 5;  // 20 rows per workgroup: one workgroup per CU for n = 5120
+constexpr int kGemvKsI = 5;  // routed calls: 20 rows per workgroup
 
 template <int I, int J, bool ROUTED = false>
 __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uint16_t* __restrict__ x, int64_t n,
@@ -382,15 +382,26 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
 }
 
 // waves = k / 512 (one 512-element slice per wavefront).
-static void launch_ks(const uint16_t* x, int64_t m, int64_t n, int64_t k, int waves, const uint8_t* packed,
-                      const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
-  constexpr int I = kGemvKsI;
+template <int I>
+static void launch_ks_rows(const uint16_t* x, int64_t m, int64_t n, int64_t k, int waves, const uint8_t* packed,
+                           const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
   const unsigned gx = (unsigned)((n + 4 * I - 1) / (4 * I));
   const int64_t max_y = 65535;
   for (int64_t m0 = 0; m0 < m; m0 += max_y) {
     const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
     gemv_ks_kernel<I, 1><<<dim3(gx, gy), 64 * waves, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale, y + m0 * n);
   }
+}
+
+// Rows per workgroup, measured at k = 5120 (10 wavefronts): 12 rows for n up to
+// 8192 (n = 5120: 427 workgroups, 5.51 us against 5.60 us with 20 rows and 6.32 us
+// with 16), 16 rows above (n = 34816: 18.2 us against 19.0 us with 20 rows and
+// 18.6 us with 12).  Fewer rows per workgroup give more workgroups to spread over
+// the CUs, more rows give each wavefront more loads in flight.
+static void launch_ks(const uint16_t* x, int64_t m, int64_t n, int64_t k, int waves, const uint8_t* packed,
+                      const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  if (n <= 8192) return launch_ks_rows<3>(x, m, n, k, waves, packed, scales, tscale, y, s);
+  launch_ks_rows<4>(x, m, n, k, waves, packed, scales, tscale, y, s);
 }
 
 template <int LPR, int R, int JB, int W, bool RAGGED = false>

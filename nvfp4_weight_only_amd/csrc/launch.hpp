@@ -23,6 +23,11 @@ void launch_tscale_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, 
                              hipStream_t s);
 void launch_quantize_from_tscale(const uint16_t* w, int64_t count, int64_t n_elems, const float* tscale,
                                  uint8_t* packed, uint8_t* scales, hipStream_t s);
+// Two launches: at most 1024 per-workgroup maxima of |w| into parts (4 KiB),
+// then the encode pass, each of whose workgroups reduces them; workgroup 0
+// writes tscale = fl32(amax / 2688).
+void launch_quantize_shared_amax(const uint16_t* w, int64_t n_elems, uint32_t* parts, float* tscale,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s);
 void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
                      uint8_t* scales, hipStream_t s);
 void launch_dequant(const uint8_t* packed, const uint8_t* scales, const float* tscale, int64_t count, int64_t n_elems,

@@ -214,6 +214,29 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* pa
   return launch_status();
 }
 
+int64_t nvfp4_quantize_workspace_bytes(void) { return 4096; }
+
+nvfp4_status nvfp4_quantize_ws(const uint16_t* w, int64_t n, int64_t k, uint8_t* packed, uint8_t* scales,
+                               float* tscale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!w || !packed || !scales || !tscale) return NVFP4_ERR_NULL;
+  WeightSizes ws;
+  nvfp4_status st = weight_sizes(n, k, &ws);
+  if (st != NVFP4_OK) return st;
+  if ((st = validate_quantize_outputs(w, ws, packed, scales, tscale)) != NVFP4_OK) return st;
+  if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+  if (workspace == nullptr || workspace_bytes < nvfp4_quantize_workspace_bytes())
+    return nvfp4_quantize(w, n, k, packed, scales, tscale, stream);
+  if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+  if (overlaps(workspace, workspace_bytes, w, ws.w_bytes) || overlaps(workspace, workspace_bytes, packed, ws.packed_bytes) ||
+      overlaps(workspace, workspace_bytes, scales, ws.scale_bytes) || overlaps(workspace, workspace_bytes, tscale, 4))
+    return NVFP4_ERR_ALIAS;
+  if ((st = check_device()) != NVFP4_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The per-workgroup maxima in the workspace: every encode workgroup reads them.
+  nvfp4::launch_quantize_shared_amax(w, ws.elems, static_cast<uint32_t*>(workspace), tscale, packed, scales, s);
+  return launch_status();
+}
+
 nvfp4_status nvfp4_amax_accumulate(const uint16_t* w, int64_t n, int64_t k, float* amax, void* stream) {
   if (!w || !amax) return NVFP4_ERR_NULL;
   WeightSizes ws;

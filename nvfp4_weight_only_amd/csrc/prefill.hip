@@ -689,15 +689,22 @@ bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) {
   return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0 && k < ((int64_t)1 << 24);
 }
 
-// K slices for a tile count that leaves CUs idle: as many as keep the
-// workgroups within one round of 256 (at most 4, at least one 256-element group
-// each); 1 when the tiles alone fill the chip.
+// K slices for a tile count that leaves CUs idle (each slice at least one
+// 256-element group):
+//   * at most 128 tiles: as many slices as keep the workgroups within one
+//     round of 256 (at most 4);
+//   * 257 to 384 tiles (a second round of 256 mostly idle): 2 slices, three
+//     rounds of half the work instead of two of the whole (the down
+//     projection 5120 x 17408 at M = 2048: 304 tiles);
+//   * otherwise 1.
 int prefill_split_slices(int64_t m, int64_t n, int64_t k) {
   if (!prefill_dma_supported(m, n, k)) return 1;
   const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM);
-  if (tiles > 128 || tiles > 4096) return 1;
-  int64_t s = 256 / tiles;
-  s = s > 4 ? 4 : s;
+  int64_t s = 1;
+  if (tiles <= 128)
+    s = 256 / tiles > 4 ? 4 : 256 / tiles;
+  else if (tiles > 256 && tiles <= 384)
+    s = 2;
   const int64_t groups = k / kPdGroupK;
   return (int)(s > groups ? groups : s);
 }
@@ -715,8 +722,9 @@ void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, cons
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = (m + kPdBM - 1) / kPdBM;
   const int64_t need = prefill_workspace_bytes(m, n, k);
   if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
-    // Split K (fewer than 129 tiles: one launch).  The workspace starts with the
-    // arrival counters (zero, and left zero by every launch), then the partial tiles.
+    // Split K (at most 384 tiles, within the 4096 counters: one launch).  The
+    // workspace starts with the arrival counters (zero, and left zero by every
+    // launch), then the partial tiles.
     const int sl = prefill_split_slices(m, n, k);
     const PdArgs a{x, m, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, nullptr, 0, 0, 0, sl,
                    reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes),

@@ -28,6 +28,7 @@ namespace nvfp4 {
 constexpr int kAmaxU = 8;
 constexpr int kAmaxBlocks = 512;          // atomic form
 constexpr int kAmaxPartialBlocks = 8192;  // partial-slot form: one pass over the data per thread
+constexpr int kAmaxSharedParts = 1024;    // form whose maxima every encode workgroup reduces (4 per thread)
 
 typedef unsigned short amax_u16x2_t __attribute__((ext_vector_type(2)));
 
@@ -241,18 +242,44 @@ __device__ __forceinline__ void store_block(int64_t blk, BlockCodes q, uint2* __
   }
 }
 
+// Where the encode pass takes amax from.
+enum AmaxSrc : int {
+  kFromAmax = 0,    // amax_p: amax (a BF16 value held in FP32)
+  kFromTscale = 1,  // amax_p: the tensor scale, amax recovered from it
+  kFromParts = 2,   // parts[0 .. nparts): per-workgroup maxima (BF16 magnitude bits) that every workgroup
+                    // reduces itself; workgroup 0 writes the tensor scale to ts_out
+};
+
+// Maximum of parts[0 .. nparts) (1 <= nparts <= 4 x 256) over a 256-thread
+// workgroup; every thread receives it.  Indices past the end load the last
+// slot again, which cannot change the maximum.
+__device__ __forceinline__ uint32_t parts_max(const uint32_t* __restrict__ parts, int nparts) {
+  uint32_t mv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = (int)threadIdx.x + 256 * u;
+    mv[u] = parts[i < nparts ? i : nparts - 1];
+  }
+  uint32_t m = wave_max_u32(max(max(mv[0], mv[1]), max(mv[2], mv[3])));
+  __shared__ uint32_t pw[4];
+  if ((threadIdx.x & 63) == 0) pw[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return max(max(pw[0], pw[1]), max(pw[2], pw[3]));
+}
+
 // Over a stack, blockIdx.y picks the matrix (n_blk blocks each).  Iterations
 // whose kQuantB blocks all exist run without a branch between loads, codes and
 // stores, so the compiler interleaves the blocks; only the grid's last
 // iteration takes the guarded path.
-// FROM_TSCALE: amax_p holds the tensor scale (amax recovered from it), else amax.
-template <bool DECODE, bool FROM_TSCALE = false>
+template <bool DECODE, int SRC = kFromAmax>
 __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_blk,
                                                        const float* __restrict__ amax_p,
                                                        uint2* __restrict__ packed,
                                                        uint8_t* __restrict__ scales,
                                                        uint4* __restrict__ decoded, const float* ts_w = nullptr,
-                                                       float* ts_x = nullptr, float* ts_y = nullptr) {
+                                                       float* ts_x = nullptr, float* ts_y = nullptr,
+                                                       const uint32_t* __restrict__ parts = nullptr, int nparts = 0,
+                                                       float* ts_out = nullptr) {
   if constexpr (DECODE) {
     // NVFP4 x NVFP4: one thread also writes ts_x = fl32(amax / 2688) and ts_y = fl32(ts_w * ts_x).  Every
     // workgroup reads only amax_p, which is neither of them; the linear that follows reads ts_y.
@@ -265,9 +292,17 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
   w += (int64_t)blockIdx.y * 2 * n_blk;
   packed += (int64_t)blockIdx.y * n_blk;
   scales += (int64_t)blockIdx.y * n_blk;
-  // amax is a BF16 value held in FP32 (or recovered from the tensor scale)
-  const uint32_t amax_b = FROM_TSCALE ? amax_bits_from_tscale(amax_p[blockIdx.y])
-                                      : __float_as_uint(amax_p[blockIdx.y]) >> 16;
+  // amax is a BF16 value held in FP32 (or recovered from the tensor scale, or
+  // the maximum of the per-workgroup maxima)
+  uint32_t amax_b;
+  if constexpr (SRC == kFromParts) {
+    amax_b = parts_max(parts + (int64_t)blockIdx.y * nparts, nparts);
+    if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[blockIdx.y] = __fdiv_rn(__uint_as_float(amax_b << 16), 2688.0f);
+  } else if constexpr (SRC == kFromTscale) {
+    amax_b = amax_bits_from_tscale(amax_p[blockIdx.y]);
+  } else {
+    amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;
+  }
   const QuantConsts qc = quant_consts(amax_b);
   const int64_t B = blockDim.x;
   const int64_t stride = (int64_t)gridDim.x * B * kQuantB;
@@ -382,10 +417,20 @@ void launch_tscale_set_stack(const uint16_t* w, int64_t count, int64_t n_elems, 
   amax_reduce_kernel<true><<<dim3(1, (unsigned)count), 256, 0, s>>>(part, (int)nb, tscale, n_vec);
 }
 
+void launch_quantize_shared_amax(const uint16_t* w, int64_t n_elems, uint32_t* parts, float* tscale,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t s) {
+  const int64_t n_vec = n_elems / 8, n_blk = n_elems / 16;
+  const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxSharedParts);
+  amax_partial_kernel<<<dim3(nb, 1u), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, parts, n_vec, n_vec);
+  quantize_kernel<false, kFromParts><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, nullptr, reinterpret_cast<uint2*>(packed), scales, nullptr, nullptr,
+      nullptr, nullptr, parts, (int)nb, tscale);
+}
+
 void launch_quantize_from_tscale(const uint16_t* w, int64_t count, int64_t n_elems, const float* tscale,
                                  uint8_t* packed, uint8_t* scales, hipStream_t s) {
   const int64_t n_blk = n_elems / 16;
-  quantize_kernel<false, true><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
+  quantize_kernel<false, kFromTscale><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
       reinterpret_cast<const uint4*>(w), n_blk, tscale, reinterpret_cast<uint2*>(packed), scales, nullptr);
 }
 

@@ -48,6 +48,7 @@ int main() {
   for (int s = -3; s < 10; ++s) (void)nvfp4_status_string(s);
   (void)nvfp4_version();
   (void)nvfp4_linear_noalloc_max_bytes();
+  (void)nvfp4_quantize_workspace_bytes();
   for (int offs = 0; offs < 3; ++offs) {
     const uint64_t o = offs == 0 ? 0 : (offs == 1 ? 8 : 16);
     for (int i = 0; i < kNumSizes; ++i) {
@@ -61,6 +62,8 @@ int main() {
         (void)nvfp4_linear_w4a4_workspace_bytes(a, b);
         note(nvfp4_quantize(fake<uint16_t>(A, o), a, b, fake<uint8_t>(B), fake<uint8_t>(C), fake<float>(D), nullptr));
         note(nvfp4_amax_accumulate(fake<uint16_t>(A, o), a, b, fake<float>(D), nullptr));
+        note(nvfp4_quantize_ws(fake<uint16_t>(A), a, b, fake<uint8_t>(B), fake<uint8_t>(C), fake<float>(D),
+                               fake<void>(F, o), a, nullptr));
         note(nvfp4_quantize_with_amax(fake<uint16_t>(A), a, b, fake<float>(D, o), fake<uint8_t>(B), fake<uint8_t>(C),
                                       fake<float>(E), nullptr));
         note(nvfp4_dequant(fake<uint8_t>(B, o), fake<uint8_t>(C), fake<float>(D), a, b, fake<uint16_t>(A), nullptr));

@@ -76,11 +76,13 @@ def test_linear_validation(L):
 def test_linear_workspace_bytes(L):
     wb = L.nvfp4_linear_workspace_bytes
     assert wb(1, 5120, 5120) == 0            # GEMV: no workspace
-    # prefill GEMM: K split only while the 128 x 272 tiles leave CUs idle (at most 128 tiles): the counter
-    # region + slices x tiles x 139,264-byte FP32 partial tiles
+    # prefill GEMM: K split only while the 128 x 272 tiles leave CUs idle (at most 128 tiles, or 257..384): the
+    # counter region + slices x tiles x 139,264-byte FP32 partial tiles
     assert wb(65, 17408, 5120) == 16384 + 4 * 64 * 139264        # 64 tiles, 4 slices
     assert wb(512, 5120, 17408) == 16384 + 3 * 76 * 139264       # 76 tiles, 3 slices
-    assert wb(512, 17408, 5120) == 0 and wb(2048, 5120, 17408) == 0   # 256 and 304 tiles
+    assert wb(512, 17408, 5120) == 0                              # 256 tiles fill the chip
+    assert wb(2048, 5120, 17408) == 16384 + 2 * 304 * 139264      # 304 tiles: 2 slices, 3 rounds of half the work
+    assert wb(2048, 17408, 5120) == 0                             # 1024 tiles
     assert wb(65, 17408, 5136) == 0                               # K not a multiple of 256: other kernel
     assert wb(8, 17408, 5120) == 0           # small-M, 68 rows x 1 K slice per workgroup
     # small-M down projection: 64 blocks of 80 rows x 4 K slices; the fixed 16 KiB counter region + 4 * m * n
@@ -280,6 +282,20 @@ def test_prepared_layout_validation(L):
     assert lp(A + 8, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_ALIGN
     assert lp(A, 8, 64, 128, Bp, D, A + 16, None, 0, None) == B.ERR_ALIAS    # y overlaps x
     assert lp(None, 0, 64, 128, Bp, D, None, None, 0, None) == B.OK          # m = 0 no-op
+
+
+def test_quantize_ws_validation(L):
+    q = L.nvfp4_quantize_ws
+    W = 0x70000000
+    assert L.nvfp4_quantize_workspace_bytes() == 4096
+    assert q(None, 16, 32, Bp, C, D, W, 4096, None) == B.ERR_NULL
+    assert q(A, 16, 30, Bp, C, D, W, 4096, None) == B.ERR_SHAPE
+    assert q(A, 16, 32, Bp, C, D, W, -1, None) == B.ERR_SHAPE
+    assert q(A, 16, 32, Bp, C, D, W + 8, 4096, None) == B.ERR_ALIGN
+    assert q(A, 16, 32, Bp, C, D, A + 16, 4096, None) == B.ERR_ALIAS      # workspace overlaps w
+    assert q(A, 16, 32, Bp, C, D, D, 4096, None) == B.ERR_ALIAS           # workspace overlaps tscale
+    assert q(A, 16, 32, Bp + 8, C, D, W, 4096, None) == B.ERR_ALIGN
+    assert q(A, 16, 32, Bp + 8, C, D, W + 8, 4095, None) == B.ERR_ALIGN    # too small: nvfp4_quantize's checks
 
 
 def test_stream_read_validation(L):

@@ -113,7 +113,11 @@ def crafted_weights():
 
 
 def _quant_compare(nv, w_bits, what):
-    packed, scales, tscale = nv.quantize(to_dev_bf16(w_bits))
+    wd = to_dev_bf16(w_bits)
+    packed, scales, tscale = nv.quantize(wd)                     # nvfp4_quantize_ws (two launches)
+    p3, s3, t3 = nv.quantize(wd, workspace=None)                 # nvfp4_quantize (three launches)
+    assert torch.equal(p3, packed) and torch.equal(s3, scales) and torch.equal(t3, tscale), \
+        f"{what}: the two quantizer forms differ"
     rp, rs, rt = O.quantize(w_bits)
     gp, gs, gt = u8_host(packed), u8_host(scales), tscale.cpu().numpy()[0]
     assert gt.view(np.uint32) == np.float32(rt).view(np.uint32), f"{what}: tscale {gt} vs {rt}"
@@ -318,7 +322,8 @@ def test_small_m_workspace_shared_by_shapes(nv):
 # Linear at full size, auto dispatch, sampled output columns.
 # ---------------------------------------------------------------------------
 FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8),
-               ("small_m_down", 32), ("prefill", 512), ("prefill", 2048), ("small_m_down", 512)]
+               ("small_m_down", 32), ("prefill", 512), ("prefill", 2048), ("small_m_down", 512),
+               ("prefill_down", 2048), ("prefill", 128)]
 
 _weights_cache = {}
 
@@ -327,7 +332,8 @@ def _quantized(nv, wname):
     """(device quantization, BF16 weight, tensor amax) of a full-size workload weight."""
     if wname not in _weights_cache:
         _weights_cache.clear()
-        w = WL.WORKLOADS["small_m_up" if wname == "prefill" else wname].weight()
+        # the prefill workloads share the small-M weights (same shapes and recipe)
+        w = WL.WORKLOADS[{"prefill": "small_m_up", "prefill_down": "small_m_down"}.get(wname, wname)].weight()
         _weights_cache[wname] = (nv.quantize(to_dev_bf16(w)), w, O.tensor_amax(w))
     return _weights_cache[wname]
 
