@@ -85,7 +85,9 @@ nvfp4_status nvfp4_quantize(const uint16_t* w, int64_t n, int64_t k,
  * nvfp4_quantize in two launches instead of three, for a caller that has a
  * workspace: at least nvfp4_quantize_workspace_bytes() bytes (4096) of device
  * memory, 16-byte aligned, overlapping no argument; its contents before the
- * call do not matter (calls that overlap on one workspace race).  The amax pass
+ * call do not matter and it is left holding partial maxima, so it must not be
+ * a split-K workspace of the linear calls, whose counters must stay zero
+ * (calls that overlap on one workspace race).  The amax pass
  * writes at most 1024 per-workgroup maxima of |W| to the workspace and every
  * workgroup of the encode pass reduces them itself (workgroup 0 also writes
  * tscale), so no reduction launch sits between the two.  The outputs are those
@@ -221,10 +223,12 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
  * nvfp4_linear_prepared: y [m, n] = x [m, k] . W_hat^T from the prepared
  * weight, for 1 <= m <= 32 (the decode and batched-decode shapes; larger m is
  * NVFP4_ERR_UNSUPPORTED: the prefill GEMM reads the checkpoint layout); m = 0
- * is a no-op.  Accumulation in FP32 in a different order than nvfp4_linear,
- * so within the same tolerance, not bit-identical to it.  Workspace: as for
- * nvfp4_linear_ws, with nvfp4_linear_prepared_workspace_bytes(m, n, k) bytes
- * (0: none needed; NULL or too small runs without a K split).
+ * is a no-op.  m = 1 runs a GEMV on the vector ALU (one workgroup per 16-row
+ * tile, no workspace); 2 <= m <= 32 the matrix-core kernel.  Accumulation in
+ * FP32 in a different order than nvfp4_linear, so within the same tolerance,
+ * not bit-identical to it.  Workspace: as for nvfp4_linear_ws, with
+ * nvfp4_linear_prepared_workspace_bytes(m, n, k) bytes (0: none needed; NULL
+ * or too small runs without a K split).
  * Errors as nvfp4_linear; a k that is not a multiple of 128 is NVFP4_ERR_SHAPE.
  */
 int64_t nvfp4_prepared_bytes(int64_t n, int64_t k);

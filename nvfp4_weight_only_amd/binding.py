@@ -134,7 +134,7 @@ def quantize(w: torch.Tensor, workspace: Union[str, None, torch.Tensor] = "auto"
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 device tensor")
-        ws = _workspace_for(w.device, stream, lib().nvfp4_quantize_workspace_bytes())
+        ws = _workspace_for(w.device, stream, lib().nvfp4_quantize_workspace_bytes(), kind="quantize")
     else:
         _need(workspace, torch.uint8, "workspace")
         ws = workspace
@@ -207,12 +207,15 @@ def linear_workspace_bytes(m: int, n: int, k: int) -> int:
 # graph captured earlier may still hold its address, and if the allocator handed
 # that memory to another tensor, replays would write partial sums into it and
 # start from counters that are not zero.
-_workspaces: Dict[Tuple[int, int], torch.Tensor] = {}
+_workspaces: Dict[Tuple[int, int, str], torch.Tensor] = {}
 _superseded: list = []
 
 
-def _workspace_for(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
-    key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+def _workspace_for(device: torch.device, stream: int, nbytes: int, kind: str = "split") -> torch.Tensor:
+    """The binding-owned workspace of one (device, stream) for one kind of call.  "split": the split-K
+    workspaces of the linear entry points, whose arrival counters every call leaves at zero; "quantize":
+    nvfp4_quantize_ws's partial maxima (any contents), kept apart so that they never land on the counters."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream, kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         if torch.cuda.is_current_stream_capturing():

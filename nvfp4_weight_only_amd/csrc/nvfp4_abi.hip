@@ -366,7 +366,7 @@ int64_t nvfp4_linear_prepared_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || nvfp4_prepared_bytes(n, k) < 0) return -1;
   int64_t ye;
   if (!mul_ok(m, n, &ye) || ye > INT64_MAX / 32) return -1;
-  if (m == 0 || !nvfp4::small_m_supported(m, n, k)) return 0;
+  if (m <= 1 || !nvfp4::small_m_supported(m, n, k)) return 0;  // m = 1: the prepared GEMV takes none
   return nvfp4::small_m_plan(m, n, k, true).ws_bytes;
 }
 
@@ -386,6 +386,11 @@ nvfp4_status nvfp4_linear_prepared(const uint16_t* x, int64_t m, int64_t n, int6
   if (!nvfp4::small_m_supported(m, n, k)) return NVFP4_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(prepared) || !aligned16(tscale) || !aligned16(y)) return NVFP4_ERR_ALIGN;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, prepared, pb) || overlaps(y, yb, tscale, 4)) return NVFP4_ERR_ALIAS;
+  if (m == 1) {
+    if ((st = check_device()) != NVFP4_OK) return st;
+    nvfp4::launch_gemv_prepared(x, n, k, prepared, tscale, y, static_cast<hipStream_t>(stream));
+    return launch_status();
+  }
   nvfp4::SmallMPlan pl = nvfp4::small_m_plan(m, n, k, true);
   if (pl.slices > 1 && (workspace == nullptr || workspace_bytes < pl.ws_bytes)) pl = nvfp4::small_m_plan(m, n, k, false);
   if (pl.slices > 1) {

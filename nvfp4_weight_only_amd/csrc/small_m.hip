@@ -280,6 +280,116 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// M = 1 on the kernel-native layout: a GEMV with the products on the vector
+// ALU (the decode path of imp "docs/quantization.md", NVFP4 kernel pipeline:
+// the packed weights streamed once, activations BF16).  One workgroup of 16
+// wavefronts per 16-row tile; wavefront w takes the tile's quads w, w + 16,
+// ..., in chunks of QW quads whose loads are all issued before the previous
+// chunk's products (two chunks in registers).
+//   * Weights: lane (r, g) = (lane % 16, lane / 16) loads slot lane of the
+//     (tile, quad) block, i.e. word i = elements 32 i + 8 g .. + 8 of row r, and
+//     the scale word 16 (g / 2) + r, whose byte i is the scale of the block
+//     those elements lie in.  Each word is decoded to exact E2M1 values
+//     (v_cvt_scalef32_pk_bf16_fp4 at scale 1), multiplied into the activations
+//     by four v_dot2_f32_bf16, and the 8-element partial sum takes its E4M3
+//     scale in one FMA: about 1.2 vector instructions per weight element.
+//   * Activations: one 16-byte load per lane fetches the chunk's QW quads
+//     (lane l: quad l / 16, piece l % 16) into the wavefront's own LDS area;
+//     the products read them back as 16-byte broadcasts (16 lanes per
+//     address).  Only the wavefront itself reads its area, so no barrier.
+//   * The 64 lanes' sums meet over g by two shuffles, the 16 wavefronts' sums
+//     in LDS in wavefront order, and y takes the tensor scale once.
+// Rows past n are the layout's zero padding and are not stored.
+// ---------------------------------------------------------------------------
+constexpr int kPgWaves = 16;
+
+__device__ __forceinline__ float pg_dot8(uint32_t w, uint4 xv, float acc) {
+  acc = dot2_bf16(e2m1x2_to_bf16<0>(w), xv.x, acc);
+  acc = dot2_bf16(e2m1x2_to_bf16<1>(w), xv.y, acc);
+  acc = dot2_bf16(e2m1x2_to_bf16<2>(w), xv.z, acc);
+  return dot2_bf16(e2m1x2_to_bf16<3>(w), xv.w, acc);
+}
+
+template <int QW>
+struct PgChunk {
+  uint4 x;       // activation piece: quad lane / 16 of the chunk, piece lane % 16
+  SmW w[QW];     // weights and scales of the chunk's quads
+};
+
+template <int QW>
+__global__ void __launch_bounds__(64 * kPgWaves) gemv_prepared_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                       int quads, const uint8_t* __restrict__ prep,
+                                                                       const float* __restrict__ tscale,
+                                                                       uint16_t* __restrict__ y) {
+  static_assert(QW >= 1 && QW <= 4, "one activation load covers at most four quads");
+  __shared__ uint4 xs[kPgWaves][64];
+  __shared__ float red[kPgWaves][16];
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tiles = (n + 15) >> 4, tile = blockIdx.x;
+  const uint8_t* tb = prep + tile * (int64_t)kSmBlock;
+  const int64_t qstride = tiles * kSmBlock;
+  // This wavefront's quads w + 16 j, j < nq; chunk c holds j = QW c .. QW c + QW - 1.
+  const int nq = quads > w ? (quads - w + kPgWaves - 1) / kPgWaves : 0;
+  const int nc = (nq + QW - 1) / QW;
+  float acc = 0.0f;
+  if (nc > 0) {  // uniform per wavefront, taken before any load is in flight
+    // Loads of chunk c; quads past the wavefront's last repeat it (never used).
+    auto load = [&](PgChunk<QW>& ch, int c) {
+      const int jx = QW * c + (lane >> 4);
+      const int qx = w + kPgWaves * ((lane >> 4) < QW && jx < nq ? jx : nq - 1);
+      ch.x = *reinterpret_cast<const uint4*>(x + (int64_t)qx * kSmQuadK + 8 * (lane & 15));
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        const int jj = QW * c + j;
+        sm_load_w(ch.w[j], tb, qstride, w + kPgWaves * (jj < nq ? jj : nq - 1), lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](const PgChunk<QW>& ch, int c) {
+      xs[w][lane] = ch.x;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        const float2 s01 = e4m3x2_to_f32<false>(ch.w[j].s), s23 = e4m3x2_to_f32<true>(ch.w[j].s);
+        const uint32_t wd[4] = {ch.w[j].w.x, ch.w[j].w.y, ch.w[j].w.z, ch.w[j].w.w};
+        const float sc[4] = {s01.x, s01.y, s23.x, s23.y};
+        float a = acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = fmaf(pg_dot8(wd[i], xs[w][16 * j + 4 * i + g], 0.0f), sc[i], a);
+        acc = QW * c + j < nq ? a : acc;  // select, not a branch: the next chunk's loads stay in flight
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // the area is rewritten by the next chunk
+    };
+    PgChunk<QW> ca, cb;
+    load(ca, 0);
+    int c = 0;
+    for (; c + 1 < nc; c += 2) {
+      load(cb, c + 1);
+      compute(ca, c);
+      load(ca, c + 2 < nc ? c + 2 : nc - 1);
+      compute(cb, c + 1);
+    }
+    if (c < nc) compute(ca, c);
+  }
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 16) red[w][lane] = acc;
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t row = tile * 16 + t;
+  if (t < 16 && row < n) {
+    float v = red[0][t];
+#pragma unroll
+    for (int ww = 1; ww < kPgWaves; ++ww) v += red[ww][t];
+    y[row] = (uint16_t)f32_to_bf16_rne(v * *tscale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // The kernel-native layout: conversion from the checkpoint layout and the
 // dequantizer that reads it.  One thread per 16 output bytes of a 1152-byte
 // (tile, quad) block: units 0..63 are the packed slots, 64..71 four scale
@@ -407,15 +517,15 @@ bool small_m_supported(int64_t m, int64_t n, int64_t k) {
 SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
   SmallMPlan pl;
   pl.quads = (int)(k / kSmQuadK);
-  // K slices: about 40 weight rows per workgroup and 256 workgroups (one per
+  // K slices: about 80 weight rows per workgroup and 256 workgroups (one per
   // CU), each slice at least eight quads (one per wavefront), at most 16.
-  // (Fewer rows per workgroup would mean more slices, whose partial-sum
-  // exchange at the end costs more than the shorter K loop saves; at the down
-  // projection 5120 x 17408, M = 8, 40 rows x 2 slices measured 15.5 us against
-  // 16.6 us for 80 x 4 and 17.8 us for 20 x 1.)
+  // Each workgroup reads the activations of its K slice, so more slices mean
+  // fewer activation bytes per CU, and more partial sums to exchange.  At the
+  // down projection 5120 x 17408: M = 8, 80 rows x 4 slices 16.5 us against
+  // 16.8 us for 40 x 2; M = 32, 26.9 us against 29.5 us.
   int64_t s = 1;
   if (split) {
-    s = (40 * 256 + n / 2) / n;
+    s = (80 * 256 + n / 2) / n;
     int64_t cap = pl.quads / kSmWaves;
     cap = cap < 16 ? cap : 16;
     s = s > cap ? cap : s;
@@ -438,6 +548,19 @@ SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
     pl.ws_bytes = kSkinnyCounterBytes + (int64_t)pl.slices * m * pl.npad * 4;
   }
   return pl;
+}
+
+void launch_gemv_prepared(const uint16_t* x, int64_t n, int64_t k, const uint8_t* prep, const float* tscale,
+                          uint16_t* y, hipStream_t s) {
+  const int quads = (int)(k / kSmQuadK);
+  const int per_wave = (quads + kPgWaves - 1) / kPgWaves;  // quads of wavefront 0
+  const dim3 grid((unsigned)sm_ceil_div(n, 16));
+  switch (per_wave < 4 ? per_wave : 4) {
+    case 1: gemv_prepared_kernel<1><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    case 2: gemv_prepared_kernel<2><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    case 3: gemv_prepared_kernel<3><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    default: gemv_prepared_kernel<4><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
+  }
 }
 
 void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,

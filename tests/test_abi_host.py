@@ -239,6 +239,9 @@ def test_binding_workspace_kept_when_superseded_and_refused_under_capture(monkey
         B._workspace_for(dev, 7, 4000)                          # but none is allocated there
     with pytest.raises(RuntimeError, match="graph capture"):
         B._workspace_for(dev, 8, 16)                            # nor for a new stream
+    capturing["on"] = False
+    q = B._workspace_for(dev, 7, 4096, kind="quantize")         # the quantizer's partial maxima: its own buffer,
+    assert q is not b and B._workspace_for(dev, 7, 16) is b     # never the counters of the split workspace
 
 
 def test_linear_noalloc_validation(L):
@@ -272,9 +275,9 @@ def test_prepared_layout_validation(L):
     assert d(Bp, D, 16, 128, Bp + 16, None) == B.ERR_ALIAS
     wb = L.nvfp4_linear_prepared_workspace_bytes
     assert wb(8, 64, 96) == -1 and wb(-1, 64, 128) == -1 and wb(0, 64, 128) == 0 and wb(33, 64, 128) == 0
-    # down projection: 128 blocks of 40 rows x 2 K slices (the fixed 16 KiB counter region + 2 * m * n FP32
+    # down projection: 64 blocks of 80 rows x 4 K slices (the fixed 16 KiB counter region + 4 * m * n FP32
     # partials); up projection: 68 rows x 1 slice, no workspace
-    assert wb(8, 5120, 17408) == 16384 + 2 * 8 * 5120 * 4 and wb(8, 17408, 5120) == 0
+    assert wb(8, 5120, 17408) == 16384 + 4 * 8 * 5120 * 4 and wb(8, 17408, 5120) == 0
     lp = L.nvfp4_linear_prepared
     assert lp(None, 8, 64, 128, Bp, D, E, None, 0, None) == B.ERR_NULL
     assert lp(A, 8, 64, 96, Bp, D, E, None, 0, None) == B.ERR_SHAPE
