@@ -223,10 +223,10 @@ nvfp4_status nvfp4_linear_noalloc(const uint16_t* x, int64_t m, int64_t n, int64
  * nvfp4_linear_prepared: y [m, n] = x [m, k] . W_hat^T from the prepared
  * weight, for 1 <= m <= 32 (the decode and batched-decode shapes; larger m is
  * NVFP4_ERR_UNSUPPORTED: the prefill GEMM reads the checkpoint layout); m = 0
- * is a no-op.  m = 1 runs a GEMV on the vector ALU (one workgroup per 16-row
- * tile, no workspace); 2 <= m <= 32 the matrix-core kernel.  Accumulation in
- * FP32 in a different order than nvfp4_linear, so within the same tolerance,
- * not bit-identical to it.  Workspace: as for nvfp4_linear_ws, with
+ * is a no-op.  m = 1 runs a GEMV on the vector ALU (no workspace); 2 <= m
+ * <= 32 the matrix-core kernel.  Accumulation in FP32 in a different order
+ * than nvfp4_linear, so within the same tolerance, not bit-identical to it.
+ * Workspace: as for nvfp4_linear_ws, with
  * nvfp4_linear_prepared_workspace_bytes(m, n, k) bytes (0: none needed; NULL
  * or too small runs without a K split).
  * Errors as nvfp4_linear; a k that is not a multiple of 128 is NVFP4_ERR_SHAPE.

@@ -72,7 +72,7 @@ struct SmallMPlan {
 };
 bool small_m_supported(int64_t m, int64_t n, int64_t k);
 SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split);
-// M = 1 on the kernel-native layout (k a multiple of 128): one workgroup per 16-row tile.
+// M = 1 on the kernel-native layout (k a multiple of 128).
 void launch_gemv_prepared(const uint16_t* x, int64_t n, int64_t k, const uint8_t* prep, const float* tscale,
                           uint16_t* y, hipStream_t s);
 void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,

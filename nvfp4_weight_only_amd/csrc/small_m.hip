@@ -282,27 +282,27 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
 // ---------------------------------------------------------------------------
 // M = 1 on the kernel-native layout: a GEMV with the products on the vector
 // ALU (the decode path of imp "docs/quantization.md", NVFP4 kernel pipeline:
-// the packed weights streamed once, activations BF16).  One workgroup of 16
-// wavefronts per 16-row tile; wavefront w takes the tile's quads w, w + 16,
-// ..., in chunks of QW quads whose loads are all issued before the previous
-// chunk's products (two chunks in registers).
-//   * Weights: lane (r, g) = (lane % 16, lane / 16) loads slot lane of the
-//     (tile, quad) block, i.e. word i = elements 32 i + 8 g .. + 8 of row r, and
-//     the scale word 16 (g / 2) + r, whose byte i is the scale of the block
-//     those elements lie in.  Each word is decoded to exact E2M1 values
+// the packed weights streamed once, activations BF16).  A workgroup of W
+// wavefronts owns T consecutive 16-row tiles; wavefront w takes the quads
+// w, w + W, ... of all T tiles, in chunks of QW quads whose loads are all
+// issued before the previous chunk's products (two chunks in registers).
+//   * Weights: lane (r, g) = (lane % 16, lane / 16) loads slot lane of each
+//     (tile, quad) block, i.e. word i = elements 32 i + 8 g .. + 8 of row r,
+//     and the scale word 16 (g / 2) + r, whose byte i is the scale of the
+//     block those elements lie in.  Each word is decoded to exact E2M1 values
 //     (v_cvt_scalef32_pk_bf16_fp4 at scale 1), multiplied into the activations
 //     by four v_dot2_f32_bf16, and the 8-element partial sum takes its E4M3
 //     scale in one FMA: about 1.2 vector instructions per weight element.
 //   * Activations: one 16-byte load per lane fetches the chunk's QW quads
 //     (lane l: quad l / 16, piece l % 16) into the wavefront's own LDS area;
 //     the products read them back as 16-byte broadcasts (16 lanes per
-//     address).  Only the wavefront itself reads its area, so no barrier.
-//   * The 64 lanes' sums meet over g by two shuffles, the 16 wavefronts' sums
+//     address), once per quad for all T tiles.  Only the wavefront itself
+//     reads its area, so no barrier.
+//   * The 64 lanes' sums meet over g by two shuffles, the W wavefronts' sums
 //     in LDS in wavefront order, and y takes the tensor scale once.
-// Rows past n are the layout's zero padding and are not stored.
+// Rows past n are the layout's zero padding (tiles past the last repeat it)
+// and are not stored.
 // ---------------------------------------------------------------------------
-constexpr int kPgWaves = 16;
-
 __device__ __forceinline__ float pg_dot8(uint32_t w, uint4 xv, float acc) {
   acc = dot2_bf16(e2m1x2_to_bf16<0>(w), xv.x, acc);
   acc = dot2_bf16(e2m1x2_to_bf16<1>(w), xv.y, acc);
@@ -310,61 +310,74 @@ __device__ __forceinline__ float pg_dot8(uint32_t w, uint4 xv, float acc) {
   return dot2_bf16(e2m1x2_to_bf16<3>(w), xv.w, acc);
 }
 
-template <int QW>
+template <int QW, int T>
 struct PgChunk {
-  uint4 x;       // activation piece: quad lane / 16 of the chunk, piece lane % 16
-  SmW w[QW];     // weights and scales of the chunk's quads
+  uint4 x;         // activation piece: quad lane / 16 of the chunk, piece lane % 16
+  SmW w[QW][T];    // weights and scales of the chunk's quads, per tile
 };
 
-template <int QW>
-__global__ void __launch_bounds__(64 * kPgWaves) gemv_prepared_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                                       int quads, const uint8_t* __restrict__ prep,
-                                                                       const float* __restrict__ tscale,
-                                                                       uint16_t* __restrict__ y) {
+template <int W, int T, int QW>
+__global__ void __launch_bounds__(64 * W) gemv_prepared_kernel(const uint16_t* __restrict__ x, int64_t n, int quads,
+                                                               const uint8_t* __restrict__ prep,
+                                                               const float* __restrict__ tscale,
+                                                               uint16_t* __restrict__ y) {
   static_assert(QW >= 1 && QW <= 4, "one activation load covers at most four quads");
-  __shared__ uint4 xs[kPgWaves][64];
-  __shared__ float red[kPgWaves][16];
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  __shared__ uint4 xs[W][64];
+  __shared__ float red[W][16 * T];
+  const int lane = threadIdx.x & 63, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tiles = (n + 15) >> 4, tile = blockIdx.x;
-  const uint8_t* tb = prep + tile * (int64_t)kSmBlock;
+  const int64_t tiles = (n + 15) >> 4, tile0 = (int64_t)blockIdx.x * T;
+  const uint8_t* tb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) tb[t] = prep + (tile0 + t < tiles ? tile0 + t : tiles - 1) * (int64_t)kSmBlock;
   const int64_t qstride = tiles * kSmBlock;
-  // This wavefront's quads w + 16 j, j < nq; chunk c holds j = QW c .. QW c + QW - 1.
-  const int nq = quads > w ? (quads - w + kPgWaves - 1) / kPgWaves : 0;
+  // This wavefront's quads w + W j, j < nq; chunk c holds j = QW c .. QW c + QW - 1.
+  const int nq = quads > w ? (quads - w + W - 1) / W : 0;
   const int nc = (nq + QW - 1) / QW;
-  float acc = 0.0f;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
   if (nc > 0) {  // uniform per wavefront, taken before any load is in flight
     // Loads of chunk c; quads past the wavefront's last repeat it (never used).
-    auto load = [&](PgChunk<QW>& ch, int c) {
+    auto load = [&](PgChunk<QW, T>& ch, int c) {
       const int jx = QW * c + (lane >> 4);
-      const int qx = w + kPgWaves * ((lane >> 4) < QW && jx < nq ? jx : nq - 1);
+      const int qx = w + W * ((lane >> 4) < QW && jx < nq ? jx : nq - 1);
       ch.x = *reinterpret_cast<const uint4*>(x + (int64_t)qx * kSmQuadK + 8 * (lane & 15));
 #pragma unroll
       for (int j = 0; j < QW; ++j) {
-        const int jj = QW * c + j;
-        sm_load_w(ch.w[j], tb, qstride, w + kPgWaves * (jj < nq ? jj : nq - 1), lane);
+        const int jj = QW * c + j, q = w + W * (jj < nq ? jj : nq - 1);
+#pragma unroll
+        for (int t = 0; t < T; ++t) sm_load_w(ch.w[j][t], tb[t], qstride, q, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    auto compute = [&](const PgChunk<QW>& ch, int c) {
+    auto compute = [&](const PgChunk<QW, T>& ch, int c) {
       xs[w][lane] = ch.x;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int j = 0; j < QW; ++j) {
-        const float2 s01 = e4m3x2_to_f32<false>(ch.w[j].s), s23 = e4m3x2_to_f32<true>(ch.w[j].s);
-        const uint32_t wd[4] = {ch.w[j].w.x, ch.w[j].w.y, ch.w[j].w.z, ch.w[j].w.w};
-        const float sc[4] = {s01.x, s01.y, s23.x, s23.y};
-        float a = acc;
+        uint4 xv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a = fmaf(pg_dot8(wd[i], xs[w][16 * j + 4 * i + g], 0.0f), sc[i], a);
-        acc = QW * c + j < nq ? a : acc;  // select, not a branch: the next chunk's loads stay in flight
+        for (int i = 0; i < 4; ++i) xv[i] = xs[w][16 * j + 4 * i + g];
+        const bool valid = QW * c + j < nq;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const SmW& r = ch.w[j][t];
+          const float2 s01 = e4m3x2_to_f32<false>(r.s), s23 = e4m3x2_to_f32<true>(r.s);
+          float a = acc[t];
+          a = fmaf(pg_dot8(r.w.x, xv[0], 0.0f), s01.x, a);
+          a = fmaf(pg_dot8(r.w.y, xv[1], 0.0f), s01.y, a);
+          a = fmaf(pg_dot8(r.w.z, xv[2], 0.0f), s23.x, a);
+          a = fmaf(pg_dot8(r.w.w, xv[3], 0.0f), s23.y, a);
+          acc[t] = valid ? a : acc[t];  // a select, not a branch: the next chunk's loads stay in flight
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();  // the area is rewritten by the next chunk
     };
-    PgChunk<QW> ca, cb;
+    PgChunk<QW, T> ca, cb;
     load(ca, 0);
     int c = 0;
     for (; c + 1 < nc; c += 2) {
@@ -375,16 +388,20 @@ __global__ void __launch_bounds__(64 * kPgWaves) gemv_prepared_kernel(const uint
     }
     if (c < nc) compute(ca, c);
   }
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
-  if (lane < 16) red[w][lane] = acc;
-  __syncthreads();
-  const int t = threadIdx.x;
-  const int64_t row = tile * 16 + t;
-  if (t < 16 && row < n) {
-    float v = red[0][t];
 #pragma unroll
-    for (int ww = 1; ww < kPgWaves; ++ww) v += red[ww][t];
+  for (int t = 0; t < T; ++t) {
+    float v = acc[t];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (lane < 16) red[w][16 * t + lane] = v;
+  }
+  __syncthreads();
+  const int tt = threadIdx.x;
+  const int64_t row = tile0 * 16 + tt;
+  if (tt < 16 * T && row < n) {
+    float v = red[0][tt];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) v += red[ww][tt];
     y[row] = (uint16_t)f32_to_bf16_rne(v * *tscale);
   }
 }
@@ -550,17 +567,36 @@ SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
   return pl;
 }
 
+template <int W, int T>
+static void launch_pg(const uint16_t* x, int64_t n, int quads, const uint8_t* prep, const float* tscale, uint16_t* y,
+                      hipStream_t s) {
+  const int per_wave = (quads + W - 1) / W;  // quads of wavefront 0
+  const dim3 grid((unsigned)sm_ceil_div(sm_ceil_div(n, 16), T));
+  switch (per_wave < 4 ? per_wave : 4) {
+    case 1: gemv_prepared_kernel<W, T, 1><<<grid, 64 * W, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    case 2: gemv_prepared_kernel<W, T, 2><<<grid, 64 * W, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    case 3: gemv_prepared_kernel<W, T, 3><<<grid, 64 * W, 0, s>>>(x, n, quads, prep, tscale, y); break;
+    default: gemv_prepared_kernel<W, T, 4><<<grid, 64 * W, 0, s>>>(x, n, quads, prep, tscale, y); break;
+  }
+}
+
+// Launch shape, from a sweep of wavefronts per workgroup (W = 1 .. 16) and
+// tiles per workgroup (T = 1 .. 4), host-launched over rotated copies:
+//   5120 x 5120: W 16, T 2 5.63 us (W 16, T 1 6.67; W 4, T 2 6.04);
+//   34816 x 5120: W 4, T 1 19.46 us (W 16, T 1 25.8; W 10, T 1 21.5);
+//   5120 x 17408: W 4, T 2 12.37 us (W 16, T 2 13.4; W 4, T 1 13.2).
+// Many tiles: small workgroups, one tile each; few tiles and long K: small
+// workgroups with two tiles; few tiles and short K: 16 wavefronts share K.
 void launch_gemv_prepared(const uint16_t* x, int64_t n, int64_t k, const uint8_t* prep, const float* tscale,
                           uint16_t* y, hipStream_t s) {
   const int quads = (int)(k / kSmQuadK);
-  const int per_wave = (quads + kPgWaves - 1) / kPgWaves;  // quads of wavefront 0
-  const dim3 grid((unsigned)sm_ceil_div(n, 16));
-  switch (per_wave < 4 ? per_wave : 4) {
-    case 1: gemv_prepared_kernel<1><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
-    case 2: gemv_prepared_kernel<2><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
-    case 3: gemv_prepared_kernel<3><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
-    default: gemv_prepared_kernel<4><<<grid, 64 * kPgWaves, 0, s>>>(x, n, quads, prep, tscale, y); break;
-  }
+  const int64_t tiles = sm_ceil_div(n, 16);
+  if (tiles >= 1024)
+    launch_pg<4, 1>(x, n, quads, prep, tscale, y, s);
+  else if (quads > 64)
+    launch_pg<4, 2>(x, n, quads, prep, tscale, y, s);
+  else
+    launch_pg<16, 2>(x, n, quads, prep, tscale, y, s);
 }
 
 void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* prep,

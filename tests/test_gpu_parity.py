@@ -1047,8 +1047,9 @@ def test_prepare_and_dequant_prepared_bit_exact(nv, n, k):
 
 PREP_LINEAR = [(1, 16, 128), (2, 100, 128), (8, 300, 1024), (16, 37, 384), (17, 64, 5120), (32, 300, 640),
                (5, 1000, 384), (8, 10240, 512), (3, 2000, 8192), (32, 68, 1280), (24, 700, 3072),
-               # m = 1 (the GEMV): fewer quads than wavefronts, 1 / 2 / 4 quads per chunk, two and three chunks
-               (1, 37, 384), (1, 300, 2176), (1, 1000, 8192), (1, 33, 10240), (1, 70, 17408)]
+               # m = 1 (the GEMV): fewer quads than wavefronts, 1 / 2 / 4 quads per chunk, two and three chunks,
+               # an odd tile count under two tiles per workgroup, and the one-tile shape for many tiles
+               (1, 37, 384), (1, 300, 2176), (1, 1000, 8192), (1, 33, 10240), (1, 70, 17408), (1, 16390, 512)]
 
 
 @pytest.mark.parametrize("m,n,k", PREP_LINEAR)
