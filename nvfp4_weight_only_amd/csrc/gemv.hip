@@ -326,6 +326,7 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
   {
     const int sp = lane % SL;
     const int64_t r = row0 + sp / (2 * J), row = r < n ? r : n - 1;
+    // plain load: 32 bytes of a line whose rest the other wavefronts read
     sg = reinterpret_cast<const uint4*>(scales + row * kb + (int64_t)w * 32 * J)[sp % (2 * J)];
   }
   __builtin_amdgcn_sched_barrier(0);  // activations and scales are issued before the weights
@@ -336,7 +337,7 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
 #pragma unroll
     for (int i = 0; i < I; ++i) {
       const int64_t r = row0 + g + 4 * i, row = r < n ? r : n - 1;
-      wv[j][i] = *reinterpret_cast<const uint4*>(packed + row * kh + (ub + 16 * j) * 16);
+      wv[j][i] = ld_stream16(packed + row * kh + (ub + 16 * j) * 16);
     }
   __builtin_amdgcn_sched_barrier(0);
   // 4. through this wavefront's LDS area: activation piece q of unit v of

@@ -83,8 +83,8 @@ struct SmX {
 // the next (tiles * 1152, quad-major layout).
 __device__ __forceinline__ void sm_load_w(SmW& r, const uint8_t* tile, int64_t qstride, int q, int lane) {
   const uint8_t* b = tile + (int64_t)q * qstride;
-  r.w = *reinterpret_cast<const uint4*>(b + 16 * lane);
-  r.s = *reinterpret_cast<const uint32_t*>(b + 1024 + 4 * (16 * ((lane >> 5) & 1) + (lane & 15)));
+  r.w = ld_stream16(b + 16 * lane);
+  r.s = ld_stream4(b + 1024 + 4 * (16 * ((lane >> 5) & 1) + (lane & 15)));
 }
 
 // Activation fragments of quad q: step i, m tile mt is row xr[mt] at elements

@@ -3,7 +3,9 @@
 // kStreamU loads in flight, and folded into an XOR per workgroup; workgroup b
 // stores its XOR to sink[b] (a few kilobytes in all, so the loads cannot be
 // dropped and the writes do not count).  Its rate is the HBM read rate the
-// weight-streaming kernels can be held against.
+// weight-streaming kernels can be held against (loaded with the nontemporal
+// hint, as they load their weights).
+#include "device_common.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
@@ -23,7 +25,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint4
 #pragma unroll
     for (int u = 0; u < kStreamU; ++u) {
       const int64_t i = i0 + (int64_t)u * kStreamThreads;
-      v[u] = src[i < n_vec ? i : n_vec - 1];  // past the end: an in-bounds load whose value is dropped below
+      v[u] = ld_stream16(src + (i < n_vec ? i : n_vec - 1));  // past the end: an in-bounds load, value dropped below
     }
 #pragma unroll
     for (int u = 0; u < kStreamU; ++u) {
