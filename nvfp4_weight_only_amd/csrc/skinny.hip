@@ -343,6 +343,13 @@ __device__ __forceinline__ void sk_lds_dma16(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
 
+// The same with the nontemporal hint, for the weight rows: each instruction
+// reads whole lines of data that no other workgroup reads.
+__device__ __forceinline__ void sk_lds_dma16_nt(const void* src, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);  // uniform per wavefront by construction
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(base) : "memory");
+}
+
 template <typename U>
 __device__ __forceinline__ uint32_t sk_lds_addr(const U* p) {
   return (uint32_t)(uintptr_t)(const sk_lds_t*)p;
@@ -465,7 +472,7 @@ __device__ __forceinline__ void sk_dma_issue(const SkinnyArgs& p, const SkDmaSrc
                                              int c0, SkStage<MX, TT>& S, uint4* sg, int lane) {
   const int cc = ci < nc ? ci : nc - 1;
 #pragma unroll
-  for (int i = 0; i < LW; ++i) sk_lds_dma16(src.w[i] + (int64_t)cc * 128, sk_lds_addr(&S.w[src.wslot[i]]));
+  for (int i = 0; i < LW; ++i) sk_lds_dma16_nt(src.w[i] + (int64_t)cc * 128, sk_lds_addr(&S.w[src.wslot[i]]));
 #pragma unroll
   for (int i = 0; i < LX; ++i) sk_lds_dma16(src.x[i] + (int64_t)cc * kSkChunk, sk_lds_addr(&S.x[src.xslot[i]]));
   if ((ci & 3) == 0) {
