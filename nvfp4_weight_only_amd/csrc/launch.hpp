@@ -79,15 +79,20 @@ void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t 
                     const float* tscale, uint16_t* y, void* workspace, hipStream_t s);
 // Prefill GEMM.  With a workspace of at least prefill_workspace_bytes(m, n, k)
 // bytes (zero-filled before its first use; left that way by every launch), a
-// tile count that leaves CUs idle is split along K (prefill_split_slices
-// workgroups per tile); with none it runs unsplit.  The workspace starts with
+// tile count that leaves CUs idle splits some tiles along K (prefill_split);
+// with none it runs one tile per workgroup.  The workspace starts with
 // kSkinnyCounterBytes of arrival counters, then the FP32 partial tiles.
 void launch_gemm_prefill(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                          const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,
                          int64_t workspace_bytes, hipStream_t s);
 // Streaming prefill GEMM (K a multiple of 256); launch_gemm_prefill uses it when supported.
 bool prefill_dma_supported(int64_t m, int64_t n, int64_t k);
-int prefill_split_slices(int64_t m, int64_t n, int64_t k);
+struct PdSplit {
+  int dp = 0;    // whole tiles, one workgroup each, launched first
+  int tail = 0;  // tiles after them, each split along K
+  int c = 0;     // slices per split tile (0: no split)
+};
+PdSplit prefill_split(int64_t m, int64_t n, int64_t k);
 int64_t prefill_workspace_bytes(int64_t m, int64_t n, int64_t k);
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
                         const uint8_t* scales, const float* tscale, uint16_t* y, void* workspace,

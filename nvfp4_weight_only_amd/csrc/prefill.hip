@@ -50,13 +50,18 @@ struct PdArgs {
   // built by the grouping kernels (see PdGroups), and the stack's layout.
   const int32_t* groups;
   int64_t topk, experts, w_stride;  // w_stride: packed bytes per expert
-  // Split K (plain form only): `slices` workgroups per tile, each over a range
-  // of whole 256-element groups, exchange FP32 partial tiles in `part` and meet
-  // at the tile's arrival counter in `count` (see pd_exchange).
-  int slices;
+  // Split K for the tiles past the last whole round (plain form only): the
+  // first sk_dp tiles run one per workgroup over the whole K (the whole grid
+  // when sk_tail = 0); each of the remaining sk_tail tiles is split into sk_c
+  // slices of whole 256-element groups, one workgroup each, launched after
+  // the whole tiles.  A split tile's workgroups exchange FP32 partial tiles in
+  // `part` (sk_c slots per tile) and meet at its arrival counter in `count`
+  // (see pd_exchange).
+  int sk_dp, sk_tail, sk_c;
   float* part;
   uint32_t* count;
 };
+
 
 // FP32 partial tile of one (tile, slice): per wavefront 34 float4 per lane
 // (its 8 accumulator tiles of 16 items, then the fifth tile's 8 items).
@@ -423,17 +428,18 @@ __device__ __forceinline__ void pd_store_tile(const PdArgs& p, const uint16_t* y
 }
 
 // Split-K exchange of one wavefront's sums (its accumulators and its row
-// tile of the fifth column tile, already summed over the wavefronts): the
-// slice's partial tile goes to the workspace, the tile's workgroups meet at
-// its arrival counter (splitk_arrive: release / acquire at device scope), and
-// the last one replaces its sums by the sum over all slices in slice order
-// (the same bits whichever workgroup arrives last).  Returns false in the
-// others, which are done.
+// tile of the fifth column tile, already summed over the wavefronts) for split
+// tile xtile, shared by cnt workgroups of which this is slice sl: the partial
+// tile goes to slot sl of the workspace, the tile's workgroups meet at its
+// arrival counter (splitk_arrive: release / acquire at device scope), and the
+// last one replaces its sums by the sum over all slices in slice order (the
+// same bits whichever workgroup arrives last).  Returns false in the others,
+// which are done.
 template <int W>
-__device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][2], float4& t5a, float4& t5b, int tile,
-                                            int sl, int lane) {
+__device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][2], float4& t5a, float4& t5b, int xtile,
+                                            int sl, int cnt, int lane) {
   auto slot = [&](int s, int j) {
-    return p.part + ((((int64_t)tile * p.slices + s) * 4 + W) * kPdPartVec + j) * 256 + 4 * lane;
+    return p.part + ((((int64_t)xtile * p.sk_c + s) * 4 + W) * kPdPartVec + j) * 256 + 4 * lane;
   };
   auto get = [&](int j) -> f32x4_t {
     if (j < 32) {
@@ -460,7 +466,7 @@ __device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][
   // acquire makes the last workgroup read it from memory.
 #pragma unroll
   for (int j = 0; j < kPdPartVec; ++j) *reinterpret_cast<f32x4_t*>(slot(sl, j)) = get(j);
-  if (!splitk_arrive(p.count + tile, p.slices)) return false;
+  if (!splitk_arrive(p.count + xtile, cnt)) return false;
   // Two halves of 17 vectors: each half's loads of every other slice are in
   // flight together.
 #pragma unroll
@@ -468,7 +474,7 @@ __device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][
     f32x4_t sum[17];
 #pragma unroll
     for (int i = 0; i < 17; ++i) sum[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < p.slices; ++s) {
+    for (int s = 0; s < cnt; ++s) {
 #pragma unroll
       for (int i = 0; i < 17; ++i)
         sum[i] += s == sl ? get(17 * h + i) : *reinterpret_cast<const f32x4_t*>(slot(s, 17 * h + i));
@@ -483,7 +489,7 @@ __device__ __forceinline__ bool pd_exchange(const PdArgs& p, f32x16_t (&acc)[4][
 // tile's operand choice is static and every accumulator stays in place).
 template <int W, bool G>
 __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds& L, int lane, int64_t m0,
-                                        int64_t n0, int nsteps, int tile, int sl) {
+                                        int64_t n0, int nsteps, int xtile, int sl, int cnt) {
   f32x16_t acc[4][2], acc5[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -558,7 +564,7 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
   }
 
   if constexpr (!G) {
-    if (p.slices > 1 && !pd_exchange<W>(p, acc, t5a, t5b, tile, sl, lane)) return;
+    if (cnt > 1 && !pd_exchange<W>(p, acc, t5a, t5b, xtile, sl, cnt, lane)) return;
   }
 
   // Epilogue: the BF16 tile goes through LDS (the X stages, free now) so that
@@ -596,28 +602,19 @@ __device__ __forceinline__ void pd_body(const PdArgs& p, const PdSrc& src, PdLds
 // use at most (V - nonempty experts) / 128 + nonempty experts of them), then
 // exit.  In the grouped form p.m holds the number of pairs until the tile's
 // row count replaces it.
+// One tile over its K groups [g0, g1) (the whole K: 0, groups): sources from
+// the tile's rows and columns, then the pipeline.  xtile / sl / cnt: the
+// stream-K exchange (cnt = 1: none).  In the grouped form `tile` is the
+// launch's tile id.
 template <bool G>
-__global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
-  __shared__ PdLds L;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
-  // Tile order: workgroups are dispatched to the 8 XCDs round-robin by id, so
-  // when the tile count allows, consecutive ids of one XCD cover all m tiles of
-  // consecutive n tiles (the weight tile is then fetched into that XCD's L2 once).
-  // With split K the slices of a tile are consecutive ids (one XCD).
-  const int nwg = p.n_tiles * p.m_tiles * p.slices;
-  int id = (int)blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
-  const int sl = id % p.slices, tile = id / p.slices;
+__device__ __forceinline__ void pd_tile(PdArgs p, PdLds& L, int tid, int lane, int w, int tile, int g0, int g1,
+                                        int xtile, int sl, int cnt) {
   const int nt = tile / p.m_tiles, mt = tile % p.m_tiles;
   int64_t m0 = (int64_t)mt * kPdBM;
   const int64_t n0 = (int64_t)nt * kPdBN;
   const int64_t kh = p.k >> 1, ks = p.k >> 4;  // row strides (the whole K)
-  // This slice's groups [g0, g1) of 256 K elements: the sources start there.
-  const int groups = (int)(p.k / kPdGroupK);
-  const int g0 = (int)((int64_t)sl * groups / p.slices), g1 = (int)((int64_t)(sl + 1) * groups / p.slices);
   const int nsteps = 4 * (g1 - g0);
+  // The sources start at group g0.
   p.x += (int64_t)g0 * kPdGroupK;
   p.packed += (int64_t)g0 * (kPdGroupK / 2);
   p.scales += (int64_t)g0 * (kPdGroupK / 16);
@@ -674,10 +671,41 @@ __global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
   }
 
   switch (w) {
-    case 0: pd_body<0, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
-    case 1: pd_body<1, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
-    case 2: pd_body<2, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
-    default: pd_body<3, G>(p, src, L, lane, m0, n0, nsteps, tile, sl); break;
+    case 0: pd_body<0, G>(p, src, L, lane, m0, n0, nsteps, xtile, sl, cnt); break;
+    case 1: pd_body<1, G>(p, src, L, lane, m0, n0, nsteps, xtile, sl, cnt); break;
+    case 2: pd_body<2, G>(p, src, L, lane, m0, n0, nsteps, xtile, sl, cnt); break;
+    default: pd_body<3, G>(p, src, L, lane, m0, n0, nsteps, xtile, sl, cnt); break;
+  }
+}
+
+template <bool G>
+__global__ void __launch_bounds__(256) prefill_dma_kernel(PdArgs p) {
+  __shared__ PdLds L;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
+  // Workgroups are dispatched to the 8 XCDs round-robin by id, so consecutive
+  // logical ids of one XCD cover all m tiles of consecutive n tiles (the
+  // weight tile is then fetched into that XCD's L2 once), and the slices of a
+  // split tile sit on one XCD.  The whole tiles come first in the launch (the
+  // split ones fill the round after them), each part remapped on its own.
+  const int nwg = (int)gridDim.x, b = (int)blockIdx.x;
+  const int groups = (int)(p.k / kPdGroupK);
+  const int nwhole = (G || p.sk_tail == 0) ? nwg : p.sk_dp;
+  if (b < nwhole) {
+    int id = b;
+    if ((nwhole & 7) == 0) id = (b & 7) * (nwhole >> 3) + (b >> 3);
+    pd_tile<G>(p, L, tid, lane, w, id, 0, groups, 0, 0, 1);
+    return;
+  }
+  if constexpr (!G) {
+    // A slice of a split tile: split tile xt, slice sl of sk_c, groups [g0, g1).
+    const int nb = nwg - nwhole;
+    int j = b - nwhole;
+    if ((nb & 7) == 0) j = (j & 7) * (nb >> 3) + (j >> 3);
+    const int xt = j / p.sk_c, sl = j - xt * p.sk_c;
+    const int g0 = (int)((int64_t)sl * groups / p.sk_c), g1 = (int)((int64_t)(sl + 1) * groups / p.sk_c);
+    pd_tile<false>(p, L, tid, lane, w, p.sk_dp + xt, g0, g1, xt, sl, p.sk_c);
   }
 }
 
@@ -689,31 +717,41 @@ bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) {
   return m > 0 && n > 0 && k > 0 && k % kPdGroupK == 0 && k < ((int64_t)1 << 24);
 }
 
-// K slices for a tile count that leaves CUs idle (each slice at least one
-// 256-element group):
-//   * at most 128 tiles: as many slices as keep the workgroups within one
-//     round of 256 (at most 4);
-//   * 257 to 384 tiles (a second round of 256 mostly idle): 2 slices, three
-//     rounds of half the work instead of two of the whole (the down
-//     projection 5120 x 17408 at M = 2048: 304 tiles);
-//   * otherwise 1.
-int prefill_split_slices(int64_t m, int64_t n, int64_t k) {
-  if (!prefill_dma_supported(m, n, k)) return 1;
-  const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM);
-  int64_t s = 1;
-  if (tiles <= 128)
-    s = 256 / tiles > 4 ? 4 : 256 / tiles;
-  else if (tiles > 256 && tiles <= 384)
-    s = 2;
-  const int64_t groups = k / kPdGroupK;
-  return (int)(s > groups ? groups : s);
+// Split plan for a tile count that leaves CUs idle:
+//   * at most 128 tiles: every tile split into min(4, 256 / tiles) slices, so
+//     that the workgroups stay within one round of 256;
+//   * 257 to 384 tiles (a second round of 256 mostly idle; the down projection
+//     5120 x 17408 at M = 2048 has 304): the first 256 tiles whole, then each
+//     of the remaining tiles in 256 / (tiles - 256) slices, so that the second
+//     round is full of workgroups with a fraction of a tile's work each;
+//   * otherwise none.
+// Each slice at least one 256-element group; no plan when no tile is split.
+PdSplit prefill_split(int64_t m, int64_t n, int64_t k) {
+  PdSplit sp;
+  if (!prefill_dma_supported(m, n, k)) return sp;
+  const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM), groups = k / kPdGroupK;
+  int64_t dp, c;
+  if (tiles <= 128) {
+    dp = 0;
+    c = 256 / tiles > 4 ? 4 : 256 / tiles;
+  } else if (tiles > 256 && tiles <= 384) {
+    dp = 256;
+    c = 256 / (tiles - 256);
+  } else {
+    return sp;
+  }
+  c = c > groups ? groups : c;
+  if (c < 2) return sp;
+  sp.dp = (int)dp;
+  sp.tail = (int)(tiles - dp);
+  sp.c = (int)c;
+  return sp;
 }
 
 int64_t prefill_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  const int s = prefill_split_slices(m, n, k);
-  if (s <= 1) return 0;
-  const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM);
-  return kSkinnyCounterBytes + s * tiles * kPdPartBytes;
+  const PdSplit sp = prefill_split(m, n, k);
+  if (sp.c < 2) return 0;
+  return kSkinnyCounterBytes + (int64_t)sp.tail * sp.c * kPdPartBytes;
 }
 
 void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
@@ -722,14 +760,14 @@ void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, cons
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = (m + kPdBM - 1) / kPdBM;
   const int64_t need = prefill_workspace_bytes(m, n, k);
   if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
-    // Split K (at most 384 tiles, within the 4096 counters: one launch).  The
+    // Split tiles (at most 128, within the 4096 counters: one launch).  The
     // workspace starts with the arrival counters (zero, and left zero by every
     // launch), then the partial tiles.
-    const int sl = prefill_split_slices(m, n, k);
-    const PdArgs a{x, m, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, nullptr, 0, 0, 0, sl,
-                   reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes),
+    const PdSplit sp = prefill_split(m, n, k);
+    const PdArgs a{x, m, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, nullptr, 0, 0, 0, sp.dp,
+                   sp.tail, sp.c, reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes),
                    static_cast<uint32_t*>(workspace)};
-    prefill_dma_kernel<false><<<dim3((unsigned)(n_tiles * m_tiles * sl)), 256, 0, s>>>(a);
+    prefill_dma_kernel<false><<<dim3((unsigned)(sp.dp + sp.tail * sp.c)), 256, 0, s>>>(a);
     return;
   }
   // One launch covers up to 2^31 - 1 workgroups; larger m is split by row.
@@ -738,7 +776,7 @@ void launch_prefill_dma(const uint16_t* x, int64_t m, int64_t n, int64_t k, cons
     const int64_t mt = m_tiles - t0 < max_m_tiles ? m_tiles - t0 : max_m_tiles;
     const int64_t mm = (m - t0 * kPdBM) < mt * kPdBM ? (m - t0 * kPdBM) : mt * kPdBM;
     const PdArgs a{x + t0 * kPdBM * k, mm, n, k, packed, scales, tscale, y + t0 * kPdBM * n, (int)n_tiles, (int)mt,
-                   nullptr, 0, 0, 0, 1, nullptr, nullptr};
+                   nullptr, 0, 0, 0, 0, 0, 0, nullptr, nullptr};
     prefill_dma_kernel<false><<<dim3((unsigned)(n_tiles * mt)), 256, 0, s>>>(a);
   }
 }
@@ -760,7 +798,7 @@ void launch_prefill_grouped(const uint16_t* x, int64_t topk, const int32_t* grou
                             uint16_t* y, hipStream_t s) {
   const int64_t n_tiles = (n + kPdBN - 1) / kPdBN, m_tiles = prefill_grouped_tile_bound(pairs, experts);
   const PdArgs a{x, pairs, n, k, packed, scales, tscale, y, (int)n_tiles, (int)m_tiles, groups, topk, experts,
-                 n * (k >> 1), 1, nullptr, nullptr};
+                 n * (k >> 1), 0, 0, 0, nullptr, nullptr};
   prefill_dma_kernel<true><<<dim3((unsigned)(n_tiles * m_tiles)), 256, 0, s>>>(a);
 }
 

@@ -77,11 +77,11 @@ def test_linear_workspace_bytes(L):
     wb = L.nvfp4_linear_workspace_bytes
     assert wb(1, 5120, 5120) == 0            # GEMV: no workspace
     # prefill GEMM: K split only while the 128 x 272 tiles leave CUs idle (at most 128 tiles, or 257..384): the
-    # counter region + slices x tiles x 139,264-byte FP32 partial tiles
+    # counter region + slices x split tiles x 139,264-byte FP32 partial tiles
     assert wb(65, 17408, 5120) == 16384 + 4 * 64 * 139264        # 64 tiles, 4 slices
     assert wb(512, 5120, 17408) == 16384 + 3 * 76 * 139264       # 76 tiles, 3 slices
     assert wb(512, 17408, 5120) == 0                              # 256 tiles fill the chip
-    assert wb(2048, 5120, 17408) == 16384 + 2 * 304 * 139264      # 304 tiles: 2 slices, 3 rounds of half the work
+    assert wb(2048, 5120, 17408) == 16384 + 5 * 48 * 139264       # 304 tiles: 256 whole, 48 split in 5 slices
     assert wb(2048, 17408, 5120) == 0                             # 1024 tiles
     assert wb(65, 17408, 5136) == 0                               # K not a multiple of 256: other kernel
     assert wb(8, 17408, 5120) == 0           # small-M, 68 rows x 1 K slice per workgroup

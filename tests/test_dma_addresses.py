@@ -85,3 +85,68 @@ def test_replay_catches_a_planted_overrun():
     with pytest.raises(AssertionError):
         prefill_dma_check(129, 545, 256, clamp=False)
     prefill_dma_check(129, 545, 256, clamp=True)
+
+
+# ---------------------------------------------------------------------------
+# The launch's tile mapping with split tiles (csrc/prefill.hip, prefill_split and
+# the head of prefill_dma_kernel), written out: every output tile is computed
+# over the whole K exactly once (whole, or as slices that partition its K
+# groups), and every split tile's slot and counter indices stay inside the
+# workspace the plan sizes.
+# ---------------------------------------------------------------------------
+def prefill_split_plan(m, n, k):
+    tiles = _cdiv(n, BN) * _cdiv(m, BM)
+    groups = k // GK
+    if tiles <= 128:
+        dp, c = 0, min(4, 256 // tiles)
+    elif 256 < tiles <= 384:
+        dp, c = 256, 256 // (tiles - 256)
+    else:
+        return None
+    c = min(c, groups)
+    if c < 2:
+        return None
+    return dp, tiles - dp, c
+
+
+def _remap(b, n):
+    return (b & 7) * (n >> 3) + (b >> 3) if n % 8 == 0 else b
+
+
+def prefill_split_cover(m, n, k):
+    tiles, groups = _cdiv(n, BN) * _cdiv(m, BM), k // GK
+    dp, tail, c = prefill_split_plan(m, n, k)
+    grid = dp + tail * c
+    cover = np.zeros((tiles, groups), dtype=np.int64)
+    slots = set()
+    for b in range(grid):
+        if b < dp:
+            cover[_remap(b, dp), :] += 1
+            continue
+        j = _remap(b - dp, grid - dp)
+        xt, sl = j // c, j % c
+        g0, g1 = sl * groups // c, (sl + 1) * groups // c
+        assert 0 <= xt < tail and 0 <= sl < c and g1 > g0
+        cover[dp + xt, g0:g1] += 1
+        assert (xt, sl) not in slots
+        slots.add((xt, sl))
+        assert 4 * xt + 4 <= 16384                                  # counter inside the counter region
+        assert (xt * c + sl + 1) * 139264 <= tail * c * 139264      # partial tile inside the workspace
+    assert (cover == 1).all(), (m, n, k)
+    return dp, tail, c
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 5120, 17408), (512, 5120, 17408), (65, 17408, 5120), (200, 560, 768),
+                                   (129, 545, 256 * 3), (4000, 2200, 512), (2049, 5120, 1024)])
+def test_prefill_split_tiles_cover_k_once(m, n, k):
+    plan = prefill_split_plan(m, n, k)
+    if plan is None:
+        pytest.skip("no split for this shape")
+    prefill_split_cover(m, n, k)
+
+
+def test_prefill_split_plan_shapes():
+    assert prefill_split_plan(2048, 5120, 17408) == (256, 48, 5)    # 304 tiles
+    assert prefill_split_plan(512, 5120, 17408) == (0, 76, 3)
+    assert prefill_split_plan(512, 17408, 5120) is None             # 256 tiles fill a round
+    assert prefill_split_plan(2048, 17408, 5120) is None            # 1024 tiles

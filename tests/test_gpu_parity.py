@@ -1028,6 +1028,27 @@ def test_graph_keeps_binding_workspace_after_growth(nv):
 # Kernel-native layout (nvfp4_prepare): conversion bit-exact against the layout
 # oracle, dequant bit-exact against the weight oracle, and the small-M linear
 # on the prepared weight within the linear's tolerance.
+# Prefill tile counts past a whole round of 256 (257..384 tiles: 256 whole tiles,
+# then the rest split along K, launched after them): the whole output against
+# the oracle, the same bits on a second call, and the unsplit call (no
+# workspace) within the same tolerance.
+@pytest.mark.parametrize("m,n,k", [(4000, 2200, 512), (2049, 5120, 1024)])
+def test_prefill_whole_then_split_tiles(nv, m, n, k):
+    w = WL.normal_bf16((n, k), 0.02, 7900 + n)
+    x = WL.normal_bf16((m, k), 1.0, 7950 + m)
+    (packed, scales, tscale), rq = q_both(nv, w)
+    y_ref, bound = O.linear_ref(x, *rq)
+    xd = to_dev_bf16(x)
+    need = nv.lib().nvfp4_linear_workspace_bytes(m, n, k)
+    assert need > 0, "this shape takes the split"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y1 = bf16_host(nv.linear(xd, packed, scales, tscale, workspace=ws))
+    check_linear(y1, y_ref, bound, f"prefill split m={m} n={n} k={k}")
+    assert np.array_equal(bf16_host(nv.linear(xd, packed, scales, tscale, workspace=ws)), y1)
+    y0 = bf16_host(nv.linear(xd, packed, scales, tscale, workspace=None))
+    check_linear(y0, y_ref, bound, f"prefill unsplit m={m} n={n} k={k}")
+
+
 # ---------------------------------------------------------------------------
 from oracle import layout_oracle as LO  # noqa: E402
 
