@@ -720,28 +720,29 @@ bool prefill_dma_supported(int64_t m, int64_t n, int64_t k) {
 // Split plan for a tile count that leaves CUs idle:
 //   * at most 128 tiles: every tile split into min(4, 256 / tiles) slices, so
 //     that the workgroups stay within one round of 256;
-//   * 257 to 384 tiles (a second round of 256 mostly idle; the down projection
-//     5120 x 17408 at M = 2048 has 304): the first 256 tiles whole, then each
-//     of the remaining tiles in 256 / (tiles - 256) slices, so that the second
-//     round is full of workgroups with a fraction of a tile's work each;
+//   * q whole rounds of 256 tiles and r <= 128 more (the down projection
+//     5120 x 17408 at M = 2048 has 304 = 256 + 48): the 256 q tiles whole, then
+//     each of the r others in min(8, 256 / r) slices, so that the last round
+//     is full of workgroups with a fraction of a tile's work each;
 //   * otherwise none.
 // Each slice at least one 256-element group; no plan when no tile is split.
 PdSplit prefill_split(int64_t m, int64_t n, int64_t k) {
   PdSplit sp;
   if (!prefill_dma_supported(m, n, k)) return sp;
   const int64_t tiles = ((n + kPdBN - 1) / kPdBN) * ((m + kPdBM - 1) / kPdBM), groups = k / kPdGroupK;
+  const int64_t r = tiles % 256;
   int64_t dp, c;
   if (tiles <= 128) {
     dp = 0;
     c = 256 / tiles > 4 ? 4 : 256 / tiles;
-  } else if (tiles > 256 && tiles <= 384) {
-    dp = 256;
-    c = 256 / (tiles - 256);
+  } else if (tiles > 256 && r > 0 && r <= 128) {
+    dp = tiles - r;
+    c = 256 / r > 8 ? 8 : 256 / r;
   } else {
     return sp;
   }
   c = c > groups ? groups : c;
-  if (c < 2) return sp;
+  if (c < 2 || dp > ((int64_t)1 << 30)) return sp;
   sp.dp = (int)dp;
   sp.tail = (int)(tiles - dp);
   sp.c = (int)c;

@@ -97,10 +97,11 @@ def test_replay_catches_a_planted_overrun():
 def prefill_split_plan(m, n, k):
     tiles = _cdiv(n, BN) * _cdiv(m, BM)
     groups = k // GK
+    r = tiles % 256
     if tiles <= 128:
         dp, c = 0, min(4, 256 // tiles)
-    elif 256 < tiles <= 384:
-        dp, c = 256, 256 // (tiles - 256)
+    elif tiles > 256 and 0 < r <= 128:
+        dp, c = tiles - r, min(8, 256 // r)
     else:
         return None
     c = min(c, groups)
@@ -137,7 +138,8 @@ def prefill_split_cover(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(2048, 5120, 17408), (512, 5120, 17408), (65, 17408, 5120), (200, 560, 768),
-                                   (129, 545, 256 * 3), (4000, 2200, 512), (2049, 5120, 1024)])
+                                   (129, 545, 256 * 3), (4000, 2200, 512), (2049, 5120, 1024), (3500, 5120, 2048),
+                                   (4200, 5120, 512), (8192, 5120, 17408)])
 def test_prefill_split_tiles_cover_k_once(m, n, k):
     plan = prefill_split_plan(m, n, k)
     if plan is None:
@@ -150,3 +152,6 @@ def test_prefill_split_plan_shapes():
     assert prefill_split_plan(512, 5120, 17408) == (0, 76, 3)
     assert prefill_split_plan(512, 17408, 5120) is None             # 256 tiles fill a round
     assert prefill_split_plan(2048, 17408, 5120) is None            # 1024 tiles
+    assert prefill_split_plan(8192, 5120, 17408) is None            # 1216 tiles: 4 rounds and 192 more
+    assert prefill_split_plan(3500, 5120, 2048) == (512, 20, 8)     # 532 tiles: 2 rounds and 20 more
+    assert prefill_split_plan(4200, 5120, 512) == (512, 115, 2)     # 627 tiles: 2 rounds and 115 more

@@ -1025,14 +1025,12 @@ def test_graph_keeps_binding_workspace_after_growth(nv):
 
 
 # ---------------------------------------------------------------------------
-# Kernel-native layout (nvfp4_prepare): conversion bit-exact against the layout
-# oracle, dequant bit-exact against the weight oracle, and the small-M linear
-# on the prepared weight within the linear's tolerance.
-# Prefill tile counts past a whole round of 256 (257..384 tiles: 256 whole tiles,
-# then the rest split along K, launched after them): the whole output against
-# the oracle, the same bits on a second call, and the unsplit call (no
-# workspace) within the same tolerance.
-@pytest.mark.parametrize("m,n,k", [(4000, 2200, 512), (2049, 5120, 1024)])
+# Prefill tile counts a little past whole rounds of 256 (q rounds and r <= 128
+# more: 256 q whole tiles, then the rest split along K, launched after them):
+# the whole output against the oracle, the same bits on a second call, and the
+# unsplit call (no workspace) within the same tolerance.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k", [(4000, 2200, 512), (2049, 5120, 1024), (3500, 5120, 2048)])
 def test_prefill_whole_then_split_tiles(nv, m, n, k):
     w = WL.normal_bf16((n, k), 0.02, 7900 + n)
     x = WL.normal_bf16((m, k), 1.0, 7950 + m)
@@ -1049,6 +1047,10 @@ def test_prefill_whole_then_split_tiles(nv, m, n, k):
     check_linear(y0, y_ref, bound, f"prefill unsplit m={m} n={n} k={k}")
 
 
+# ---------------------------------------------------------------------------
+# Kernel-native layout (nvfp4_prepare): conversion bit-exact against the layout
+# oracle, dequant bit-exact against the weight oracle, and the small-M linear
+# on the prepared weight within the linear's tolerance.
 # ---------------------------------------------------------------------------
 from oracle import layout_oracle as LO  # noqa: E402
 
