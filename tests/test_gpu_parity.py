@@ -140,6 +140,37 @@ def test_quantize_dequant_bit_exact_crafted(nv):
         _quant_compare(nv, w, name)
 
 
+def test_quantize_ws_ignores_workspace_contents(nv):
+    """nvfp4_quantize_ws writes its partial maxima before reading them: a workspace full of 0xFF bytes (and one
+    holding a previous call's maxima of a larger tensor) gives the same bits as the three-launch form."""
+    w_big = WL.normal_bf16((1000, 4096), 0.5, 8101)
+    w = WL.normal_bf16((300, 1040), 0.02, 8102)
+    ws = torch.full((nv.lib().nvfp4_quantize_workspace_bytes(),), 0xFF, dtype=torch.uint8, device="cuda")
+    for src in (w, w_big, w):
+        wd = to_dev_bf16(src)
+        a = nv.quantize(wd, workspace=ws)
+        b = nv.quantize(wd, workspace=None)
+        assert all(torch.equal(u, v) for u, v in zip(a, b))
+
+
+def test_quantize_then_split_linear_share_a_stream(nv):
+    """The binding's quantizer and split-K linear workspaces on one stream: a quantize between two split-K calls
+    leaves the second one's arrival counters at zero (it has its own buffer), so both calls give the same bits as
+    a call on a fresh zeroed workspace."""
+    m, n, k = 8, 512, 17408
+    w = WL.normal_bf16((n, k), 0.02, 8103)
+    x = to_dev_bf16(WL.normal_bf16((m, k), 1.0, 8104))
+    packed, scales, tscale = nv.quantize(to_dev_bf16(w))
+    need = nv.lib().nvfp4_linear_workspace_bytes(m, n, k)
+    assert need > 0, "this shape splits K"
+    fresh = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    want = bf16_host(nv.linear(x, packed, scales, tscale, workspace=fresh))
+    y1 = bf16_host(nv.linear(x, packed, scales, tscale))
+    nv.quantize(to_dev_bf16(WL.normal_bf16((64, 4096), 1.0, 8105)))
+    y2 = bf16_host(nv.linear(x, packed, scales, tscale))
+    assert np.array_equal(y1, want) and np.array_equal(y2, want)
+
+
 def test_quantize_crafted_ties_tiled(nv):
     """The crafted tie rows tiled to 640 x 1024, so that most blocks take the quantize kernel's whole-iteration
     path (the small crafted cases above take only its guarded tail); also as NVFP4 x NVFP4 activations, with
