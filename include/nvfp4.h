@@ -141,16 +141,19 @@ nvfp4_status nvfp4_linear(const uint16_t* x, int64_t m, int64_t n, int64_t k,
 
 /*
  * The linear with a caller-provided workspace (same model card and page as
- * nvfp4_linear).  For 2 <= m <= 64 the small-M kernel can then split K across
- * workgroups: each workgroup writes FP32 partial sums of its K slice to the
- * workspace, and the last workgroup of each row block to finish adds the
- * slices in slice order and writes y.  The result is therefore the same bits
- * on every run, but may differ in the last FP32 bits from nvfp4_linear's
- * unsplit summation.
+ * nvfp4_linear).  Two kernels can then split K across workgroups: the small-M
+ * kernel (2 <= m <= 64) when its row blocks alone would not fill the device,
+ * and the prefill GEMM when its 128 x 272 tiles would leave CUs idle (at most
+ * 128 tiles, or up to 128 tiles past whole rounds of 256: those tiles only).
+ * Each workgroup writes the FP32 partial sums of its K slice to the workspace,
+ * and the last workgroup of each row block or tile to finish adds the slices
+ * in slice order and writes y.  The result is therefore the same bits on every
+ * run, but may differ in the last FP32 bits from nvfp4_linear's unsplit
+ * summation.
  *
  * nvfp4_linear_workspace_bytes(m, n, k) returns the bytes this shape can use:
- * 0 when the chosen kernel needs none (m = 1, m > 64, or no split), -1 for an
- * invalid shape.  It makes no HIP call.
+ * 0 when the chosen kernel needs none (m = 1, or no split), -1 for an invalid
+ * shape.  It makes no HIP call.
  *
  * Workspace contract:
  *   - a device pointer, 16-byte aligned, not overlapping any argument buffer;
@@ -180,10 +183,12 @@ nvfp4_status nvfp4_linear_ws(const uint16_t* x, int64_t m, int64_t n, int64_t k,
  * GPU, held until the process ends; its address is looked up once per device,
  * on the first call with that device current, which also clears its counter
  * region with a kernel on `stream`.  No call allocates or frees memory.
- * Same arguments, results (bit for bit those of nvfp4_linear_ws with a
- * workspace of at least nvfp4_linear_workspace_bytes(m, n, k) bytes) and
- * errors as nvfp4_linear; a shape whose workspace would exceed the array
- * returns NVFP4_ERR_SHAPE, and a failed address lookup NVFP4_ERR_DEVICE.
+ * Same arguments and errors as nvfp4_linear; results bit for bit those of
+ * nvfp4_linear_ws with a workspace of at least nvfp4_linear_workspace_bytes(m,
+ * n, k) bytes for m <= 64, and those of nvfp4_linear (unsplit) for the prefill
+ * GEMM, whose split needs more than the array holds.  A shape whose workspace
+ * would exceed the array returns NVFP4_ERR_SHAPE, and a failed address lookup
+ * NVFP4_ERR_DEVICE.
  * Every call on one GPU shares that GPU's array and leaves its counters at
  * zero: calls that may overlap on one GPU (other streams, other threads)
  * race and must not be issued.
