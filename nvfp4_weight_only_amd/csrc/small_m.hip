@@ -408,43 +408,53 @@ __global__ void __launch_bounds__(64 * W) gemv_prepared_kernel(const uint16_t* _
 
 // ---------------------------------------------------------------------------
 // The kernel-native layout: conversion from the checkpoint layout and the
-// dequantizer that reads it.  One thread per 16 output bytes of a 1152-byte
-// (tile, quad) block: units 0..63 are the packed slots, 64..71 four scale
-// words each.  Rows past n are zero.
+// dequantizer that reads it.
+//
+// Conversion: one wavefront per (tile, quad) block.  Lane (r, c) = (lane / 4,
+// lane % 4) loads bytes 16 c .. 16 c + 16 of row 16 t + r's 64-byte quad
+// segment: word g of those 16 bytes is word i = c of slot 16 g + r.  The words
+// go through the wavefront's own LDS area to their slots, and lane u stores
+// slot u: the block's first kilobyte in one 16-byte-per-lane instruction.
+// Lanes 0..15 load row r's 8 scale bytes and store its two scale words
+// (bytes 0, 2, 4, 6 and 1, 3, 5, 7).  A workgroup's four wavefronts take four
+// consecutive quads of one tile, so the row segments they read complete each
+// other's lines.  Rows past n are zero.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) prepare_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales, int64_t n, int64_t k,
-                                                      int64_t blocks, uint8_t* __restrict__ out) {
-  const int64_t tiles = (n + 15) >> 4, kh = k >> 1, ks = k >> 4;
-  const int64_t units = blocks * 72;
-  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < units;
-       id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = id / 72, q = b / tiles, t = b - q * tiles;  // block b = q * tiles + t
-    const int u = (int)(id - b * 72);
+                                                      uint8_t* __restrict__ out) {
+  __shared__ uint32_t tr[4][256];  // per wavefront: word (row r, slot group g, word c) at (4 r + g) * 4 + c
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t tiles = (n + 15) >> 4, quads = k / kSmQuadK, kh = k >> 1, ks = k >> 4;
+  const int64_t qgroups = (quads + 3) >> 2, jobs = tiles * qgroups;
+  const int r = lane >> 2, c = lane & 3;
+  for (int64_t job = blockIdx.x; job < jobs; job += gridDim.x) {
+    const int64_t t = job / qgroups, q = 4 * (job - t * qgroups) + w;
+    if (q >= quads) continue;  // uniform per wavefront; no workgroup barrier below
+    const int64_t row = t * 16 + r;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (u < 64) {
-      const int g = u >> 4, r = u & 15;
-      const int64_t row = t * 16 + r;
-      if (row < n) {
-        const uint8_t* src = packed + row * kh + q * 64 + 4 * g;
-        v = make_uint4(*reinterpret_cast<const uint32_t*>(src), *reinterpret_cast<const uint32_t*>(src + 16),
-                       *reinterpret_cast<const uint32_t*>(src + 32), *reinterpret_cast<const uint32_t*>(src + 48));
-      }
-    } else {
-      uint32_t wv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int word = 4 * (u - 64) + j, h = word >> 4, r = word & 15;
-        const int64_t row = t * 16 + r;
-        wv[j] = 0u;
-        if (row < n) {
-          const uint2 s8 = *reinterpret_cast<const uint2*>(scales + row * ks + q * 8);
-          wv[j] = __builtin_amdgcn_perm(s8.y, s8.x, h ? 0x07050301u : 0x06040200u);
-        }
-      }
-      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    if (row < n) v = *reinterpret_cast<const uint4*>(packed + row * kh + q * 64 + 16 * c);
+    tr[w][(4 * r + 0) * 4 + c] = v.x;
+    tr[w][(4 * r + 1) * 4 + c] = v.y;
+    tr[w][(4 * r + 2) * 4 + c] = v.z;
+    tr[w][(4 * r + 3) * 4 + c] = v.w;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int g2 = lane >> 4, r2 = lane & 15;  // this lane's slot 16 g2 + r2
+    const uint4 o = *reinterpret_cast<const uint4*>(&tr[w][(4 * r2 + g2) * 4]);
+    uint8_t* blk = out + (q * tiles + t) * (int64_t)kSmBlock;
+    *reinterpret_cast<uint4*>(blk + 16 * lane) = o;
+    if (lane < 16) {
+      const int64_t srow = t * 16 + lane;
+      uint2 s8 = make_uint2(0u, 0u);
+      if (srow < n) s8 = *reinterpret_cast<const uint2*>(scales + srow * ks + q * 8);
+      uint32_t* sw = reinterpret_cast<uint32_t*>(blk + 1024);
+      sw[lane] = __builtin_amdgcn_perm(s8.y, s8.x, 0x06040200u);
+      sw[16 + lane] = __builtin_amdgcn_perm(s8.y, s8.x, 0x07050301u);
     }
-    *reinterpret_cast<uint4*>(out + b * kSmBlock + 16 * u) = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the area is rewritten by the next block
   }
 }
 
@@ -517,8 +527,8 @@ int64_t sm_max_tiles(int64_t n, int64_t rows) {
 int64_t prepared_bytes(int64_t n, int64_t k) { return sm_ceil_div(n, 16) * (k / kSmQuadK) * kSmBlock; }
 
 void launch_prepare(const uint8_t* packed, const uint8_t* scales, int64_t n, int64_t k, uint8_t* out, hipStream_t s) {
-  const int64_t blocks = sm_ceil_div(n, 16) * (k / kSmQuadK);
-  prepare_kernel<<<sm_grid(blocks * 72, 1 << 20), 256, 0, s>>>(packed, scales, n, k, blocks, out);
+  const int64_t jobs = sm_ceil_div(n, 16) * sm_ceil_div(k / kSmQuadK, 4);  // (tile, four quads) per workgroup
+  prepare_kernel<<<(unsigned)(jobs < (1 << 20) ? jobs : (1 << 20)), 256, 0, s>>>(packed, scales, n, k, out);
 }
 
 void launch_dequant_prepared(const uint8_t* prep, const float* tscale, int64_t n, int64_t k, uint16_t* out,
