@@ -153,6 +153,22 @@ def test_quantize_ws_ignores_workspace_contents(nv):
         assert all(torch.equal(u, v) for u, v in zip(a, b))
 
 
+@pytest.mark.parametrize("n,k", [(4096, 4096), (4353, 4096), (5120, 5120)])
+def test_quantize_ws_amax_at_either_end(nv, n, k):
+    """The amax pass of nvfp4_quantize_ws sees the first and the last element: a spike placed at either end sets
+    the tensor scale.  4096 x 4096 fills its 1,024 workgroups' loads exactly once; the two larger shapes take a
+    second, partial pass (4353 x 4096: its last load vector ends inside a workgroup's share)."""
+    base = WL.weight_plain(n, k)
+    for where, val in (((n - 1, k - 1), 300.0), ((0, 0), -400.0)):
+        w = base.copy()
+        w[where] = WL.bf16_bits_from_f32(np.array([val], dtype=np.float32))[0]
+        log(f"quantize_ws amax spike {val} at {where}, {n}x{k}")
+        _, _, tscale = nv.quantize(to_dev_bf16(w))
+        want = O.tensor_scale(O.tensor_amax(w))
+        assert float(O.tensor_amax(w)) == abs(val)
+        assert tscale.cpu().numpy()[0].view(np.uint32) == np.float32(want).view(np.uint32)
+
+
 def test_quantize_then_split_linear_share_a_stream(nv):
     """The binding's quantizer and split-K linear workspaces on one stream: a quantize between two split-K calls
     leaves the second one's arrival counters at zero (it has its own buffer), so both calls give the same bits as
