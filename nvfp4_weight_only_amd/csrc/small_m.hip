@@ -135,6 +135,80 @@ __device__ __forceinline__ void sm_store_y(const SmArgs& p, f32x4_t v, int64_t t
   }
 }
 
+// End of a small-M workgroup: the eight wavefronts' sums of each (row tile,
+// m tile) pair meet in red (kSmWaves * T * NMT * 64 entries) and are added
+// in wavefront order by wavefront pair % 8; then y, or with several K slices
+// the workspace exchange.
+template <int NMT, int T>
+__device__ __forceinline__ void sm_finish(const SmArgs& p, f32x4_t (&acc)[T][NMT], f32x4_t* red, int w,
+                                          int lane, int64_t tile0, int64_t row0, int64_t row_end, int rb,
+                                          int sl) {
+  constexpr int NP = T * NMT;  // (row tile, m tile) pairs
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) red[((w * T + t) * NMT + mt) * 64 + lane] = acc[t][mt];
+  __syncthreads();
+  constexpr int PPW = (NP + kSmWaves - 1) / kSmWaves;  // pairs per wavefront (1 or 2)
+  f32x4_t sum[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    sum[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (pi < NP) {
+#pragma unroll
+      for (int ww = 0; ww < kSmWaves; ++ww) sum[i] += red[(ww * NP + pi) * 64 + lane];
+    }
+  }
+  auto pair_rows = [&](int pi, int64_t& tile_row, int64_t& gm) {
+    tile_row = (tile0 + pi / NMT) * 16;
+    gm = 16 * (pi % NMT) + (lane & 15);
+  };
+  if (p.slices == 1) {
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int pi = w + kSmWaves * i;
+      if (pi < NP) {
+        int64_t tr, gm;
+        pair_rows(pi, tr, gm);
+        sm_store_y(p, sum[i], tr, row0, row_end, gm, lane);
+      }
+    }
+    return;
+  }
+
+  // Several K slices: this slice's sums go to the workspace, then the
+  // workgroups of the row block meet at the arrival counter (splitk_arrive);
+  // the last one adds the slices in slice order and stores y.
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    if (pi < NP) {
+      int64_t tr, gm;
+      pair_rows(pi, tr, gm);
+      const int64_t n0 = tr + 4 * (lane >> 4);
+      if (gm < p.m && n0 >= row0 && n0 < row_end)
+        splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, sum[i]);
+    }
+  }
+  if (!splitk_arrive(p.count + rb, p.slices)) return;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int pi = w + kSmWaves * i;
+    if (pi < NP) {
+      int64_t tr, gm;
+      pair_rows(pi, tr, gm);
+      const int64_t n0 = tr + 4 * (lane >> 4);
+      f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (gm < p.m && n0 >= row0 && n0 < row_end) {
+        for (int s = 0; s < p.slices; ++s)
+          v += s == sl ? sum[i] : splitk_load4(p.part + ((int64_t)s * p.m + gm) * p.npad + n0);
+      }
+      sm_store_y(p, v, tr, row0, row_end, gm, lane);
+    }
+  }
+}
+
 // NMT: MFMA m tiles (16 activation rows each; rows past m repeat the last one
 // and are never stored); T: tiles read per workgroup.
 template <int NMT, int T>
@@ -212,70 +286,165 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_kernel(SmArgs p) {
     if (j < nq) compute(xa, wa);
   }
 
-  // The eight wavefronts' sums of each (row tile, m tile) pair, added in
-  // wavefront order by wavefront pair % 8.
+  sm_finish<NMT, T>(p, acc, red, w, lane, tile0, row0, row_end, rb, sl);
+}
+
+// The same product with the activations staged through LDS.  Loaded straight
+// into MFMA fragments, a quad's activations take 16 rows x 64 bytes (half
+// cache lines) per instruction; here each wavefront copies its quad's MX rows
+// x 256 bytes into its own LDS area with global_load_lds_dwordx4, four whole
+// rows (eight cache lines) per instruction, and reads the fragments back with
+// 16-byte LDS reads.  Slot s of row r holds the row's 16-byte piece s ^ (r %
+// 16), so a fragment read (16 rows, one piece each) touches every 16-byte bank
+// group once.  Two areas per wavefront: quad j + 1 is copied while quad j's
+// products run.  Weights load into registers as above.  Only the wavefront
+// reads its own area, so the K loop has no barrier; the wait for a quad's copy
+// is a vmcnt that also covers its weight loads (loads complete in order).
+typedef __attribute__((address_space(3))) const void sm_lds_t;
+
+template <typename U>
+__device__ __forceinline__ uint32_t sm_lds_addr(const U* ptr) {
+  return (uint32_t)(uintptr_t)(const sm_lds_t*)ptr;
+}
+
+// 64 lanes x 16 bytes from per-lane global addresses to LDS bytes [lds, lds + 1024).
+__device__ __forceinline__ void sm_lds_dma16(const void* src, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);  // uniform per wavefront by construction
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void sm_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// MX: activation rows staged per quad (8, 16 or 32; m <= MX); T: tiles read
+// per workgroup.
+template <int MX, int T>
+__global__ void __launch_bounds__(64 * kSmWaves) small_m_xl_kernel(SmArgs p) {
+  constexpr int NMT = (MX + 15) / 16;
+  constexpr int D = MX / 4;         // copy instructions per quad (four rows each)
+  constexpr int XB = MX * 256;      // bytes of one quad's activations
+  constexpr int RING = kSmWaves * 2 * XB;
+  constexpr int RED = kSmWaves * T * NMT * 64 * 16;
+  __shared__ uint4 lds[(RING > RED ? RING : RED) / 16];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const unsigned id = blockIdx.x;
+  const unsigned lid = p.xcd_order ? (id & 7u) * (gridDim.x >> 3) + (id >> 3) : id;
+  const int rb = (int)(lid / (unsigned)p.slices), sl = (int)(lid % (unsigned)p.slices);
+  const int64_t row0 = (int64_t)rb * p.rows;
+  const int64_t row_end = row0 + p.rows < p.n ? row0 + p.rows : p.n;
+  const int64_t tile0 = row0 >> 4;
+  const int64_t tiles = (p.n + 15) >> 4;
+  const int64_t qstride = tiles * kSmBlock;
+  const int Q0 = (int)((int64_t)sl * p.quads / p.slices), Q1 = (int)((int64_t)(sl + 1) * p.quads / p.slices);
+  const int qw = Q0 + w;
+  const int nq = Q1 > qw ? (Q1 - qw + kSmWaves - 1) / kSmWaves : 0;
+
+  const uint8_t* tb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t ti = tile0 + t < tiles ? tile0 + t : tiles - 1;
+    tb[t] = p.prep + ti * (int64_t)kSmBlock;
+  }
+  // Copy sources: instruction d, lane l covers row r = 4 d + l / 16 (rows past
+  // m repeat row m - 1) and LDS slot l % 16, i.e. piece (l % 16) ^ (r % 16).
+  const uint16_t* xsrc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int r = 4 * d + (lane >> 4);
+    const int64_t gr = r < p.m ? r : p.m - 1;
+    xsrc[d] = p.x + gr * p.k + 8 * ((lane & 15) ^ (r & 15));
+  }
+  // Fragment reads: step i, m tile mt is row rr = 16 mt + lane % 16 (rows past
+  // m read row m - 1), piece 4 i + g, at slot (4 i + g) ^ (rr % 16).
+  uint32_t xoff[4][NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    int rr = 16 * mt + (lane & 15);
+    rr = rr < (int)p.m ? rr : (int)p.m - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xoff[i][mt] = (uint32_t)(rr * 256 + (((4 * i + g) ^ (rr & 15)) * 16));
+  }
+  const uint32_t area = sm_lds_addr(&lds[0]) + (uint32_t)(w * 2 * XB);
+  const char* lds_bytes = reinterpret_cast<const char*>(&lds[0]) + w * 2 * XB;
+
+  f32x4_t acc[T][NMT];
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) red[((w * T + t) * NMT + mt) * 64 + lane] = acc[t][mt];
-  __syncthreads();
-  constexpr int PPW = (NP + kSmWaves - 1) / kSmWaves;  // pairs per wavefront (1 or 2)
-  f32x4_t sum[PPW];
-#pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int pi = w + kSmWaves * i;
-    sum[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    if (pi < NP) {
-#pragma unroll
-      for (int ww = 0; ww < kSmWaves; ++ww) sum[i] += red[(ww * NP + pi) * 64 + lane];
-    }
-  }
-  auto pair_rows = [&](int pi, int64_t& tile_row, int64_t& gm) {
-    tile_row = (tile0 + pi / NMT) * 16;
-    gm = 16 * (pi % NMT) + (lane & 15);
-  };
-  if (p.slices == 1) {
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-      const int pi = w + kSmWaves * i;
-      if (pi < NP) {
-        int64_t tr, gm;
-        pair_rows(pi, tr, gm);
-        sm_store_y(p, sum[i], tr, row0, row_end, gm, lane);
-      }
-    }
-    return;
-  }
+    for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Several K slices: this slice's sums go to the workspace, then the
-  // workgroups of the row block meet at the arrival counter (splitk_arrive);
-  // the last one adds the slices in slice order and stores y.
+  if (nq > 0) {
+    SmW wa[T], wb[T];
+    auto load_w = [&](SmW* wq, int j) {
+      const int q = qw + kSmWaves * j;
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int pi = w + kSmWaves * i;
-    if (pi < NP) {
-      int64_t tr, gm;
-      pair_rows(pi, tr, gm);
-      const int64_t n0 = tr + 4 * (lane >> 4);
-      if (gm < p.m && n0 >= row0 && n0 < row_end)
-        splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, sum[i]);
-    }
-  }
-  if (!splitk_arrive(p.count + rb, p.slices)) return;
+      for (int t = 0; t < T; ++t) sm_load_w(wq[t], tb[t], qstride, q, lane);
+    };
+    auto copy_x = [&](int j, int buf) {
+      const int64_t q = qw + kSmWaves * j;
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int pi = w + kSmWaves * i;
-    if (pi < NP) {
-      int64_t tr, gm;
-      pair_rows(pi, tr, gm);
-      const int64_t n0 = tr + 4 * (lane >> 4);
-      f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if (gm < p.m && n0 >= row0 && n0 < row_end) {
-        for (int s = 0; s < p.slices; ++s)
-          v += s == sl ? sum[i] : splitk_load4(p.part + ((int64_t)s * p.m + gm) * p.npad + n0);
+      for (int d = 0; d < D; ++d) sm_lds_dma16(xsrc[d] + q * kSmQuadK, area + (uint32_t)(buf * XB + d * 1024));
+    };
+    // Quad j: weights in wq, activations in area buf.  In issue order, quad
+    // j's weight loads and copy precede quad j + 1's 2 T weight loads, so
+    // vmcnt(2 T) after those means quad j has landed; quad j + 1's copy (into
+    // the other area, whose reads finished in the previous step) follows.  The
+    // empty asm statements with a memory clobber keep the loads above the
+    // wait and the LDS reads below it.
+    auto step = [&](int j, const SmW* wq, SmW* wn, int buf) {
+      if (j + 1 < nq) {
+        load_w(wn, j + 1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        sm_wait_vmcnt<2 * T>();
+        __builtin_amdgcn_sched_barrier(0);
+        copy_x(j + 1, buf ^ 1);
+      } else {
+        sm_wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
       }
-      sm_store_y(p, v, tr, row0, row_end, gm, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      SmX<NMT> xq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+          xq.v[i][mt] = *reinterpret_cast<const uint4*>(lds_bytes + buf * XB + xoff[i][mt]);
+      __builtin_amdgcn_sched_barrier(0);  // all fragment reads in flight before the first product
+#pragma unroll
+      for (int t = 0; t < T; ++t) sm_quad<NMT>(wq[t], xq, acc[t]);
+    };
+    load_w(wa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_x(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    int j = 0;
+    for (; j + 1 < nq; j += 2) {
+      step(j, wa, wb, 0);
+      step(j + 1, wb, wa, 1);
     }
+    if (j < nq) step(j, wa, wb, 0);
+  }
+  // Every copy has landed (the last step waited for all loads); the areas
+  // become the reduction buffer once every wavefront is past its reads.
+  __syncthreads();
+  sm_finish<NMT, T>(p, acc, reinterpret_cast<f32x4_t*>(&lds[0]), w, lane, tile0, row0, row_end, rb, sl);
+}
+
+template <int MX>
+void launch_xl(const SmallMPlan& pl, const SmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(pl.row_blocks * pl.slices));
+  switch (pl.tiles) {
+    case 1: small_m_xl_kernel<MX, 1><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 2: small_m_xl_kernel<MX, 2><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 3: small_m_xl_kernel<MX, 3><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    case 4: small_m_xl_kernel<MX, 4><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
+    default: small_m_xl_kernel<MX, 5><<<grid, 64 * kSmWaves, 0, s>>>(a); break;
   }
 }
 
@@ -559,11 +728,12 @@ SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
     s = s < 1 ? 1 : s;
   }
   pl.slices = (int)s;
-  // Rows per workgroup: one workgroup per CU (or per half CU, ... when that
-  // needs more), a multiple of 4, covering at most five tiles.
+  // Rows per workgroup: at most 256 workgroups (one per CU; or per half CU,
+  // ... when that needs more), a multiple of 4, covering at most five tiles.
   int64_t rows = 0;
   for (int64_t per_cu = 1;; ++per_cu) {
-    rows = sm_round_up(sm_ceil_div(n * s, 256 * per_cu), 4);
+    const int64_t blocks = (256 * per_cu) / s;
+    rows = sm_round_up(sm_ceil_div(n, blocks > 1 ? blocks : 1), 4);
     if (sm_max_tiles(n, rows) <= 5) break;
   }
   pl.rows = (int)rows;
@@ -617,10 +787,18 @@ void launch_small_m(const SmallMPlan& pl, const uint16_t* x, int64_t m, int64_t 
     a.count = static_cast<uint32_t*>(workspace);
     a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkinnyCounterBytes);
   }
-  if (m <= 16)
+  // m > 16: activations through LDS (128 KiB per workgroup, so only where the
+  // plan has one workgroup per CU).  Measured against the register form on the
+  // 17408 x 5120 and 5120 x 17408 weights: M = 32 17.8 / 24.1 us against 20.2 /
+  // 27.7 us; at M = 8 the LDS form (8 rows) was slower, 13.7 / 16.4 against
+  // 13.0 / 15.9 us.
+  if (m > 16 && pl.row_blocks * pl.slices <= 256) {
+    launch_xl<32>(pl, a, s);
+  } else if (m <= 16) {
     launch_nmt<1>(pl, a, s);
-  else
+  } else {
     launch_nmt<2>(pl, a, s);
+  }
 }
 
 }  // namespace nvfp4

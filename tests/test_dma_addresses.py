@@ -155,3 +155,67 @@ def test_prefill_split_plan_shapes():
     assert prefill_split_plan(8192, 5120, 17408) is None            # 1216 tiles: 4 rounds and 192 more
     assert prefill_split_plan(3500, 5120, 2048) == (512, 20, 8)     # 532 tiles: 2 rounds and 20 more
     assert prefill_split_plan(4200, 5120, 512) == (512, 115, 2)     # 627 tiles: 2 rounds and 115 more
+
+
+# ---------------------------------------------------------------------------
+# Small-M kernel with activations staged through LDS (csrc/small_m.hip,
+# small_m_xl_kernel): each wavefront copies a quad's MX activation rows x 256
+# bytes into its own LDS area, instruction d and lane l covering row
+# r = 4 d + l / 16 (rows past m repeat row m - 1) at slot l % 16, which holds
+# the row's 16-byte piece (l % 16) ^ (r % 16); the fragment read of step i,
+# m tile mt by lane (c, g) = (l % 16, l / 16) takes row rr = min(16 mt + c,
+# m - 1) at slot (4 i + g) ^ (rr % 16).
+# ---------------------------------------------------------------------------
+SM_QUAD_K = 128
+
+
+def small_m_xl_check(m, k, mx):
+    """Replays one wavefront's copies and fragment reads for every quad: every copy source lies inside x [m, k],
+    every LDS byte written or read lies inside the wavefront's quad area, and each fragment read finds exactly
+    the 8 activations x[row, 128 q + 32 i + 8 g, + 8) that the MFMA step expects."""
+    assert 1 <= m <= mx and mx in (8, 16, 32) and k % SM_QUAD_K == 0
+    D, XB = mx // 4, mx * 256
+    nmt = (mx + 15) // 16
+    lane = np.arange(64)
+    quads = k // SM_QUAD_K
+    for q in range(quads):
+        area = {}                               # LDS byte offset in the area -> global element index
+        for d in range(D):
+            r = 4 * d + (lane >> 4)
+            gr = np.minimum(r, m - 1)
+            piece = (lane & 15) ^ (r & 15)
+            src = gr * k + 8 * piece + q * SM_QUAD_K          # element index of the lane's 16 bytes
+            assert src.min() >= 0 and (src + 8).max() <= m * k
+            dst = d * 1024 + 16 * lane
+            assert dst.min() >= 0 and (dst + 16).max() <= XB
+            for l in range(64):
+                area[int(dst[l])] = int(src[l])
+        for mt in range(nmt):
+            rr = np.minimum(16 * mt + (lane & 15), m - 1)
+            for i in range(4):
+                g = lane >> 4
+                off = rr * 256 + ((4 * i + g) ^ (rr & 15)) * 16
+                assert off.min() >= 0 and (off + 16).max() <= XB
+                want = rr * k + q * SM_QUAD_K + 32 * i + 8 * g
+                got = np.array([area[int(o)] for o in off])
+                assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("mx", [8, 16, 32])
+def test_small_m_xl_copies_and_reads(mx):
+    lo = {8: 1, 16: 9, 32: 17}[mx]
+    for m in sorted({lo, lo + 1, (lo + mx) // 2, mx - 1, mx}):
+        for k in (128, 384, 5120):
+            small_m_xl_check(m, k, mx)
+
+
+def test_small_m_xl_reads_hit_distinct_bank_groups():
+    """The 16 lanes of a fragment read that share g read 16 different rows at 16 different 16-byte slots of
+    their 256-byte rows: one pass of the LDS banks, no conflict."""
+    lane = np.arange(16)
+    for mt in range(2):
+        rr = 16 * mt + lane
+        for i in range(4):
+            for g in range(4):
+                slot = (4 * i + g) ^ (rr & 15)
+                assert len(set(slot.tolist())) == 16

@@ -1117,6 +1117,9 @@ def test_prepare_and_dequant_prepared_bit_exact(nv, n, k):
 
 PREP_LINEAR = [(1, 16, 128), (2, 100, 128), (8, 300, 1024), (16, 37, 384), (17, 64, 5120), (32, 300, 640),
                (5, 1000, 384), (8, 10240, 512), (3, 2000, 8192), (32, 68, 1280), (24, 700, 3072),
+               # m > 16 through LDS with 2 and 1 K slices, the last tile ragged; and m > 16 with more than 256
+               # workgroups (two per CU), which keeps the activations in registers
+               (20, 9000, 4096), (32, 17000, 2048), (24, 21000, 256),
                # m = 1 (the GEMV): fewer quads than wavefronts, 1 / 2 / 4 quads per chunk, two and three chunks,
                # an odd tile count under two tiles per workgroup, and the one-tile shape for many tiles
                (1, 37, 384), (1, 300, 2176), (1, 1000, 8192), (1, 33, 10240), (1, 70, 17408), (1, 16390, 512)]
