@@ -216,23 +216,35 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Partial sums of a split-K exchange: device-scope relaxed atomic stores and
-// loads of FP32 (written through to the device's coherence point, so the
-// release below finds no dirty L2 lines of them to write back).
-__device__ __forceinline__ void splitk_store4(float* dst, f32x4_t v) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Partial sums of a split-K exchange, four consecutive output rows n0 .. n0 + 3
+// (n0 a multiple of 4) of one activation row; row points at that activation
+// row's partial sums (a multiple of 16 values long).  Inside the aligned
+// 16-row span s = n0 & ~15, the 4-row group j = (n0 / 4) % 4 keeps its values
+// 0 and 1 at s + 2 j and values 2 and 3 at s + 8 + 2 j, so the four groups of
+// a span, stored by one instruction, fill whole 32-byte sectors (in row order
+// each instruction's 4-byte pieces would lie 16 bytes apart).  Device-scope
+// relaxed atomic stores and loads of 8 bytes: written through to the device's
+// coherence point, so the release that follows finds no dirty L2 lines of
+// them to write back.
+__device__ __forceinline__ void splitk_store_rows4(float* row, int64_t n0, f32x4_t v) {
+  float* p = row + (n0 & ~(int64_t)15) + 2 * ((n0 >> 2) & 3);
+  const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+  const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p + 8), hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ f32x4_t splitk_load4(const float* src) {
-  f32x4_t v;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
+__device__ __forceinline__ f32x4_t splitk_load_rows4(const float* row, int64_t n0) {
+  const float* p = row + (n0 & ~(int64_t)15) + 2 * ((n0 >> 2) & 3);
+  const uint64_t lo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi =
+      __hip_atomic_load(reinterpret_cast<const uint64_t*>(p + 8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4_t{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)), __uint_as_float((uint32_t)hi),
+                 __uint_as_float((uint32_t)(hi >> 32))};
 }
 
 // ---------------------------------------------------------------------------
 // Split-K hand-off between the workgroups that share one block of outputs,
-// each having stored its FP32 partial sums (splitk_store4).  In HIP's
+// each having stored its FP32 partial sums (splitk_store_rows4).  In HIP's
 // memory model: the first barrier orders every thread's stores before thread
 // 0's release read-modify-write of the block's arrival counter (device
 // scope); the workgroup whose increment completes the count performs a

@@ -52,7 +52,7 @@ struct SkinnyArgs {
   uint16_t* y;            // [m, n]
   float* part;            // [slices, m, npad] FP32 partial sums (slices > 1)
   uint32_t* count;        // [row_blocks, gridDim.y] arrival counters (slices > 1)
-  int64_t npad;           // n rounded up to a multiple of 4
+  int64_t npad;           // n rounded up to a multiple of 16
   int rows;               // weight rows per workgroup (a multiple of 4, <= 16 T)
   int slices;             // K slices (<= chunks)
   int chunks;             // ceil(k / 256)
@@ -146,7 +146,7 @@ __device__ __forceinline__ void sk_store_y(const SkinnyArgs& p, const f32x4_t* a
 // With several K slices: this slice's FP32 sums of one tile go to the
 // workspace.  rows and row_start are multiples of 4, so a 4-row group is
 // either wholly inside the block or starts past its end (the last block's
-// padding columns n .. npad-1 are written and never read).  sk_arrive
+// padding columns n .. npad-1 may be written and are never read).  sk_arrive
 // (splitk_arrive) orders these stores before the other slices' loads.
 template <int NMT>
 __device__ __forceinline__ void sk_publish(const SkinnyArgs& p, const f32x4_t* acc, int sl, int64_t tile_row,
@@ -155,7 +155,7 @@ __device__ __forceinline__ void sk_publish(const SkinnyArgs& p, const f32x4_t* a
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int64_t gm = m0 + 16 * mt + (lane & 15);
-    if (gm < p.m && n0 < row_end) splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, acc[mt]);
+    if (gm < p.m && n0 < row_end) splitk_store_rows4(p.part + ((int64_t)sl * p.m + gm) * p.npad, n0, acc[mt]);
   }
 }
 
@@ -179,8 +179,7 @@ __device__ __forceinline__ void sk_reduce_tile(const SkinnyArgs& p, const f32x4_
     const int64_t gm = m0 + 16 * mt + (lane & 15);
     if (gm >= p.m || n0 >= row_end) continue;
     for (int s = 0; s < p.slices; ++s) {
-      const float* src = p.part + ((int64_t)s * p.m + gm) * p.npad + n0;
-      v[mt] += s == sl ? acc[mt] : splitk_load4(src);
+      v[mt] += s == sl ? acc[mt] : splitk_load_rows4(p.part + ((int64_t)s * p.m + gm) * p.npad, n0);
     }
   }
   sk_store_y<NMT>(p, v, tile_row, row_end, m0, lane);
@@ -675,7 +674,7 @@ SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k, bool split) {
   if (pl.mt == 64 && pl.t == 5) pl.t = 8;  // 64 activation rows on 5 wavefronts would spill registers
   pl.gy = ceil_div(m, pl.mt);
   pl.row_blocks = ceil_div(n, rows);
-  pl.npad = round_up(n, 4);
+  pl.npad = round_up(n, 16);  // whole 16-row spans of partial sums (splitk_store_rows4)
   if (pl.slices > 1) {
     // The arrival counters sit in a region of fixed size at the start of the
     // workspace, the same for every shape, so that a workspace shared by

@@ -58,9 +58,9 @@ struct SmArgs {
   const uint8_t* prep;   // kernel-native weight
   const float* tscale;
   uint16_t* y;           // [m, n]
-  float* part;           // [slices, m, npad] FP32 partial sums (slices > 1)
+  float* part;           // [slices, m, npad] FP32 partial sums (slices > 1), see splitk_store_rows4
   uint32_t* count;       // [row blocks] arrival counters (slices > 1)
-  int64_t npad;          // n rounded up to a multiple of 4
+  int64_t npad;          // n rounded up to a multiple of 16
   int rows;              // output rows per workgroup (a multiple of 4)
   int slices;            // K slices
   int quads;             // k / 128
@@ -188,7 +188,7 @@ __device__ __forceinline__ void sm_finish(const SmArgs& p, f32x4_t (&acc)[T][NMT
       pair_rows(pi, tr, gm);
       const int64_t n0 = tr + 4 * (lane >> 4);
       if (gm < p.m && n0 >= row0 && n0 < row_end)
-        splitk_store4(p.part + ((int64_t)sl * p.m + gm) * p.npad + n0, sum[i]);
+        splitk_store_rows4(p.part + ((int64_t)sl * p.m + gm) * p.npad, n0, sum[i]);
     }
   }
   if (!splitk_arrive(p.count + rb, p.slices)) return;
@@ -202,7 +202,7 @@ __device__ __forceinline__ void sm_finish(const SmArgs& p, f32x4_t (&acc)[T][NMT
       f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       if (gm < p.m && n0 >= row0 && n0 < row_end) {
         for (int s = 0; s < p.slices; ++s)
-          v += s == sl ? sum[i] : splitk_load4(p.part + ((int64_t)s * p.m + gm) * p.npad + n0);
+          v += s == sl ? sum[i] : splitk_load_rows4(p.part + ((int64_t)s * p.m + gm) * p.npad, n0);
       }
       sm_store_y(p, v, tr, row0, row_end, gm, lane);
     }
@@ -739,7 +739,7 @@ SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
   pl.rows = (int)rows;
   pl.tiles = (int)sm_max_tiles(n, rows);
   pl.row_blocks = sm_ceil_div(n, rows);
-  pl.npad = sm_round_up(n, 4);
+  pl.npad = sm_round_up(n, 16);  // whole 16-row spans of partial sums (splitk_store_rows4)
   if (pl.slices > 1) {
     if (pl.row_blocks * 4 > kSkinnyCounterBytes) return small_m_plan(m, n, k, false);
     pl.ws_bytes = kSkinnyCounterBytes + (int64_t)pl.slices * m * pl.npad * 4;

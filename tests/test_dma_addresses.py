@@ -219,3 +219,19 @@ def test_small_m_xl_reads_hit_distinct_bank_groups():
             for g in range(4):
                 slot = (4 * i + g) ^ (rr & 15)
                 assert len(set(slot.tolist())) == 16
+
+
+def test_splitk_partial_slots_are_a_permutation():
+    """The split-K partial-sum layout (csrc/device_common.hpp, splitk_store_rows4): the 4-row group at n0 of an
+    activation row keeps its four values at slots s + 2j, s + 2j + 1, s + 8 + 2j, s + 9 + 2j, with s = n0 & ~15
+    and j = (n0 / 4) % 4; over every group of a row padded to a multiple of 16 the slots are each used once, and a
+    store instruction's four groups of one span write the two 32-byte halves of the span."""
+    for npad in (16, 32, 5120, 13664):
+        slots = []
+        for n0 in range(0, npad, 4):
+            s, j = n0 & ~15, (n0 >> 2) & 3
+            slots += [s + 2 * j, s + 2 * j + 1, s + 8 + 2 * j, s + 9 + 2 * j]
+        assert sorted(slots) == list(range(npad))
+    first = sorted(s for n0 in range(0, 16, 4) for s in ((n0 & ~15) + 2 * ((n0 >> 2) & 3),
+                                                         (n0 & ~15) + 2 * ((n0 >> 2) & 3) + 1))
+    assert first == list(range(8))
