@@ -970,6 +970,9 @@ def test_graph_replays_match_eager(nv):
     xm = to_dev_bf16(_mx_inputs(64, 512, 4010, spread=4))
     mws = torch.empty(nv.lib().nvfp4_mx_linear_w4a4_workspace_bytes(64, 512), dtype=torch.uint8, device="cuda")
     ep, es, et = nv.quantize_experts(stack)
+    w64 = to_dev_bf16(WL.normal_bf16((64, 5120), 0.02, 4011))
+    p64, s64, t64 = nv.quantize(w64)
+    x24 = to_dev_bf16(WL.normal_bf16((24, 5120), 1.0, 4012))
     torch.cuda.synchronize()
 
     outs = {
@@ -982,6 +985,14 @@ def test_graph_replays_match_eager(nv):
         "kv": torch.empty((100, 2, 64), dtype=torch.float16, device="cuda"),
         "w4a4": torch.empty((64, 256), dtype=torch.bfloat16, device="cuda"),
         "nv_w4a4": torch.empty((300, 272), dtype=torch.bfloat16, device="cuda"),
+        # kernel-native layout: the conversion, its dequantizer, the GEMV, the small-M kernel and its
+        # activations-through-LDS form with a K split (64 x 5120 at m = 24: five slices)
+        "prep": torch.empty(nv.lib().nvfp4_prepared_bytes(272, 1024), dtype=torch.uint8, device="cuda"),
+        "prep64": torch.empty(nv.lib().nvfp4_prepared_bytes(64, 5120), dtype=torch.uint8, device="cuda"),
+        "dq_prep": torch.empty((272, 1024), dtype=torch.bfloat16, device="cuda"),
+        "prep_gemv": torch.empty((1, 272), dtype=torch.bfloat16, device="cuda"),
+        "prep_small_m": torch.empty((8, 272), dtype=torch.bfloat16, device="cuda"),
+        "prep_xl_split": torch.empty((24, 64), dtype=torch.bfloat16, device="cuda"),
     }
     nws = torch.empty(nv.linear_w4a4_workspace_bytes(300, 1024), dtype=torch.uint8, device="cuda")
     quant = {}
@@ -1005,6 +1016,13 @@ def test_graph_replays_match_eager(nv):
         nv.kv_gather(kc, ks_, kts, table, klen, kdst, outs["kv"], fmt="nvfp4")
         nv.mx_linear_w4a4(xm, mxw[0], mxw[1], out=outs["w4a4"], workspace=mws)
         nv.linear_w4a4(x300, p, s, t, out=outs["nv_w4a4"], workspace=nws)
+        assert L.nvfp4_prepare(p.data_ptr(), s.data_ptr(), 272, 1024, outs["prep"].data_ptr(), sid) == 0
+        assert L.nvfp4_prepare(p64.data_ptr(), s64.data_ptr(), 64, 5120, outs["prep64"].data_ptr(), sid) == 0
+        assert L.nvfp4_dequant_prepared(outs["prep"].data_ptr(), t.data_ptr(), 272, 1024, outs["dq_prep"].data_ptr(),
+                                        sid) == 0
+        nv.linear_prepared(x1, outs["prep"], t, 272, out=outs["prep_gemv"])
+        nv.linear_prepared(x8, outs["prep"], t, 272, out=outs["prep_small_m"])
+        nv.linear_prepared(x24, outs["prep64"], t64, 64, out=outs["prep_xl_split"])
 
     with torch.cuda.stream(st):
         for o in outs.values():
