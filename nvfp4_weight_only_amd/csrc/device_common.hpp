@@ -207,6 +207,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Lanes of one wavefront exchanging data through LDS: the stores before this
+// point are visible to every lane's loads after it.  Without it the exchange
+// is a data race in HIP's memory model, and the compiler may legally move a
+// lane's load of another lane's slot above that lane's store (per thread, the
+// two addresses differ).  Costs no instruction at wavefront scope.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

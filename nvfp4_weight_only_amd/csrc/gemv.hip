@@ -345,6 +345,7 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
 #pragma unroll
   for (int j = 0; j < J; ++j) xs[w][64 * j + 16 * (lane & 3) + (lane >> 2)] = xg[j];
   ss[w][lane] = sg;
+  wave_lds_sync();
   uint4 xv[J][4];
 #pragma unroll
   for (int j = 0; j < J; ++j)

@@ -269,43 +269,27 @@ __device__ __forceinline__ uint32_t parts_max(const uint32_t* __restrict__ parts
   return max(max(pw[0], pw[1]), max(pw[2], pw[3]));
 }
 
-// Over a stack, blockIdx.y picks the matrix (n_blk blocks each).  Iterations
-// whose kQuantB blocks all exist run without a branch between loads, codes and
-// stores, so the compiler interleaves the blocks; only the grid's last
-// iteration takes the guarded path.
-template <bool DECODE, int SRC = kFromAmax>
-__global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__ w, int64_t n_blk,
-                                                       const float* __restrict__ amax_p,
-                                                       uint2* __restrict__ packed,
-                                                       uint8_t* __restrict__ scales,
-                                                       uint4* __restrict__ decoded, const float* ts_w = nullptr,
-                                                       float* ts_x = nullptr, float* ts_y = nullptr,
-                                                       const uint32_t* __restrict__ parts = nullptr, int nparts = 0,
-                                                       float* ts_out = nullptr) {
-  if constexpr (DECODE) {
-    // NVFP4 x NVFP4: one thread also writes ts_x = fl32(amax / 2688) and ts_y = fl32(ts_w * ts_x).  Every
-    // workgroup reads only amax_p, which is neither of them; the linear that follows reads ts_y.
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      const float tx = __fdiv_rn(amax_p[0], 2688.0f);
-      ts_x[0] = tx;
-      ts_y[0] = ts_w[0] * tx;
-    }
+// The activation quantizer of the NVFP4 x NVFP4 linear: the encode pass that
+// also writes each element's exact BF16 value E2M1 x E4M3 (DECODE of
+// store_block), one thread per block.  Iterations whose kQuantB blocks all
+// exist run without a branch between loads, codes and stores, so the compiler
+// interleaves the blocks; only the grid's last iteration takes the guarded
+// path.  One thread also writes ts_x = fl32(amax / 2688) and ts_y =
+// fl32(ts_w * ts_x).  Every workgroup reads only amax_p, which is neither of
+// them; the linear that follows reads ts_y.
+__global__ void __launch_bounds__(256) quantize_decode_kernel(const uint4* __restrict__ w, int64_t n_blk,
+                                                              const float* __restrict__ amax_p,
+                                                              uint2* __restrict__ packed,
+                                                              uint8_t* __restrict__ scales,
+                                                              uint4* __restrict__ decoded, const float* ts_w,
+                                                              float* ts_x, float* ts_y) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const float tx = __fdiv_rn(amax_p[0], 2688.0f);
+    ts_x[0] = tx;
+    ts_y[0] = ts_w[0] * tx;
   }
-  w += (int64_t)blockIdx.y * 2 * n_blk;
-  packed += (int64_t)blockIdx.y * n_blk;
-  scales += (int64_t)blockIdx.y * n_blk;
-  // amax is a BF16 value held in FP32 (or recovered from the tensor scale, or
-  // the maximum of the per-workgroup maxima)
-  uint32_t amax_b;
-  if constexpr (SRC == kFromParts) {
-    amax_b = parts_max(parts + (int64_t)blockIdx.y * nparts, nparts);
-    if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[blockIdx.y] = __fdiv_rn(__uint_as_float(amax_b << 16), 2688.0f);
-  } else if constexpr (SRC == kFromTscale) {
-    amax_b = amax_bits_from_tscale(amax_p[blockIdx.y]);
-  } else {
-    amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;
-  }
-  const QuantConsts qc = quant_consts(amax_b);
+  // amax is a BF16 value held in FP32
+  const QuantConsts qc = quant_consts(__float_as_uint(amax_p[0]) >> 16);
   const int64_t B = blockDim.x;
   const int64_t stride = (int64_t)gridDim.x * B * kQuantB;
   for (int64_t b0 = (int64_t)blockIdx.x * B * kQuantB + threadIdx.x; b0 < n_blk; b0 += stride) {
@@ -322,15 +306,71 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint4* __restrict__
 #pragma unroll
       for (int u = 0; u < kQuantB; ++u) q[u] = quantize_block(v[2 * u], v[2 * u + 1], qc);
 #pragma unroll
-      for (int u = 0; u < kQuantB; ++u) store_block<DECODE>(b0 + u * B, q[u], packed, scales, decoded);
+      for (int u = 0; u < kQuantB; ++u) store_block<true>(b0 + u * B, q[u], packed, scales, decoded);
     } else {
 #pragma unroll
       for (int u = 0; u < kQuantB; ++u) {
         const int64_t blk = b0 + u * B;
         if (blk < n_blk) {
-          store_block<DECODE>(blk, quantize_block(w[2 * blk], w[2 * blk + 1], qc), packed, scales, decoded);
+          store_block<true>(blk, quantize_block(w[2 * blk], w[2 * blk + 1], qc), packed, scales, decoded);
         }
       }
+    }
+  }
+}
+
+// The encode pass (without the BF16 decode) with whole-line loads.  A wavefront takes 64 kQuantB
+// consecutive blocks per iteration (2 KiB of W per block row of lanes): load
+// instruction j brings vector 64 j + lane of that range (1 KiB of contiguous
+// lines), the vectors go through the wavefront's own LDS area, and lane l
+// reads back the two vectors of block 64 u + l.  Only the wavefront uses its
+// area, so a wavefront-scope synchronization (wave_lds_sync) is all it needs.  The stores are as above (8 bytes of codes and one
+// scale byte per lane and block, consecutive lanes on consecutive blocks).
+template <int SRC>
+__global__ void __launch_bounds__(256) quantize_lines_kernel(const uint4* __restrict__ w, int64_t n_blk,
+                                                             const float* __restrict__ amax_p,
+                                                             uint2* __restrict__ packed,
+                                                             uint8_t* __restrict__ scales,
+                                                             const uint32_t* __restrict__ parts, int nparts,
+                                                             float* ts_out) {
+  constexpr int V = 2 * kQuantB;  // vectors per lane and iteration
+  __shared__ uint4 area[4][64 * V];
+  w += (int64_t)blockIdx.y * 2 * n_blk;
+  packed += (int64_t)blockIdx.y * n_blk;
+  scales += (int64_t)blockIdx.y * n_blk;
+  uint32_t amax_b;
+  if constexpr (SRC == kFromParts) {
+    amax_b = parts_max(parts + (int64_t)blockIdx.y * nparts, nparts);
+    if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[blockIdx.y] = __fdiv_rn(__uint_as_float(amax_b << 16), 2688.0f);
+  } else if constexpr (SRC == kFromTscale) {
+    amax_b = amax_bits_from_tscale(amax_p[blockIdx.y]);
+  } else {
+    amax_b = __float_as_uint(amax_p[blockIdx.y]) >> 16;
+  }
+  const QuantConsts qc = quant_consts(amax_b);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint4* my = area[wv];
+  const int64_t n_vec = 2 * n_blk;
+  const int64_t chunk = 64 * kQuantB;  // blocks per wavefront and iteration
+  const int64_t stride = (int64_t)gridDim.x * 4 * chunk;
+  for (int64_t c0 = ((int64_t)blockIdx.x * 4 + wv) * chunk; c0 < n_blk; c0 += stride) {
+    uint4 v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = 2 * c0 + 64 * j + lane;
+      v[j] = w[i < n_vec ? i : n_vec - 1];  // past the end: an in-bounds load, never stored
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) my[64 * j + lane] = v[j];
+    wave_lds_sync();
+    BlockCodes q[kQuantB];
+#pragma unroll
+    for (int u = 0; u < kQuantB; ++u) q[u] = quantize_block(my[128 * u + 2 * lane], my[128 * u + 2 * lane + 1], qc);
+    wave_lds_sync();  // the next iteration rewrites the area
+#pragma unroll
+    for (int u = 0; u < kQuantB; ++u) {
+      const int64_t blk = c0 + 64 * u + lane;
+      if (blk < n_blk) store_block<false>(blk, q[u], packed, scales, nullptr);
     }
   }
 }
@@ -428,16 +468,18 @@ void launch_quantize_shared_amax(const uint16_t* w, int64_t n_elems, uint32_t* p
   const int64_t n_vec = n_elems / 8, n_blk = n_elems / 16;
   const unsigned nb = grid_for(n_vec, 256 * kAmaxU, kAmaxSharedParts);
   amax_partial_kernel<<<dim3(nb, 1u), 256, 0, s>>>(reinterpret_cast<const uint4*>(w), n_vec, parts, n_vec, n_vec);
-  quantize_kernel<false, kFromParts><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_blk, nullptr, reinterpret_cast<uint2*>(packed), scales, nullptr, nullptr,
-      nullptr, nullptr, parts, (int)nb, tscale);
+  quantize_lines_kernel<kFromParts><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, nullptr, reinterpret_cast<uint2*>(packed), scales, parts, (int)nb,
+      tscale);
 }
 
 void launch_quantize_from_tscale(const uint16_t* w, int64_t count, int64_t n_elems, const float* tscale,
                                  uint8_t* packed, uint8_t* scales, hipStream_t s) {
   const int64_t n_blk = n_elems / 16;
-  quantize_kernel<false, kFromTscale><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_blk, tscale, reinterpret_cast<uint2*>(packed), scales, nullptr);
+  quantize_lines_kernel<kFromTscale>
+      <<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
+          reinterpret_cast<const uint4*>(w), n_blk, tscale, reinterpret_cast<uint2*>(packed), scales, nullptr, 0,
+          nullptr);
 }
 
 void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hipStream_t s) {
@@ -447,14 +489,14 @@ void launch_finalize_tscale(const float* amax, float* tscale, int64_t count, hip
 void launch_quantize(const uint16_t* w, int64_t count, int64_t n_elems, const float* amax, uint8_t* packed,
                      uint8_t* scales, hipStream_t s) {
   const int64_t n_blk = n_elems / 16;
-  quantize_kernel<false><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
-      reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales, nullptr);
+  quantize_lines_kernel<kFromAmax><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), (unsigned)count), 256, 0, s>>>(
+      reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales, nullptr, 0, nullptr);
 }
 
 void launch_quantize_decode(const uint16_t* w, int64_t n_elems, const float* amax, uint8_t* packed, uint8_t* scales,
                             uint16_t* decoded, const float* ts_w, float* ts_x, float* ts_y, hipStream_t s) {
   const int64_t n_blk = n_elems / 16;
-  quantize_kernel<true><<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
+  quantize_decode_kernel<<<dim3(grid_for(n_blk, 256 * kQuantB, 1 << 20), 1u), 256, 0, s>>>(
       reinterpret_cast<const uint4*>(w), n_blk, amax, reinterpret_cast<uint2*>(packed), scales,
       reinterpret_cast<uint4*>(decoded), ts_w, ts_x, ts_y);
 }
