@@ -395,7 +395,9 @@ __global__ void __launch_bounds__(64 * kSmWaves) small_m_xl_kernel(SmArgs p) {
     // vmcnt(2 T) after those means quad j has landed; quad j + 1's copy (into
     // the other area, whose reads finished in the previous step) follows.  The
     // empty asm statements with a memory clobber keep the loads above the
-    // wait and the LDS reads below it.
+    // wait and the LDS reads below it.  Should the compiler split a weight load
+    // into more instructions, the wait only gets stricter (loads complete in
+    // order); it cannot issue fewer than one per load.
     auto step = [&](int j, const SmW* wq, SmW* wn, int buf) {
       if (j + 1 < nq) {
         load_w(wn, j + 1);
