@@ -725,8 +725,8 @@ def main():
 
     rows = {}
     if args.rows == "all":
-        for wname, mm, reps in [("gate_up", 1, 30), ("small_m_up", 8, 30), ("small_m_up", 32, 30),
-                                ("small_m_down", 8, 30), ("small_m_down", 32, 30),
+        for wname, mm, reps in [("gate_up", 1, 30), ("small_m_down", 1, 30), ("small_m_up", 8, 30),
+                                ("small_m_up", 32, 30), ("small_m_down", 8, 30), ("small_m_down", 32, 30),
                                 ("prefill", 512, 10), ("prefill", 2048, 3),
                                 ("prefill_down", 512, 10), ("prefill_down", 2048, 3)]:
             key = f"linear_{wname}_m{mm}"
@@ -734,7 +734,8 @@ def main():
             rows[key] = bench_linear_row(wname, mm, reps)
             log(f"  {rows[key]}")
         for wname, mm, reps in [("small_m_up", 8, 30), ("small_m_up", 32, 30), ("small_m_down", 8, 30),
-                                ("small_m_down", 32, 30), ("gate_up", 1, 30), ("decode", 1, 30)]:
+                                ("small_m_down", 32, 30), ("gate_up", 1, 30), ("decode", 1, 30),
+                                ("small_m_down", 1, 30)]:
             key = f"prepared_{wname}_m{mm}"
             log(f"row {key}")
             rows[key] = bench_prepared_row(wname, mm, reps)

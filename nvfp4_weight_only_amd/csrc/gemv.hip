@@ -10,12 +10,15 @@
 //     (scale 1.0: exact E2M1 values), products accumulate with
 //     v_dot2_f32_bf16 in FP32; the E4M3 block scale is one FMA per 16
 //     elements and the tensor scale one multiply per output.
-// Three kernels, by k:
+// Four kernels, by k:
 //   - gemv_ks_kernel (k a multiple of 512, k <= 5120): K split across the
-//     wavefronts of a 20-row workgroup, activations and scales staged per
-//     wavefront with one wide load each, no barrier before the products;
-//   - gemv_lds_kernel (k a multiple of 32, k <= 16384): each wavefront owns
-//     whole rows, the activation row is staged once per workgroup in LDS;
+//     wavefronts of a 12- or 16-row workgroup, one 512-element slice each,
+//     activations and scales staged per wavefront with one wide load each, no
+//     barrier before the products;
+//   - gemv_ksl_kernel (k a multiple of 512, 5120 < k <= 32768): the same with
+//     up to four slices per wavefront, all their loads issued first;
+//   - gemv_lds_kernel (other k, a multiple of 32, up to 8192): each wavefront
+//     owns whole rows, the activation row is staged once per workgroup in LDS;
 //   - gemv_loop_kernel (any k a multiple of 16): rows per wavefront, K in
 //     batches, activations read straight into registers.
 #include "device_common.hpp"
@@ -382,6 +385,143 @@ __global__ void __launch_bounds__(64 * kGemvKsMaxWaves) gemv_ks_kernel(const uin
   }
 }
 
+// Long K (k a multiple of 512, more than 10 slices of 512): the same product
+// with W <= 16 wavefronts, slice s going to wavefront s % W, so each wavefront
+// owns up to S slices (w, w + W, ...).  Every load of all its slices is issued
+// first (a slice past the end repeats the last one, in bounds, and its products
+// are dropped by a select); then the slices are staged through the
+// wavefront's LDS area one after another and accumulated in slice order.
+// Slice i of a wavefront's share in gemv_ksl_kernel, then the next one: the
+// activation piece and the scale pieces through the wavefront's LDS area, the
+// products of its I rows added to acc when the slice exists.
+typedef uint32_t ksl_u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ksl_u4(ksl_u32x4_t v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+template <int I, int S, int i>
+__device__ __forceinline__ void ksl_slices(const ksl_u32x4_t (&xg)[S], const ksl_u32x4_t (&sg)[S],
+                                           const ksl_u32x4_t (&wv)[S][I], float (&acc)[I], uint4* xs, uint4* ss,
+                                           int lane, int w, int nw, int nsl) {
+  if constexpr (i < S) {
+    const int u = lane & 15, g = lane >> 4;
+    xs[16 * (lane & 3) + (lane >> 2)] = ksl_u4(xg[i]);
+    ss[lane] = ksl_u4(sg[i]);
+    wave_lds_sync();
+    uint4 xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = xs[16 * q + u];
+    const uint16_t* srw = reinterpret_cast<const uint16_t*>(ss);
+    const bool valid = w + nw * i < nsl;  // uniform per wavefront
+#pragma unroll
+    for (int ii = 0; ii < I; ++ii) {
+      const float2 sc = e4m3x2_to_f32<false>(srw[(g + 4 * ii) * 16 + u]);
+      float p0 = dot8(wv[i][ii].x, xv[0], 0.0f);
+      p0 = dot8(wv[i][ii].y, xv[1], p0);
+      float p1 = dot8(wv[i][ii].z, xv[2], 0.0f);
+      p1 = dot8(wv[i][ii].w, xv[3], p1);
+      const float a = fmaf(p1, sc.y, fmaf(p0, sc.x, acc[ii]));
+      acc[ii] = valid ? a : acc[ii];  // a select, not a branch: no wait for the loads still in flight
+    }
+    wave_lds_sync();  // the area is rewritten for the next slice
+    ksl_slices<I, S, i + 1>(xg, sg, wv, acc, xs, ss, lane, w, nw, nsl);
+  }
+}
+
+template <int I, int S>
+__global__ void __launch_bounds__(1024) gemv_ksl_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t k,
+                                                        const uint8_t* __restrict__ packed,
+                                                        const uint8_t* __restrict__ scales,
+                                                        const float* __restrict__ tscale_p,
+                                                        uint16_t* __restrict__ y) {
+  constexpr int RB = 4 * I;
+  constexpr int SL = 8 * I;  // lanes that load scales: 2 pieces of 16 bytes per row and slice
+  static_assert(SL <= 64, "scale pieces per wavefront");
+  __shared__ uint4 xs[16][64];
+  __shared__ uint4 ss[16][64];
+  __shared__ float red[16][RB];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int u = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * RB;
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const int nsl = (int)(k >> 9);
+  x += (int64_t)blockIdx.y * k;
+  y += (int64_t)blockIdx.y * n;
+
+  int sl[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int s = w + nw * i;
+    sl[i] = s < nsl ? s : nsl - 1;
+  }
+  ksl_u32x4_t xg[S], sg[S];
+  const int sp = lane % SL;
+  const int64_t sr = row0 + sp / 2, srow = sr < n ? sr : n - 1;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    xg[i] = reinterpret_cast<const ksl_u32x4_t*>(x + (int64_t)sl[i] * 512)[lane];
+    sg[i] = reinterpret_cast<const ksl_u32x4_t*>(scales + srow * kb + (int64_t)sl[i] * 32)[sp % 2];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // activations and scales are issued before the weights
+  ksl_u32x4_t wv[S][I];
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+#pragma unroll
+    for (int ii = 0; ii < I; ++ii) {
+      const int64_t r = row0 + g + 4 * ii, row = r < n ? r : n - 1;
+      const uint4 v = ld_stream16(packed + row * kh + ((int64_t)sl[i] * 16 + u) * 16);
+      wv[i][ii] = ksl_u32x4_t{v.x, v.y, v.z, v.w};
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[I];
+#pragma unroll
+  for (int ii = 0; ii < I; ++ii) acc[ii] = 0.0f;
+  // Slices in order, each index a constant (a loop here, with its wavefront
+  // barriers, stays rolled and puts the register arrays in scratch memory).
+  ksl_slices<I, S, 0>(xg, sg, wv, acc, xs[w], ss[w], lane, w, nw, nsl);
+#pragma unroll
+  for (int ii = 0; ii < I; ++ii) {
+    const float v = group_sum<16>(acc[ii]);
+    if (u == 0) red[w][g + 4 * ii] = v;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < RB && row0 + t < n) {
+    float v = red[0][t];
+    for (int ww = 1; ww < nw; ++ww) v += red[ww][t];
+    y[row0 + t] = (uint16_t)f32_to_bf16_rne(v * *tscale_p);
+  }
+}
+
+template <int I, int S>
+static void launch_ksl_rows(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                            const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  const unsigned gx = (unsigned)((n + 4 * I - 1) / (4 * I));
+  const int nsl = (int)(k >> 9), waves = (nsl + S - 1) / S;  // the fewest wavefronts with S slices each
+  const int64_t max_y = 65535;
+  for (int64_t m0 = 0; m0 < m; m0 += max_y) {
+    const unsigned gy = (unsigned)((m - m0) < max_y ? (m - m0) : max_y);
+    gemv_ksl_kernel<I, S><<<dim3(gx, gy), 64 * waves, 0, s>>>(x + m0 * k, n, k, packed, scales, tscale,
+                                                                y + m0 * n);
+  }
+}
+
+// 10 < k / 512 <= 64: S = ceil(slices / 16) slices per wavefront on the fewest
+// wavefronts that cover them (5120 x 17408: 34 slices, 12 wavefronts of 3, 427
+// workgroups of 12 rows), measured against the alternatives at that shape:
+// 11.8 us; sixteen wavefronts (two to three slices each, 14 of them loading a
+// repeated slice) 14.6 us; 8 rows per workgroup 12.1 us, 16 rows 14.8 us; the
+// row-per-wavefront loop kernel it replaced 15.7 us.
+static void launch_ksl(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8_t* packed,
+                       const uint8_t* scales, const float* tscale, uint16_t* y, hipStream_t s) {
+  switch ((int)((k >> 9) + 15) / 16) {
+    case 1: return launch_ksl_rows<3, 1>(x, m, n, k, packed, scales, tscale, y, s);
+    case 2: return launch_ksl_rows<3, 2>(x, m, n, k, packed, scales, tscale, y, s);
+    case 3: return launch_ksl_rows<3, 3>(x, m, n, k, packed, scales, tscale, y, s);
+    default: return launch_ksl_rows<3, 4>(x, m, n, k, packed, scales, tscale, y, s);
+  }
+}
+
 // waves = k / 512 (one 512-element slice per wavefront).
 template <int I>
 static void launch_ks_rows(const uint16_t* x, int64_t m, int64_t n, int64_t k, int waves, const uint8_t* packed,
@@ -463,6 +603,7 @@ void launch_gemv(const uint16_t* x, int64_t m, int64_t n, int64_t k, const uint8
                  const float* tscale, uint16_t* y, hipStream_t s) {
   if ((k & 511) == 0 && (k >> 9) <= kGemvKsMaxWaves)
     return launch_ks(x, m, n, k, (int)(k >> 9), packed, scales, tscale, y, s);
+  if ((k & 511) == 0 && (k >> 9) <= 64) return launch_ksl(x, m, n, k, packed, scales, tscale, y, s);
   const int64_t units = k >> 5;
   if ((k & 31) == 0 && k <= kLdsMaxK) {
     if (units % 32 == 0) {

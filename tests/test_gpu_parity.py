@@ -271,11 +271,12 @@ def test_gate_up_shared_scale(nv):
 LIN_SHAPES = [(1, 256, 512), (3, 300, 1040), (8, 77, 48), (17, 130, 272), (32, 64, 5120), (33, 200, 512),
               (100, 300, 1040), (130, 257, 2064), (1, 1, 16), (5, 3, 16),
               # GEMV dispatch branches.  K split across wavefronts (k a multiple of 512 up to 5120):
-              # 2, 6 and 9 wavefronts, ragged last 20-row workgroup, many workgroups.  LDS-staged rows:
-              # 32 lanes/row (k = 6144), ragged 64 lanes/row (k = 1056, 4640), the large-n tiling
-              # (n >= 16384, k = 6144), and k beyond the LDS-staged range (k = 17408)
-              (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (2, 70, 6144), (1, 100, 1056),
-              (1, 33, 4640), (1, 16400, 6144), (1, 40, 17408),
+              # 2, 6 and 9 wavefronts, ragged last 20-row workgroup, many workgroups.  Long K (a multiple of
+              # 512 above 5120) on 16 wavefronts: 11 slices (five wavefronts without one), 12 slices, many
+              # workgroups, 34 slices (two or three per wavefront) and 64 (four each).  LDS-staged rows:
+              # ragged 64 lanes/row (k = 1056, 4640).  Neither (k = 5200)
+              (1, 100, 1024), (2, 70, 3072), (1, 33, 4608), (1, 16500, 1024), (3, 300, 5632), (2, 70, 6144),
+              (1, 100, 1056), (1, 33, 4640), (1, 16400, 6144), (1, 40, 17408), (1, 37, 32768), (1, 50, 5200),
               # prefill with K a multiple of 256: several 128 x 272 tiles with ragged edges, one K group
               (200, 560, 768), (129, 545, 256), (300, 300, 2560),
               # more small-M shapes: k = 128 and 384, 4-row workgroups, ragged n with two m tiles, large n
@@ -368,7 +369,8 @@ def test_small_m_workspace_shared_by_shapes(nv):
 # ---------------------------------------------------------------------------
 # Linear at full size, auto dispatch, sampled output columns.
 # ---------------------------------------------------------------------------
-FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_up", 8), ("small_m_up", 32), ("small_m_down", 8),
+FULL_LINEAR = [("decode", 1), ("gate_up", 1), ("small_m_down", 1), ("small_m_up", 8), ("small_m_up", 32),
+               ("small_m_down", 8),
                ("small_m_down", 32), ("prefill", 512), ("prefill", 2048), ("small_m_down", 512),
                ("prefill_down", 2048), ("prefill", 128)]
 
