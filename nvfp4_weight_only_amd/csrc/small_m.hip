@@ -720,7 +720,9 @@ SmallMPlan small_m_plan(int64_t m, int64_t n, int64_t k, bool split) {
   // Each workgroup reads the activations of its K slice, so more slices mean
   // fewer activation bytes per CU, and more partial sums to exchange.  At the
   // down projection 5120 x 17408: M = 8, 80 rows x 4 slices 16.5 us against
-  // 16.8 us for 40 x 2; M = 32, 26.9 us against 29.5 us.
+  // 16.8 us for 40 x 2; M = 32, 26.9 us against 29.5 us.  With the exchange in
+  // whole sectors (splitk_store_rows4): 15.6 / 21.1 us against 16.4 / 23.5 us
+  // for 40 x 2, and 64 rows x 3 slices within 1 % (15.6 / 21.0 us).
   int64_t s = 1;
   if (split) {
     s = (80 * 256 + n / 2) / n;
