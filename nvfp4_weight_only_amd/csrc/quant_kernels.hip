@@ -319,13 +319,14 @@ __global__ void __launch_bounds__(256) quantize_decode_kernel(const uint4* __res
   }
 }
 
-// The encode pass (without the BF16 decode) with whole-line loads.  A wavefront takes 64 kQuantB
-// consecutive blocks per iteration (2 KiB of W per block row of lanes): load
-// instruction j brings vector 64 j + lane of that range (1 KiB of contiguous
-// lines), the vectors go through the wavefront's own LDS area, and lane l
-// reads back the two vectors of block 64 u + l.  Only the wavefront uses its
-// area, so a wavefront-scope synchronization (wave_lds_sync) is all it needs.  The stores are as above (8 bytes of codes and one
-// scale byte per lane and block, consecutive lanes on consecutive blocks).
+// The encode pass (without the BF16 decode) with whole-line loads.  A
+// wavefront takes 64 kQuantB consecutive blocks per iteration (4 KiB of W):
+// load instruction j brings vector 64 j + lane of that range (1 KiB of
+// contiguous lines), the vectors go through the wavefront's own LDS area, and
+// lane l reads back the two vectors of block 64 u + l.  Only the wavefront
+// uses its area, so a wavefront-scope synchronization (wave_lds_sync) is all
+// it needs.  The stores are as above (8 bytes of codes and one scale byte per
+// lane and block, consecutive lanes on consecutive blocks).
 template <int SRC>
 __global__ void __launch_bounds__(256) quantize_lines_kernel(const uint4* __restrict__ w, int64_t n_blk,
                                                              const float* __restrict__ amax_p,
